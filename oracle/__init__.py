@@ -1,0 +1,27 @@
+"""CPU oracle of the codebook-TTS decode path (numpy, float64).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product library never does, and
+shares no code, table or constant generator with it.  Its only shared input is
+the seeded generator in ``synthetic``.
+
+Parity status of each function (what pins it, in the CPU test suite):
+* numerics.round_bf16          -- bit-level agreement with torch.bfloat16
+* numerics.e4m3_*              -- exhaustive round trip of all 256 codes,
+                                  every midpoint (ties to even), saturation,
+                                  agreement with torch.float8_e4m3fn
+* numerics.rmsnorm             -- closed form of the output rms, scale invariance
+* numerics.rope                -- norm preservation, identity at p = 0,
+                                  relative-position property, hd = 2 closed form
+* numerics.attention_one       -- L = 1 gives v, equal keys give mean(V),
+                                  split-K/LSE combine equals the one-pass form
+* model.OracleModel            -- batched prefill equals step-by-step decode
+                                  (causal-mask equivalence), GQA equals MHA with
+                                  repeated K/V, mode S equals mode E with a
+                                  precision-free format; whole-model values:
+                                  parity unpinned (no page prints a worked example)
+* delay.*                      -- brute-force enumeration over every EOC step
+                                  against an independent restatement; undelay
+                                  inverts delay
+* model.calibrate              -- the quantised site maximum lands exactly on 448
+"""
