@@ -1,0 +1,595 @@
+// Host runtime behind the C ABI (include/hta.h): workspace layout, weight
+// packing, the position-agnostic frame graph, prefill, calibration and taps.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "hta_internal.h"
+
+using namespace hta;
+
+struct hta_ctx {
+  Ctx c;
+};
+
+namespace hta {
+
+float host_act_scale(const Ctx& c, int site) {
+  if (c.cfg.precision != HTA_FP8_E4M3) return 1.0f;
+  return c.h_scales.empty() ? 1.0f : c.h_scales[site];
+}
+
+static int wbytes(const hta_config& c) { return c.precision == HTA_FP8_E4M3 ? 1 : 2; }
+
+Layout make_layout(const hta_config& c) {
+  Layout L{};
+  const size_t d = c.hidden, hd = c.head_dim, qd = (size_t)c.n_q_heads * hd, kvd = (size_t)c.n_kv_heads * hd;
+  const size_t F = c.ffn, W = qd + 2 * kvd, wb = wbytes(c), ms = c.max_seq, Pm = c.max_prefill;
+  const size_t CV = (size_t)c.n_codebooks * c.codebook_size;
+  const bool fp8 = c.precision == HTA_FP8_E4M3;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+  // one layer block
+  size_t lo = 0;
+  auto ltake = [&](size_t bytes) { size_t r = lo; lo = align256(lo + bytes); return r; };
+  L.off_wqkv = ltake(W * d * wb);
+  L.off_wo = ltake(d * qd * wb);
+  L.off_wgu = ltake(2 * F * d * wb);
+  L.off_wd = ltake(d * F * wb);
+  L.off_sqkv = ltake(fp8 ? W * 4 : 0);
+  L.off_so = ltake(fp8 ? d * 4 : 0);
+  L.off_sgu = ltake(fp8 ? 2 * F * 4 : 0);
+  L.off_sd = ltake(fp8 ? d * 4 : 0);
+  L.off_gattn = ltake(d * 4);
+  L.off_gq = ltake(hd * 4);
+  L.off_gk = ltake(hd * 4);
+  L.off_gmlp = ltake(d * 4);
+  L.off_k = ltake((size_t)c.n_kv_heads * ms * hd * 2);
+  L.off_v = ltake((size_t)c.n_kv_heads * ms * hd * 2);
+  L.layer_stride = lo;
+  L.layer_base = take(lo * c.n_layers);
+  L.off_etext = take((size_t)c.text_vocab * d * 2);
+  L.off_eaud = take(CV * d * 2);
+  L.off_gfinal = take(d * 4);
+  L.off_whead = take(CV * d * wb);
+  L.off_shead = take(fp8 ? CV * 4 : 0);
+  L.off_rope_cos = take(ms * (hd / 2) * 4);
+  L.off_rope_sin = take(ms * (hd / 2) * 4);
+  const size_t nsites = (size_t)kSitesPerLayer * c.n_layers + 1;
+  L.off_act_scales = take(nsites * 4);
+  L.off_amax = take(nsites * 4);
+  L.off_state = take(sizeof(DevState));
+  L.off_hist = take(ms * c.n_codebooks * 4);
+  L.off_counters = take(64 * 4);
+  int splits = 256 / c.n_kv_heads;
+  if (splits > 64) splits = 64;
+  if (splits < 1) splits = 1;
+  L.attn_splits = splits;
+  L.off_h = take(d * 4);
+  L.off_qkv = take(W * 4);
+  L.off_attn_part = take((size_t)c.n_q_heads * splits * (hd + 2) * 4);
+  L.off_o_act = take(qd * 2);
+  L.off_a_act = take(F * 2);
+  L.off_logits = take(CV * 4);
+  L.off_tok = take(Pm * 4);
+  L.off_x = take(Pm * d * 4);
+  L.off_u = take(Pm * (d > F ? d : F) * 2);
+  L.off_pqkv = take(Pm * W * 4);
+  L.off_pq = take(Pm * qd * 4);
+  L.off_po = take(Pm * qd * 2);
+  size_t nmax = W;
+  if (2 * F > nmax) nmax = 2 * F;
+  if (d > nmax) nmax = d;
+  L.off_pgu = take(Pm * 2 * F * 4 + 8 * Pm * nmax * 4);  // gate/up rows, then GEMM split partials
+  L.off_pa = 0;
+  L.total = o;
+  return L;
+}
+
+}  // namespace hta
+
+// ---------------------------------------------------------------------------- helpers
+static int fail(Ctx& c, int code, const std::string& msg) {
+  c.err = msg;
+  return code;
+}
+static int hip_fail(Ctx& c, hipError_t e, const char* where) {
+  c.err = std::string(where) + ": " + hipGetErrorString(e);
+  return HTA_E_HIP;
+}
+#define HIPCK(expr, where)                          \
+  do {                                              \
+    hipError_t _e = (expr);                         \
+    if (_e != hipSuccess) return hip_fail(c, _e, where); \
+  } while (0)
+
+static bool shape_ok(const hta_config& f, std::string* why) {
+  auto bad = [&](const char* m) { if (why) *why = m; return false; };
+  if (f.n_layers < 1 || f.hidden < 64 || f.n_q_heads < 1 || f.n_kv_heads < 1) return bad("non-positive shape");
+  if (f.head_dim != 64 && f.head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (f.n_q_heads % f.n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
+  if (f.n_q_heads / f.n_kv_heads > 4) return bad("GQA group size above 4 is not supported");
+  if (f.n_kv_heads > 32) return bad("n_kv_heads above 32 is not supported");
+  if (f.hidden % 128 || f.ffn % 128 || (f.n_q_heads * f.head_dim) % 128) return bad("hidden, ffn and q width must be multiples of 128");
+  if (f.n_codebooks < 1 || f.n_codebooks > kMaxCodebooks) return bad("n_codebooks must be in 1..16");
+  if (f.codebook_size < 2 || f.codebook_size > 2048) return bad("codebook_size must be in 2..2048");
+  if (f.bos_id < 0 || f.bos_id >= f.codebook_size || f.eos_id < 0 || f.eos_id >= f.codebook_size) return bad("bos/eos ids out of range");
+  if (f.text_vocab < 1) return bad("text_vocab must be positive");
+  if (f.max_seq < 2 || f.max_prefill < 1 || f.max_prefill > f.max_seq) return bad("bad max_seq / max_prefill");
+  if (f.precision != HTA_BF16 && f.precision != HTA_FP8_E4M3) return bad("unknown precision");
+  if (f.hidden > 16384 || f.ffn > 16384 || f.n_q_heads * f.head_dim > 16384) return bad("widths above 16384 exceed the GEMV LDS budget");
+  return true;
+}
+
+static void set_pointers(Ctx& c) {
+  const hta_config& f = c.cfg;
+  const Layout& L = c.lay;
+  char* w = c.ws;
+  const bool fp8 = f.precision == HTA_FP8_E4M3;
+  for (int l = 0; l < f.n_layers; ++l) {
+    char* b = w + L.layer_base + (size_t)l * L.layer_stride;
+    LayerW& lw = c.layers[l];
+    lw.w_qkv = b + L.off_wqkv;
+    lw.w_o = b + L.off_wo;
+    lw.w_gu = b + L.off_wgu;
+    lw.w_d = b + L.off_wd;
+    lw.s_qkv = fp8 ? reinterpret_cast<float*>(b + L.off_sqkv) : nullptr;
+    lw.s_o = fp8 ? reinterpret_cast<float*>(b + L.off_so) : nullptr;
+    lw.s_gu = fp8 ? reinterpret_cast<float*>(b + L.off_sgu) : nullptr;
+    lw.s_d = fp8 ? reinterpret_cast<float*>(b + L.off_sd) : nullptr;
+    lw.g_attn = reinterpret_cast<float*>(b + L.off_gattn);
+    lw.g_q = reinterpret_cast<float*>(b + L.off_gq);
+    lw.g_k = reinterpret_cast<float*>(b + L.off_gk);
+    lw.g_mlp = reinterpret_cast<float*>(b + L.off_gmlp);
+    lw.k_cache = reinterpret_cast<uint16_t*>(b + L.off_k);
+    lw.v_cache = reinterpret_cast<uint16_t*>(b + L.off_v);
+  }
+  c.e_text = reinterpret_cast<uint16_t*>(w + L.off_etext);
+  c.e_aud = reinterpret_cast<uint16_t*>(w + L.off_eaud);
+  c.g_final = reinterpret_cast<float*>(w + L.off_gfinal);
+  c.w_head = w + L.off_whead;
+  c.s_head = fp8 ? reinterpret_cast<float*>(w + L.off_shead) : nullptr;
+  c.rope_cos = reinterpret_cast<float*>(w + L.off_rope_cos);
+  c.rope_sin = reinterpret_cast<float*>(w + L.off_rope_sin);
+  c.act_scales = reinterpret_cast<float*>(w + L.off_act_scales);
+  c.amax = reinterpret_cast<float*>(w + L.off_amax);
+  c.state = reinterpret_cast<DevState*>(w + L.off_state);
+  c.hist = reinterpret_cast<int32_t*>(w + L.off_hist);
+  c.counters = reinterpret_cast<unsigned*>(w + L.off_counters);
+  c.h = reinterpret_cast<float*>(w + L.off_h);
+  c.qkv = reinterpret_cast<float*>(w + L.off_qkv);
+  c.attn_part = reinterpret_cast<float*>(w + L.off_attn_part);
+  c.o_act = w + L.off_o_act;
+  c.a_act = w + L.off_a_act;
+  c.logits = reinterpret_cast<float*>(w + L.off_logits);
+  c.tok = reinterpret_cast<int32_t*>(w + L.off_tok);
+  c.px = reinterpret_cast<float*>(w + L.off_x);
+  c.pu = w + L.off_u;
+  c.pqkv = reinterpret_cast<float*>(w + L.off_pqkv);
+  c.pq = reinterpret_cast<float*>(w + L.off_pq);
+  c.po = w + L.off_po;
+  c.pgu = reinterpret_cast<float*>(w + L.off_pgu);
+}
+
+static void drop_graph(Ctx& c) {
+  if (c.frame_exec) (void)hipGraphExecDestroy(c.frame_exec);
+  if (c.frame_graph) (void)hipGraphDestroy(c.frame_graph);
+  c.frame_exec = nullptr;
+  c.frame_graph = nullptr;
+}
+
+static hipError_t enqueue_frame(Ctx& c, bool record) {
+  hipError_t e = launch_frame_begin(c);
+  if (e != hipSuccess) return e;
+  for (int l = 0; l < c.cfg.n_layers; ++l)
+    if ((e = launch_layer_decode(c, l, c.h, record)) != hipSuccess) return e;
+  return launch_head(c, record);
+}
+
+static int ensure_graph(Ctx& c) {
+  if (c.frame_exec) return HTA_OK;
+  HIPCK(hipStreamBeginCapture(c.stream, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
+  hipError_t e = enqueue_frame(c, false);
+  hipGraph_t g = nullptr;
+  hipError_t e2 = hipStreamEndCapture(c.stream, &g);
+  if (e != hipSuccess) { if (g) (void)hipGraphDestroy(g); return hip_fail(c, e, "frame capture"); }
+  if (e2 != hipSuccess) return hip_fail(c, e2, "hipStreamEndCapture");
+  c.frame_graph = g;
+  HIPCK(hipGraphInstantiate(&c.frame_exec, g, nullptr, nullptr, 0), "hipGraphInstantiate");
+  return HTA_OK;
+}
+
+static int ready(Ctx& c) {
+  if (!c.ws) return fail(c, HTA_E_STATE, "no workspace bound");
+  if (!c.weights_loaded) return fail(c, HTA_E_STATE, "weights not loaded");
+  return HTA_OK;
+}
+
+// ---------------------------------------------------------------------------- ABI
+extern "C" {
+
+const char* hta_version(void) { return "hta 0.1 gfx950"; }
+
+size_t hta_workspace_bytes(const hta_config* cfg) {
+  if (!cfg || !shape_ok(*cfg, nullptr)) return 0;
+  return make_layout(*cfg).total;
+}
+
+int hta_create(const hta_config* cfg, void* hip_stream, hta_ctx** out) {
+  if (!cfg || !out) return HTA_E_ARG;
+  *out = nullptr;
+  std::string why;
+  hta_ctx* x = new (std::nothrow) hta_ctx();
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  if (!shape_ok(*cfg, &why)) { delete x; return HTA_E_UNSUPPORTED; }
+  c.cfg = *cfg;
+  hipError_t e = hipGetDevice(&c.device);
+  if (e != hipSuccess) { delete x; return HTA_E_HIP; }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, c.device) != hipSuccess) { delete x; return HTA_E_HIP; }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) { delete x; return HTA_E_UNSUPPORTED; }
+  if (hip_stream) {
+    c.stream = static_cast<hipStream_t>(hip_stream);
+  } else {
+    if (hipStreamCreateWithFlags(&c.stream, hipStreamNonBlocking) != hipSuccess) { delete x; return HTA_E_HIP; }
+    c.own_stream = true;
+  }
+  c.lay = make_layout(c.cfg);
+  c.layers = new LayerW[c.cfg.n_layers]();
+  c.h_stage_elems = (size_t)c.cfg.max_seq * c.cfg.n_codebooks;
+  if ((size_t)c.cfg.max_prefill > c.h_stage_elems) c.h_stage_elems = c.cfg.max_prefill;
+  if (hipHostMalloc((void**)&c.h_stage, c.h_stage_elems * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&c.h_state, sizeof(DevState), hipHostMallocDefault) != hipSuccess) {
+    hta_destroy(x);
+    return HTA_E_HIP;
+  }
+  *out = x;
+  return HTA_OK;
+}
+
+int hta_bind_workspace(hta_ctx* x, void* dev_ptr, size_t bytes) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  if (!dev_ptr) return fail(c, HTA_E_ARG, "null workspace");
+  if (reinterpret_cast<uintptr_t>(dev_ptr) % 256) return fail(c, HTA_E_ARG, "workspace not 256-byte aligned");
+  if (bytes < c.lay.total) return fail(c, HTA_E_ARG, "workspace too small");
+  drop_graph(c);
+  c.ws = static_cast<char*>(dev_ptr);
+  c.weights_loaded = false;
+  set_pointers(c);
+  const hta_config& f = c.cfg;
+  // RoPE table: phi = p * theta^(-2i/hd) in double, stored as float cos / sin
+  const int h2 = f.head_dim / 2;
+  std::vector<float> cs((size_t)f.max_seq * h2), sn((size_t)f.max_seq * h2);
+  for (int p = 0; p < f.max_seq; ++p)
+    for (int i = 0; i < h2; ++i) {
+      const double inv = std::pow((double)f.rope_theta, -2.0 * i / f.head_dim);
+      const double phi = (double)p * inv;
+      cs[(size_t)p * h2 + i] = (float)std::cos(phi);
+      sn[(size_t)p * h2 + i] = (float)std::sin(phi);
+    }
+  HIPCK(hipStreamSynchronize(c.stream), "sync");
+  HIPCK(hipMemcpy(c.rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice), "rope table");
+  HIPCK(hipMemcpy(c.rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice), "rope table");
+  const size_t nsites = (size_t)kSitesPerLayer * f.n_layers + 1;
+  HIPCK(launch_fill_u32(c.counters, 0u, 64, c.stream), "fill");
+  HIPCK(launch_fill_u32(c.amax, 0u, nsites, c.stream), "fill");
+  HIPCK(launch_fill_u32(c.act_scales, 0x3f800000u, nsites, c.stream), "fill");
+  HIPCK(launch_fill_u32(c.state, 0u, sizeof(DevState) / 4, c.stream), "fill");
+  HIPCK(launch_reset_state(c, 0), "reset");
+  HIPCK(hipStreamSynchronize(c.stream), "sync");
+  c.len = 0;
+  c.t = 0;
+  return HTA_OK;
+}
+
+int hta_load_weights(hta_ctx* x, const void* const* t, int n, int src_dtype, const float* act_scales) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  const hta_config& f = c.cfg;
+  if (!c.ws) return fail(c, HTA_E_STATE, "no workspace bound");
+  if (!t || n != 4 + 11 * f.n_layers) return fail(c, HTA_E_ARG, "expected 4 + 11 * n_layers tensors");
+  if (src_dtype != HTA_SRC_F32 && src_dtype != HTA_SRC_BF16) return fail(c, HTA_E_ARG, "bad src dtype");
+  for (int i = 0; i < n; ++i) if (!t[i]) return fail(c, HTA_E_ARG, "null weight tensor");
+  const bool fp8 = f.precision == HTA_FP8_E4M3;
+  if (fp8 && !act_scales) return fail(c, HTA_E_ARG, "FP8 needs activation scales");
+  const int nsites = kSitesPerLayer * f.n_layers + 1;
+  c.h_scales.assign(nsites, 1.0f);
+  if (fp8) {
+    for (int i = 0; i < nsites; ++i) {
+      if (!(act_scales[i] > 0.0f) || !std::isfinite(act_scales[i])) return fail(c, HTA_E_ARG, "activation scales must be positive");
+      c.h_scales[i] = act_scales[i];
+    }
+  }
+  drop_graph(c);
+  const int d = f.hidden, hd = f.head_dim, qd = f.n_q_heads * hd, kvd = f.n_kv_heads * hd, F = f.ffn;
+  const int CV = f.n_codebooks * f.codebook_size;
+  hipStream_t s = c.stream;
+  const int q8 = fp8 ? 1 : 0;
+  HIPCK(launch_pack_rows(c.e_text, 0, 1, t[0], src_dtype, f.text_vocab, d, 0, nullptr, s), "pack e_text");
+  HIPCK(launch_pack_rows(c.e_aud, 0, 1, t[1], src_dtype, CV, d, 0, nullptr, s), "pack e_aud");
+  for (int l = 0; l < f.n_layers; ++l) {
+    const void* const* T = t + 2 + 11 * l;
+    LayerW& L = c.layers[l];
+    HIPCK(launch_copy_f32(L.g_attn, T[0], src_dtype, d, s), "gain");
+    HIPCK(launch_pack_rows(L.w_qkv, 0, 1, T[1], src_dtype, qd, d, q8, L.s_qkv, s), "pack wq");
+    HIPCK(launch_pack_rows(L.w_qkv, qd, 1, T[2], src_dtype, kvd, d, q8, L.s_qkv, s), "pack wk");
+    HIPCK(launch_pack_rows(L.w_qkv, qd + kvd, 1, T[3], src_dtype, kvd, d, q8, L.s_qkv, s), "pack wv");
+    HIPCK(launch_copy_f32(L.g_q, T[4], src_dtype, hd, s), "gain");
+    HIPCK(launch_copy_f32(L.g_k, T[5], src_dtype, hd, s), "gain");
+    HIPCK(launch_pack_rows(L.w_o, 0, 1, T[6], src_dtype, d, qd, q8, L.s_o, s), "pack wo");
+    HIPCK(launch_copy_f32(L.g_mlp, T[7], src_dtype, d, s), "gain");
+    HIPCK(launch_pack_rows(L.w_gu, 0, 2, T[8], src_dtype, F, d, q8, L.s_gu, s), "pack wg");
+    HIPCK(launch_pack_rows(L.w_gu, 1, 2, T[9], src_dtype, F, d, q8, L.s_gu, s), "pack wu");
+    HIPCK(launch_pack_rows(L.w_d, 0, 1, T[10], src_dtype, d, F, q8, L.s_d, s), "pack wd");
+  }
+  const void* const* T = t + 2 + 11 * f.n_layers;
+  HIPCK(launch_copy_f32(c.g_final, T[0], src_dtype, d, s), "gain");
+  HIPCK(launch_pack_rows(c.w_head, 0, 1, T[1], src_dtype, CV, d, q8, c.s_head, s), "pack head");
+  HIPCK(hipMemcpyAsync(c.act_scales, c.h_scales.data(), nsites * 4, hipMemcpyHostToDevice, s), "scales");
+  HIPCK(hipStreamSynchronize(s), "load sync");
+  c.weights_loaded = true;
+  return HTA_OK;
+}
+
+int hta_reset(hta_ctx* x, int keep_len) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  if (!c.ws) return fail(c, HTA_E_STATE, "no workspace bound");
+  if (keep_len < 0 || keep_len > c.len) return fail(c, HTA_E_ARG, "keep_len out of range");
+  HIPCK(launch_reset_state(c, keep_len), "reset");
+  c.len = keep_len;
+  c.t = 0;
+  c.done = false;
+  return HTA_OK;
+}
+
+int hta_prefill(hta_ctx* x, const int32_t* tokens, int P) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  int r = ready(c);
+  if (r) return r;
+  if (!tokens || P <= 0) return fail(c, HTA_E_ARG, "empty prompt");
+  if (P > c.cfg.max_prefill) return fail(c, HTA_E_CAPACITY, "P exceeds max_prefill");
+  if (c.len + P > c.cfg.max_seq) return fail(c, HTA_E_CAPACITY, "prompt exceeds max_seq");
+  for (int i = 0; i < P; ++i)
+    if (tokens[i] < 0 || tokens[i] >= c.cfg.text_vocab) return fail(c, HTA_E_RANGE, "token id out of range");
+  HIPCK(hipStreamSynchronize(c.stream), "sync");
+  std::memcpy(c.h_stage, tokens, (size_t)P * 4);
+  HIPCK(hipMemcpyAsync(c.tok, c.h_stage, (size_t)P * 4, hipMemcpyHostToDevice, c.stream), "tokens");
+  HIPCK(launch_prefill(c, P, false), "prefill");
+  HIPCK(launch_set_len(c, c.len + P), "set len");
+  HIPCK(hipStreamSynchronize(c.stream), "prefill sync");
+  c.len += P;
+  c.last_prefill_P = P;
+  return HTA_OK;
+}
+
+static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out) {
+  int r = ready(c);
+  if (r) return r;
+  if (n <= 0 || !codes_out) return fail(c, HTA_E_ARG, "bad frame count or output");
+  if (c.len + n > c.cfg.max_seq) return fail(c, HTA_E_CAPACITY, "KV cache full");
+  if (c.use_graph) {
+    if ((r = ensure_graph(c)) != HTA_OK) return r;
+    for (int i = 0; i < n; ++i) HIPCK(hipGraphLaunch(c.frame_exec, c.stream), "hipGraphLaunch");
+  } else {
+    for (int i = 0; i < n; ++i) HIPCK(enqueue_frame(c, false), "frame");
+  }
+  const int C = c.cfg.n_codebooks;
+  const int t0 = c.t;
+  HIPCK(hipMemcpyAsync(c.h_stage, c.hist + (size_t)t0 * C, (size_t)n * C * 4, hipMemcpyDeviceToHost, c.stream), "codes");
+  HIPCK(hipMemcpyAsync(c.h_state, c.state, sizeof(DevState), hipMemcpyDeviceToHost, c.stream), "state");
+  HIPCK(hipStreamSynchronize(c.stream), "decode sync");
+  std::memcpy(codes_out, c.h_stage, (size_t)n * C * 4);
+  c.len += n;
+  c.t += n;
+  if (c.h_state->len != c.len || c.h_state->t != c.t) return fail(c, HTA_E_STATE, "device state out of step with host");
+  c.done = c.h_state->done != 0;
+  if (n_done_out) *n_done_out = c.h_state->n_done;
+  return c.done ? HTA_DONE : HTA_OK;
+}
+
+int hta_decode_frame(hta_ctx* x, int32_t* codes_out) {
+  if (!x) return HTA_E_ARG;
+  return decode_n(x->c, 1, codes_out, nullptr);
+}
+
+int hta_decode_frames(hta_ctx* x, int n, int32_t* codes_out, int* n_done) {
+  if (!x) return HTA_E_ARG;
+  return decode_n(x->c, n, codes_out, n_done);
+}
+
+int hta_force_codes(hta_ctx* x, const int32_t* codes) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  if (!c.ws) return fail(c, HTA_E_STATE, "no workspace bound");
+  if (!codes) return fail(c, HTA_E_ARG, "null codes");
+  for (int k = 0; k < c.cfg.n_codebooks; ++k)
+    if (codes[k] < 0 || codes[k] >= c.cfg.codebook_size) return fail(c, HTA_E_RANGE, "code out of range");
+  HIPCK(launch_set_prev(c, codes), "force codes");
+  return HTA_OK;
+}
+
+int hta_read_tap(hta_ctx* x, int tap, int layer, void* host_out, size_t bytes) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  const hta_config& f = c.cfg;
+  if (!c.ws) return fail(c, HTA_E_STATE, "no workspace bound");
+  if (!host_out) return fail(c, HTA_E_ARG, "null output");
+  HIPCK(hipStreamSynchronize(c.stream), "sync");
+  const int C = f.n_codebooks;
+  switch (tap) {
+    case HTA_TAP_HIDDEN:
+      if (bytes < (size_t)f.hidden * 4) return fail(c, HTA_E_ARG, "buffer too small");
+      HIPCK(hipMemcpy(host_out, c.h, (size_t)f.hidden * 4, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    case HTA_TAP_LOGITS: {
+      const size_t nb = (size_t)C * f.codebook_size * 4;
+      if (bytes < nb) return fail(c, HTA_E_ARG, "buffer too small");
+      HIPCK(hipMemcpy(host_out, c.logits, nb, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    }
+    case HTA_TAP_STATE: {
+      if (bytes < (size_t)(4 + 2 * C) * 4) return fail(c, HTA_E_ARG, "buffer too small");
+      DevState s;
+      HIPCK(hipMemcpy(&s, c.state, sizeof(s), hipMemcpyDeviceToHost), "tap");
+      int32_t* o = static_cast<int32_t*>(host_out);
+      o[0] = s.len; o[1] = s.t; o[2] = s.eoc; o[3] = s.done;
+      for (int k = 0; k < C; ++k) { o[4 + k] = s.prev[k]; o[4 + C + k] = s.codes[k]; }
+      return HTA_OK;
+    }
+    case HTA_TAP_KV: {
+      // as many positions as the buffer holds: bytes / (2 * Hkv * hd * 2), at most max_seq
+      if (layer < 0 || layer >= f.n_layers) return fail(c, HTA_E_ARG, "bad layer");
+      const size_t per_pos = 2 * (size_t)f.n_kv_heads * f.head_dim * 2;
+      size_t npos = bytes / per_pos;
+      if (npos > (size_t)f.max_seq) npos = f.max_seq;
+      if (npos == 0) return fail(c, HTA_E_ARG, "buffer too small");
+      const size_t row = npos * f.head_dim * 2;
+      const size_t half = (size_t)f.n_kv_heads * row;
+      const size_t pitch = (size_t)f.max_seq * f.head_dim * 2;
+      char* o = static_cast<char*>(host_out);
+      HIPCK(hipMemcpy2D(o, row, c.layers[layer].k_cache, pitch, row, f.n_kv_heads, hipMemcpyDeviceToHost), "tap");
+      HIPCK(hipMemcpy2D(o + half, row, c.layers[layer].v_cache, pitch, row, f.n_kv_heads, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    }
+    case HTA_TAP_AMAX: {
+      const size_t nb = ((size_t)kSitesPerLayer * f.n_layers + 1) * 4;
+      if (bytes < nb) return fail(c, HTA_E_ARG, "buffer too small");
+      HIPCK(hipMemcpy(host_out, c.amax, nb, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    }
+    case HTA_TAP_PREFILL_HIDDEN: {
+      const size_t nb = (size_t)c.last_prefill_P * f.hidden * 4;
+      if (bytes < nb) return fail(c, HTA_E_ARG, "buffer too small");
+      if (nb) HIPCK(hipMemcpy(host_out, c.px, nb, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    }
+    case HTA_TAP_W_QKV:
+    case HTA_TAP_S_QKV:
+    case HTA_TAP_W_GU:
+    case HTA_TAP_S_GU: {
+      if (layer < 0 || layer >= f.n_layers) return fail(c, HTA_E_ARG, "bad layer");
+      const bool fp8 = f.precision == HTA_FP8_E4M3;
+      const bool qkv = tap == HTA_TAP_W_QKV || tap == HTA_TAP_S_QKV;
+      const bool scales = tap == HTA_TAP_S_QKV || tap == HTA_TAP_S_GU;
+      const size_t rows = qkv ? (size_t)(f.n_q_heads + 2 * f.n_kv_heads) * f.head_dim : (size_t)2 * f.ffn;
+      if (scales && !fp8) return fail(c, HTA_E_ARG, "no scales in a BF16 context");
+      const size_t nb = scales ? rows * 4 : rows * f.hidden * (fp8 ? 1 : 2);
+      if (bytes < nb) return fail(c, HTA_E_ARG, "buffer too small");
+      const LayerW& L = c.layers[layer];
+      const void* src = scales ? (const void*)(qkv ? L.s_qkv : L.s_gu) : (const void*)(qkv ? L.w_qkv : L.w_gu);
+      HIPCK(hipMemcpy(host_out, src, nb, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    }
+    default:
+      return fail(c, HTA_E_ARG, "unknown tap");
+  }
+}
+
+int hta_calibrate(hta_ctx* x, const int32_t* tokens, int P, int n_frames, const int32_t* forced, float* scales_out) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  const hta_config& f = c.cfg;
+  int r = ready(c);
+  if (r) return r;
+  if (f.precision != HTA_BF16) return fail(c, HTA_E_STATE, "calibration runs on a BF16 context");
+  if (!tokens || P <= 0 || P > f.max_prefill || n_frames < 0 || !scales_out) return fail(c, HTA_E_ARG, "bad calibration arguments");
+  if (P + n_frames > f.max_seq) return fail(c, HTA_E_CAPACITY, "calibration run exceeds max_seq");
+  for (int i = 0; i < P; ++i)
+    if (tokens[i] < 0 || tokens[i] >= f.text_vocab) return fail(c, HTA_E_RANGE, "token id out of range");
+  if (forced)
+    for (int i = 0; i < n_frames * f.n_codebooks; ++i)
+      if (forced[i] < 0 || forced[i] >= f.codebook_size) return fail(c, HTA_E_RANGE, "forced code out of range");
+  const int nsites = kSitesPerLayer * f.n_layers + 1;
+  c.len = 0;  // cold start
+  HIPCK(launch_reset_state(c, 0), "reset");
+  HIPCK(launch_fill_u32(c.amax, 0u, nsites, c.stream), "fill");
+  HIPCK(hipStreamSynchronize(c.stream), "sync");
+  std::memcpy(c.h_stage, tokens, (size_t)P * 4);
+  HIPCK(hipMemcpyAsync(c.tok, c.h_stage, (size_t)P * 4, hipMemcpyHostToDevice, c.stream), "tokens");
+  HIPCK(launch_prefill(c, P, true), "calibration prefill");
+  HIPCK(launch_set_len(c, P), "set len");
+  for (int fr = 0; fr < n_frames; ++fr) {
+    HIPCK(enqueue_frame(c, true), "calibration frame");
+    if (forced) HIPCK(launch_set_prev(c, forced + (size_t)fr * f.n_codebooks), "force");
+  }
+  std::vector<float> amax(nsites);
+  HIPCK(hipStreamSynchronize(c.stream), "sync");
+  HIPCK(hipMemcpy(amax.data(), c.amax, nsites * 4, hipMemcpyDeviceToHost), "amax");
+  for (int i = 0; i < nsites; ++i) scales_out[i] = amax[i] > 0.0f ? amax[i] / 448.0f : 1.0f;
+  c.len = P + n_frames;
+  c.last_prefill_P = P;
+  HIPCK(launch_reset_state(c, 0), "reset");
+  HIPCK(hipStreamSynchronize(c.stream), "sync");
+  c.len = 0;
+  c.t = 0;
+  c.done = false;
+  return HTA_OK;
+}
+
+int hta_layer_step(hta_ctx* x, int layer, int kv_len, const void* k_init, const void* v_init, void* h_io) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  const hta_config& f = c.cfg;
+  int r = ready(c);
+  if (r) return r;
+  if (layer < 0 || layer >= f.n_layers) return fail(c, HTA_E_ARG, "bad layer");
+  if (kv_len < 1 || kv_len > f.max_seq) return fail(c, HTA_E_CAPACITY, "kv_len out of range");
+  if (!h_io) return fail(c, HTA_E_ARG, "null hidden state");
+  if ((k_init == nullptr) != (v_init == nullptr)) return fail(c, HTA_E_ARG, "k_init and v_init go together");
+  if (k_init)
+    HIPCK(launch_kv_init(c.layers[layer].k_cache, c.layers[layer].v_cache, k_init, v_init, f.n_kv_heads, kv_len - 1,
+                         f.max_seq, f.head_dim, c.stream), "kv init");
+  HIPCK(launch_layer_decode_at(c, layer, static_cast<float*>(h_io), false, kv_len - 1), "layer step");
+  HIPCK(hipStreamSynchronize(c.stream), "sync");
+  return HTA_OK;
+}
+
+int hta_undelay(const int32_t* steps, int T, int C, int eos, int32_t* frames_out, int* n_frames) {
+  if (!steps || !frames_out || !n_frames || T < 0 || C < 1) return HTA_E_ARG;
+  int eoc = -1;
+  for (int t = 0; t < T; ++t)
+    if (steps[(size_t)t * C] == eos) { eoc = t; break; }
+  int n = eoc >= 0 ? eoc : T - (C - 1);
+  if (n < 0) n = 0;
+  if (n + C - 1 > T) n = T - (C - 1) < 0 ? 0 : T - (C - 1);
+  for (int fr = 0; fr < n; ++fr)
+    for (int k = 0; k < C; ++k) frames_out[(size_t)fr * C + k] = steps[(size_t)(fr + k) * C + k];
+  *n_frames = n;
+  return HTA_OK;
+}
+
+int hta_set_option(hta_ctx* x, int option, int value) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  if (option == HTA_OPT_USE_GRAPH) {
+    c.use_graph = value != 0;
+    return HTA_OK;
+  }
+  return fail(c, HTA_E_ARG, "unknown option");
+}
+
+void hta_destroy(hta_ctx* x) {
+  if (!x) return;
+  Ctx& c = x->c;
+  if (c.stream) (void)hipStreamSynchronize(c.stream);
+  drop_graph(c);
+  if (c.h_stage) (void)hipHostFree(c.h_stage);
+  if (c.h_state) (void)hipHostFree(c.h_state);
+  if (c.own_stream && c.stream) (void)hipStreamDestroy(c.stream);
+  delete[] c.layers;
+  delete x;
+}
+
+const char* hta_last_error(const hta_ctx* x) {
+  if (!x) return "null context";
+  return x->c.err.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,432 @@
+// Batched prefill (M = P rows) for gfx950: embedding gather, row RMSNorm +
+// activation rounding, MFMA GEMMs (bf16 16x16x32; e4m3 operands widened to
+// bf16 in registers) with a
+// fixed, P-independent reduction order, fused q/k-norm + RoPE + KV write, and
+// causal attention over key tiles aligned to absolute positions.
+//
+// Reference: FlashRT "Higgs Audio v3 TTS-4B" page, section 7 (the prompt is
+// prefilled in one batched M = P forward; a shared preamble's KV is reused and
+// the result is bit-identical to a cold prefill) and the Performance section
+// (batched BF16/FP8 prefill).  Bit-identity under prefix reuse requires that
+// every output row is computed the same way whatever P or the start offset is:
+// the GEMM's K order and split depend only on (N, K), and attention walks key
+// tiles at absolute multiples of 64.
+#include "device_common.h"
+#include "hta_internal.h"
+
+namespace hta {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// 8 e4m3 codes (two dwords) -> 8 bf16 values, exactly (hardware pair convert, scale 1).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+extern float host_act_scale(const Ctx& c, int site);
+
+// ============================================================================ rows
+__global__ __launch_bounds__(256) void k_embed_rows(const int32_t* __restrict__ tok, const uint16_t* __restrict__ e_text,
+                                                    float* __restrict__ X, int d) {
+  const int i = blockIdx.x;
+  const size_t t = (size_t)tok[i];
+  for (int k = threadIdx.x; k < d; k += blockDim.x) X[(size_t)i * d + k] = bf16_to_f32(e_text[t * d + k]);
+}
+
+template <int P>
+__global__ __launch_bounds__(256) void k_rmsnorm_act_rows(const float* __restrict__ X, const float* __restrict__ g,
+                                                          float eps, void* __restrict__ U, int d, float scale,
+                                                          float* amax) {
+  __shared__ float red[16];
+  const int i = blockIdx.x;
+  const float* x = X + (size_t)i * d;
+  float ss = 0.0f;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) ss = fmaf(x[k], x[k], ss);
+  ss = block_sum(ss, red);
+  const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
+  float mx = 0.0f;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    const float u = x[k] * rstd * g[k];
+    mx = fmaxf(mx, fabsf(u));
+    if (P == kBF16) static_cast<uint16_t*>(U)[(size_t)i * d + k] = (uint16_t)act_encode<P>(u, scale);
+    else static_cast<uint8_t*>(U)[(size_t)i * d + k] = (uint8_t)act_encode<P>(u, scale);
+  }
+  if (amax) {
+    mx = block_max(mx, red);
+    if (threadIdx.x == 0) record_amax(amax, mx);
+  }
+}
+
+template <int P>
+__global__ __launch_bounds__(256) void k_silu_mul_rows(const float* __restrict__ GU, void* __restrict__ A, int F,
+                                                       float scale, float* amax) {
+  __shared__ float red[16];
+  const int i = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  float mx = 0.0f;
+  if (j < F) {
+    const float gt = GU[(size_t)i * 2 * F + 2 * j], up = GU[(size_t)i * 2 * F + 2 * j + 1];
+    const float v = silu(gt) * up;
+    mx = fabsf(v);
+    if (P == kBF16) static_cast<uint16_t*>(A)[(size_t)i * F + j] = (uint16_t)act_encode<P>(v, scale);
+    else static_cast<uint8_t*>(A)[(size_t)i * F + j] = (uint8_t)act_encode<P>(v, scale);
+  }
+  if (amax) {
+    mx = block_max(mx, red);
+    if (threadIdx.x == 0) record_amax(amax, mx);
+  }
+}
+
+// q/k RMSNorm + RoPE for one row of heads; rotated values rounded to bf16.
+template <int HD>
+__device__ __forceinline__ void norm_rope_row(const float* __restrict__ src, const float* __restrict__ g,
+                                              const float* __restrict__ cs, const float* __restrict__ sn, float eps,
+                                              int lane, float* a_out, float* b_out) {
+  constexpr int H2 = HD / 2;
+  const bool act = lane < H2;
+  const float x0 = act ? src[lane] : 0.0f;
+  const float x1 = act ? src[lane + H2] : 0.0f;
+  const float ss = wave_sum(x0 * x0 + x1 * x1);
+  const float rstd = 1.0f / sqrtf(ss / (float)HD + eps);
+  const float a = x0 * rstd * (act ? g[lane] : 0.0f);
+  const float b = x1 * rstd * (act ? g[lane + H2] : 0.0f);
+  const float c = act ? cs[lane] : 0.0f, s = act ? sn[lane] : 0.0f;
+  *a_out = round_bf16(a * c - b * s);
+  *b_out = round_bf16(b * c + a * s);
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ QKV, const float* __restrict__ g_q,
+                                                      const float* __restrict__ g_k, const float* __restrict__ rope_cos,
+                                                      const float* __restrict__ rope_sin, float* __restrict__ Q,
+                                                      uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int len0,
+                                                      int Hq, int Hkv, int max_seq, float eps) {
+  constexpr int H2 = HD / 2;
+  const int i = blockIdx.x, pos = len0 + i;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int W = (Hq + 2 * Hkv) * HD;
+  const float* row = QKV + (size_t)i * W;
+  const float* cs = rope_cos + (size_t)pos * H2;
+  const float* sn = rope_sin + (size_t)pos * H2;
+  for (int h = w; h < Hq + Hkv; h += nw) {
+    float a, b;
+    if (h < Hq) {
+      norm_rope_row<HD>(row + (size_t)h * HD, g_q, cs, sn, eps, lane, &a, &b);
+      if (lane < H2) {
+        Q[(size_t)i * Hq * HD + (size_t)h * HD + lane] = a;
+        Q[(size_t)i * Hq * HD + (size_t)h * HD + lane + H2] = b;
+      }
+    } else {
+      const int j = h - Hq;
+      norm_rope_row<HD>(row + (size_t)h * HD, g_k, cs, sn, eps, lane, &a, &b);
+      if (lane < H2) {
+        kc[((size_t)j * max_seq + pos) * HD + lane] = (uint16_t)f32_to_bf16(a);
+        kc[((size_t)j * max_seq + pos) * HD + lane + H2] = (uint16_t)f32_to_bf16(b);
+      }
+    }
+  }
+  for (int e = threadIdx.x; e < Hkv * HD; e += blockDim.x) {
+    const int j = e / HD, dd = e % HD;
+    vc[((size_t)j * max_seq + pos) * HD + dd] = (uint16_t)f32_to_bf16(row[(size_t)(Hq + Hkv) * HD + e]);
+  }
+}
+
+// ============================================================================ causal attention
+// One block: 16 queries of one q head; keys in 64-wide tiles at absolute
+// positions 0, 64, 128, ... up to the last query's position.
+template <int P, int HD>
+__global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ Q, const uint16_t* __restrict__ kc,
+                                                      const uint16_t* __restrict__ vc, void* __restrict__ O, int len0,
+                                                      int n_rows, int Hq, int Hkv, int max_seq, float scale,
+                                                      float* amax) {
+  constexpr int T = kAttnTile;
+  constexpr int QT = 16;
+  constexpr int DPT = HD / 16;  // output dims per thread
+  __shared__ float qs[QT][HD];
+  __shared__ float Kt[T][HD + 1];
+  __shared__ float Vt[T][HD];
+  __shared__ float ps[QT][T + 1];
+  __shared__ float red[16];
+  const int h = blockIdx.x, i0 = blockIdx.y * QT;
+  const int G = Hq / Hkv, j = h / G;
+  const int tid = threadIdx.x, r = tid / 16, sub = tid % 16;
+  const int qi = i0 + r;
+  const bool qvalid = qi < n_rows;
+  const int qpos = len0 + qi;
+  for (int e = tid; e < QT * HD; e += blockDim.x) {
+    const int rr = e / HD, dd = e % HD;
+    qs[rr][dd] = (i0 + rr < n_rows) ? Q[((size_t)(i0 + rr) * Hq + h) * HD + dd] : 0.0f;
+  }
+  const int last_pos = len0 + min(i0 + QT, n_rows) - 1;
+  const int n_tiles = last_pos / T + 1;
+  const uint16_t* kb = kc + (size_t)j * max_seq * HD;
+  const uint16_t* vb = vc + (size_t)j * max_seq * HD;
+  const float inv_sqrt = 1.0f / sqrtf((float)HD);
+  float m = -INFINITY, l = 0.0f;
+  float o[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) o[e] = 0.0f;
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int t0 = tile * T;
+    __syncthreads();
+    constexpr int SEG = HD / 8;
+    for (int idx = tid; idx < T * SEG; idx += blockDim.x) {
+      const int key = idx / SEG, seg = idx % SEG;
+      const int kp = t0 + key;
+      if (kp <= last_pos) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(kb + (size_t)kp * HD + seg * 8);
+        const uint4 vw = *reinterpret_cast<const uint4*>(vb + (size_t)kp * HD + seg * 8);
+        const uint32_t ks[4] = {kw.x, kw.y, kw.z, kw.w}, vs[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          Kt[key][seg * 8 + 2 * q] = bf16lo(ks[q]); Kt[key][seg * 8 + 2 * q + 1] = bf16hi(ks[q]);
+          Vt[key][seg * 8 + 2 * q] = bf16lo(vs[q]); Vt[key][seg * 8 + 2 * q + 1] = bf16hi(vs[q]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) { Kt[key][seg * 8 + q] = 0.0f; Vt[key][seg * 8 + q] = 0.0f; }
+      }
+    }
+    __syncthreads();
+    // scores: thread (r, sub) takes keys sub, sub+16, sub+32, sub+48
+    float s[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int kk = sub + 16 * q;
+      const int kp = t0 + kk;
+      float d = 0.0f;
+#pragma unroll 8
+      for (int e = 0; e < HD; ++e) d = fmaf(qs[r][e], Kt[kk][e], d);
+      s[q] = (qvalid && kp <= qpos) ? d * inv_sqrt : -INFINITY;
+      tmax = fmaxf(tmax, s[q]);
+    }
+#pragma unroll
+    for (int o2 = 8; o2 > 0; o2 >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o2, 16));
+    const float mnew = fmaxf(m, tmax);
+    float psum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float p = (s[q] == -INFINITY) ? 0.0f : __expf(s[q] - mnew);
+      ps[r][sub + 16 * q] = p;
+      psum += p;
+    }
+#pragma unroll
+    for (int o2 = 8; o2 > 0; o2 >>= 1) psum += __shfl_xor(psum, o2, 16);
+    const float sc = (m == -INFINITY) ? 0.0f : __expf(m - mnew);
+    l = l * sc + psum;
+    m = mnew;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) o[e] *= sc;
+    for (int kk = 0; kk < T; ++kk) {
+      const float p = ps[r][kk];
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) o[e] = fmaf(p, Vt[kk][sub * DPT + e], o[e]);
+    }
+  }
+  float mx = 0.0f;
+  if (qvalid) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) {
+      const float v = o[e] * inv;
+      mx = fmaxf(mx, fabsf(v));
+      const size_t idx = ((size_t)qi * Hq + h) * HD + sub * DPT + e;
+      if (P == kBF16) static_cast<uint16_t*>(O)[idx] = (uint16_t)act_encode<P>(v, scale);
+      else static_cast<uint8_t*>(O)[idx] = (uint8_t)act_encode<P>(v, scale);
+    }
+  }
+  if (amax) {
+    mx = block_max(mx, red);
+    if (tid == 0) record_amax(amax, mx);
+  }
+}
+
+// ============================================================================ MFMA GEMM
+// C[M][N] (+)= A[M][K] . B[N][K]^T, A = activations (bf16 bits / e4m3 codes),
+// B = packed weights.  A wave computes 32 rows x 16 columns; a block is 4 waves
+// (64 columns); the K range is split into `ksplit` contiguous parts (a function
+// of N and K only) whose partial sums land in Cpart[ksplit][M][N] and are added
+// in split order by k_gemm_reduce.  Each 16x16 MFMA tile accumulates its K
+// range in increasing order, so a row's result does not depend on M.
+template <int P>
+__global__ __launch_bounds__(256) void k_gemm(const void* __restrict__ A, const void* __restrict__ B,
+                                              float* __restrict__ Cpart, int M, int N, int K, int ksplit) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int m0 = blockIdx.x * 32;
+  const int n0 = (blockIdx.y * 4 + w) * 16;
+  const int ks = blockIdx.z;
+  if (n0 >= N) return;
+  constexpr int KSTEP = 128;
+  const int nsteps = K / KSTEP;
+  const int s_beg = (int)((long)nsteps * ks / ksplit), s_end = (int)((long)nsteps * (ks + 1) / ksplit);
+  const int rA0 = m0 + (lane & 15), rA1 = m0 + 16 + (lane & 15);
+  const int rB = n0 + (lane & 15);
+  const int grp = lane >> 4;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (P == kBF16) {
+    const uint16_t* Ab = static_cast<const uint16_t*>(A);
+    const uint16_t* Bb = static_cast<const uint16_t*>(B);
+    for (int st = s_beg; st < s_end; ++st) {
+      const int kb = st * KSTEP;
+      uint4 a0[4], a1[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = kb + q * 32 + grp * 8;
+        b[q] = ld_stream16(Bb + (size_t)rB * K + k);
+        a0[q] = rA0 < M ? *reinterpret_cast<const uint4*>(Ab + (size_t)rA0 * K + k) : make_uint4(0, 0, 0, 0);
+        a1[q] = rA1 < M ? *reinterpret_cast<const uint4*>(Ab + (size_t)rA1 * K + k) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, b[q]);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0[q]), bv, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1[q]), bv, acc1, 0, 0, 0);
+      }
+    }
+  } else {
+    // e4m3 operands are widened to bf16 in registers (exact: 4 significant bits)
+    // and multiplied on the bf16 MFMA, which accumulates at full fp32 precision;
+    // the e4m3 MFMA forms accumulate internally with fewer bits.  Each lane's
+    // 16-byte packet covers k = kb + 16*grp .. +16 for both operands; bytes 0-7
+    // feed one MFMA and bytes 8-15 the next (the same permutation of k on both
+    // sides, so the products summed are unchanged).
+    const uint8_t* Ab = static_cast<const uint8_t*>(A);
+    const uint8_t* Bb = static_cast<const uint8_t*>(B);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    for (int st = s_beg; st < s_end; ++st) {
+      uint4 b[2], a0[2], a1[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int k = st * KSTEP + q * 64 + grp * 16;
+        b[q] = ld_stream16(Bb + (size_t)rB * K + k);
+        a0[q] = rA0 < M ? *reinterpret_cast<const uint4*>(Ab + (size_t)rA0 * K + k) : z;
+        a1[q] = rA1 < M ? *reinterpret_cast<const uint4*>(Ab + (size_t)rA1 * K + k) : z;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const bf16x8 bl = fp8x8_to_bf16(b[q].x, b[q].y), bh = fp8x8_to_bf16(b[q].z, b[q].w);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(a0[q].x, a0[q].y), bl, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(a1[q].x, a1[q].y), bl, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(a0[q].z, a0[q].w), bh, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(a1[q].z, a1[q].w), bh, acc1, 0, 0, 0);
+      }
+    }
+  }
+  // output layout: lane holds rows 4*grp + i of the 16x16 tile, column lane & 15
+  const int col = n0 + (lane & 15);
+  float* Cp = Cpart + (size_t)ks * M * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r0 = m0 + grp * 4 + i, r1 = m0 + 16 + grp * 4 + i;
+    if (r0 < M && col < N) Cp[(size_t)r0 * N + col] = acc0[i];
+    if (r1 < M && col < N) Cp[(size_t)r1 * N + col] = acc1[i];
+  }
+}
+
+// out = sum over splits (in order) * in_scale * w_scale[n]; mode 0 store, 1 add to out.
+__global__ __launch_bounds__(256) void k_gemm_reduce(const float* __restrict__ Cpart, float* __restrict__ out,
+                                                     const float* __restrict__ w_scale, float in_scale, int M, int N,
+                                                     int ksplit, int resid) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t MN = (size_t)M * N;
+  if (idx >= MN) return;
+  float s = 0.0f;
+  for (int k = 0; k < ksplit; ++k) s += Cpart[(size_t)k * MN + idx];
+  if (w_scale) s *= in_scale * w_scale[idx % N];
+  if (resid) out[idx] += s;
+  else out[idx] = s;
+}
+
+// Number of K splits: a function of (N, K) only, so prefix reuse stays bit-identical.
+static int gemm_ksplit(int N, int K) {
+  const int nsteps = K / 128;
+  const int nblk = N / 16;
+  int s = (1024 + nblk - 1) / nblk;
+  if (s > 8) s = 8;
+  if (s > nsteps) s = nsteps;
+  if (s < 1) s = 1;
+  return s;
+}
+
+template <int P>
+static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scale, float in_scale, float* out, int M,
+                       int N, int K, int resid) {
+  const int ks = gemm_ksplit(N, K);
+  dim3 grid((M + 31) / 32, (N + 63) / 64, ks);
+  float* part = c.pgu + (size_t)c.cfg.max_prefill * 2 * c.cfg.ffn;  // split partials after the gate/up buffer
+  hipLaunchKernelGGL(k_gemm<P>, grid, dim3(256), 0, c.stream, A, B, part, M, N, K, ks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t MN = (size_t)M * N;
+  hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, c.stream, part, out,
+                     P == kFP8 ? w_scale : nullptr, in_scale, M, N, ks, resid);
+  return hipGetLastError();
+}
+
+template <int P>
+static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
+  const auto& f = c.cfg;
+  const int d = f.hidden, hd = f.head_dim, Hq = f.n_q_heads, Hkv = f.n_kv_heads;
+  const int qd = Hq * hd, kvd = Hkv * hd, F = f.ffn, W = qd + 2 * kvd;
+  const int len0 = c.len;
+  float* amax = record ? c.amax : nullptr;
+  hipError_t e;
+  hipLaunchKernelGGL(k_embed_rows, dim3(Pn), dim3(256), 0, c.stream, c.tok, c.e_text, c.px, d);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int layer = 0; layer < f.n_layers; ++layer) {
+    const LayerW& L = c.layers[layer];
+    const int s0 = kSitesPerLayer * layer;
+    hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, L.g_attn, f.rms_eps, c.pu, d,
+                       host_act_scale(c, s0), amax ? amax + s0 : nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = gemm<P>(c, c.pu, L.w_qkv, L.s_qkv, host_act_scale(c, s0), c.pqkv, Pn, W, d, 0)) != hipSuccess) return e;
+    if (hd == 128)
+      hipLaunchKernelGGL(k_qk_rope_rows<128>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
+                         c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps);
+    else
+      hipLaunchKernelGGL(k_qk_rope_rows<64>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
+                         c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+      dim3 grid(Hq, (Pn + 15) / 16);
+      const float so = host_act_scale(c, s0 + 1);
+      float* am = amax ? amax + s0 + 1 : nullptr;
+      if (hd == 128)
+        hipLaunchKernelGGL((k_attn_prefill<P, 128>), grid, dim3(256), 0, c.stream, c.pq, L.k_cache, L.v_cache, c.po,
+                           len0, Pn, Hq, Hkv, f.max_seq, so, am);
+      else
+        hipLaunchKernelGGL((k_attn_prefill<P, 64>), grid, dim3(256), 0, c.stream, c.pq, L.k_cache, L.v_cache, c.po,
+                           len0, Pn, Hq, Hkv, f.max_seq, so, am);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = gemm<P>(c, c.po, L.w_o, L.s_o, host_act_scale(c, s0 + 1), c.px, Pn, d, qd, 1)) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, L.g_mlp, f.rms_eps, c.pu, d,
+                       host_act_scale(c, s0 + 2), amax ? amax + s0 + 2 : nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = gemm<P>(c, c.pu, L.w_gu, L.s_gu, host_act_scale(c, s0 + 2), c.pgu, Pn, 2 * F, d, 0)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL((k_silu_mul_rows<P>), dim3((F + 255) / 256, Pn), dim3(256), 0, c.stream, c.pgu, c.pu, F,
+                       host_act_scale(c, s0 + 3), amax ? amax + s0 + 3 : nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = gemm<P>(c, c.pu, L.w_d, L.s_d, host_act_scale(c, s0 + 3), c.px, Pn, d, F, 1)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_prefill(Ctx& c, int P, bool record) {
+  if (c.cfg.precision == HTA_FP8_E4M3) return prefill_p<kFP8>(c, P, record);
+  return prefill_p<kBF16>(c, P, record);
+}
+
+}  // namespace hta

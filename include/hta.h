@@ -1,0 +1,185 @@
+/*
+ * hta.h -- C ABI of the MI355X (gfx950) batch-1 codebook-TTS decode library.
+ *
+ * What it computes (reference pages):
+ *  - FlashRT "Higgs Audio v3 TTS-4B" page, summary: a dense Qwen3-4B-shaped
+ *    backbone (GQA, SwiGLU, RoPE theta 1e6) driving a fused head of
+ *    8 codebooks x 1026 under a delay pattern.
+ *  - same page, section 5: the per-frame chain RMSNorm (+quant) -> qkv GEMV ->
+ *    q/k-norm + RoPE (+KV write) -> attention -> o_proj GEMV with residual ->
+ *    RMSNorm -> gate/up GEMV -> SiLU*mul (+quant) -> down GEMV with residual
+ *    -> final RMSNorm (+quant) -> fused head GEMV -> greedy argmax with the
+ *    delay mask -> embedding of the chosen codes as the next input.
+ *  - same page, section 7: one batched prefill pass over the prompt; a kept
+ *    preamble KV is reused and only a suffix is prefilled.
+ *  - same page, section 8: FP8 W8A8 with per-tensor static activation scales
+ *    (amax / 448) from a BF16 calibration run.
+ *  - SGLang-Omni Higgs Audio v3 page, architecture paragraph: the next input
+ *    is the sum of the 8 codebook embeddings of the previous frame.
+ *
+ * Conventions for every call:
+ *  - Return value: HTA_OK (0), HTA_DONE (1, decode only) or a negative
+ *    error code; hta_last_error() gives a message.  Nothing throws.
+ *  - "device" pointers are HIP device addresses (e.g. a torch CUDA tensor's
+ *    data_ptr); "host" pointers are ordinary host memory, read or written
+ *    before the call returns.
+ *  - All GPU work is enqueued on the stream given to hta_create; calls that
+ *    return results to the host synchronise that stream.
+ *  - A context is not thread-safe; use one per thread.
+ *  - The caller owns all device memory (weights, workspace); the library owns
+ *    only its graph objects and a small pinned host staging buffer.
+ *    hta_destroy must run before the caller frees the workspace, because the
+ *    captured graphs reference it.
+ */
+#ifndef HTA_H
+#define HTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  HTA_OK = 0,
+  HTA_DONE = 1,            /* decode: this step completed the utterance (codebook 7 emitted EOS) */
+  HTA_E_ARG = -1,          /* null pointer, size mismatch, bad enum */
+  HTA_E_STATE = -2,        /* call out of order (e.g. decode before load) */
+  HTA_E_CAPACITY = -3,     /* length + P would exceed max_seq, or P > max_prefill */
+  HTA_E_RANGE = -4,        /* token id >= text_vocab or code id >= codebook_size */
+  HTA_E_UNSUPPORTED = -5,  /* device is not gfx950, or a shape the kernels do not cover */
+  HTA_E_HIP = -6,          /* HIP runtime error; message in hta_last_error */
+  HTA_E_TIMEOUT = -7       /* a device-side bounded wait expired (the kernel exited early) */
+};
+
+typedef enum { HTA_BF16 = 0, HTA_FP8_E4M3 = 1 } hta_precision;
+typedef enum { HTA_SRC_F32 = 0, HTA_SRC_BF16 = 1 } hta_src_dtype;
+
+typedef struct {
+  int n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, text_vocab;
+  int n_codebooks;   /* 8 */
+  int codebook_size; /* 1026: codes 0..1023, BOS 1024, EOS 1025 */
+  int bos_id, eos_id;
+  float rope_theta;  /* 1e6 */
+  float rms_eps;     /* 1e-6 */
+  int max_seq;       /* KV capacity in positions */
+  int max_prefill;   /* largest P accepted by one hta_prefill call */
+  int precision;     /* hta_precision */
+} hta_config;
+
+typedef struct hta_ctx hta_ctx;
+
+/* Shape limits the kernels support: head_dim 64 or 128; hidden, q and kv widths
+ * multiples of 64; ffn a multiple of 64; n_codebooks <= 16; codebook_size <= 2048;
+ * n_q_heads a multiple of n_kv_heads with group size <= 8. */
+
+/* Create a context for cfg on the current HIP device, enqueueing on hip_stream
+ * (a hipStream_t, e.g. torch.cuda.current_stream().cuda_stream; NULL = the null
+ * stream).  Fails with HTA_E_UNSUPPORTED on a device other than gfx950 or an
+ * unsupported shape.  *out receives the context. */
+int hta_create(const hta_config* cfg, void* hip_stream, hta_ctx** out);
+
+/* Bytes of device workspace the context needs: packed weights, KV cache
+ * [layer][kv_head][max_seq][head_dim] bf16 x 2, RoPE table, decode state and
+ * scratch.  Usable before hta_create. */
+size_t hta_workspace_bytes(const hta_config* cfg);
+
+/* Bind caller-owned device memory of at least hta_workspace_bytes(cfg) bytes,
+ * 256-byte aligned.  The library never frees it. */
+int hta_bind_workspace(hta_ctx* ctx, void* dev_ptr, size_t bytes);
+
+/* Load weights from device tensors in the fixed order: e_text [Vt][d],
+ * e_aud [C][V][d], then per layer g_attn [d], wq [Hq*hd][d], wk [Hkv*hd][d],
+ * wv [Hkv*hd][d], g_q [hd], g_k [hd], wo [d][Hq*hd], g_mlp [d], wg [F][d],
+ * wu [F][d], wd [d][F]; then g_final [d], w_head [C*V][d]; all row-major,
+ * src_dtype elements (hta_src_dtype).  n_tensors must be 4 + 11*n_layers.
+ * BF16 contexts store projections, embeddings and head in bfloat16 (RNE);
+ * FP8 contexts store projections and head as e4m3 codes with per-row scales
+ * max|row| / 448 (FlashRT page, section 8 and its FP8 notes), embeddings in
+ * bfloat16.  act_scales (host, FP8 only, else NULL): 4*n_layers+1 static
+ * activation scales in site order (per layer: attention input, attention
+ * output, MLP input, down input; then the head input).  The source tensors
+ * may be freed after the call returns. */
+int hta_load_weights(hta_ctx* ctx, const void* const* dev_tensors, int n_tensors, int src_dtype,
+                     const float* act_scales);
+
+/* Append a prompt of P text tokens (host int32) at positions len .. len+P-1 in
+ * one batched pass that writes the KV cache (FlashRT page, section 7); no head
+ * is evaluated.  Errors: HTA_E_RANGE for an id outside [0, text_vocab),
+ * HTA_E_CAPACITY if len + P > max_seq or P > max_prefill. */
+int hta_prefill(hta_ctx* ctx, const int32_t* tokens, int P);
+
+/* One decode frame (FlashRT page, section 5): embed the previous codes (all
+ * BOS for the first frame), run the backbone at position len, the fused head,
+ * the greedy argmax under the delay pattern; write the 8 delayed codes of this
+ * step to codes_out (host).  Returns HTA_OK, or HTA_DONE when this step
+ * completed the utterance; later calls keep returning all-EOS frames with the
+ * same work.  HTA_E_CAPACITY when len == max_seq. */
+int hta_decode_frame(hta_ctx* ctx, int32_t* codes_out);
+
+/* n decode frames back to back with one device-to-host copy at the end;
+ * codes_out (host) receives n*C codes; *n_done (may be NULL) receives the
+ * number of steps that ended in the done state. */
+int hta_decode_frames(hta_ctx* ctx, int n, int32_t* codes_out, int* n_done);
+
+/* Start a new utterance: keep the KV of positions [0, keep_len) (prefix reuse,
+ * FlashRT page, section 4) and reset the delay state.  keep_len = 0 is a cold
+ * start; keep_len must not exceed the current length. */
+int hta_reset(hta_ctx* ctx, int keep_len);
+
+/* Teacher forcing: the next frame embeds codes_in (host, C codes each in
+ * [0, codebook_size)) instead of the last chosen codes; the EOC bookkeeping
+ * follows the forced code of codebook 0. */
+int hta_force_codes(hta_ctx* ctx, const int32_t* codes_in);
+
+/* Read device state for tests: tap HTA_TAP_HIDDEN -> float32 [d] final
+ * residual of the last frame; HTA_TAP_LOGITS -> float32 [C*V] raw logits of the
+ * last frame; HTA_TAP_STATE -> int32 [4 + 2*C] {len, t, eoc, done, prev[C],
+ * codes[C]}; HTA_TAP_KV -> bf16 bits [2][Hkv][n][hd] of layer `layer`, n = the
+ * number of positions the buffer holds (bytes / (4*Hkv*hd), at most max_seq);
+ * HTA_TAP_AMAX -> float32 [4L+1] recorded activation maxima; HTA_TAP_PREFILL_HIDDEN
+ * -> float32 [P][d] residual after the last layer of the last prefill;
+ * HTA_TAP_W_QKV -> packed q/k/v rows of `layer` ([Hq*hd + 2*Hkv*hd][d], bf16 bits
+ * or e4m3 codes); HTA_TAP_S_QKV -> their float32 FP8 row scales;
+ * HTA_TAP_W_GU / HTA_TAP_S_GU -> the packed gate/up rows (interleaved
+ * gate_0, up_0, gate_1, ...) and scales. */
+enum { HTA_TAP_HIDDEN = 0, HTA_TAP_LOGITS = 1, HTA_TAP_STATE = 2, HTA_TAP_KV = 3, HTA_TAP_AMAX = 4,
+       HTA_TAP_PREFILL_HIDDEN = 5, HTA_TAP_W_QKV = 6, HTA_TAP_S_QKV = 7, HTA_TAP_W_GU = 8, HTA_TAP_S_GU = 9 };
+int hta_read_tap(hta_ctx* ctx, int tap, int layer, void* host_out, size_t bytes);
+
+/* FP8 calibration on a BF16 context (FlashRT page, section 8: a short BF16
+ * free run of a fixed prompt, scale = amax / 448): reset, prefill the P
+ * calibration tokens, decode n_frames frames (fed with forced_codes
+ * [n_frames][C] when not NULL, else greedy), recording max |x| at every
+ * activation site; writes 4*n_layers+1 scales (host) and leaves the context
+ * reset to length 0. */
+int hta_calibrate(hta_ctx* ctx, const int32_t* tokens, int P, int n_frames, const int32_t* forced_codes,
+                  float* scales_out);
+
+/* One decoder layer for tests and per-layer timing: set layer `layer`'s KV
+ * length to kv_len - 1 from k_init/v_init (device bf16 [Hkv][kv_len-1][hd],
+ * NULL to keep the cache), then run the decode step of that layer on h_io
+ * (device float32 [d], updated in place) at position kv_len - 1.  Uses the
+ * same kernels as the frame. */
+int hta_layer_step(hta_ctx* ctx, int layer, int kv_len, const void* k_init, const void* v_init, void* h_io);
+
+/* Un-delay (host only): frames[f][k] = step_codes[f+k][k] for f < n, with
+ * n = EOC step if codebook 0 emitted EOS, else T - (C - 1); frames_out needs
+ * room for T*C codes; *n_frames receives n. */
+int hta_undelay(const int32_t* step_codes, int T, int n_codebooks, int eos_id, int32_t* frames_out, int* n_frames);
+
+/* Options: HTA_OPT_USE_GRAPH (default 1) replays the captured position-agnostic
+ * frame graph; 0 launches the same kernels one by one (for tests that compare
+ * the two). */
+enum { HTA_OPT_USE_GRAPH = 0 };
+int hta_set_option(hta_ctx* ctx, int option, int value);
+
+void hta_destroy(hta_ctx* ctx);
+const char* hta_last_error(const hta_ctx* ctx);
+const char* hta_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HTA_H */

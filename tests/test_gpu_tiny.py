@@ -1,0 +1,280 @@
+"""GPU parity of the whole decode path on the tiny backbone (2 layers, hidden
+256, GQA 4q/2kv, head_dim 64, FFN 768, 8 x 1026 head) against the CPU oracle,
+plus the exact checks: weight packing, delay bookkeeping, KV slots, graph
+replay == eager launches, determinism, prefix reuse and error codes."""
+import numpy as np
+import pytest
+
+import synthetic as S
+from autoregressive_codebook_tts_amd import hta
+from gpu_common import (COS_MIN, HIDDEN_TOL, cosines, gpu_context, id_agreement, rel_l2, teacher_forced_run,
+                        tiny_weights)
+from oracle import numerics as nx
+from oracle.model import OracleModel, calibrate
+
+pytestmark = pytest.mark.gpu
+SH = S.TINY
+
+
+@pytest.fixture(scope="module")
+def w():
+    return tiny_weights()
+
+
+@pytest.fixture(scope="module")
+def prompt():
+    return S.token_ids(S.SEEDS["tiny_prompt"], 8, SH.text_vocab)
+
+
+@pytest.fixture(scope="module")
+def oracle_scales(w):
+    calib = S.token_ids(S.SEEDS["calib_prompt"], 16, SH.text_vocab)
+    scales, amax, codes = calibrate(SH, w, calib, 16)
+    return scales, amax, codes, calib
+
+
+# ----------------------------------------------------------------------------- weight packing (exact)
+def test_bf16_packing_is_rne_of_source(w):
+    ctx = gpu_context(SH, w, "bf16")
+    for layer in range(SH.n_layers):
+        p = f"layers.{layer}."
+        qkv = np.concatenate([w[p + "wq"], w[p + "wk"], w[p + "wv"]], axis=0)
+        ref = (nx.round_bf16(qkv).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(ctx.tap_packed(layer, "qkv"), ref)
+        gu = np.empty((2 * SH.ffn, SH.hidden), np.float32)
+        gu[0::2], gu[1::2] = w[p + "wg"], w[p + "wu"]
+        ref = (nx.round_bf16(gu).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(ctx.tap_packed(layer, "gu"), ref)
+    ctx.close()
+
+
+def test_fp8_packing_matches_oracle_quantiser(w, oracle_scales):
+    ctx = gpu_context(SH, w, "fp8", act_scales=oracle_scales[0])
+    for layer in range(SH.n_layers):
+        p = f"layers.{layer}."
+        for which, parts in (("qkv", [w[p + "wq"], w[p + "wk"], w[p + "wv"]]), ("gu", None)):
+            if which == "gu":
+                src = np.empty((2 * SH.ffn, SH.hidden), np.float32)
+                src[0::2], src[1::2] = w[p + "wg"], w[p + "wu"]
+            else:
+                src = np.concatenate(parts, axis=0)
+            q, s = nx.quantize_weight_rows(src)
+            assert np.array_equal(ctx.tap_packed(layer, "s_" + which), s)
+            assert np.array_equal(ctx.tap_packed(layer, which), nx.e4m3_encode(q))
+    ctx.close()
+
+
+# ----------------------------------------------------------------------------- teacher-forced parity
+def test_tiny_bf16_teacher_forced(w, prompt):
+    recs, _ = teacher_forced_run(SH, w, prompt, 16, "bf16", oracle_modes=("E", "S"))
+    worst_rel, worst_cos = 0.0, 1.0
+    for rec in recs:
+        worst_rel = max(worst_rel, rel_l2(rec["gpu"]["hidden"], rec["E"]["hidden"]))
+        worst_cos = min(worst_cos, cosines(rec["gpu"]["logits"], rec["E"]["logits"]).min())
+    print(f"tiny bf16: worst hidden rel {worst_rel:.3e}, worst logits cos {worst_cos:.6f}")
+    assert worst_rel <= HIDDEN_TOL["bf16"]
+    assert worst_cos >= COS_MIN
+    n, bad = id_agreement(SH, recs, "E")
+    print(f"tiny bf16 ids: {n} robust decisions, {len(bad)} mismatches {bad[:5]}")
+    assert n > 50 and not bad
+
+
+def test_tiny_fp8_teacher_forced(w, prompt, oracle_scales):
+    """FP8 is gated against the storage-faithful FP8 oracle (the quantised model the path
+    computes); its distance to the exact model is W8A8 quantisation error, reported here."""
+    scales = oracle_scales[0]
+    recs, _ = teacher_forced_run(SH, w, prompt, 16, "fp8", act_scales=scales, oracle_modes=("S", "E"))
+    rel_s = max(rel_l2(r["gpu"]["hidden"], r["S"]["hidden"]) for r in recs)
+    cos_s = min(cosines(r["gpu"]["logits"], r["S"]["logits"]).min() for r in recs)
+    rel_e = max(rel_l2(r["gpu"]["hidden"], r["E"]["hidden"]) for r in recs)
+    cos_e = min(cosines(r["gpu"]["logits"], r["E"]["logits"]).min() for r in recs)
+    q_rel = max(rel_l2(r["S"]["hidden"], r["E"]["hidden"]) for r in recs)
+    print(f"tiny fp8: hidden rel vs fp8 oracle {rel_s:.3e} (cos {cos_s:.6f}); vs exact {rel_e:.3e} "
+          f"(cos {cos_e:.6f}); oracle fp8 vs exact {q_rel:.3e}")
+    assert rel_s <= HIDDEN_TOL["fp8"]
+    assert cos_s >= COS_MIN
+    # the GPU is no further from the exact model than the quantised oracle is, up to rounding noise
+    assert rel_e <= q_rel + HIDDEN_TOL["fp8"]
+    n, bad = id_agreement(SH, recs, "S")
+    print(f"tiny fp8 ids vs fp8 oracle: {n} robust decisions, {len(bad)} mismatches {bad[:5]}")
+    assert n > 50 and not bad
+
+
+def test_calibration_matches_oracle(w, oracle_scales):
+    scales, amax, codes, calib = oracle_scales
+    ctx = gpu_context(SH, w, "bf16")
+    gpu_scales = ctx.calibrate(calib, 16, forced_codes=codes)
+    rel = np.abs(gpu_scales.astype(np.float64) - scales) / scales
+    print(f"calibration: max per-site rel diff {rel.max():.3e}")
+    assert rel.max() <= 1e-2
+    # calibration leaves the context cold and reusable
+    st = ctx.tap_state()
+    assert st["len"] == 0 and st["t"] == 0
+    ctx.close()
+
+
+# ----------------------------------------------------------------------------- exact structure
+def _run(ctx, prompt, n, force=None):
+    ctx.reset(0)
+    ctx.prefill(prompt)
+    out = []
+    for f in range(n):
+        c, d = ctx.decode_frame()
+        out.append((c.copy(), d, ctx.tap_hidden().copy(), ctx.tap_logits().copy()))
+        if force is not None:
+            ctx.force_codes(force[f])
+    return out
+
+
+def test_graph_replay_equals_eager_and_is_deterministic(w, prompt):
+    ctx = gpu_context(SH, w, "bf16")
+    a = _run(ctx, prompt, 12)
+    b = _run(ctx, prompt, 12)
+    ctx.set_option(hta.OPT_USE_GRAPH, 0)
+    c = _run(ctx, prompt, 12)
+    ctx.close()
+    for x, y, z in zip(a, b, c):
+        assert np.array_equal(x[0], y[0]) and np.array_equal(x[0], z[0])
+        assert np.array_equal(x[2], y[2]) and np.array_equal(x[2], z[2])
+        assert np.array_equal(x[3], y[3]) and np.array_equal(x[3], z[3])
+
+
+def test_decode_frames_equals_single_frames(w, prompt):
+    ctx = gpu_context(SH, w, "bf16")
+    singles = np.array([x[0] for x in _run(ctx, prompt, 10)])
+    ctx.reset(0)
+    ctx.prefill(prompt)
+    batch, _ = ctx.decode_frames(10)
+    ctx.close()
+    assert np.array_equal(singles, batch)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp8"])
+def test_prefix_reuse_is_bit_identical(w, oracle_scales, precision):
+    pre = S.token_ids(S.SEEDS["preamble"], 64, SH.text_vocab)
+    suf = S.token_ids(S.SEEDS["suffix_base"], 16, SH.text_vocab)
+    other = S.token_ids(S.SEEDS["suffix_base"] + 1, 16, SH.text_vocab)
+    sc = oracle_scales[0] if precision == "fp8" else None
+    ctx = gpu_context(SH, w, precision, max_prefill=128, act_scales=sc)
+    cold = _run(ctx, np.concatenate([pre, suf]), 8)
+    k_cold = [ctx.tap_kv(l, 80) for l in range(SH.n_layers)]
+    # warm: preamble once, an unrelated request, then reuse the preamble's KV
+    ctx.reset(0)
+    ctx.prefill(pre)
+    ctx.prefill(other)
+    ctx.decode_frames(3)
+    ctx.reset(64)
+    ctx.prefill(suf)
+    k_warm = [ctx.tap_kv(l, 80) for l in range(SH.n_layers)]
+    warm = []
+    for f in range(8):
+        c, d = ctx.decode_frame()
+        warm.append((c.copy(), d, ctx.tap_hidden().copy(), ctx.tap_logits().copy()))
+    ctx.close()
+    for (ka, va), (kb, vb) in zip(k_cold, k_warm):
+        assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+    for x, y in zip(cold, warm):
+        assert np.array_equal(x[0], y[0])
+        assert np.array_equal(x[2], y[2])
+        assert np.array_equal(x[3], y[3])
+
+
+def test_kv_slots_exact_and_untouched_beyond_length(w, prompt):
+    ctx = gpu_context(SH, w, "bf16", max_seq=64, max_prefill=16, fill_byte=0x7F)
+    ctx.prefill(prompt)
+    ref = OracleModel(SH, w, "bf16", "S", max_seq=64)
+    ref.prefill(prompt)
+    for f in range(5):
+        codes, _ = ref.decode_frame()
+        ctx.decode_frame()
+        ctx.force_codes(codes)
+        ref.force_codes(codes)
+    L = 13
+    assert ctx.tap_state()["len"] == L
+    for layer in range(SH.n_layers):
+        k_all, v_all = ctx.tap_kv(layer, 64)
+        k_f = nx.bf16_bits_to_float(k_all)
+        v_f = nx.bf16_bits_to_float(v_all)
+        # written slots: the oracle's K/V (stored in bf16) to within rounding
+        ko = ref.k_cache[layer, :L].transpose(1, 0, 2)
+        vo = ref.v_cache[layer, :L].transpose(1, 0, 2)
+        assert rel_l2(k_f[:, :L], ko) < 1e-2 and rel_l2(v_f[:, :L], vo) < 1e-2
+        # every slot at or beyond the length still holds the sentinel
+        assert np.all(k_all[:, L:] == 0x7F7F) and np.all(v_all[:, L:] == 0x7F7F)
+    ctx.close()
+
+
+def test_forced_eos_weight_set_stops_at_step_zero(w):
+    w2 = dict(w)
+    head = w2["w_head"].copy()
+    head[SH.eos_id] *= 100.0  # EOS row of codebook 0
+    w2["w_head"] = head
+    ctx = gpu_context(SH, w2, "bf16")
+    ctx.prefill(S.token_ids(3, 4, SH.text_vocab))
+    steps = []
+    for t in range(12):
+        c, done = ctx.decode_frame()
+        steps.append(c.copy())
+        for k in range(SH.n_codebooks):
+            assert c[k] == (SH.eos_id if k <= t else SH.bos_id)
+        assert done == (t >= 7)
+    st = ctx.tap_state()
+    assert st["eoc"] == 0 and st["done"] == 1 and st["t"] == 12
+    assert hta.undelay(np.array(steps)).shape == (0, SH.n_codebooks)
+    ctx.close()
+
+
+def test_teacher_forced_eoc_bookkeeping(w, prompt):
+    """Forcing EOS into codebook 0 after step 2 makes step 2 the EOC step; the GPU
+    bookkeeping follows the oracle's DelayState step for step."""
+    from oracle.delay import DelayState
+
+    ctx = gpu_context(SH, w, "bf16")
+    ctx.prefill(prompt)
+    ref = DelayState()
+    forced = [[5, 6, 7, 8, 9, 10, 11, 12]] * 2 + [[SH.eos_id, 1, 2, 3, 4, 5, 6, 7]]
+    for t in range(3):
+        ctx.decode_frame()
+        ref.begin_frame()
+        ref.finish(np.zeros(8, np.int64))
+        ctx.force_codes(forced[t])
+        ref.prev = np.array(forced[t])
+    for t in range(3, 12):
+        c, done = ctx.decode_frame()
+        ref.begin_frame()
+        lg = ctx.tap_logits()
+        expect = ref.choose(lg.astype(np.float64))
+        assert np.array_equal(c, expect), (t, c, expect)
+        assert done == ref.finish(expect)
+        assert ctx.tap_state()["eoc"] == 2
+    # step 3: codebooks 0 and 1 forced to EOS, 2 and 3 free, 4.. still BOS
+    ctx.close()
+
+
+def test_error_codes(w, prompt):
+    ctx = hta.Hta(SH, "bf16", max_seq=16, max_prefill=8)
+    with pytest.raises(hta.HtaError) as e:
+        ctx.prefill(prompt)
+    assert e.value.code == -2  # HTA_E_STATE: no weights
+    tensors, src = hta.weights_to_device(w, SH.n_layers)
+    ctx.load_weights(tensors, src)
+    with pytest.raises(hta.HtaError) as e:
+        ctx.prefill(np.arange(9))
+    assert e.value.code == -3  # P > max_prefill
+    with pytest.raises(hta.HtaError) as e:
+        ctx.prefill(np.array([0, SH.text_vocab]))
+    assert e.value.code == -4
+    ctx.prefill(prompt)
+    with pytest.raises(hta.HtaError) as e:
+        ctx.force_codes([0, 0, 0, 0, 0, 0, 0, SH.codebook_size])
+    assert e.value.code == -4
+    with pytest.raises(hta.HtaError) as e:
+        ctx.reset(9)
+    assert e.value.code == -1
+    ctx.decode_frames(8)
+    with pytest.raises(hta.HtaError) as e:
+        ctx.decode_frame()
+    assert e.value.code == -3  # KV full
+    ctx.reset(0)
+    ctx.prefill(prompt)
+    ctx.close()
