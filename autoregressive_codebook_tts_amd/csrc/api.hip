@@ -68,12 +68,21 @@ Layout make_layout(const hta_config& c) {
   if (splits > 64) splits = 64;
   if (splits < 1) splits = 1;
   L.attn_splits = splits;
+  const int part_splits = 64;  // the persistent kernel may use up to 64 splits
   L.off_h = take(d * 4);
   L.off_qkv = take(W * 4);
-  L.off_attn_part = take((size_t)c.n_q_heads * splits * (hd + 2) * 4);
+  L.off_attn_part = take((size_t)c.n_q_heads * part_splits * (hd + 2) * 4);
   L.off_o_act = take(qd * 2);
   L.off_a_act = take(F * 2);
   L.off_logits = take(CV * 4);
+  L.off_layer_table = take((size_t)c.n_layers * sizeof(LayerW));
+  L.off_xh = take(d * 8);
+  L.off_xqkv = take(W * 8);
+  L.off_xo = take(qd * 4);
+  L.off_xa = take(F * 4);
+  L.off_xpart = take((size_t)c.n_q_heads * part_splits * (hd + 2) * 8);
+  L.off_xlogits = take(CV * 8);
+  L.off_sync = take(1024 * 4);
   L.off_tok = take(Pm * 4);
   L.off_x = take(Pm * d * 4);
   L.off_u = take(Pm * (d > F ? d : F) * 2);
@@ -120,7 +129,8 @@ static bool shape_ok(const hta_config& f, std::string* why) {
   if (f.text_vocab < 1) return bad("text_vocab must be positive");
   if (f.max_seq < 2 || f.max_prefill < 1 || f.max_prefill > f.max_seq) return bad("bad max_seq / max_prefill");
   if (f.precision != HTA_BF16 && f.precision != HTA_FP8_E4M3) return bad("unknown precision");
-  if (f.hidden > 16384 || f.ffn > 16384 || f.n_q_heads * f.head_dim > 16384) return bad("widths above 16384 exceed the GEMV LDS budget");
+  if (f.hidden > 5120 || f.ffn > 10240 || f.n_q_heads * f.head_dim > 10240)
+    return bad("hidden above 5120 or ffn / q width above 10240 exceed the GEMV prologue budget");
   return true;
 }
 
@@ -165,6 +175,14 @@ static void set_pointers(Ctx& c) {
   c.o_act = w + L.off_o_act;
   c.a_act = w + L.off_a_act;
   c.logits = reinterpret_cast<float*>(w + L.off_logits);
+  c.d_layers = reinterpret_cast<LayerW*>(w + L.off_layer_table);
+  c.x_h = reinterpret_cast<uint64_t*>(w + L.off_xh);
+  c.x_qkv = reinterpret_cast<uint64_t*>(w + L.off_xqkv);
+  c.x_o = reinterpret_cast<uint32_t*>(w + L.off_xo);
+  c.x_a = reinterpret_cast<uint32_t*>(w + L.off_xa);
+  c.x_part = reinterpret_cast<uint64_t*>(w + L.off_xpart);
+  c.x_logits = reinterpret_cast<uint64_t*>(w + L.off_xlogits);
+  c.sync = reinterpret_cast<unsigned*>(w + L.off_sync);
   c.tok = reinterpret_cast<int32_t*>(w + L.off_tok);
   c.px = reinterpret_cast<float*>(w + L.off_x);
   c.pu = w + L.off_u;
@@ -181,7 +199,15 @@ static void drop_graph(Ctx& c) {
   c.frame_graph = nullptr;
 }
 
+// Zero the persistent kernel's tagged exchange words and its launch counter / abort flag.
+static hipError_t clear_exchange(Ctx& c) {
+  const Layout& L = c.lay;
+  const size_t n = (L.off_sync + 1024 * 4 - L.off_xh) / 4;
+  return launch_fill_u32(c.ws + L.off_xh, 0u, n, c.stream);
+}
+
 static hipError_t enqueue_frame(Ctx& c, bool record) {
+  if (!record && c.use_persistent && c.frame_ok) return launch_frame_persistent(c);
   hipError_t e = launch_frame_begin(c);
   if (e != hipSuccess) return e;
   for (int l = 0; l < c.cfg.n_layers; ++l)
@@ -240,6 +266,9 @@ int hta_create(const hta_config* cfg, void* hip_stream, hta_ctx** out) {
   }
   c.lay = make_layout(c.cfg);
   c.layers = new LayerW[c.cfg.n_layers]();
+  if (frame_setup(c) == hipSuccess && frame_max_packets(c.cfg, c.frame_blocks) <= frame_part_capacity())
+    c.frame_ok = true;
+  (void)hipGetLastError();
   c.h_stage_elems = (size_t)c.cfg.max_seq * c.cfg.n_codebooks;
   if ((size_t)c.cfg.max_prefill > c.h_stage_elems) c.h_stage_elems = c.cfg.max_prefill;
   if (hipHostMalloc((void**)&c.h_stage, c.h_stage_elems * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
@@ -280,6 +309,7 @@ int hta_bind_workspace(hta_ctx* x, void* dev_ptr, size_t bytes) {
   HIPCK(launch_fill_u32(c.amax, 0u, nsites, c.stream), "fill");
   HIPCK(launch_fill_u32(c.act_scales, 0x3f800000u, nsites, c.stream), "fill");
   HIPCK(launch_fill_u32(c.state, 0u, sizeof(DevState) / 4, c.stream), "fill");
+  HIPCK(clear_exchange(c), "fill");
   HIPCK(launch_reset_state(c, 0), "reset");
   HIPCK(hipStreamSynchronize(c.stream), "sync");
   c.len = 0;
@@ -331,6 +361,7 @@ int hta_load_weights(hta_ctx* x, const void* const* t, int n, int src_dtype, con
   HIPCK(launch_copy_f32(c.g_final, T[0], src_dtype, d, s), "gain");
   HIPCK(launch_pack_rows(c.w_head, 0, 1, T[1], src_dtype, CV, d, q8, c.s_head, s), "pack head");
   HIPCK(hipMemcpyAsync(c.act_scales, c.h_scales.data(), nsites * 4, hipMemcpyHostToDevice, s), "scales");
+  HIPCK(hipMemcpyAsync(c.d_layers, c.layers, (size_t)f.n_layers * sizeof(LayerW), hipMemcpyHostToDevice, s), "layer table");
   HIPCK(hipStreamSynchronize(s), "load sync");
   c.weights_loaded = true;
   return HTA_OK;
@@ -384,7 +415,16 @@ static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out) {
   const int t0 = c.t;
   HIPCK(hipMemcpyAsync(c.h_stage, c.hist + (size_t)t0 * C, (size_t)n * C * 4, hipMemcpyDeviceToHost, c.stream), "codes");
   HIPCK(hipMemcpyAsync(c.h_state, c.state, sizeof(DevState), hipMemcpyDeviceToHost, c.stream), "state");
+  unsigned aborted = 0;
+  if (c.use_persistent && c.frame_ok)
+    HIPCK(hipMemcpyAsync(&aborted, c.sync + 64, sizeof(unsigned), hipMemcpyDeviceToHost, c.stream), "status");
   HIPCK(hipStreamSynchronize(c.stream), "decode sync");
+  if (aborted) {
+    // a bounded wait expired: clear the exchange words so the next launch starts clean
+    HIPCK(clear_exchange(c), "fill");
+    HIPCK(hipStreamSynchronize(c.stream), "sync");
+    return fail(c, HTA_E_TIMEOUT, "a bounded wait of the frame kernel expired; the utterance must be reset");
+  }
   std::memcpy(codes_out, c.h_stage, (size_t)n * C * 4);
   c.len += n;
   c.t += n;
@@ -565,11 +605,57 @@ int hta_undelay(const int32_t* steps, int T, int C, int eos, int32_t* frames_out
   return HTA_OK;
 }
 
+int hta_time_kernels(hta_ctx* x, int n_frames, float* avg_us, int n_classes) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  int r = ready(c);
+  if (r) return r;
+  if (n_frames <= 0 || !avg_us || n_classes <= 0) return fail(c, HTA_E_ARG, "bad arguments");
+  if (c.len + n_frames > c.cfg.max_seq) return fail(c, HTA_E_CAPACITY, "KV cache full");
+  const int per_frame = 2 * (3 + 5 * c.cfg.n_layers);
+  std::vector<hipEvent_t> ev(per_frame);
+  std::vector<int> cls(per_frame / 2);
+  for (auto& e : ev) HIPCK(hipEventCreate(&e), "hipEventCreate");
+  double sum[HTA_K_COUNT] = {0};
+  long cnt[HTA_K_COUNT] = {0};
+  int rc = HTA_OK;
+  for (int fr = 0; fr < n_frames && rc == HTA_OK; ++fr) {
+    c.tev = ev.data();
+    c.tev_cap = per_frame;
+    c.tev_next = 0;
+    c.tev_class = cls.data();
+    hipError_t e = enqueue_frame(c, false);
+    const int used = c.tev_next;
+    c.tev = nullptr;
+    if (e != hipSuccess) { rc = hip_fail(c, e, "timed frame"); break; }
+    if ((e = hipStreamSynchronize(c.stream)) != hipSuccess) { rc = hip_fail(c, e, "sync"); break; }
+    for (int i = 0; i < used / 2; ++i) {
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) == hipSuccess && cls[i] >= 0 && cls[i] < HTA_K_COUNT) {
+        sum[cls[i]] += ms * 1000.0;
+        cnt[cls[i]] += 1;
+      }
+    }
+    c.len += 1;
+    c.t += 1;
+  }
+  for (auto& e : ev) (void)hipEventDestroy(e);
+  for (int k = 0; k < n_classes; ++k) avg_us[k] = (k < HTA_K_COUNT && cnt[k]) ? (float)(sum[k] / cnt[k]) : 0.0f;
+  return rc;
+}
+
 int hta_set_option(hta_ctx* x, int option, int value) {
   if (!x) return HTA_E_ARG;
   Ctx& c = x->c;
   if (option == HTA_OPT_USE_GRAPH) {
     c.use_graph = value != 0;
+    return HTA_OK;
+  }
+  if (option == HTA_OPT_PERSISTENT) {
+    const bool v = value != 0;
+    if (v && !c.frame_ok) return fail(c, HTA_E_UNSUPPORTED, "the persistent frame kernel does not fit this device");
+    if (v != c.use_persistent) drop_graph(c);
+    c.use_persistent = v;
     return HTA_OK;
   }
   return fail(c, HTA_E_ARG, "unknown option");

@@ -23,11 +23,15 @@ __global__ __launch_bounds__(256) void k_frame_begin(const uint16_t* __restrict_
   }
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= d) return;
+  int code[kMaxCodebooks];
+#pragma unroll
+  for (int c = 0; c < kMaxCodebooks; ++c) code[c] = c < C ? st->prev[c] : 0;
+  float v[kMaxCodebooks];
+#pragma unroll
+  for (int c = 0; c < kMaxCodebooks; ++c) v[c] = c < C ? bf16_to_f32(e_aud[((size_t)c * V + code[c]) * d + k]) : 0.0f;
   float s = 0.0f;
-  for (int c = 0; c < C; ++c) {
-    const int code = st->prev[c];
-    s += bf16_to_f32(e_aud[((size_t)c * V + code) * d + k]);
-  }
+#pragma unroll
+  for (int c = 0; c < kMaxCodebooks; ++c) s += v[c];  // codebook order
   h[k] = s;
 }
 
@@ -88,7 +92,12 @@ __device__ __forceinline__ float dot16(const uint4& w, const float* __restrict__
   return s;
 }
 
-template <int P, int ROWS, int PRO, int EPI>
+// Each wave owns ROWS consecutive rows and issues every 16-byte weight packet of
+// those rows (MAXC packets per row and lane) before the prologue, so the
+// prologue's own loads and reductions overlap the weight stream.
+constexpr int kProMax = 5;  // 16-byte prologue packets per thread (K <= 5120 fp32 / 10240 bf16)
+
+template <int P, int ROWS, int MAXC, int PRO, int EPI>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   extern __shared__ float smem[];
   float* xs = smem;            // [K] activations in GEMV units
@@ -97,68 +106,112 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   __shared__ int sh_arg[kMaxCodebooks];
   const int K = a.K, N = a.N;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nthr = blockDim.x;
+  constexpr int E = WTraits<P>::E;
+  constexpr int CH = kWave * E;
+  const int row0 = (blockIdx.x * (blockDim.x >> 6) + wv) * ROWS;
+  const int nch = (K + CH - 1) / CH;
 
-  // ---- prologue: the input vector in LDS
+  // ---- prologue inputs first (small), so they return ahead of the weights
+  float4 hv[kProMax], gv[kProMax];
+  uint4 xv[kProMax];
+  if (PRO == kProNorm) {
+#pragma unroll
+    for (int p = 0; p < kProMax; ++p) {
+      const int idx = (p * nthr + tid) * 4;
+      if (idx < K) {
+        hv[p] = *reinterpret_cast<const float4*>(a.h + idx);
+        gv[p] = *reinterpret_cast<const float4*>(a.g + idx);
+      }
+    }
+  } else {
+    constexpr int XE = (P == kBF16) ? 8 : 16;  // elements per 16-byte packet
+#pragma unroll
+    for (int p = 0; p < kProMax; ++p) {
+      const int idx = (p * nthr + tid) * XE;
+      if (idx < K) xv[p] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.x_act) + (size_t)idx * WTraits<P>::B);
+    }
+  }
+
+  // ---- the weight stream of this wave
+  uint4 wr[ROWS][MAXC];
+  const uint8_t* wb = static_cast<const uint8_t*>(a.w);
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const int e = c * CH + lane * E;
+    const bool ok = (c < nch) && (e < K);
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int row = row0 + r;
+      if (ok && row < N) wr[r][c] = ld_stream16(wb + ((size_t)row * K + e) * WTraits<P>::B);
+      else wr[r][c] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+
+  // ---- prologue: the input vector in LDS, in GEMV units
   if (PRO == kProNorm) {
     float ss = 0.0f;
-    for (int k = tid; k < K; k += blockDim.x) { const float v = a.h[k]; ss = fmaf(v, v, ss); }
+#pragma unroll
+    for (int p = 0; p < kProMax; ++p) {
+      const int idx = (p * nthr + tid) * 4;
+      if (idx < K) {
+        ss = fmaf(hv[p].x, hv[p].x, ss); ss = fmaf(hv[p].y, hv[p].y, ss);
+        ss = fmaf(hv[p].z, hv[p].z, ss); ss = fmaf(hv[p].w, hv[p].w, ss);
+      }
+    }
     ss = block_sum(ss, red);
     const float rstd = 1.0f / sqrtf(ss / (float)K + a.eps);
     float mx = 0.0f;
-    for (int k = tid; k < K; k += blockDim.x) {
-      const float u = a.h[k] * rstd * a.g[k];
-      mx = fmaxf(mx, fabsf(u));
-      xs[k] = act_round<P>(u, a.in_scale);
+#pragma unroll
+    for (int p = 0; p < kProMax; ++p) {
+      const int idx = (p * nthr + tid) * 4;
+      if (idx < K) {
+        const float u0 = hv[p].x * rstd * gv[p].x, u1 = hv[p].y * rstd * gv[p].y;
+        const float u2 = hv[p].z * rstd * gv[p].z, u3 = hv[p].w * rstd * gv[p].w;
+        mx = fmaxf(fmaxf(mx, fmaxf(fabsf(u0), fabsf(u1))), fmaxf(fabsf(u2), fabsf(u3)));
+        xs[idx] = act_round<P>(u0, a.in_scale);
+        xs[idx + 1] = act_round<P>(u1, a.in_scale);
+        xs[idx + 2] = act_round<P>(u2, a.in_scale);
+        xs[idx + 3] = act_round<P>(u3, a.in_scale);
+      }
     }
     if (a.amax_in != nullptr && blockIdx.x == 0) {
       mx = block_max(mx, red);
       if (tid == 0) record_amax(a.amax_in, mx);
     }
   } else {
-    if (P == kBF16) {
-      const uint16_t* x = static_cast<const uint16_t*>(a.x_act);
-      for (int k = tid; k < K; k += blockDim.x) xs[k] = bf16_to_f32(x[k]);
-    } else {
-      const uint8_t* x = static_cast<const uint8_t*>(a.x_act);
-      for (int k = tid; k < K; k += blockDim.x) xs[k] = e4m3_to_f32(x[k]);
+    constexpr int XE = (P == kBF16) ? 8 : 16;
+#pragma unroll
+    for (int p = 0; p < kProMax; ++p) {
+      const int idx = (p * nthr + tid) * XE;
+      if (idx < K) {
+        const uint32_t ws[4] = {xv[p].x, xv[p].y, xv[p].z, xv[p].w};
+        if (P == kBF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { xs[idx + 2 * q] = bf16lo(ws[q]); xs[idx + 2 * q + 1] = bf16hi(ws[q]); }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[q], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)ws[q], true);
+            xs[idx + 4 * q] = lo[0]; xs[idx + 4 * q + 1] = lo[1]; xs[idx + 4 * q + 2] = hi[0]; xs[idx + 4 * q + 3] = hi[1];
+          }
+        }
+      }
     }
   }
   __syncthreads();
 
-  // ---- main loop: each wave owns ROWS consecutive rows
-  constexpr int E = WTraits<P>::E;
-  constexpr int CH = kWave * E;
-  constexpr int U = (P == kBF16) ? 4 : 2;
-  const int row0 = (blockIdx.x * (blockDim.x >> 6) + wv) * ROWS;
-  const int nch = (K + CH - 1) / CH;
+  // ---- dot products
   float acc[ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) acc[r] = 0.0f;
-  if (row0 < N) {
-    const uint8_t* wb = static_cast<const uint8_t*>(a.w);
-    for (int c0 = 0; c0 < nch; c0 += U) {
-      uint4 wr[ROWS][U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = (c0 + u) * CH + lane * E;
-        const bool ok = (c0 + u < nch) && (e < K);
+  for (int c = 0; c < MAXC; ++c) {
+    const int e = c * CH + lane * E;
+    if ((c < nch) && (e < K)) {
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          const int row = row0 + r;
-          if (ok && row < N)
-            wr[r][u] = ld_stream16(wb + ((size_t)row * K + e) * WTraits<P>::B);
-          else
-            wr[r][u] = make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = (c0 + u) * CH + lane * E;
-        if ((c0 + u < nch) && (e < K)) {
-#pragma unroll
-          for (int r = 0; r < ROWS; ++r) acc[r] += dot16<P>(wr[r][u], xs + e);
-        }
-      }
+      for (int r = 0; r < ROWS; ++r) acc[r] += dot16<P>(wr[r][c], xs + e);
     }
   }
 #pragma unroll
@@ -208,15 +261,22 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   if (!sh_flag) return;
   __threadfence();
   const int nw = blockDim.x >> 6;
+  constexpr int kVPL = 32;  // logits per lane: codebook_size <= 2048
   for (int k = wv; k < a.C; k += nw) {
+    const float* lg = a.out + (size_t)k * a.V;
+    float v[kVPL];
+#pragma unroll
+    for (int q = 0; q < kVPL; ++q) {
+      const int i = q * kWave + lane;
+      v[q] = i < a.V ? lg[i] : -INFINITY;
+    }
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    const float* lg = a.out + (size_t)k * a.V;
-    for (int i = lane; i < a.V; i += kWave) {
-      const bool allowed = (i < a.bos) || (k == 0 && i == a.eos);
-      if (!allowed) continue;
-      const float v = lg[i];
-      if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+#pragma unroll
+    for (int q = 0; q < kVPL; ++q) {
+      const int i = q * kWave + lane;
+      const bool allowed = i < a.V && ((i < a.bos) || (k == 0 && i == a.eos));
+      if (allowed && (v[q] > bv || (v[q] == bv && i < bi))) { bv = v[q]; bi = i; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -293,6 +353,13 @@ __device__ __forceinline__ void norm_rope_head(const float* __restrict__ src, co
   }
 }
 
+// Split-K flash decoding.  Grid (splits, Hkv); block = 4 waves, wave w owns q
+// head j*G + w of the kv head's group.  Keys are cut into `splits` chunks of a
+// whole number of 64-key tiles (the chunk depends only on the length), so
+// only ceil(L / chunk) splits hold keys; the others exit at once.  Each active
+// split stages its K/V tiles in LDS, keeps an online softmax (m, l, o) and
+// writes it; the last active split to finish merges the partials with the
+// log-sum-exp rule and writes the rounded attention output.
 template <int P, int HD>
 __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
   constexpr int H2 = HD / 2;
@@ -310,6 +377,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
   const int L = pos + 1;
   int chunk = (L + a.splits - 1) / a.splits;
   chunk = (chunk + T - 1) / T * T;
+  const int n_active = (L + chunk - 1) / chunk;
+  if (split >= n_active) return;
   const int beg = split * chunk;
   const int end = min(L, beg + chunk);
   const float* cs = a.rope_cos + (size_t)pos * H2;
@@ -320,7 +389,6 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
     // the new key (q/k-norm + RoPE) and value, rounded to the bf16 cache format
     norm_rope_head<HD>(a.qkv + (size_t)a.Hq * HD + (size_t)j * HD, a.g_k, cs, sn, a.eps, lane, kn);
   }
-  __syncthreads();
   if (tid < HD) vn[tid] = round_bf16(a.qkv[(size_t)(a.Hq + a.Hkv) * HD + (size_t)j * HD + tid]);
   __syncthreads();
   uint16_t* kc = a.k_cache + (size_t)j * a.max_seq * HD;
@@ -333,19 +401,32 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
   const float inv_sqrt = 1.0f / sqrtf((float)HD);
   float m = -INFINITY, lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
   for (int t0 = beg; t0 < end; t0 += T) {
-    // stage the K/V tile in LDS (16-byte packets)
     constexpr int SEG = HD / 8;
-    for (int idx = tid; idx < T * SEG; idx += blockDim.x) {
+    constexpr int PER = T * SEG / 256;  // 16-byte packets per thread per tile
+    uint4 kw[PER], vw[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = q * 256 + tid;
+      const int key = idx / SEG, seg = idx % SEG;
+      const int kp = t0 + key;
+      if (kp < end && kp != pos) {
+        kw[q] = *reinterpret_cast<const uint4*>(kc + (size_t)kp * HD + seg * 8);
+        vw[q] = *reinterpret_cast<const uint4*>(vc + (size_t)kp * HD + seg * 8);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int idx = q * 256 + tid;
       const int key = idx / SEG, seg = idx % SEG;
       const int kp = t0 + key;
       float kv[8], vv[8];
       if (kp < end && kp != pos) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(kc + (size_t)kp * HD + seg * 8);
-        const uint4 vw = *reinterpret_cast<const uint4*>(vc + (size_t)kp * HD + seg * 8);
-        kv[0] = bf16lo(kw.x); kv[1] = bf16hi(kw.x); kv[2] = bf16lo(kw.y); kv[3] = bf16hi(kw.y);
-        kv[4] = bf16lo(kw.z); kv[5] = bf16hi(kw.z); kv[6] = bf16lo(kw.w); kv[7] = bf16hi(kw.w);
-        vv[0] = bf16lo(vw.x); vv[1] = bf16hi(vw.x); vv[2] = bf16lo(vw.y); vv[3] = bf16hi(vw.y);
-        vv[4] = bf16lo(vw.z); vv[5] = bf16hi(vw.z); vv[6] = bf16lo(vw.w); vv[7] = bf16hi(vw.w);
+        const uint32_t ks[4] = {kw[q].x, kw[q].y, kw[q].z, kw[q].w}, vs[4] = {vw[q].x, vw[q].y, vw[q].z, vw[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv[2 * e] = bf16lo(ks[e]); kv[2 * e + 1] = bf16hi(ks[e]);
+          vv[2 * e] = bf16lo(vs[e]); vv[2 * e + 1] = bf16hi(vs[e]);
+        }
       } else if (kp == pos && kp < end) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) { kv[e] = kn[seg * 8 + e]; vv[e] = vn[seg * 8 + e]; }
@@ -362,10 +443,13 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
       const int kp = t0 + lane;
       float s = -INFINITY;
       if (kp < end) {
-        float d = 0.0f;
+        float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll 8
-        for (int e = 0; e < HD; ++e) d = fmaf(qs[w][e], Kt[lane][e], d);
-        s = d * inv_sqrt;
+        for (int e = 0; e < HD; e += 2) {
+          d0 = fmaf(qs[w][e], Kt[lane][e], d0);
+          d1 = fmaf(qs[w][e + 1], Kt[lane][e + 1], d1);
+        }
+        s = (d0 + d1) * inv_sqrt;
       }
       mnew = fmaxf(m, wave_max(s));
       const float p = (kp < end) ? __expf(s - mnew) : 0.0f;
@@ -377,7 +461,8 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
     if (w < G) {
       o0 *= scale;
       o1 *= scale;
-      for (int kk = 0; kk < T; ++kk) {
+      const int nk = min(T, end - t0);
+      for (int kk = 0; kk < nk; ++kk) {
         const float p = ps[w][kk];
         if (lane < HD) o0 = fmaf(p, Vt[kk][lane], o0);
         if (HD > 64) o1 = fmaf(p, Vt[kk][(lane + 64) % HD], o1);
@@ -385,6 +470,31 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
       m = mnew;
     }
     __syncthreads();
+  }
+
+  // ---- one active split: no merge needed
+  if (n_active == 1) {
+    if (w < G) {
+      const int h = j * G + w;
+      const float inv = 1.0f / lsum;
+      const float v0 = o0 * inv, v1 = o1 * inv;
+      float mx = (lane < HD) ? fabsf(v0) : 0.0f;
+      if (HD > 64) mx = fmaxf(mx, fabsf(v1));
+      if (P == kBF16) {
+        uint16_t* o = static_cast<uint16_t*>(a.o_act) + (size_t)h * HD;
+        if (lane < HD) o[lane] = (uint16_t)act_encode<P>(v0, a.o_scale);
+        if (HD > 64) o[lane + 64] = (uint16_t)act_encode<P>(v1, a.o_scale);
+      } else {
+        uint8_t* o = static_cast<uint8_t*>(a.o_act) + (size_t)h * HD;
+        if (lane < HD) o[lane] = (uint8_t)act_encode<P>(v0, a.o_scale);
+        if (HD > 64) o[lane + 64] = (uint8_t)act_encode<P>(v1, a.o_scale);
+      }
+      if (a.amax) {
+        mx = wave_max(mx);
+        if (lane == 0) record_amax(a.amax, mx);
+      }
+    }
+    return;
   }
 
   // ---- split partial (m, l, o)
@@ -399,29 +509,40 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
   if (tid == 0) {
     __threadfence();
     const unsigned prev = atomicAdd(a.counters + j, 1u);
-    sh_last = (prev == (unsigned)a.splits - 1) ? 1 : 0;
+    sh_last = (prev == (unsigned)n_active - 1) ? 1 : 0;
   }
   __syncthreads();
   if (!sh_last) return;
   __threadfence();
-  // ---- the last split block of this kv head merges the partials (log-sum-exp)
+  // ---- the last active split of this kv head merges the partials (log-sum-exp)
   if (w < G) {
     const int h = j * G + w;
     const float* pb = a.part + (size_t)h * a.splits * (HD + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) {
-      const float ls = pb[(size_t)s * (HD + 2) + HD + 1];
-      if (ls > 0.0f) M = fmaxf(M, pb[(size_t)s * (HD + 2) + HD]);
-    }
-    float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float* q = pb + (size_t)s * (HD + 2);
-      const float ls = q[HD + 1];
-      if (!(ls > 0.0f)) continue;
-      const float f = __expf(q[HD] - M);
-      den = fmaf(f, ls, den);
-      if (lane < HD) n0 = fmaf(f, q[lane], n0);
-      if (HD > 64) n1 = fmaf(f, q[lane + 64], n1);
+    // lane s holds split s's (m, l); n_active <= splits <= 64
+    const bool has = lane < n_active;
+    const float ms = has ? pb[(size_t)lane * (HD + 2) + HD] : -INFINITY;
+    const float ls = has ? pb[(size_t)lane * (HD + 2) + HD + 1] : 0.0f;
+    const float M = wave_max(ls > 0.0f ? ms : -INFINITY);
+    const float f = (ls > 0.0f) ? __expf(ms - M) : 0.0f;
+    const float den = wave_sum(f * ls);
+    float n0 = 0.0f, n1 = 0.0f;
+    for (int s0 = 0; s0 < n_active; s0 += 8) {
+      float x0[8], x1[8], fs[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sp = s0 + u;
+        fs[u] = __shfl(f, sp < n_active ? sp : 0, kWave);
+        const float* q = pb + (size_t)sp * (HD + 2);
+        x0[u] = (sp < n_active && lane < HD) ? q[lane] : 0.0f;
+        x1[u] = (sp < n_active && HD > 64) ? q[lane + 64] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (s0 + u < n_active) {
+          n0 = fmaf(fs[u], x0[u], n0);
+          n1 = fmaf(fs[u], x1[u], n1);
+        }
+      }
     }
     const float inv = 1.0f / den;
     const float v0 = n0 * inv, v1 = n1 * inv;
@@ -470,20 +591,43 @@ __global__ void k_set_len(DevState* st, int len) {
 }
 
 // ============================================================================ launchers
-template <int P, int ROWS, int PRO, int EPI>
-static hipError_t gemv(const Ctx& c, GemvArgs a) {
+template <int P, int ROWS, int MAXC, int PRO, int EPI>
+static hipError_t gemv_launch(Ctx& c, const GemvArgs& a, int kclass) {
   const int waves = 4;
   const int rows_per_block = waves * ROWS;
   const int grid = (a.N + rows_per_block - 1) / rows_per_block;
   const size_t lds = (size_t)a.K * sizeof(float);
-  hipLaunchKernelGGL((k_gemv<P, ROWS, PRO, EPI>), dim3(grid), dim3(64 * waves), lds, c.stream, a);
+  time_begin(c, kclass);
+  hipLaunchKernelGGL((k_gemv<P, ROWS, MAXC, PRO, EPI>), dim3(grid), dim3(64 * waves), lds, c.stream, a);
+  time_end(c);
   return hipGetLastError();
+}
+
+// Picks the register budget (16-byte packets per row and lane) from K.
+template <int P, int ROWS, int PRO, int EPI>
+static hipError_t gemv(Ctx& c, GemvArgs a, int kclass) {
+  constexpr int CH = kWave * WTraits<P>::E;
+  const int nch = (a.K + CH - 1) / CH;
+  if (nch <= 2) return gemv_launch<P, ROWS, 2, PRO, EPI>(c, a, kclass);
+  if (nch <= 3) return gemv_launch<P, ROWS, 3, PRO, EPI>(c, a, kclass);
+  if (nch <= 5) return gemv_launch<P, ROWS, 5, PRO, EPI>(c, a, kclass);
+  if constexpr (ROWS == 4) {
+    return gemv<P, 2, PRO, EPI>(c, a, kclass);  // wide rows: halve the rows per wave
+  } else {
+    if (nch <= 8) return gemv_launch<P, ROWS, 8, PRO, EPI>(c, a, kclass);
+    if (nch <= 10) return gemv_launch<P, ROWS, 10, PRO, EPI>(c, a, kclass);
+    if (nch <= 19) return gemv_launch<P, ROWS, 19, PRO, EPI>(c, a, kclass);
+    if (nch <= 32) return gemv_launch<P, ROWS, 32, PRO, EPI>(c, a, kclass);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_frame_begin(Ctx& c) {
   const auto& f = c.cfg;
+  time_begin(c, HTA_K_EMBED);
   hipLaunchKernelGGL(k_frame_begin, dim3((f.hidden + 255) / 256), dim3(256), 0, c.stream, c.e_aud, c.state, c.h,
                      f.hidden, f.n_codebooks, f.codebook_size, f.eos_id);
+  time_end(c);
   return hipGetLastError();
 }
 
@@ -504,7 +648,7 @@ static hipError_t layer_decode_p(Ctx& c, int layer, float* h, bool record, int p
     a.w = L.w_qkv; a.w_scale = L.s_qkv; a.N = qd + 2 * kvd; a.K = d;
     a.h = h; a.g = L.g_attn; a.eps = f.rms_eps; a.in_scale = host_act_scale(c, s0);
     a.amax_in = amax ? amax + s0 : nullptr; a.out = c.qkv;
-    if ((e = gemv<P, 4, kProNorm, kEpiStore>(c, a)) != hipSuccess) return e;
+    if ((e = gemv<P, 4, kProNorm, kEpiStore>(c, a, HTA_K_QKV)) != hipSuccess) return e;
   }
   // attention (q/k-norm + RoPE + KV write + split-K + combine)
   {
@@ -515,8 +659,10 @@ static hipError_t layer_decode_p(Ctx& c, int layer, float* h, bool record, int p
     a.amax = amax ? amax + s0 + 1 : nullptr; a.eps = f.rms_eps; a.max_seq = f.max_seq;
     a.Hq = f.n_q_heads; a.Hkv = f.n_kv_heads; a.splits = c.lay.attn_splits; a.pos_override = pos_override;
     dim3 grid(a.splits, f.n_kv_heads);
+    time_begin(c, HTA_K_ATTN);
     if (hd == 128) hipLaunchKernelGGL((k_attn_decode<P, 128>), grid, dim3(256), 0, c.stream, a);
     else hipLaunchKernelGGL((k_attn_decode<P, 64>), grid, dim3(256), 0, c.stream, a);
+    time_end(c);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // h += W_o . o
@@ -524,7 +670,7 @@ static hipError_t layer_decode_p(Ctx& c, int layer, float* h, bool record, int p
     GemvArgs a{};
     a.w = L.w_o; a.w_scale = L.s_o; a.N = d; a.K = qd; a.x_act = c.o_act; a.in_scale = host_act_scale(c, s0 + 1);
     a.out = h;
-    if ((e = gemv<P, 1, kProAct, kEpiResid>(c, a)) != hipSuccess) return e;
+    if ((e = gemv<P, 1, kProAct, kEpiResid>(c, a, HTA_K_O)) != hipSuccess) return e;
   }
   // a = round(silu(W_g . u2) * (W_u . u2)), u2 = round(rmsnorm(h))
   {
@@ -533,14 +679,14 @@ static hipError_t layer_decode_p(Ctx& c, int layer, float* h, bool record, int p
     a.h = h; a.g = L.g_mlp; a.eps = f.rms_eps; a.in_scale = host_act_scale(c, s0 + 2);
     a.amax_in = amax ? amax + s0 + 2 : nullptr;
     a.out_act = c.a_act; a.out_scale = host_act_scale(c, s0 + 3); a.amax_out = amax ? amax + s0 + 3 : nullptr;
-    if ((e = gemv<P, 4, kProNorm, kEpiSilu>(c, a)) != hipSuccess) return e;
+    if ((e = gemv<P, 4, kProNorm, kEpiSilu>(c, a, HTA_K_GATEUP)) != hipSuccess) return e;
   }
   // h += W_d . a
   {
     GemvArgs a{};
     a.w = L.w_d; a.w_scale = L.s_d; a.N = d; a.K = F; a.x_act = c.a_act; a.in_scale = host_act_scale(c, s0 + 3);
     a.out = h;
-    if ((e = gemv<P, 1, kProAct, kEpiResid>(c, a)) != hipSuccess) return e;
+    if ((e = gemv<P, 1, kProAct, kEpiResid>(c, a, HTA_K_DOWN)) != hipSuccess) return e;
   }
   return hipSuccess;
 }
@@ -564,7 +710,7 @@ static hipError_t head_p(Ctx& c, bool record) {
   a.amax_in = record ? c.amax + site : nullptr; a.out = c.logits;
   a.counter = c.counters + 32; a.st = c.state; a.hist = c.hist;
   a.C = f.n_codebooks; a.V = f.codebook_size; a.bos = f.bos_id; a.eos = f.eos_id;
-  return gemv<P, 2, kProNorm, kEpiHead>(c, a);
+  return gemv<P, 2, kProNorm, kEpiHead>(c, a, HTA_K_HEAD);
 }
 
 hipError_t launch_head(Ctx& c, bool record) {

@@ -11,9 +11,24 @@ constexpr float kE4m3Max = 448.0f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Global (address space 1) views of pointers whose address space the compiler
+// cannot infer (e.g. read from a device-side table): they then compile to
+// global_* instead of flat_* accesses, and flat accesses would also count
+// against lgkmcnt, so every LDS wait or barrier would drain the weight stream.
+#define HTA_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ const HTA_GLOBAL T* gp(const T* p) { return (const HTA_GLOBAL T*)p; }
+template <class T>
+__device__ __forceinline__ HTA_GLOBAL T* gpw(T* p) { return (HTA_GLOBAL T*)p; }
+
 // 16-byte streaming load of weight data that is read once per frame.
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  const u32x4 v = __builtin_nontemporal_load(gp(reinterpret_cast<const u32x4*>(p)));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// 16-byte ordinary global load.
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4 v = *gp(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 

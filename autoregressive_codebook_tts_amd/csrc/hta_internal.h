@@ -53,6 +53,7 @@ struct Layout {
   size_t off_rope_cos, off_rope_sin, off_act_scales, off_amax;
   size_t off_state, off_hist, off_counters;
   size_t off_h, off_qkv, off_attn_part, off_o_act, off_a_act, off_logits;
+  size_t off_layer_table, off_xh, off_xqkv, off_xo, off_xa, off_xpart, off_xlogits, off_sync;
   // prefill scratch
   size_t off_tok, off_x, off_u, off_pqkv, off_pq, off_po, off_pgu, off_pa;
   int attn_splits;
@@ -78,7 +79,14 @@ struct Ctx {
   std::string err;
   std::vector<float> h_scales;  // host copy of the activation scales (FP8)
   bool use_graph = true;
+  // per-kernel timing: when set, launchers bracket each kernel with events from this pool
+  hipEvent_t* tev = nullptr;
+  int tev_next = 0, tev_cap = 0;
+  int* tev_class = nullptr;
   bool own_stream = false;
+  bool use_persistent = true;
+  bool frame_ok = false;      // the persistent frame kernel fits this device and shape
+  int frame_blocks = 0, frame_splits = 0;
   // derived device pointers
   LayerW* layers = nullptr;  // host array of n_layers
   uint16_t* e_text = nullptr;
@@ -99,6 +107,15 @@ struct Ctx {
   void* o_act = nullptr;        // [qd]
   void* a_act = nullptr;        // [F]
   float* logits = nullptr;      // [C*V]
+  LayerW* d_layers = nullptr;   // device copy of `layers`
+  // persistent kernel exchange words (value + phase tag)
+  uint64_t* x_h = nullptr;      // [d]
+  uint64_t* x_qkv = nullptr;    // [qd + 2kvd]
+  uint32_t* x_o = nullptr;      // [qd]
+  uint32_t* x_a = nullptr;      // [F]
+  uint64_t* x_part = nullptr;   // [Hq][64][hd + 2]
+  uint64_t* x_logits = nullptr; // [C*V]
+  unsigned* sync = nullptr;     // [0] launch count, [64] abort flag
   int32_t* tok = nullptr;       // [max_prefill]
   float* px = nullptr;          // [Pmax][d]
   void* pu = nullptr;           // [Pmax][max(d, qd, F)] act
@@ -109,6 +126,20 @@ struct Ctx {
   int last_prefill_P = 0;
 };
 
+// Event pair around one kernel launch when per-kernel timing is on (kernel class k).
+inline void time_begin(Ctx& c, int k) {
+  if (c.tev && c.tev_next + 2 <= c.tev_cap) {
+    c.tev_class[c.tev_next / 2] = k;
+    (void)hipEventRecord(c.tev[c.tev_next], c.stream);
+  }
+}
+inline void time_end(Ctx& c) {
+  if (c.tev && c.tev_next + 2 <= c.tev_cap) {
+    (void)hipEventRecord(c.tev[c.tev_next + 1], c.stream);
+    c.tev_next += 2;
+  }
+}
+
 // ---------------------------------------------------------------- launchers (decode.hip)
 hipError_t launch_frame_begin(Ctx& c);
 hipError_t launch_layer_decode(Ctx& c, int layer, float* h, bool record);
@@ -117,6 +148,12 @@ hipError_t launch_head(Ctx& c, bool record);
 hipError_t launch_set_prev(Ctx& c, const int32_t* codes);
 hipError_t launch_reset_state(Ctx& c, int keep_len);
 hipError_t launch_set_len(Ctx& c, int len);
+
+// ---------------------------------------------------------------- persistent frame (frame.hip)
+hipError_t frame_setup(Ctx& c);
+hipError_t launch_frame_persistent(Ctx& c);
+int frame_max_packets(const hta_config& f, int blocks);
+int frame_part_capacity();
 
 // ---------------------------------------------------------------- launchers (prefill.hip)
 hipError_t launch_prefill(Ctx& c, int P, bool record);

@@ -22,6 +22,7 @@ HTA_BF16, HTA_FP8_E4M3 = 0, 1
 HTA_SRC_F32, HTA_SRC_BF16 = 0, 1
 TAP_HIDDEN, TAP_LOGITS, TAP_STATE, TAP_KV, TAP_AMAX, TAP_PREFILL_HIDDEN, TAP_W_QKV, TAP_S_QKV, TAP_W_GU, TAP_S_GU = range(10)
 OPT_USE_GRAPH = 0
+OPT_PERSISTENT = 1
 SITES_PER_LAYER = 4
 
 LAYER_TENSORS = ("g_attn", "wq", "wk", "wv", "g_q", "g_k", "wo", "g_mlp", "wg", "wu", "wd")
@@ -65,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "hta_layer_step": (I, [P, I, I, P, P, P]),
             "hta_undelay": (I, [P, I, I, I, P, P]),
             "hta_set_option": (I, [P, I, I]),
+            "hta_time_kernels": (I, [P, I, P, I]),
             "hta_destroy": (None, [P]),
             "hta_last_error": (ctypes.c_char_p, [P]),
             "hta_version": (ctypes.c_char_p, []),
@@ -188,6 +190,15 @@ class Hta:
     def force_codes(self, codes) -> None:
         c = np.ascontiguousarray(codes, dtype=np.int32)
         self._check(lib().hta_force_codes(self.ctx, _ptr(c)), "hta_force_codes")
+
+    KERNEL_CLASSES = ("embed", "qkv", "attn", "o_proj", "gate_up", "down", "head", "frame")
+
+    def time_kernels(self, n_frames: int) -> dict:
+        """Average device microseconds per launch of each decode kernel class over n_frames
+        eagerly launched frames (events on the context stream)."""
+        out = np.zeros(len(self.KERNEL_CLASSES), np.float32)
+        self._check(lib().hta_time_kernels(self.ctx, n_frames, _ptr(out), out.shape[0]), "hta_time_kernels")
+        return dict(zip(self.KERNEL_CLASSES, out.tolist()))
 
     def set_option(self, option: int, value: int) -> None:
         self._check(lib().hta_set_option(self.ctx, option, value), "hta_set_option")

@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-1 codebook-TTS decode path on one MI355X.
+
+Workload (one "step" = one utterance through the whole hot path): the
+36-layer Qwen3-4B-shaped backbone with the fused 8 x 1026 head in FP8 e4m3
+W8A8 (per-row weight scales, static activation scales calibrated on a seeded
+16-token prompt plus 16 BF16 frames), a P = 13 prompt prefilled in one batched
+pass, then 1017 greedy delay-pattern decode frames (KV 14 -> 1030), each frame
+one replay of the position-agnostic frame graph.  Weights and prompts are
+seeded synthetic draws (no trained checkpoint exists here).
+
+The JSON line reports decode ms/frame (FP8) as the metric, plus BF16 decode
+ms/frame, prefill ms/token, the roofline of the dominant kernel (the gate/up
+GEMV) measured with HIP events on the library's stream, and the CPU oracle
+timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+KV_BYTES_PER_POS = 147456  # 36 layers x 2 (K, V) x 8 kv heads x 128 x 2 bytes
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def frame_bytes(shape, precision: str, kv_len: float) -> float:
+    """Algorithmic HBM bytes of one decode frame: every projection and the head read once,
+    FP8 row scales, norm gains, the 8 embedding rows, and the K/V of kv_len positions."""
+    d, hd, F, L = shape.hidden, shape.head_dim, shape.ffn, shape.n_layers
+    qd, kvd = shape.q_dim, shape.kv_dim
+    per_layer = (qd + 2 * kvd) * d + d * qd + 2 * F * d + d * F
+    head = shape.n_codebooks * shape.codebook_size * d
+    wb = 1 if precision == "fp8" else 2
+    scales = 4 * (L * (qd + 2 * kvd + d + 2 * F + d) + shape.n_codebooks * shape.codebook_size) if precision == "fp8" else 0
+    gains = 4 * (L * (2 * d + 2 * hd) + d)
+    emb = shape.n_codebooks * d * 2
+    kv = kv_len * L * 2 * shape.n_kv_heads * hd * 2
+    return (per_layer * L + head) * wb + scales + gains + emb + kv
+
+
+def gateup_bytes(shape, precision: str) -> float:
+    """Algorithmic bytes of one gate/up GEMV launch: the interleaved [2F][d] weights (+ FP8
+    row scales), the residual input and gains read, the SiLU*mul output written."""
+    d, F = shape.hidden, shape.ffn
+    wb = 1 if precision == "fp8" else 2
+    return 2 * F * d * wb + (2 * F * 4 if precision == "fp8" else 0) + d * 4 * 2 + F * wb
+
+
+def cpu_oracle_baseline(shape, weights, scales, prompt, n_layers_sample=4, n_frames=3):
+    """The CPU oracle (FP8 storage-faithful mode, float32 weight storage) on a sample of
+    the workload: the first n_layers_sample layers plus the head, prefill of the prompt,
+    then n_frames decode frames; ms/frame scaled by 36 / n_layers_sample."""
+    from oracle.model import OracleModel, SITES_PER_LAYER
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    sub = shape.with_layers(n_layers_sample)
+    keep = {k: v for k, v in weights.items()
+            if not k.startswith("layers.") or int(k.split(".")[1]) < n_layers_sample}
+    sc = np.concatenate([scales[: SITES_PER_LAYER * n_layers_sample], scales[-1:]])
+    t0 = time.perf_counter()
+    m = OracleModel(sub, keep, "fp8", "S", act_scales=sc, storage=np.float32, max_seq=len(prompt) + n_frames + 1)
+    t_build = time.perf_counter() - t0
+    m.prefill(prompt)
+    t1 = time.perf_counter()
+    for _ in range(n_frames):
+        m.decode_frame()
+    t2 = time.perf_counter()
+    ms = (t2 - t1) / n_frames * 1e3 * shape.n_layers / n_layers_sample
+    return {"value": round(ms, 2), "unit": "ms/frame", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_frames} FP8 decode frames of the first {n_layers_sample} of 36 layers (+ head) after a "
+                      f"P={len(prompt)} prefill, scaled x{shape.n_layers / n_layers_sample:g}; weight quantisation "
+                      f"({t_build:.1f} s) excluded"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--frames", type=int, default=1017, help="decode frames per FP8 utterance")
+    ap.add_argument("--bf16-frames", type=int, default=256)
+    ap.add_argument("--prompt", type=int, default=13)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--layers", type=int, default=36, help="backbone depth (36 = the benchmark model)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this path runs on one GPU; multi-GPU runs are not part of this build "
+              "(each GPU would run its own independent utterances)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synthetic as S
+    from autoregressive_codebook_tts_amd import hta
+
+    shape = S.QWEN3_4B.with_layers(args.layers)
+    max_seq = args.prompt + args.frames + 8
+    log(f"drawing weights ({shape.n_layers} layers, bf16, seed {S.SEEDS['full_weights']})")
+    w = S.make_weights(shape, S.SEEDS["full_weights"], "bf16")
+    log("uploading weights")
+    tensors, src = hta.weights_to_device(w, shape.n_layers)
+    prompt = S.token_ids(S.SEEDS["full_prompt"], args.prompt, shape.text_vocab)
+    calib = S.token_ids(S.SEEDS["calib_prompt"], 16, shape.text_vocab)
+    extra = {}
+
+    # ---------------------------------------------------------------- BF16 context: calibration + BF16 numbers
+    log("BF16 context: load + FP8 calibration")
+    b_seq = max(max_seq, args.prompt + args.bf16_frames + 8)
+    bctx = hta.Hta(shape, "bf16", max_seq=b_seq, max_prefill=min(512, b_seq))
+    bctx.load_weights(tensors, src)
+    scales = bctx.calibrate(calib, 16)
+    if not args.no_bf16:
+        log("BF16 decode timing")
+        ms_b = []
+        for i in range(args.warmup + args.steps):
+            bctx.reset(0)
+            bctx.prefill(prompt)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(bctx.stream)
+            bctx.decode_frames(args.bf16_frames)
+            e1.record(bctx.stream)
+            e1.synchronize()
+            if i >= args.warmup:
+                ms_b.append(e0.elapsed_time(e1) / args.bf16_frames)
+        extra["decode_ms_per_frame_bf16"] = round(statistics.mean(ms_b), 4)
+        kv_mean = args.prompt + (args.bf16_frames + 1) / 2
+        extra["frame_hbm_frac_bf16"] = round(frame_bytes(shape, "bf16", kv_mean) / (extra["decode_ms_per_frame_bf16"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        extra["prefill_ms_per_token_bf16_p13"] = round(_prefill_ms(bctx, prompt) / len(prompt), 4)
+        bctx.reset(0)
+        bctx.prefill(prompt)
+        extra["kernel_us_bf16"] = {k: round(v, 2) for k, v in bctx.time_kernels(16).items() if v > 0}
+    bctx.close()
+    del bctx
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- FP8 context: the timed workload
+    log("FP8 context: load")
+    ctx = hta.Hta(shape, "fp8", max_seq=max_seq, max_prefill=min(512, max_seq))
+    ctx.load_weights(tensors, src, act_scales=scales)
+    del tensors
+    torch.cuda.empty_cache()
+    log(f"FP8 timed region: {args.warmup} warmup + {args.steps} steps of prefill {args.prompt} + {args.frames} frames")
+    dec_ms = []
+    for i in range(args.warmup):
+        ctx.reset(0)
+        ctx.prefill(prompt)
+        ctx.decode_frames(args.frames)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ctx.reset(0)
+        ctx.prefill(prompt)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(ctx.stream)
+        codes, done = ctx.decode_frames(args.frames)
+        e1.record(ctx.stream)
+        e1.synchronize()
+        dec_ms.append(e0.elapsed_time(e1) / args.frames)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_frame = statistics.mean(dec_ms)
+    kv_mean = args.prompt + (args.frames + 1) / 2
+    extra["frame_hbm_frac_fp8"] = round(frame_bytes(shape, "fp8", kv_mean) / (ms_frame * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    extra["frame_bytes_fp8_mean"] = int(frame_bytes(shape, "fp8", kv_mean))
+    extra["prefill_ms_per_token_fp8_p13"] = round(_prefill_ms(ctx, prompt) / len(prompt), 4)
+    log("per-kernel timing (FP8)")
+    ctx.reset(0)
+    ctx.prefill(prompt)
+    n_timed = 32
+    kus = ctx.time_kernels(n_timed)
+    extra["kernel_us_fp8"] = {k: round(v, 2) for k, v in kus.items() if v > 0}
+    if kus.get("frame", 0) > 0:
+        # the persistent frame kernel is the whole decode step: all weights + KV once per launch
+        kv_t = args.prompt + (n_timed + 1) / 2
+        k_bytes = frame_bytes(shape, "fp8", kv_t)
+        k_us = kus["frame"]
+        k_name = "k_frame<fp8> (persistent decode frame: 36 layers + head in one launch)"
+    else:
+        k_bytes = gateup_bytes(shape, "fp8")
+        k_us = kus["gate_up"]
+        k_name = "k_gemv<fp8> gate/up (SiLU*mul epilogue)"
+    achieved = k_bytes / (k_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": k_name, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "bytes_per_launch": int(k_bytes), "avg_launch_us": round(k_us, 3)}
+    ctx.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline (bounded sample)")
+        cpu = cpu_oracle_baseline(shape, w, scales, prompt)
+
+    line = {
+        "metric": "decode ms/frame @bs1 (FP8 e4m3 W8A8), 36-layer Qwen3-4B-shaped TTS backbone + 8x1026 head",
+        "value": round(ms_frame, 4), "unit": "ms/frame", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 2), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": f"FP8 W8A8 decode, P={args.prompt} prompt then {args.frames} greedy delay-pattern "
+                               f"frames (KV {args.prompt + 1}->{args.prompt + args.frames}), seeded random weights",
+                   "layers": shape.n_layers, "hidden": shape.hidden, "heads": f"{shape.n_q_heads}q/{shape.n_kv_heads}kv",
+                   "ffn": shape.ffn, "codebooks": f"{shape.n_codebooks}x{shape.codebook_size}",
+                   "prompt_tokens": args.prompt, "frames": args.frames},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _prefill_ms(ctx, prompt, reps: int = 20) -> float:
+    """Median of reps (reset + prefill) device times, after one warm-up."""
+    import torch
+
+    ts = []
+    for i in range(reps + 1):
+        ctx.reset(0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(ctx.stream)
+        ctx.prefill(prompt)
+        e1.record(ctx.stream)
+        e1.synchronize()
+        if i:
+            ts.append(e0.elapsed_time(e1))
+    return statistics.median(ts)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -169,10 +169,23 @@ int hta_layer_step(hta_ctx* ctx, int layer, int kv_len, const void* k_init, cons
  * room for T*C codes; *n_frames receives n. */
 int hta_undelay(const int32_t* step_codes, int T, int n_codebooks, int eos_id, int32_t* frames_out, int* n_frames);
 
+/* Per-kernel timing for the benchmark: decode n_frames frames launching the
+ * frame's kernels one by one with a HIP event pair around each launch on the
+ * context's stream; avg_us_out (host, n_classes floats) receives the average
+ * device time per launch of each kernel class: HTA_K_EMBED, HTA_K_QKV,
+ * HTA_K_ATTN, HTA_K_O, HTA_K_GATEUP, HTA_K_DOWN, HTA_K_HEAD for the per-kernel
+ * frame, HTA_K_FRAME for the persistent frame kernel (whichever the context
+ * decodes with).  The frames are real decode steps (the state advances). */
+enum { HTA_K_EMBED = 0, HTA_K_QKV = 1, HTA_K_ATTN = 2, HTA_K_O = 3, HTA_K_GATEUP = 4, HTA_K_DOWN = 5, HTA_K_HEAD = 6,
+       HTA_K_FRAME = 7, HTA_K_COUNT = 8 };
+int hta_time_kernels(hta_ctx* ctx, int n_frames, float* avg_us_out, int n_classes);
+
 /* Options: HTA_OPT_USE_GRAPH (default 1) replays the captured position-agnostic
  * frame graph; 0 launches the same kernels one by one (for tests that compare
- * the two). */
-enum { HTA_OPT_USE_GRAPH = 0 };
+ * the two).  HTA_OPT_PERSISTENT (default 1 where the device fits it) decodes
+ * each frame with one cooperative persistent kernel (one block per compute
+ * unit, grid barriers between phases); 0 uses one kernel per phase. */
+enum { HTA_OPT_USE_GRAPH = 0, HTA_OPT_PERSISTENT = 1 };
 int hta_set_option(hta_ctx* ctx, int option, int value);
 
 void hta_destroy(hta_ctx* ctx);

@@ -278,3 +278,23 @@ def test_error_codes(w, prompt):
     ctx.reset(0)
     ctx.prefill(prompt)
     ctx.close()
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp8"])
+def test_persistent_frame_matches_per_kernel_frame(w, prompt, oracle_scales, precision):
+    """The one-launch persistent frame and the one-kernel-per-phase frame compute the
+    same step (different reduction orders): hidden states agree to fp32 rounding,
+    codes agree wherever the decision is not a near-tie, and the persistent frame
+    is deterministic run to run."""
+    sc = oracle_scales[0] if precision == "fp8" else None
+    ctx = gpu_context(SH, w, precision, act_scales=sc)
+    forced = S.code_frames(91, 10)
+    a = _run(ctx, prompt, 10, force=forced)
+    a2 = _run(ctx, prompt, 10, force=forced)
+    ctx.set_option(hta.OPT_PERSISTENT, 0)
+    b = _run(ctx, prompt, 10, force=forced)
+    ctx.close()
+    for x, x2, y in zip(a, a2, b):
+        assert np.array_equal(x[0], x2[0]) and np.array_equal(x[2], x2[2]) and np.array_equal(x[3], x2[3])
+        assert rel_l2(x[2], y[2]) < 1e-4
+        assert cosines(x[3], y[3]).min() > 0.99999
