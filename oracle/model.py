@@ -57,13 +57,19 @@ class OracleModel:
         self.record = None
         sh = shape
         self.layers = []
-        for layer in range(sh.n_layers):
+
+        def build(layer):
             p = f"layers.{layer}."
             L = {"g_attn": self._plain(weights[p + "g_attn"]), "g_q": self._plain(weights[p + "g_q"]),
                  "g_k": self._plain(weights[p + "g_k"]), "g_mlp": self._plain(weights[p + "g_mlp"])}
             for name in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
                 L[name] = self._matrix(weights[p + name])
-            self.layers.append(L)
+            return L
+
+        # layers are independent: build them on a few threads (numpy releases the GIL)
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max(1, min(8, sh.n_layers))) as ex:
+            self.layers = list(ex.map(build, range(sh.n_layers)))
         if not layers_only:
             self.e_text = self._embedding(weights["e_text"])
             self.e_aud = self._embedding(weights["e_aud"])
@@ -143,11 +149,16 @@ class OracleModel:
         self.v_cache[layer, positions] = v
         o = np.empty((T, Hq, hd), dtype=np.float64)
         group = Hq // Hkv
-        for i in range(T):
-            n_keys = int(positions[i]) + 1  # causal: keys at positions 0..p_i
-            for h in range(Hq):
-                j = h // group
-                o[i, h] = nx.attention_one(q[i, h], self.k_cache[layer, :n_keys, j], self.v_cache[layer, :n_keys, j])
+        n_keys = int(positions.max()) + 1
+        # causal mask: query i sees the keys at positions 0..p_i
+        visible = np.arange(n_keys)[None, :] <= np.asarray(positions)[:, None]
+        for h in range(Hq):
+            j = h // group
+            K = self.k_cache[layer, :n_keys, j]
+            V = self.v_cache[layer, :n_keys, j]
+            scores = (q[:, h] @ K.T) / np.sqrt(hd)
+            scores = np.where(visible, scores, -np.inf)
+            o[:, h] = nx.softmax(scores, axis=-1) @ V
         oa = self._act(o.reshape(T, Hq * hd), s0 + 1)
         H = H + self._linear(oa, Lw["wo"], s0 + 1)
         u2 = self._act(nx.rmsnorm(H, Lw["g_mlp"], sh.rms_eps), s0 + 2)
