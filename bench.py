@@ -10,9 +10,9 @@ one replay of the position-agnostic frame graph.  Weights and prompts are
 seeded synthetic draws (no trained checkpoint exists here).
 
 The JSON line reports decode ms/frame (FP8) as the metric, plus BF16 decode
-ms/frame, prefill ms/token, the roofline of the dominant kernel (the gate/up
-GEMV) measured with HIP events on the library's stream, and the CPU oracle
-timed on a bounded sample on this host.
+ms/frame, prefill ms/token, the roofline of the dominant kernel (the
+persistent frame kernel) measured with HIP events on the library's stream,
+and the CPU oracle timed on a bounded sample on this host.
 """
 from __future__ import annotations
 
@@ -49,14 +49,6 @@ def frame_bytes(shape, precision: str, kv_len: float) -> float:
     emb = shape.n_codebooks * d * 2
     kv = kv_len * L * 2 * shape.n_kv_heads * hd * 2
     return (per_layer * L + head) * wb + scales + gains + emb + kv
-
-
-def gateup_bytes(shape, precision: str) -> float:
-    """Algorithmic bytes of one gate/up GEMV launch: the interleaved [2F][d] weights (+ FP8
-    row scales), the residual input and gains read, the SiLU*mul output written."""
-    d, F = shape.hidden, shape.ffn
-    wb = 1 if precision == "fp8" else 2
-    return 2 * F * d * wb + (2 * F * 4 if precision == "fp8" else 0) + d * 4 * 2 + F * wb
 
 
 def cpu_oracle_baseline(shape, weights, scales, prompt, n_layers_sample=4, n_frames=3):
@@ -100,6 +92,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--layers", type=int, default=36, help="backbone depth (36 = the benchmark model)")
+    ap.add_argument("--no-kernel-classes", action="store_true",
+                    help="skip the per-kernel-class event timing that follows the timed region")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain elementwise copy of this many MiB before the timed region (a known-size "
+                         "kernel that calibrates the HBM byte counters of a rocprofv3 --pmc run)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -145,19 +142,26 @@ def main() -> int:
         kv_mean = args.prompt + (args.bf16_frames + 1) / 2
         extra["frame_hbm_frac_bf16"] = round(frame_bytes(shape, "bf16", kv_mean) / (extra["decode_ms_per_frame_bf16"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         extra["prefill_ms_per_token_bf16_p13"] = round(_prefill_ms(bctx, prompt) / len(prompt), 4)
+    if not args.no_bf16 and not args.no_kernel_classes:
         bctx.reset(0)
         bctx.prefill(prompt)
         extra["kernel_us_bf16"] = {k: round(v, 2) for k, v in bctx.time_kernels(16).items() if v > 0}
     bctx.close()
     del bctx
-    torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- FP8 context: the timed workload
     log("FP8 context: load")
     ctx = hta.Hta(shape, "fp8", max_seq=max_seq, max_prefill=min(512, max_seq))
     ctx.load_weights(tensors, src, act_scales=scales)
     del tensors
-    torch.cuda.empty_cache()
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * 1024 * 1024 // 4
+        src_t = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst_t = torch.empty_like(src_t)
+        with torch.cuda.stream(ctx.stream):
+            torch.neg(src_t, out=dst_t)
+        torch.cuda.synchronize()
+        del src_t, dst_t
     log(f"FP8 timed region: {args.warmup} warmup + {args.steps} steps of prefill {args.prompt} + {args.frames} frames")
     dec_ms = []
     for i in range(args.warmup):
@@ -182,26 +186,24 @@ def main() -> int:
     extra["frame_hbm_frac_fp8"] = round(frame_bytes(shape, "fp8", kv_mean) / (ms_frame * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     extra["frame_bytes_fp8_mean"] = int(frame_bytes(shape, "fp8", kv_mean))
     extra["prefill_ms_per_token_fp8_p13"] = round(_prefill_ms(ctx, prompt) / len(prompt), 4)
-    log("per-kernel timing (FP8)")
-    ctx.reset(0)
-    ctx.prefill(prompt)
-    n_timed = 32
-    kus = ctx.time_kernels(n_timed)
-    extra["kernel_us_fp8"] = {k: round(v, 2) for k, v in kus.items() if v > 0}
-    if kus.get("frame", 0) > 0:
-        # the persistent frame kernel is the whole decode step: all weights + KV once per launch
-        kv_t = args.prompt + (n_timed + 1) / 2
-        k_bytes = frame_bytes(shape, "fp8", kv_t)
-        k_us = kus["frame"]
-        k_name = "k_frame<fp8> (persistent decode frame: 36 layers + head in one launch)"
-    else:
-        k_bytes = gateup_bytes(shape, "fp8")
-        k_us = kus["gate_up"]
-        k_name = "k_gemv<fp8> gate/up (SiLU*mul epilogue)"
+    # roofline of the dominant kernel: the persistent frame kernel is the whole decode step (every
+    # weight, scale, gain and the KV once per launch); its average launch duration is the event-timed
+    # decode region divided by the frame count (back-to-back launches on the library's stream, so the
+    # few-microsecond launch gaps are included)
+    workload = (f"FP8 W8A8 decode, P={args.prompt} prompt then {args.frames} greedy delay-pattern frames "
+                f"(KV {args.prompt + 1}->{args.prompt + args.frames}), seeded random weights")
+    k_bytes = frame_bytes(shape, "fp8", kv_mean)
+    k_us = ms_frame * 1e3
     achieved = k_bytes / (k_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": k_name, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+    roofline = {"bound": "hbm", "kernel": "k_frame<1, 128> (persistent decode frame: 36 layers + head)",
+                "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": _traffic(workload, shape),
                 "bytes_per_launch": int(k_bytes), "avg_launch_us": round(k_us, 3)}
+    if not args.no_kernel_classes:
+        log("per-kernel timing (FP8)")
+        ctx.reset(0)
+        ctx.prefill(prompt)
+        extra["kernel_us_fp8"] = {k: round(v, 2) for k, v in ctx.time_kernels(32).items() if v > 0}
     ctx.close()
 
     cpu = None
@@ -214,8 +216,7 @@ def main() -> int:
         "value": round(ms_frame, 4), "unit": "ms/frame", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 2), "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
-        "config": {"workload": f"FP8 W8A8 decode, P={args.prompt} prompt then {args.frames} greedy delay-pattern "
-                               f"frames (KV {args.prompt + 1}->{args.prompt + args.frames}), seeded random weights",
+        "config": {"workload": workload,
                    "layers": shape.n_layers, "hidden": shape.hidden, "heads": f"{shape.n_q_heads}q/{shape.n_kv_heads}kv",
                    "ffn": shape.ffn, "codebooks": f"{shape.n_codebooks}x{shape.codebook_size}",
                    "prompt_tokens": args.prompt, "frames": args.frames},
@@ -224,6 +225,21 @@ def main() -> int:
     line.update(extra)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def _traffic(workload: str, shape):
+    """HBM bytes per frame-kernel launch from the rocprofv3 counter runs recorded in traffic.json,
+    or None when they were taken on another workload or before the kernel's sources last changed."""
+    from autoregressive_codebook_tts_amd import pmc_traffic
+
+    path = os.path.join(ROOT, "autoregressive_codebook_tts_amd", "traffic.json")
+    if shape.n_layers != 36 or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("workload") != workload or t.get("source_sha256") != pmc_traffic.source_digest():
+        return None
+    return t["traffic_bytes_per_launch"]
 
 
 def _prefill_ms(ctx, prompt, reps: int = 20) -> float:
@@ -244,4 +260,6 @@ def _prefill_ms(ctx, prompt, reps: int = 20) -> float:
 
 
 if __name__ == "__main__":
-    sys.exit(main())
+    rc = main()
+    if rc:  # a clean run returns from the script instead of raising SystemExit
+        sys.exit(rc)
