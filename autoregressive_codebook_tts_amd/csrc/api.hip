@@ -94,6 +94,8 @@ Layout make_layout(const hta_config& c) {
   if (d > nmax) nmax = d;
   L.off_pgu = take(Pm * 2 * F * 4 + 8 * Pm * nmax * 4);  // gate/up rows, then GEMM split partials
   L.off_pa = 0;
+  L.off_taps = take(((size_t)c.n_layers + 1) * d * 4);
+  L.off_ptaps = take(2 * Pm * d * 4);
   L.total = o;
   return L;
 }
@@ -183,6 +185,8 @@ static void set_pointers(Ctx& c) {
   c.x_part = reinterpret_cast<uint64_t*>(w + L.off_xpart);
   c.x_logits = reinterpret_cast<uint64_t*>(w + L.off_xlogits);
   c.sync = reinterpret_cast<unsigned*>(w + L.off_sync);
+  c.taps_h = reinterpret_cast<float*>(w + L.off_taps);
+  c.taps_p = reinterpret_cast<float*>(w + L.off_ptaps);
   c.tok = reinterpret_cast<int32_t*>(w + L.off_tok);
   c.px = reinterpret_cast<float*>(w + L.off_x);
   c.pu = w + L.off_u;
@@ -208,10 +212,16 @@ static hipError_t clear_exchange(Ctx& c) {
 
 static hipError_t enqueue_frame(Ctx& c, bool record) {
   if (!record && c.use_persistent && c.frame_ok) return launch_frame_persistent(c);
+  const size_t hb = (size_t)c.cfg.hidden * 4;
   hipError_t e = launch_frame_begin(c);
   if (e != hipSuccess) return e;
-  for (int l = 0; l < c.cfg.n_layers; ++l)
+  if (c.taps && (e = hipMemcpyAsync(c.taps_h, c.h, hb, hipMemcpyDeviceToDevice, c.stream)) != hipSuccess) return e;
+  for (int l = 0; l < c.cfg.n_layers; ++l) {
     if ((e = launch_layer_decode(c, l, c.h, record)) != hipSuccess) return e;
+    if (c.taps && (e = hipMemcpyAsync(c.taps_h + (size_t)(l + 1) * c.cfg.hidden, c.h, hb, hipMemcpyDeviceToDevice,
+                                      c.stream)) != hipSuccess)
+      return e;
+  }
   return launch_head(c, record);
 }
 
@@ -405,7 +415,7 @@ static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out) {
   if (r) return r;
   if (n <= 0 || !codes_out) return fail(c, HTA_E_ARG, "bad frame count or output");
   if (c.len + n > c.cfg.max_seq) return fail(c, HTA_E_CAPACITY, "KV cache full");
-  if (c.use_graph) {
+  if (c.use_graph && !c.taps) {
     if ((r = ensure_graph(c)) != HTA_OK) return r;
     for (int i = 0; i < n; ++i) HIPCK(hipGraphLaunch(c.frame_exec, c.stream), "hipGraphLaunch");
   } else {
@@ -525,6 +535,24 @@ int hta_read_tap(hta_ctx* x, int tap, int layer, void* host_out, size_t bytes) {
       const LayerW& L = c.layers[layer];
       const void* src = scales ? (const void*)(qkv ? L.s_qkv : L.s_gu) : (const void*)(qkv ? L.w_qkv : L.w_gu);
       HIPCK(hipMemcpy(host_out, src, nb, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    }
+    case HTA_TAP_LAYER_H: {
+      const size_t nb = ((size_t)f.n_layers + 1) * f.hidden * 4;
+      if (!c.taps) return fail(c, HTA_E_STATE, "taps are off");
+      if (bytes < nb) return fail(c, HTA_E_ARG, "buffer too small");
+      HIPCK(hipMemcpy(host_out, c.taps_h, nb, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    }
+    case HTA_TAP_PREFILL_LAYER: {
+      const size_t nb = (size_t)c.last_prefill_P * f.hidden * 4;
+      if (!c.taps) return fail(c, HTA_E_STATE, "taps are off");
+      if (bytes < 2 * nb) return fail(c, HTA_E_ARG, "buffer too small");
+      if (nb) {
+        char* o = static_cast<char*>(host_out);
+        HIPCK(hipMemcpy(o, c.taps_p, nb, hipMemcpyDeviceToHost), "tap");
+        HIPCK(hipMemcpy(o + nb, c.taps_p + (size_t)f.max_prefill * f.hidden, nb, hipMemcpyDeviceToHost), "tap");
+      }
       return HTA_OK;
     }
     default:
@@ -656,6 +684,17 @@ int hta_set_option(hta_ctx* x, int option, int value) {
     if (v && !c.frame_ok) return fail(c, HTA_E_UNSUPPORTED, "the persistent frame kernel does not fit this device");
     if (v != c.use_persistent) drop_graph(c);
     c.use_persistent = v;
+    return HTA_OK;
+  }
+  if (option == HTA_OPT_TAPS) {
+    const bool v = value != 0;
+    if (v != c.taps) drop_graph(c);  // the captured launch holds the tap pointer
+    c.taps = v;
+    return HTA_OK;
+  }
+  if (option == HTA_OPT_PREFILL_TAP_LAYER) {
+    if (value < 0 || value >= c.cfg.n_layers) return fail(c, HTA_E_ARG, "tap layer out of range");
+    c.prefill_tap_layer = value;
     return HTA_OK;
   }
   return fail(c, HTA_E_ARG, "unknown option");

@@ -61,6 +61,7 @@ struct FrameArgs {
   uint64_t* xlogits;         // [C*V]                      (value | tag << 32)
   float* h_out;              // [d]    final residual (plain, for taps)
   float* logits_out;         // [C*V]  logits (plain, for taps)
+  float* taps;               // [n_layers + 1][d] residual entering each layer, or null
   unsigned* sync;            // [0] launch count, [64] abort flag
   DevState* st;
   int32_t* hist;
@@ -674,6 +675,7 @@ __global__ __launch_bounds__(kFT) void k_frame(FrameArgs a) {
       float v = 0.0f;
       for (int c = 0; c < a.C; ++c) v += bf16_to_f32(*gp(a.e_aud + ((size_t)c * a.V + sh_state[4 + c]) * d + k));
       st64(a.xh + k, v, base);
+      if (a.taps) *gpw(a.taps + k) = v;
     }
     ss = block_sum(ss, red);
     const float rstd = 1.0f / sqrtf(ss / (float)d + a.eps);
@@ -752,6 +754,7 @@ __global__ __launch_bounds__(kFT) void k_frame(FrameArgs a) {
           const float hn = __uint_as_float((uint32_t)ld64(a.xh + row)) + y;
           st64(a.xh + row, hn, tag);
           if (kind == kDOWN && layer + 1 == a.n_layers) *gpw(a.h_out + row) = hn;
+          if (kind == kDOWN && a.taps) *gpw(a.taps + (size_t)(layer + 1) * d + row) = hn;
         }
       }
       if (kind == kO || kind == kDOWN) tag_h = tag;
@@ -855,6 +858,7 @@ hipError_t launch_frame_persistent(Ctx& c) {
   a.rope_cos = c.rope_cos; a.rope_sin = c.rope_sin; a.act_scales = c.act_scales;
   a.xh = c.x_h; a.xqkv = c.x_qkv; a.xo = c.x_o; a.xa = c.x_a; a.xpart = c.x_part; a.xlogits = c.x_logits;
   a.h_out = c.h; a.logits_out = c.logits;
+  a.taps = c.taps ? c.taps_h : nullptr;
   a.sync = c.sync; a.st = c.state; a.hist = c.hist;
   a.splits = c.frame_splits;
   const size_t lds = frame_lds_bytes();

@@ -56,6 +56,7 @@ struct Layout {
   size_t off_layer_table, off_xh, off_xqkv, off_xo, off_xa, off_xpart, off_xlogits, off_sync;
   // prefill scratch
   size_t off_tok, off_x, off_u, off_pqkv, off_pq, off_po, off_pgu, off_pa;
+  size_t off_taps, off_ptaps;
   int attn_splits;
 };
 
@@ -124,6 +125,12 @@ struct Ctx {
   void* po = nullptr;           // [Pmax][qd] act
   float* pgu = nullptr;         // [Pmax][2F]
   int last_prefill_P = 0;
+  // test taps: the residual entering every layer of each decode frame (and the final one),
+  // and the rows entering / leaving layer prefill_tap_layer of each prefill
+  bool taps = false;
+  int prefill_tap_layer = 0;
+  float* taps_h = nullptr;      // [n_layers + 1][d]
+  float* taps_p = nullptr;      // [2][Pmax][d]
 };
 
 // Event pair around one kernel launch when per-kernel timing is on (kernel class k).

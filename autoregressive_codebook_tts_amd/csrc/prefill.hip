@@ -384,9 +384,13 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
   hipError_t e;
   hipLaunchKernelGGL(k_embed_rows, dim3(Pn), dim3(256), 0, c.stream, c.tok, c.e_text, c.px, d);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t tap_bytes = (size_t)Pn * d * 4;
   for (int layer = 0; layer < f.n_layers; ++layer) {
     const LayerW& L = c.layers[layer];
     const int s0 = kSitesPerLayer * layer;
+    const bool tap = c.taps && layer == c.prefill_tap_layer;
+    if (tap && (e = hipMemcpyAsync(c.taps_p, c.px, tap_bytes, hipMemcpyDeviceToDevice, c.stream)) != hipSuccess)
+      return e;
     hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, L.g_attn, f.rms_eps, c.pu, d,
                        host_act_scale(c, s0), amax ? amax + s0 : nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -420,6 +424,9 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
                        host_act_scale(c, s0 + 3), amax ? amax + s0 + 3 : nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = gemm<P>(c, c.pu, L.w_d, L.s_d, host_act_scale(c, s0 + 3), c.px, Pn, d, F, 1)) != hipSuccess) return e;
+    if (tap && (e = hipMemcpyAsync(c.taps_p + (size_t)f.max_prefill * d, c.px, tap_bytes, hipMemcpyDeviceToDevice,
+                                   c.stream)) != hipSuccess)
+      return e;
   }
   return hipSuccess;
 }

@@ -143,9 +143,15 @@ int hta_force_codes(hta_ctx* ctx, const int32_t* codes_in);
  * HTA_TAP_W_QKV -> packed q/k/v rows of `layer` ([Hq*hd + 2*Hkv*hd][d], bf16 bits
  * or e4m3 codes); HTA_TAP_S_QKV -> their float32 FP8 row scales;
  * HTA_TAP_W_GU / HTA_TAP_S_GU -> the packed gate/up rows (interleaved
- * gate_0, up_0, gate_1, ...) and scales. */
+ * gate_0, up_0, gate_1, ...) and scales.  With HTA_OPT_TAPS on:
+ * HTA_TAP_LAYER_H -> float32 [n_layers + 1][d], the residual entering each
+ * layer of the last decode frame and, last, the final residual;
+ * HTA_TAP_PREFILL_LAYER -> float32 [2][P][d], the rows entering and leaving
+ * layer HTA_OPT_PREFILL_TAP_LAYER in the last prefill (HTA_E_STATE when the
+ * taps are off).  A buffer smaller than the tap gives HTA_E_ARG. */
 enum { HTA_TAP_HIDDEN = 0, HTA_TAP_LOGITS = 1, HTA_TAP_STATE = 2, HTA_TAP_KV = 3, HTA_TAP_AMAX = 4,
-       HTA_TAP_PREFILL_HIDDEN = 5, HTA_TAP_W_QKV = 6, HTA_TAP_S_QKV = 7, HTA_TAP_W_GU = 8, HTA_TAP_S_GU = 9 };
+       HTA_TAP_PREFILL_HIDDEN = 5, HTA_TAP_W_QKV = 6, HTA_TAP_S_QKV = 7, HTA_TAP_W_GU = 8, HTA_TAP_S_GU = 9,
+       HTA_TAP_LAYER_H = 10, HTA_TAP_PREFILL_LAYER = 11 };
 int hta_read_tap(hta_ctx* ctx, int tap, int layer, void* host_out, size_t bytes);
 
 /* FP8 calibration on a BF16 context (FlashRT page, section 8: a short BF16
@@ -184,8 +190,13 @@ int hta_time_kernels(hta_ctx* ctx, int n_frames, float* avg_us_out, int n_classe
  * frame graph; 0 launches the same kernels one by one (for tests that compare
  * the two).  HTA_OPT_PERSISTENT (default 1 where the device fits it) decodes
  * each frame with one cooperative persistent kernel (one block per compute
- * unit, grid barriers between phases); 0 uses one kernel per phase. */
-enum { HTA_OPT_USE_GRAPH = 0, HTA_OPT_PERSISTENT = 1 };
+ * unit; blocks hand values to each other through phase-tagged words, no grid
+ * barrier); 0 uses one kernel per phase.  HTA_OPT_TAPS (default 0) makes decode
+ * frames and prefills also write the per-layer residuals read by
+ * HTA_TAP_LAYER_H / HTA_TAP_PREFILL_LAYER (frames then launch without the
+ * graph); HTA_OPT_PREFILL_TAP_LAYER selects the prefill layer (0..n_layers-1,
+ * else HTA_E_ARG). */
+enum { HTA_OPT_USE_GRAPH = 0, HTA_OPT_PERSISTENT = 1, HTA_OPT_TAPS = 2, HTA_OPT_PREFILL_TAP_LAYER = 3 };
 int hta_set_option(hta_ctx* ctx, int option, int value);
 
 void hta_destroy(hta_ctx* ctx);

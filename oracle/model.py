@@ -210,12 +210,18 @@ class OracleModel:
         self.length += 1
         h = H[0]
         self.last_hidden = h
-        z = self._act(nx.rmsnorm(h[None, :], self.g_final, sh.rms_eps), SITES_PER_LAYER * sh.n_layers)
-        logits = self._linear(z, self.w_head, SITES_PER_LAYER * sh.n_layers)[0]
-        self.last_logits = logits.reshape(sh.n_codebooks, sh.codebook_size)
+        self.last_logits = self.head(h)
         codes = self.state.choose(self.last_logits)
         done = self.state.finish(codes)
         return codes, done
+
+    def head(self, h) -> np.ndarray:
+        """Logits [C][V] of the fused codebook head for a final residual h [d]:
+        final RMSNorm, the head-input rounding of the mode, the head GEMV."""
+        sh = self.shape
+        z = self._act(nx.rmsnorm(np.asarray(h, np.float64)[None, :], self.g_final, sh.rms_eps),
+                      SITES_PER_LAYER * sh.n_layers)
+        return self._linear(z, self.w_head, SITES_PER_LAYER * sh.n_layers)[0].reshape(sh.n_codebooks, sh.codebook_size)
 
     def force_codes(self, codes) -> None:
         """Teacher forcing: the next frame embeds ``codes`` instead of the last choice."""
