@@ -96,6 +96,8 @@ Layout make_layout(const hta_config& c) {
   L.off_pa = 0;
   L.off_taps = take(((size_t)c.n_layers + 1) * d * 4);
   L.off_ptaps = take(2 * Pm * d * 4);
+  L.off_trace = take((size_t)kTraceBlocks * (5 * c.n_layers + 1) * 8 * 4);
+  L.off_fargs = take(kFrameArgsBytes);
   L.total = o;
   return L;
 }
@@ -187,6 +189,8 @@ static void set_pointers(Ctx& c) {
   c.sync = reinterpret_cast<unsigned*>(w + L.off_sync);
   c.taps_h = reinterpret_cast<float*>(w + L.off_taps);
   c.taps_p = reinterpret_cast<float*>(w + L.off_ptaps);
+  c.trace_buf = reinterpret_cast<uint32_t*>(w + L.off_trace);
+  c.fargs = w + L.off_fargs;
   c.tok = reinterpret_cast<int32_t*>(w + L.off_tok);
   c.px = reinterpret_cast<float*>(w + L.off_x);
   c.pu = w + L.off_u;
@@ -322,6 +326,7 @@ int hta_bind_workspace(hta_ctx* x, void* dev_ptr, size_t bytes) {
   HIPCK(clear_exchange(c), "fill");
   HIPCK(launch_reset_state(c, 0), "reset");
   HIPCK(hipStreamSynchronize(c.stream), "sync");
+  HIPCK(frame_write_args(c), "frame arguments");
   c.len = 0;
   c.t = 0;
   return HTA_OK;
@@ -555,6 +560,13 @@ int hta_read_tap(hta_ctx* x, int tap, int layer, void* host_out, size_t bytes) {
       }
       return HTA_OK;
     }
+    case HTA_TAP_TRACE: {
+      const size_t nb = (size_t)c.frame_blocks * (5 * f.n_layers + 1) * 8 * 4;
+      if (!c.trace) return fail(c, HTA_E_STATE, "trace is off");
+      if (bytes < nb) return fail(c, HTA_E_ARG, "buffer too small");
+      HIPCK(hipMemcpy(host_out, c.trace_buf, nb, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    }
     default:
       return fail(c, HTA_E_ARG, "unknown tap");
   }
@@ -688,8 +700,16 @@ int hta_set_option(hta_ctx* x, int option, int value) {
   }
   if (option == HTA_OPT_TAPS) {
     const bool v = value != 0;
-    if (v != c.taps) drop_graph(c);  // the captured launch holds the tap pointer
+    if (v != c.taps) drop_graph(c);
     c.taps = v;
+    HIPCK(frame_write_args(c), "frame arguments");
+    return HTA_OK;
+  }
+  if (option == HTA_OPT_TRACE) {
+    const bool v = value != 0;
+    if (v != c.trace) drop_graph(c);
+    c.trace = v;
+    HIPCK(frame_write_args(c), "frame arguments");
     return HTA_OK;
   }
   if (option == HTA_OPT_PREFILL_TAP_LAYER) {

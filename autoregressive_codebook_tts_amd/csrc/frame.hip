@@ -8,18 +8,19 @@
 // per frame; the frame is replayed as one position-agnostic graph).
 //
 // Design (MI355X):
-//  * Every GEMV phase splits its rows across the blocks; a block's rows are cut
-//    into 16-byte-per-lane packets along K (1 KB per wave), dealt round-robin to
-//    the block's waves, kD packets per wave in flight.  A register slot is
-//    refilled as soon as it is consumed, and the last group of a phase refills
-//    from the first group of the next GEMV phase, so the weight stream runs
-//    ahead of the activations it will be multiplied with.
+//  * Every GEMV phase splits its rows across the blocks; a block's rows are one
+//    contiguous byte range, cut into one piece per wave.  Each wave fetches its
+//    pieces, phase after phase, as 1 KB packets straight into an LDS ring of
+//    kRD slots (global_load_lds_dwordx4), kRD packets ahead of consumption, so
+//    the weight stream runs on through the waits for the next phase's inputs
+//    and through attention without holding registers.
+//  * Constant operands (norm gains, FP8 row scales, the first attention key
+//    tile, RoPE rows) are issued before a phase waits for its inputs.
 //  * No grid barriers.  Every value handed from one block to another inside the
 //    launch travels with a tag in the same atomic word (64-bit value+tag, or a
 //    16-bit payload with a 16-bit tag); the tag is a running phase number, so a
 //    consumer polls exactly the inputs it needs until they carry the current
-//    phase's tag.  Producers never wait and need no release fence, and no
-//    s_waitcnt ever drains the in-flight weight loads.  A buffer is rewritten
+//    phase's tag.  Producers never wait and need no release fence.  A buffer is rewritten
 //    only after every consumer of its previous content has finished (each
 //    rewrite depends, through the layer's data flow, on all of them).
 //  * The exchange words are read and written with agent-scope atomic accesses,
@@ -38,7 +39,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFT = 512;            // threads per block
 constexpr int kFW = kFT / kWave;    // waves per block
-constexpr int kD = 8;               // packets per wave per group
+constexpr int kRD = 12;             // LDS ring slots (1 KB packets) per wave
 constexpr int kPartMax = 1024;      // packet partial sums per block per phase
 constexpr uint64_t kSpinLimit = 50000000ull;  // 0.5 s at the 100 MHz constant clock
 
@@ -46,6 +47,9 @@ struct FrameArgs {
   int d, hd, Hq, Hkv, F, C, V, bos, eos, n_layers, max_seq, splits;
   float eps;
   const LayerW* layers;      // device copy of the per-layer pointers
+  const unsigned char* wl0;  // layer 0's block; layer l's weights are at wl0 + l * lstride + off_*
+  unsigned long long lstride;
+  unsigned long long off_wqkv, off_wo, off_wgu, off_wd;
   const uint16_t* e_aud;
   const float* g_final;
   const void* w_head;
@@ -62,10 +66,15 @@ struct FrameArgs {
   float* h_out;              // [d]    final residual (plain, for taps)
   float* logits_out;         // [C*V]  logits (plain, for taps)
   float* taps;               // [n_layers + 1][d] residual entering each layer, or null
+  uint32_t* trace;           // [blocks][5 * n_layers + 1][8] phase timestamps and counters, or null
   unsigned* sync;            // [0] launch count, [64] abort flag
   DevState* st;
   int32_t* hist;
 };
+
+// The kernel reads FrameArgs through the constant address space: every field is a
+// scalar (s_load) read that never waits on vector-memory counters.
+typedef const __attribute__((address_space(4))) FrameArgs CFA;
 
 // ---------------------------------------------------------------- tagged exchange words
 __device__ __forceinline__ uint64_t ld64(const uint64_t* p) {
@@ -81,16 +90,36 @@ __device__ __forceinline__ void st32(uint32_t* p, uint32_t bits16, unsigned tag)
   __hip_atomic_store(gpw(p), ((tag & 0xffffu) << 16) | (bits16 & 0xffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Compiler barrier: loads written before it are issued before it, so that
+// operands that do not depend on the frame travel with (or ahead of) a poll
+// instead of being sunk to their first use after it.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
+// An opaque copy of a (wave-uniform) pointer.  Taken inside the phase loop it keeps
+// the compiler from hoisting every per-thread address derived from the pointer out
+// of the loop, which would hold dozens of 64-bit addresses in registers for the
+// whole frame.
+template <class T>
+__device__ __forceinline__ T* launder(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 // Bounded poll state of one thread.
 struct Poll {
   unsigned* abort_flag;
   uint64_t t0;
+  unsigned n;
   bool ok;
-  __device__ void start(unsigned* f) { abort_flag = f; t0 = __builtin_amdgcn_s_memrealtime(); ok = true; }
-  // one more round of waiting; false when the frame must be abandoned
+  __device__ void start(unsigned* f) { abort_flag = f; t0 = __builtin_amdgcn_s_memrealtime(); n = 0; ok = true; }
+  // one more round of waiting; false when the frame must be abandoned.  The abort
+  // flag costs a memory round trip, so it is read on every 16th round only.
   __device__ bool again() {
     __builtin_amdgcn_s_sleep(1);
-    if (__hip_atomic_load(gp(abort_flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { ok = false; return false; }
+    if ((++n & 15u) == 0u &&
+        __hip_atomic_load(gp(abort_flag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { ok = false; return false; }
     if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinLimit) {
       __hip_atomic_store(gpw(abort_flag), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ok = false;
@@ -109,24 +138,20 @@ __device__ __forceinline__ bool block_ok(bool ok, int* flag) {
   return *flag != 0;
 }
 
-// ---------------------------------------------------------------- packet stream of one GEMV phase
-// A block's rows are a run of packets in row-major order (a packet is 16 bytes
-// per lane, 1 KB per wave, along K).  Wave w takes the contiguous run
-// [w*n/kFW, (w+1)*n/kFW) of the block's n packets, so the waves' work differs by
-// at most one packet; lanes accumulate a row across its packets and reduce once
-// when the row ends, writing one partial per (row, wave) to LDS.
+// ---------------------------------------------------------------- the rows of one GEMV phase
+// A block owns the rows [r0, r0 + nrows) of the phase's row-major weight
+// matrix: one contiguous byte range.  It is cut into kFW contiguous pieces, one
+// per wave, at 16-byte boundaries, so the waves' shares differ by at most 16
+// bytes; a wave streams its piece as consecutive 1 KB packets (16 bytes per
+// lane), whatever the row length, so no lane is ever idle on a row tail.
 template <int P>
 struct Stream {
   const uint8_t* w;
   int K;        // elements per row
   int r0;       // first row of this block
   int nrows;    // rows of this block
-  int nch;      // packets per row
   static constexpr int E = (P == kBF16) ? 8 : 16;  // elements per 16-byte lane packet
   static constexpr int B = (P == kBF16) ? 2 : 1;   // bytes per element
-  static constexpr int CH = kWave * E;             // elements per packet
-  __device__ int npk() const { return nrows * nch; }
-  __device__ int run_begin(int wave) const { return (int)((long)npk() * wave / kFW); }
 };
 
 template <int P>
@@ -139,44 +164,28 @@ __device__ __forceinline__ Stream<P> make_stream(const void* w, int N, int K, in
   const int u1 = (int)((long)units * (blockIdx.x + 1) / gridDim.x);
   s.r0 = pair_rows ? 2 * u0 : u0;
   s.nrows = pair_rows ? 2 * (u1 - u0) : (u1 - u0);
-  s.nch = (K + Stream<P>::CH - 1) / Stream<P>::CH;
   return s;
 }
 
-// Position in a wave's run: packet j of the run, at (row, ch).
-struct Cursor {
-  int j, n;      // packets taken, run length
-  int row, ch;   // local row, packet within the row
+// One wave's piece of a phase: bytes [b0, b1) counted from the block's first row.
+struct Piece {
+  const uint8_t* base;  // first byte of the block's first row
+  int rowbytes;
+  int b0, b1;
+  int npk;              // 1 KB packets
 };
 
 template <int P>
-__device__ __forceinline__ Cursor cursor_begin(const Stream<P>& s) {
-  const int w = threadIdx.x >> 6;
-  Cursor c;
-  const int p0 = s.run_begin(w);
-  c.j = 0;
-  c.n = s.run_begin(w + 1) - p0;
-  c.row = s.nch > 0 ? p0 / s.nch : 0;
-  c.ch = p0 - c.row * s.nch;
-  return c;
-}
-__device__ __forceinline__ void cursor_step(Cursor& c, int nch) {
-  ++c.j;
-  if (++c.ch == nch) { c.ch = 0; ++c.row; }
-}
-
-// One packet load per call, always issued (an address inside the stream when the
-// packet is outside the run or past K, then zeroed), so the number of loads in
-// flight is the same on every path and s_waitcnt can count them exactly.
-template <int P>
-__device__ __forceinline__ uint4 load_at(const Stream<P>& s, const Cursor& c) {
-  const int lane = threadIdx.x & 63;
-  const int e = c.ch * Stream<P>::CH + lane * Stream<P>::E;
-  const bool ok = (c.j < c.n) && (e < s.K);
-  const size_t off = ok ? ((size_t)(s.r0 + c.row) * s.K + e) * Stream<P>::B : 0;
-  uint4 v = ld_stream16(s.w + off);
-  if (!ok) v = make_uint4(0u, 0u, 0u, 0u);
-  return v;
+__device__ __forceinline__ Piece make_piece(const Stream<P>& s) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Piece q;
+  q.rowbytes = s.K * Stream<P>::B;
+  q.base = s.w + (size_t)s.r0 * q.rowbytes;
+  const int total = s.nrows * q.rowbytes;  // a multiple of 16
+  q.b0 = (int)(((long)total * w / kFW) & ~15L);
+  q.b1 = w + 1 == kFW ? total : (int)(((long)total * (w + 1) / kFW) & ~15L);
+  q.npk = (q.b1 - q.b0 + 1023) >> 10;
+  return q;
 }
 
 // bf16-pair dot of one packet with the activations xs (bf16 pairs in LDS)
@@ -203,76 +212,6 @@ __device__ __forceinline__ float packet_dot(const uint4& wv, const uint32_t* __r
     }
     return s;
   }
-}
-
-// The register ring of one wave: kD packets in flight.  `iss` is the issue
-// cursor, kD packets ahead of consumption; while it lies in the phase's own run
-// it loads from `s`, after the run it loads from the next phase's run.
-template <int P>
-struct Ring {
-  uint4 buf[kD];
-  Cursor iss;
-  int iss_next;  // 1: the issue cursor is in the next stream's run
-};
-
-template <int P>
-__device__ __forceinline__ void ring_prime(Ring<P>& r, const Stream<P>& s) {
-  r.iss = cursor_begin(s);
-  r.iss_next = 0;
-#pragma unroll
-  for (int i = 0; i < kD; ++i) {
-    r.buf[i] = load_at(s, r.iss);
-    cursor_step(r.iss, s.nch);
-  }
-}
-
-// Consume this wave's run of `s` (the ring already holds its first kD packets);
-// every consumed slot is refilled kD packets ahead, running on into the first
-// kD packets of `next` (if any).  Row partials go to part[row * kFW + wave]; the
-// caller zeroes part beforehand.
-template <int P>
-__device__ __forceinline__ void run_stream(const Stream<P>& s, const Stream<P>& next, Ring<P>& r,
-                                           const uint32_t* __restrict__ xs, float* __restrict__ part) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  Cursor c = cursor_begin(s);
-  const int ng = (c.n + kD - 1) / kD;
-  float acc = 0.0f;
-  for (int g = 0; g < ng; ++g) {
-#pragma unroll
-    for (int i = 0; i < kD; ++i) {
-      // consume slot i (pad slots hold zeros)
-      const int e = c.ch * Stream<P>::CH + lane * Stream<P>::E;
-      acc = packet_dot<P>(r.buf[i], xs + (e < s.K ? e : 0) / 2, acc);
-      if (c.j < c.n) {
-        const int row = c.row;
-        cursor_step(c, s.nch);
-        if (c.row != row || c.j == c.n) {
-          const float v = wave_sum(acc);
-          if (lane == 0) part[row * kFW + w] = v;
-          acc = 0.0f;
-        }
-      } else {
-        ++c.j;
-      }
-      // refill slot i, kD packets ahead (the run is padded to whole groups of kD)
-      if (!r.iss_next && r.iss.j >= ng * kD) { r.iss = cursor_begin(next); r.iss_next = 1; }
-      const Stream<P>& src = r.iss_next ? next : s;
-      r.buf[i] = load_at(src, r.iss);
-      cursor_step(r.iss, src.nch);
-    }
-  }
-  if (ng == 0) {
-    // nothing of this phase for this wave: prime the ring with the next phase
-    r.iss = cursor_begin(next);
-#pragma unroll
-    for (int i = 0; i < kD; ++i) {
-      r.buf[i] = load_at(next, r.iss);
-      cursor_step(r.iss, next.nch);
-    }
-  }
-  // the ring holds the first kD packets of `next`; its issue cursor is kD packets into next's run
-  r.iss_next = 0;
-  __syncthreads();
 }
 
 // Sum of a row's per-wave partials in wave order (deterministic); zeroes them for the next phase.
@@ -345,7 +284,15 @@ __device__ __forceinline__ bool norm_to_lds(const uint64_t* xh, unsigned tag, co
                                             float scale, uint32_t* xs, float* red, unsigned* abort_flag, int* okf) {
   Poll pl;
   pl.start(abort_flag);
-  constexpr int kMaxPer = 16;  // K <= 16 * kFT
+  constexpr int kMaxPer = 10;  // K <= 10 * kFT
+  // the gains do not depend on the frame: their loads travel with the first poll round
+  float gv[kMaxPer];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int k = i * kFT + threadIdx.x;
+    gv[i] = k < K ? *gp(g + k) : 0.0f;
+  }
+  issue_fence();
   uint64_t wv[kMaxPer];
   const bool got = poll_batch64<kMaxPer>(xh, kFT, K, tag, wv, pl);
   if (!block_ok(got, okf)) return false;
@@ -362,7 +309,7 @@ __device__ __forceinline__ bool norm_to_lds(const uint64_t* xh, unsigned tag, co
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i) {
     const int k = i * kFT + threadIdx.x;
-    if (k < K) xs16[k] = (uint16_t)act_bits<P>(__uint_as_float((uint32_t)wv[i]) * rstd * *gp(g + k), scale);
+    if (k < K) xs16[k] = (uint16_t)act_bits<P>(__uint_as_float((uint32_t)wv[i]) * rstd * gv[i], scale);
   }
   __syncthreads();
   return true;
@@ -385,13 +332,25 @@ __device__ __forceinline__ bool act_to_lds(const uint32_t* x, unsigned tag, int 
   return block_ok(got, okf);
 }
 
+// Phase timestamps for profiling the persistent kernel (the constant 100 MHz clock):
+// [0] phase start, [1] inputs ready, [2] weights streamed, [3] phase done; and, for
+// wave 0 of the block during the weight stream (core clock cycles): [4] waiting for
+// ring packets, [5] packets consumed, [6] row sums closed, [7] issuing fetches.
+__device__ __forceinline__ void trace_mark(CFA& a, int n_phases, int phase, int i) {
+  if (a.trace && threadIdx.x == 0)
+    *gpw(a.trace + ((size_t)blockIdx.x * n_phases + phase) * 8 + i) = (uint32_t)__builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void trace_put(CFA& a, int n_phases, int phase, int i, uint32_t v) {
+  if (a.trace && threadIdx.x == 0) *gpw(a.trace + ((size_t)blockIdx.x * n_phases + phase) * 8 + i) = v;
+}
+
 // ---------------------------------------------------------------- attention task (split-K, one kv head)
 struct AttnLds {
-  float qs[8][128];
-  float kn[128], vn[128];
-  float Kt[kAttnTile][129];
-  float Vt[kAttnTile][128];
-  float ps[8][kAttnTile];
+  float qs[4][128];                 // the kv group's rotated queries (group <= 4)
+  float kn[128], vn[128];           // this frame's key and value
+  uint32_t Kt[kAttnTile][65];       // the tile's keys as bf16 pairs (rows padded against bank conflicts)
+  uint32_t Vt[kAttnTile][64];       // the tile's values as bf16 pairs
+  float ps[4][kAttnTile];
 };
 
 template <int HD>
@@ -399,6 +358,10 @@ __device__ __forceinline__ void attn_norm_rope(const uint64_t* src, unsigned tag
                                                const float* sn, float eps, int lane, float* dst, Poll& pl) {
   constexpr int H2 = HD / 2;
   const bool act = lane < H2;
+  // frame-independent operands first, so their latency overlaps the poll
+  const float g0 = act ? *gp(g + lane) : 0.0f, g1 = act ? *gp(g + lane + H2) : 0.0f;
+  const float c = act ? *gp(cs + lane) : 0.0f, s = act ? *gp(sn + lane) : 0.0f;
+  issue_fence();
   uint64_t w0 = act ? ld64(src + lane) : ((uint64_t)tag << 32);
   uint64_t w1 = act ? ld64(src + lane + H2) : ((uint64_t)tag << 32);
   while (pl.ok && ((unsigned)(w0 >> 32) != tag || (unsigned)(w1 >> 32) != tag)) {
@@ -411,9 +374,8 @@ __device__ __forceinline__ void attn_norm_rope(const uint64_t* src, unsigned tag
   const float ss = wave_sum(x0 * x0 + x1 * x1);
   const float rstd = 1.0f / sqrtf(ss / (float)HD + eps);
   if (act) {
-    const float a = x0 * rstd * *gp(g + lane);
-    const float b = x1 * rstd * *gp(g + lane + H2);
-    const float c = *gp(cs + lane), s = *gp(sn + lane);
+    const float a = x0 * rstd * g0;
+    const float b = x1 * rstd * g1;
     dst[lane] = round_bf16(a * c - b * s);
     dst[lane + H2] = round_bf16(b * c + a * s);
   }
@@ -423,7 +385,7 @@ __device__ __forceinline__ void attn_norm_rope(const uint64_t* src, unsigned tag
 // other active splits' partials (polled by tag) and publishes the attention output.
 // Returns false if the frame was abandoned.
 template <int P, int HD>
-__device__ __forceinline__ bool attn_task(const FrameArgs a, const LayerW L, int layer, int pos, unsigned tag_qkv,
+__device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int pos, unsigned tag_qkv,
                           unsigned tag_part, unsigned tag_o, AttnLds& sm, unsigned* abort_flag, int* okf) {
   constexpr int H2 = HD / 2;
   constexpr int T = kAttnTile;
@@ -439,14 +401,40 @@ __device__ __forceinline__ bool attn_task(const FrameArgs a, const LayerW L, int
   const int n_active = (nkeys + chunk - 1) / chunk;
   if (split >= n_active) return true;
   const int beg = split * chunk, end = min(nkeys, beg + chunk);
-  const float* cs = a.rope_cos + (size_t)pos * H2;
-  const float* sn = a.rope_sin + (size_t)pos * H2;
+  const float* cs = launder(a.rope_cos) + (size_t)pos * H2;
+  const float* sn = launder(a.rope_sin) + (size_t)pos * H2;
+  uint64_t* xqkv = launder(a.xqkv);
+  uint64_t* xpart = launder(a.xpart);
+  uint32_t* xo = launder(a.xo);
+  uint16_t* kc = L.k_cache + (size_t)j * a.max_seq * HD;
+  uint16_t* vc = L.v_cache + (size_t)j * a.max_seq * HD;
+  // the first key tile comes from earlier positions only (the new key at pos is
+  // written below): load it before waiting for this frame's q, k, v
+  constexpr int SEG = HD / 8;                       // 16-byte segments per key
+  constexpr int NPT = (T * SEG + kFT - 1) / kFT;    // tile segments per thread
+  uint4 kr[NPT], vr[NPT];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int idx = u * kFT + tid;
+      const int kp = t0 + idx / SEG, seg = idx % SEG;
+      if (idx < T * SEG && kp < end && kp != pos) {
+        kr[u] = ld16(kc + (size_t)kp * HD + seg * 8);
+        vr[u] = ld16(vc + (size_t)kp * HD + seg * 8);
+      } else {
+        kr[u] = make_uint4(0u, 0u, 0u, 0u);
+        vr[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+  load_tile(beg);
+  issue_fence();
   Poll pl;
   pl.start(abort_flag);
-  if (w < G) attn_norm_rope<HD>(a.xqkv + (size_t)(j * G + w) * HD, tag_qkv, L.g_q, cs, sn, a.eps, lane, sm.qs[w], pl);
-  if (w == G) attn_norm_rope<HD>(a.xqkv + (size_t)a.Hq * HD + (size_t)j * HD, tag_qkv, L.g_k, cs, sn, a.eps, lane, sm.kn, pl);
+  if (w < G) attn_norm_rope<HD>(xqkv + (size_t)(j * G + w) * HD, tag_qkv, L.g_q, cs, sn, a.eps, lane, sm.qs[w], pl);
+  if (w == G) attn_norm_rope<HD>(xqkv + (size_t)a.Hq * HD + (size_t)j * HD, tag_qkv, L.g_k, cs, sn, a.eps, lane, sm.kn, pl);
   if (w == G + 1) {
-    const uint64_t* vsrc = a.xqkv + (size_t)(a.Hq + a.Hkv) * HD + (size_t)j * HD;
+    const uint64_t* vsrc = xqkv + (size_t)(a.Hq + a.Hkv) * HD + (size_t)j * HD;
     const uint64_t want = (uint64_t)tag_qkv << 32;
     uint64_t v0 = lane < HD ? ld64(vsrc + lane) : want;
     uint64_t v1 = HD > 64 ? ld64(vsrc + lane + 64) : want;
@@ -459,38 +447,33 @@ __device__ __forceinline__ bool attn_task(const FrameArgs a, const LayerW L, int
     if (HD > 64) sm.vn[lane + 64] = round_bf16(__uint_as_float((uint32_t)v1));
   }
   if (!block_ok(pl.ok, okf)) return false;
-  uint16_t* kc = L.k_cache + (size_t)j * a.max_seq * HD;
-  uint16_t* vc = L.v_cache + (size_t)j * a.max_seq * HD;
+  trace_mark(a, 5 * a.n_layers + 1, 5 * layer + 1, 1);
   if (beg <= pos && pos < end && tid < HD) {
     *gpw(kc + (size_t)pos * HD + tid) = (uint16_t)f32_to_bf16(sm.kn[tid]);
     *gpw(vc + (size_t)pos * HD + tid) = (uint16_t)f32_to_bf16(sm.vn[tid]);
   }
   const float inv_sqrt = 1.0f / sqrtf((float)HD);
   float m = -INFINITY, lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  constexpr int SEG = HD / 8;
   for (int t0 = beg; t0 < end; t0 += T) {
-    for (int idx = tid; idx < T * SEG; idx += kFT) {
+    if (t0 != beg) load_tile(t0);
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int idx = u * kFT + tid;
+      if (idx >= T * SEG) continue;
       const int key = idx / SEG, seg = idx % SEG;
       const int kp = t0 + key;
-      float kv[8], vv[8];
-      if (kp < end && kp != pos) {
-        const uint4 kw = ld16(kc + (size_t)kp * HD + seg * 8);
-        const uint4 vw = ld16(vc + (size_t)kp * HD + seg * 8);
-        const uint32_t ks[4] = {kw.x, kw.y, kw.z, kw.w}, vs[4] = {vw.x, vw.y, vw.z, vw.w};
+      uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w}, vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+      if (kp == pos && kp < end) {
+        // the new key/value (bf16-rounded values, so the conversion is exact)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kv[2 * e] = bf16lo(ks[e]); kv[2 * e + 1] = bf16hi(ks[e]);
-          vv[2 * e] = bf16lo(vs[e]); vv[2 * e + 1] = bf16hi(vs[e]);
+          kw[e] = f32_to_bf16(sm.kn[seg * 8 + 2 * e]) | (f32_to_bf16(sm.kn[seg * 8 + 2 * e + 1]) << 16);
+          vw[e] = f32_to_bf16(sm.vn[seg * 8 + 2 * e]) | (f32_to_bf16(sm.vn[seg * 8 + 2 * e + 1]) << 16);
         }
-      } else if (kp == pos && kp < end) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { kv[e] = sm.kn[seg * 8 + e]; vv[e] = sm.vn[seg * 8 + e]; }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { kv[e] = 0.0f; vv[e] = 0.0f; }
       }
+      // keys past the split hold zero words (load_tile zeroed them)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { sm.Kt[key][seg * 8 + e] = kv[e]; sm.Vt[key][seg * 8 + e] = vv[e]; }
+      for (int e = 0; e < 4; ++e) { sm.Kt[key][seg * 4 + e] = kw[e]; sm.Vt[key][seg * 4 + e] = vw[e]; }
     }
     __syncthreads();
     float scale = 1.0f, mnew = m;
@@ -500,9 +483,10 @@ __device__ __forceinline__ bool attn_task(const FrameArgs a, const LayerW L, int
       if (kp < end) {
         float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll 8
-        for (int e = 0; e < HD; e += 2) {
-          d0 = fmaf(sm.qs[w][e], sm.Kt[lane][e], d0);
-          d1 = fmaf(sm.qs[w][e + 1], sm.Kt[lane][e + 1], d1);
+        for (int e2 = 0; e2 < HD / 2; ++e2) {
+          const uint32_t kk2 = sm.Kt[lane][e2];
+          d0 = fmaf(sm.qs[w][2 * e2], bf16lo(kk2), d0);
+          d1 = fmaf(sm.qs[w][2 * e2 + 1], bf16hi(kk2), d1);
         }
         s = (d0 + d1) * inv_sqrt;
       }
@@ -519,19 +503,27 @@ __device__ __forceinline__ bool attn_task(const FrameArgs a, const LayerW L, int
       const int nk = min(T, end - t0);
       for (int kk = 0; kk < nk; ++kk) {
         const float p = sm.ps[w][kk];
-        if (lane < HD) o0 = fmaf(p, sm.Vt[kk][lane], o0);
-        if (HD > 64) o1 = fmaf(p, sm.Vt[kk][(lane + 64) % HD], o1);
+        if (lane < HD) {
+          const uint32_t v2 = sm.Vt[kk][lane >> 1];
+          o0 = fmaf(p, (lane & 1) ? bf16hi(v2) : bf16lo(v2), o0);
+        }
+        if (HD > 64) {
+          const int dd = (lane + 64) % HD;
+          const uint32_t v2 = sm.Vt[kk][dd >> 1];
+          o1 = fmaf(p, (dd & 1) ? bf16hi(v2) : bf16lo(v2), o1);
+        }
       }
       m = mnew;
     }
     __syncthreads();
   }
+  trace_mark(a, 5 * a.n_layers + 1, 5 * layer + 1, 2);
   const float so = P == kFP8 ? *gp(a.act_scales + kSitesPerLayer * layer + 1) : 1.0f;
   if (split != 0) {
     // publish this split's (o, m, l)
     if (w < G) {
       const int h = j * G + w;
-      uint64_t* pp = a.xpart + ((size_t)h * a.splits + split) * (HD + 2);
+      uint64_t* pp = xpart + ((size_t)h * a.splits + split) * (HD + 2);
       if (lane < HD) st64(pp + lane, o0, tag_part);
       if (HD > 64) st64(pp + lane + 64, o1, tag_part);
       if (lane == 0) { st64(pp + HD, m, tag_part); st64(pp + HD + 1, lsum, tag_part); }
@@ -543,7 +535,7 @@ __device__ __forceinline__ bool attn_task(const FrameArgs a, const LayerW L, int
   pm.start(abort_flag);
   if (w < G) {
     const int h = j * G + w;
-    const uint64_t* pb = a.xpart + (size_t)h * a.splits * (HD + 2);
+    const uint64_t* pb = xpart + (size_t)h * a.splits * (HD + 2);
     // lane s (1 <= s < n_active) holds split s's (m, l); lane 0 holds split 0's own
     const bool other = lane > 0 && lane < n_active;
     uint64_t wm = other ? ld64(pb + (size_t)lane * (HD + 2) + HD) : ((uint64_t)tag_part << 32);
@@ -594,8 +586,8 @@ __device__ __forceinline__ bool attn_task(const FrameArgs a, const LayerW L, int
       }
     }
     const float inv = 1.0f / den;
-    if (lane < HD) st32(a.xo + (size_t)h * HD + lane, act_bits<P>(n0 * inv, so), tag_o);
-    if (HD > 64) st32(a.xo + (size_t)h * HD + lane + 64, act_bits<P>(n1 * inv, so), tag_o);
+    if (lane < HD) st32(xo + (size_t)h * HD + lane, act_bits<P>(n0 * inv, so), tag_o);
+    if (HD > 64) st32(xo + (size_t)h * HD + lane + 64, act_bits<P>(n1 * inv, so), tag_o);
   }
   return block_ok(pm.ok, okf);
 }
@@ -607,25 +599,187 @@ __device__ __forceinline__ bool attn_task(const FrameArgs a, const LayerW L, int
 enum PhaseKind { kQKV = 0, kATTN = 1, kO = 2, kGU = 3, kDOWN = 4, kHEAD = 5 };
 
 template <int P, int HD>
-__device__ __forceinline__ Stream<P> phase_stream(const FrameArgs& a, int phase) {
+__device__ __forceinline__ Stream<P> phase_stream(CFA& a, int phase) {
   const int layer = phase / 5, kind = phase % 5;
   const int d = a.d, qd = a.Hq * HD, W = (a.Hq + 2 * a.Hkv) * HD;
   if (layer >= a.n_layers) return make_stream<P>(a.w_head, a.C * a.V, d, 0);
-  const LayerW* L = a.layers + layer;
+  // arithmetic on the argument block only (no dependent load on the issue path)
+  const unsigned char* lb = a.wl0 + (size_t)layer * a.lstride;
   switch (kind) {
-    case kQKV: return make_stream<P>(L->w_qkv, W, d, 0);
-    case kO: return make_stream<P>(L->w_o, d, qd, 0);
-    case kGU: return make_stream<P>(L->w_gu, 2 * a.F, d, 1);
-    default: return make_stream<P>(L->w_d, d, a.F, 0);
+    case kQKV: return make_stream<P>(lb + a.off_wqkv, W, d, 0);
+    case kO: return make_stream<P>(lb + a.off_wo, d, qd, 0);
+    case kGU: return make_stream<P>(lb + a.off_wgu, 2 * a.F, d, 1);
+    default: return make_stream<P>(lb + a.off_wd, d, a.F, 0);
   }
 }
 
+// ---------------------------------------------------------------- weight stream through an LDS ring
+// Every wave owns kRD ring slots of 1 KB in LDS.  Its weight packets (its run
+// of each GEMV phase, phase after phase through the whole frame) are fetched
+// with global_load_lds_dwordx4 straight into the slots, kRD packets ahead of
+// consumption, so the fetch runs on across phase boundaries, through the waits
+// for the next phase's inputs and through attention, without holding any
+// registers.  Loads complete in issue order, so "packet k has landed" is
+// "at most issued - k - 1 younger loads are outstanding" (s_waitcnt vmcnt).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void glb_void_t;
+
+__device__ __forceinline__ int next_gemv_phase(int phase, int n_layers) {
+  int p = phase + 1;
+  if (p / 5 < n_layers && p % 5 == kATTN) ++p;
+  return p;
+}
+
+// Sum over the wave's 64 lanes with DPP row shifts and row broadcasts (no LDS
+// round trips); the total is read from lane 63 and returned to every lane.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true);
+  return x + __int_as_float(y);
+}
+__device__ __forceinline__ float wave_total(float x) {
+  x = dpp_add<0x111, 0xf>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);  // row_shr:8   (lane 15 of each row: the row's sum)
+  x = dpp_add<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3 (lane 63: the total)
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+template <int P>
+struct Issuer {
+  const uint8_t* src;   // this lane's address in the next packet to fetch
+  const uint8_t* safe;  // an in-bounds address for lanes past the piece's end
+  int left;             // packets of the current piece still to fetch
+  int tail;             // byte offset of the piece's end from the next packet's start
+  int phase;            // phase of the current piece; n_phases once all are issued
+  int slot;             // ring slot of the next fetch
+  uint32_t m0base;      // LDS byte address of this wave's ring
+  int inflight;         // fetches not yet consumed
+};
+
+template <int P>
+__device__ __forceinline__ void issuer_piece(Issuer<P>& is, const Piece& q) {
+  is.src = q.base + q.b0 + 16 * (int)(threadIdx.x & 63);
+  is.safe = q.base + q.b0;
+  is.left = q.npk;
+  is.tail = q.b1 - q.b0;
+}
+
 template <int P, int HD>
-__global__ __launch_bounds__(kFT) void k_frame(FrameArgs a) {
+__device__ __forceinline__ void issue_one(CFA& a, Issuer<P>& is, int n_phases) {
+  while (is.left == 0 && is.phase < n_phases) {
+    is.phase = next_gemv_phase(is.phase, a.n_layers);
+    if (is.phase < n_phases) issuer_piece(is, make_piece<P>(phase_stream<P, HD>(a, is.phase)));
+  }
+  if (is.left == 0) return;
+  // lanes past the piece's end (last packet only) fetch its first bytes and are ignored
+  const uint8_t* src = 16 * (int)(threadIdx.x & 63) < is.tail ? is.src : is.safe;
+  // Written as inline assembly so that the compiler does not see an LDS write it
+  // cannot attribute to a slot (it would wait for every fetch in flight before each
+  // ring read); the ring's waits are the explicit ones in run_stream.  M0 holds the
+  // slot's LDS byte address; each lane's 16 bytes land at M0 + 16 * lane.
+  const uint32_t m0 = is.m0base + (uint32_t)is.slot * 1024u;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+  is.src += 1024;
+  is.tail -= 1024;
+  --is.left;
+  is.slot = is.slot + 1 == kRD ? 0 : is.slot + 1;
+  ++is.inflight;
+}
+
+template <int P, int HD>
+__device__ __forceinline__ void issuer_begin(CFA& a, Issuer<P>& is, unsigned char* ring_w, int n_phases) {
+  is.m0base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)ring_w);
+  is.phase = 0;
+  is.slot = 0;
+  is.inflight = 0;
+  issuer_piece(is, make_piece<P>(phase_stream<P, HD>(a, 0)));
+  for (int i = 0; i < kRD; ++i) issue_one<P, HD>(a, is, n_phases);
+}
+
+// Wait until every fetch into the ring has landed (before the block leaves the kernel).
+__device__ __forceinline__ void ring_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Consume this wave's piece of `s` from the ring, refilling each freed slot with
+// the wave's next packet.  Each lane follows its own (row, byte-in-row) position;
+// a row's partial sum is closed when the row ends inside the packet just
+// consumed and written to part[row * kFW + wave] (rows local to the block; the
+// caller zeroes part beforehand).  `cslot` is the ring slot of the next packet.
+template <int P, int HD>
+__device__ __forceinline__ void run_stream(CFA& a, const Stream<P>& s, Issuer<P>& is, int& cslot,
+                                           const unsigned char* ring_w, const uint32_t* __restrict__ xs,
+                                           float* __restrict__ part, int n_phases, int phase) {
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const Piece q = make_piece<P>(s);
+  if (q.npk > 0) {
+    const int rb = q.rowbytes;
+    int bi = q.b0 + 16 * lane;   // this lane's byte in the piece
+    int lr = bi / rb;            // its row (local)
+    int kb = bi - lr * rb;       // its byte within the row
+    int cur = q.b0 / rb;         // the open row (uniform)
+    int row_end = (cur + 1) * rb;
+    float acc = 0.0f;
+    bool open = false;
+    const bool tr = a.trace != nullptr && w == 0;
+    uint64_t t_wait = 0, t_issue = 0;
+    uint32_t n_close = 0;
+    for (int i = 0; i < q.npk; ++i) {
+      const uint64_t t0 = tr ? __builtin_amdgcn_s_memtime() : 0;
+      if (is.inflight >= kRD) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (tr) t_wait += __builtin_amdgcn_s_memtime() - t0;
+      const uint4 wv = *reinterpret_cast<const uint4*>(ring_w + cslot * 1024 + lane * 16);
+      cslot = cslot + 1 == kRD ? 0 : cslot + 1;
+      --is.inflight;
+      const float d = bi < q.b1 ? packet_dot<P>(wv, xs + kb / Stream<P>::B / 2, 0.0f) : 0.0f;
+      const int pkt_end = min(q.b0 + (i + 1) * 1024, q.b1);
+      while (row_end <= pkt_end) {  // the open row ends in this packet
+        const float v = wave_total(acc + (lr == cur ? d : 0.0f));
+        if (lane == 0) part[cur * kFW + w] = v;
+        acc = 0.0f;
+        open = false;
+        ++cur;
+        row_end += rb;
+        ++n_close;
+      }
+      if (row_end - rb < pkt_end) {  // the open row continues into the next packet
+        acc += lr == cur ? d : 0.0f;
+        open = true;
+      }
+      bi += 1024;
+      kb += 1024;
+      while (kb >= rb) { kb -= rb; ++lr; }
+      const uint64_t t1 = tr ? __builtin_amdgcn_s_memtime() : 0;
+      issue_one<P, HD>(a, is, n_phases);
+      if (tr) t_issue += __builtin_amdgcn_s_memtime() - t1;
+    }
+    if (open) {
+      const float v = wave_total(acc);
+      if (lane == 0) part[cur * kFW + w] = v;
+    }
+    if (tr) {
+      trace_put(a, n_phases, phase, 4, (uint32_t)t_wait);
+      trace_put(a, n_phases, phase, 5, (uint32_t)q.npk);
+      trace_put(a, n_phases, phase, 6, n_close);
+      trace_put(a, n_phases, phase, 7, (uint32_t)t_issue);
+    }
+  }
+  __syncthreads();
+}
+static_assert(kRD == 12, "run_stream's s_waitcnt immediate is kRD - 1");
+
+template <int P, int HD>
+__global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
+  CFA* ap = (CFA*)ap_generic;
+  CFA& a = *ap;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  uint32_t* xs = reinterpret_cast<uint32_t*>(smem_raw);                    // activations, bf16 pairs (<= 10240)
-  float* part = reinterpret_cast<float*>(smem_raw + 5120 * 4);              // per-(row, wave) partials
-  AttnLds& sm = *reinterpret_cast<AttnLds*>(smem_raw + 5120 * 4 + kPartMax * 4);
+  unsigned char* ring_w = smem_raw + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kRD * 1024;  // this wave's ring
+  unsigned char* lds1 = smem_raw + kFW * kRD * 1024;
+  uint32_t* xs = reinterpret_cast<uint32_t*>(lds1);                          // activations, bf16 pairs (<= 10240)
+  float* part = reinterpret_cast<float*>(lds1 + 5120 * 4);                   // per-(row, wave) partials
+  AttnLds& sm = *reinterpret_cast<AttnLds*>(lds1 + 5120 * 4 + kPartMax * 4);
   __shared__ float red[16];
   __shared__ int sh_state[4 + kMaxCodebooks];
   __shared__ int okf;
@@ -647,16 +801,19 @@ __global__ __launch_bounds__(kFT) void k_frame(FrameArgs a) {
   const int pos = sh_state[0];
   const int d = a.d;
 
-  Ring<P> ring;
-  Stream<P> cur = phase_stream<P, HD>(a, 0);
-  ring_prime(ring, cur);
+  const int n_phases = 5 * a.n_layers + 1;
+  Issuer<P> is;
+  issuer_begin<P, HD>(a, is, ring_w, n_phases);
+  int cslot = 0;  // ring slot of the next packet to consume
   for (int i = tid; i < kPartMax; i += kFT) part[i] = 0.0f;
 
   // frame input: h = sum_k E_aud[k][prev_k]; every block forms the whole vector for
-  // the first norm and publishes the rows it owns (the O/DOWN row split of d)
+  // the first norm and publishes the rows it owns (the O/DOWN row split of d).  The
+  // owned rows (at most one per thread) stay in h_own for the residual updates.
+  float h_own = 0.0f;
   {
     const Stream<P> own = make_stream<P>(nullptr, d, 1, 0);
-    constexpr int kMaxPer = 16;
+    constexpr int kMaxPer = 10;  // d <= 10 * kFT
     float hv[kMaxPer];
     float ss = 0.0f;
 #pragma unroll
@@ -670,10 +827,11 @@ __global__ __launch_bounds__(kFT) void k_frame(FrameArgs a) {
         ss = fmaf(v, v, ss);
       }
     }
-    for (int r = tid; r < own.nrows; r += kFT) {
-      const int k = own.r0 + r;
+    if (tid < own.nrows) {
+      const int k = own.r0 + tid;
       float v = 0.0f;
       for (int c = 0; c < a.C; ++c) v += bf16_to_f32(*gp(a.e_aud + ((size_t)c * a.V + sh_state[4 + c]) * d + k));
+      h_own = v;
       st64(a.xh + k, v, base);
       if (a.taps) *gpw(a.taps + k) = v;
     }
@@ -690,77 +848,86 @@ __global__ __launch_bounds__(kFT) void k_frame(FrameArgs a) {
     __syncthreads();
   }
 
-  const int n_phases = 5 * a.n_layers + 1;
   unsigned tag_h = base;   // tag of the residual's latest value
   for (int phase = 0; phase < n_phases; ++phase) {
     const int layer = phase / 5;
     const int kind = layer >= a.n_layers ? kHEAD : phase % 5;
+    CFA& a = *launder(ap);
     const unsigned tag = base + 1u + (unsigned)phase;
+    trace_mark(a, n_phases, phase, 0);
+    uint64_t* xh = launder(a.xh);
     if (kind == kATTN) {
       const LayerW L = a.layers[layer];
       // inputs: the QKV phase (tag - 1); partials and output carry this phase's tag
-      if (!attn_task<P, HD>(a, L, layer, pos, tag - 1u, tag, tag, sm, abort_flag, &okf)) return;
+      if (!attn_task<P, HD>(a, L, layer, pos, tag - 1u, tag, tag, sm, abort_flag, &okf)) { ring_drain(); return; }
+      trace_mark(a, n_phases, phase, 3);
       continue;
     }
     const int site = kind == kHEAD ? kSitesPerLayer * a.n_layers
                    : kSitesPerLayer * layer + (kind == kQKV ? 0 : kind == kO ? 1 : kind == kGU ? 2 : 3);
     const float sc_in = P == kFP8 ? a.act_scales[site] : 1.0f;
+    const Stream<P> cur = phase_stream<P, HD>(a, phase);
+    // FP8 row scales of this block's rows (at most one row, or one gate/up pair, per
+    // thread), loaded before the prologue waits so that the epilogue finds them ready
+    float ws0 = 1.0f, ws1 = 1.0f;
+    if (P == kFP8) {
+      const LayerW* L = a.layers + layer;
+      const float* wsc = kind == kHEAD ? a.s_head
+                       : kind == kQKV ? L->s_qkv : kind == kO ? L->s_o : kind == kGU ? L->s_gu : L->s_d;
+      if (kind == kGU) {
+        if (tid < cur.nrows / 2) { ws0 = *gp(wsc + cur.r0 + 2 * tid); ws1 = *gp(wsc + cur.r0 + 2 * tid + 1); }
+      } else if (tid < cur.nrows) {
+        ws0 = *gp(wsc + cur.r0 + tid);
+      }
+      issue_fence();
+    }
     // ---- prologue: the phase input in LDS
     if (kind == kQKV || kind == kGU || kind == kHEAD) {
       if (!(kind == kQKV && layer == 0)) {
         const float* g = kind == kHEAD ? a.g_final : (kind == kQKV ? a.layers[layer].g_attn : a.layers[layer].g_mlp);
-        if (!norm_to_lds<P>(a.xh, tag_h, g, d, a.eps, sc_in, xs, red, abort_flag, &okf)) return;
+        if (!norm_to_lds<P>(xh, tag_h, g, d, a.eps, sc_in, xs, red, abort_flag, &okf)) { ring_drain(); return; }
       }
     } else {
       // O reads the attention output (phase tag - 1), DOWN the SiLU*mul output (tag - 1)
-      const uint32_t* src = kind == kO ? a.xo : a.xa;
+      const uint32_t* src = kind == kO ? launder(a.xo) : launder(a.xa);
       const int K = kind == kO ? a.Hq * HD : a.F;
-      if (!act_to_lds(src, tag - 1u, K, xs, abort_flag, &okf)) return;
+      if (!act_to_lds(src, tag - 1u, K, xs, abort_flag, &okf)) { ring_drain(); return; }
     }
-    // ---- stream the weights; the next GEMV phase's first packets follow
-    int nphase = phase + 1;
-    if (nphase < n_phases && nphase / 5 < a.n_layers && nphase % 5 == kATTN) ++nphase;
-    Stream<P> nxt = cur;
-    if (nphase < n_phases) nxt = phase_stream<P, HD>(a, nphase);
-    else nxt.nrows = 0;
-    run_stream<P>(cur, nxt, ring, xs, part);
-    // ---- epilogue
-    const float* wsc = nullptr;
-    if (P == kFP8) {
-      if (kind == kHEAD) wsc = a.s_head;
-      else {
-        const LayerW* L = a.layers + layer;
-        wsc = kind == kQKV ? L->s_qkv : kind == kO ? L->s_o : kind == kGU ? L->s_gu : L->s_d;
-      }
-    }
+    trace_mark(a, n_phases, phase, 1);
+    // ---- stream the weights from the ring (its fetches run ahead into the next phases)
+    run_stream<P, HD>(a, cur, is, cslot, ring_w, xs, part, n_phases, phase);
+    trace_mark(a, n_phases, phase, 2);
+    // ---- epilogue (rows per block <= 128 < kFT, so one row or pair per thread)
     if (kind == kGU) {
       const float sc_out = P == kFP8 ? a.act_scales[site + 1] : 1.0f;
-      for (int r2 = tid; r2 < cur.nrows / 2; r2 += kFT) {
-        const int row = cur.r0 + 2 * r2;
-        const float g = row_sum(part, 2 * r2) * (P == kFP8 ? sc_in * *gp(wsc + row) : 1.0f);
-        const float u = row_sum(part, 2 * r2 + 1) * (P == kFP8 ? sc_in * *gp(wsc + row + 1) : 1.0f);
-        st32(a.xa + row / 2, act_bits<P>(silu(g) * u, sc_out), tag);
+      if (tid < cur.nrows / 2) {
+        const int row = cur.r0 + 2 * tid;
+        const float g = row_sum(part, 2 * tid) * (P == kFP8 ? sc_in * ws0 : 1.0f);
+        const float u = row_sum(part, 2 * tid + 1) * (P == kFP8 ? sc_in * ws1 : 1.0f);
+        st32(launder(a.xa) + row / 2, act_bits<P>(silu(g) * u, sc_out), tag);
       }
     } else {
-      for (int r = tid; r < cur.nrows; r += kFT) {
-        const int row = cur.r0 + r;
-        const float y = row_sum(part, r) * (P == kFP8 ? sc_in * *gp(wsc + row) : 1.0f);
+      if (tid < cur.nrows) {
+        const int row = cur.r0 + tid;
+        const float y = row_sum(part, tid) * (P == kFP8 ? sc_in * ws0 : 1.0f);
         if (kind == kQKV) {
-          st64(a.xqkv + row, y, tag);
+          st64(launder(a.xqkv) + row, y, tag);
         } else if (kind == kHEAD) {
-          st64(a.xlogits + row, y, tag);
+          st64(launder(a.xlogits) + row, y, tag);
         } else {
-          // O / DOWN: residual update of this block's own rows
-          const float hn = __uint_as_float((uint32_t)ld64(a.xh + row)) + y;
-          st64(a.xh + row, hn, tag);
+          // O / DOWN: residual update of this block's own rows (the same rows as the frame input's)
+          const float hn = h_own + y;
+          h_own = hn;
+          st64(xh + row, hn, tag);
           if (kind == kDOWN && layer + 1 == a.n_layers) *gpw(a.h_out + row) = hn;
           if (kind == kDOWN && a.taps) *gpw(a.taps + (size_t)(layer + 1) * d + row) = hn;
         }
       }
       if (kind == kO || kind == kDOWN) tag_h = tag;
     }
-    cur = nxt;
+    trace_mark(a, n_phases, phase, 3);
   }
+  ring_drain();  // every packet was consumed by the head phase; nothing is left in flight
   const unsigned tag_logits = base + (unsigned)n_phases;
   if (blockIdx.x != 0) return;
 
@@ -846,23 +1013,42 @@ __global__ __launch_bounds__(kFT) void k_frame(FrameArgs a) {
 }
 
 // ---------------------------------------------------------------- launcher
-size_t frame_lds_bytes() { return 5120 * 4 + kPartMax * 4 + sizeof(AttnLds); }
+size_t frame_lds_bytes() { return (size_t)kFW * kRD * 1024 + 5120 * 4 + kPartMax * 4 + sizeof(AttnLds); }
 
-hipError_t launch_frame_persistent(Ctx& c) {
+// The kernel reads its arguments from device memory (fields are re-read where
+// they are used instead of pinning dozens of scalar registers for the whole
+// frame); they are written when the workspace is bound and when an option that
+// changes them is set, never while a frame runs.
+hipError_t frame_write_args(Ctx& c) {
+  static_assert(sizeof(FrameArgs) <= kFrameArgsBytes, "FrameArgs does not fit its workspace slot");
+  if (!c.frame_ok || !c.fargs) return hipSuccess;
   const hta_config& f = c.cfg;
   FrameArgs a{};
   a.d = f.hidden; a.hd = f.head_dim; a.Hq = f.n_q_heads; a.Hkv = f.n_kv_heads; a.F = f.ffn;
   a.C = f.n_codebooks; a.V = f.codebook_size; a.bos = f.bos_id; a.eos = f.eos_id; a.n_layers = f.n_layers;
   a.max_seq = f.max_seq; a.eps = f.rms_eps;
-  a.layers = c.d_layers; a.e_aud = c.e_aud; a.g_final = c.g_final; a.w_head = c.w_head; a.s_head = c.s_head;
+  a.layers = c.d_layers;
+  a.wl0 = reinterpret_cast<const unsigned char*>(c.ws + c.lay.layer_base);
+  a.lstride = c.lay.layer_stride;
+  a.off_wqkv = c.lay.off_wqkv; a.off_wo = c.lay.off_wo; a.off_wgu = c.lay.off_wgu; a.off_wd = c.lay.off_wd;
+  a.e_aud = c.e_aud; a.g_final = c.g_final; a.w_head = c.w_head; a.s_head = c.s_head;
   a.rope_cos = c.rope_cos; a.rope_sin = c.rope_sin; a.act_scales = c.act_scales;
   a.xh = c.x_h; a.xqkv = c.x_qkv; a.xo = c.x_o; a.xa = c.x_a; a.xpart = c.x_part; a.xlogits = c.x_logits;
   a.h_out = c.h; a.logits_out = c.logits;
   a.taps = c.taps ? c.taps_h : nullptr;
+  a.trace = c.trace ? c.trace_buf : nullptr;
   a.sync = c.sync; a.st = c.state; a.hist = c.hist;
   a.splits = c.frame_splits;
+  hipError_t e = hipStreamSynchronize(c.stream);
+  if (e != hipSuccess) return e;
+  return hipMemcpy(c.fargs, &a, sizeof(a), hipMemcpyHostToDevice);
+}
+
+hipError_t launch_frame_persistent(Ctx& c) {
+  const hta_config& f = c.cfg;
   const size_t lds = frame_lds_bytes();
-  void* args[] = {&a};
+  void* ap = c.fargs;
+  void* args[] = {&ap};
   void* fn;
   if (f.precision == HTA_FP8_E4M3) fn = f.head_dim == 128 ? (void*)k_frame<kFP8, 128> : (void*)k_frame<kFP8, 64>;
   else fn = f.head_dim == 128 ? (void*)k_frame<kBF16, 128> : (void*)k_frame<kBF16, 64>;
@@ -886,7 +1072,7 @@ hipError_t frame_setup(Ctx& c) {
   int per_cu = 0;
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kFT, lds)) != hipSuccess) return e;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
-  c.frame_blocks = cus;  // one block per CU
+  c.frame_blocks = cus < kTraceBlocks ? cus : kTraceBlocks;  // one block per CU
   int splits = c.frame_blocks / c.cfg.n_kv_heads;
   if (splits > 64) splits = 64;
   if (splits < 1) splits = 1;

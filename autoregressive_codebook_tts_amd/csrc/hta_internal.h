@@ -12,6 +12,8 @@ namespace hta {
 constexpr int kSitesPerLayer = 4;   // attention input, attention output, MLP input, down input
 constexpr int kAttnTile = 64;       // keys per attention tile (aligned to absolute positions)
 constexpr int kMaxCodebooks = 16;
+constexpr int kTraceBlocks = 1024;  // most blocks the persistent kernel's trace records
+constexpr size_t kFrameArgsBytes = 1024;  // device slot of the persistent kernel's arguments
 
 // Decode state kept on the device (one per context).
 struct DevState {
@@ -56,7 +58,7 @@ struct Layout {
   size_t off_layer_table, off_xh, off_xqkv, off_xo, off_xa, off_xpart, off_xlogits, off_sync;
   // prefill scratch
   size_t off_tok, off_x, off_u, off_pqkv, off_pq, off_po, off_pgu, off_pa;
-  size_t off_taps, off_ptaps;
+  size_t off_taps, off_ptaps, off_trace, off_fargs;
   int attn_splits;
 };
 
@@ -131,6 +133,9 @@ struct Ctx {
   int prefill_tap_layer = 0;
   float* taps_h = nullptr;      // [n_layers + 1][d]
   float* taps_p = nullptr;      // [2][Pmax][d]
+  bool trace = false;           // persistent frame kernel phase timestamps
+  uint32_t* trace_buf = nullptr;  // [kTraceBlocks][5 * n_layers + 1][4]
+  void* fargs = nullptr;          // the persistent kernel's arguments (device)
 };
 
 // Event pair around one kernel launch when per-kernel timing is on (kernel class k).
@@ -159,6 +164,7 @@ hipError_t launch_set_len(Ctx& c, int len);
 // ---------------------------------------------------------------- persistent frame (frame.hip)
 hipError_t frame_setup(Ctx& c);
 hipError_t launch_frame_persistent(Ctx& c);
+hipError_t frame_write_args(Ctx& c);
 int frame_max_packets(const hta_config& f, int blocks);
 int frame_part_capacity();
 

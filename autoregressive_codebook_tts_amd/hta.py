@@ -21,11 +21,12 @@ ERRORS = {-1: "HTA_E_ARG", -2: "HTA_E_STATE", -3: "HTA_E_CAPACITY", -4: "HTA_E_R
 HTA_BF16, HTA_FP8_E4M3 = 0, 1
 HTA_SRC_F32, HTA_SRC_BF16 = 0, 1
 (TAP_HIDDEN, TAP_LOGITS, TAP_STATE, TAP_KV, TAP_AMAX, TAP_PREFILL_HIDDEN, TAP_W_QKV, TAP_S_QKV, TAP_W_GU, TAP_S_GU,
- TAP_LAYER_H, TAP_PREFILL_LAYER) = range(12)
+ TAP_LAYER_H, TAP_PREFILL_LAYER, TAP_TRACE) = range(13)
 OPT_USE_GRAPH = 0
 OPT_PERSISTENT = 1
 OPT_TAPS = 2
 OPT_PREFILL_TAP_LAYER = 3
+OPT_TRACE = 4
 SITES_PER_LAYER = 4
 
 LAYER_TENSORS = ("g_attn", "wq", "wk", "wv", "g_q", "g_k", "wo", "g_mlp", "wg", "wu", "wd")
@@ -251,6 +252,11 @@ class Hta:
     def tap_prefill_layer(self, P: int) -> np.ndarray:
         """[2][P][d]: the rows entering and leaving the selected layer in the last prefill (OPT_TAPS on)."""
         return self._tap(TAP_PREFILL_LAYER, 0, np.zeros((2, P, self.shape.hidden), np.float32))
+
+    def tap_trace(self, blocks: int) -> np.ndarray:
+        """[blocks][5 * n_layers + 1][8] uint32 phase timestamps (100 MHz clock) and stream
+        counters of the last persistent frame (needs OPT_TRACE on)."""
+        return self._tap(TAP_TRACE, 0, np.zeros((blocks, 5 * self.shape.n_layers + 1, 8), np.uint32))
 
     def tap_prefill_hidden(self, P: int) -> np.ndarray:
         return self._tap(TAP_PREFILL_HIDDEN, 0, np.zeros((P, self.shape.hidden), np.float32))

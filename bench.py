@@ -142,6 +142,8 @@ def main() -> int:
         kv_mean = args.prompt + (args.bf16_frames + 1) / 2
         extra["frame_hbm_frac_bf16"] = round(frame_bytes(shape, "bf16", kv_mean) / (extra["decode_ms_per_frame_bf16"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         extra["prefill_ms_per_token_bf16_p13"] = round(_prefill_ms(bctx, prompt) / len(prompt), 4)
+        if shape.n_layers == 36:
+            extra.update(_prefill_sizes(bctx, shape, "bf16"))
     if not args.no_bf16 and not args.no_kernel_classes:
         bctx.reset(0)
         bctx.prefill(prompt)
@@ -186,6 +188,8 @@ def main() -> int:
     extra["frame_hbm_frac_fp8"] = round(frame_bytes(shape, "fp8", kv_mean) / (ms_frame * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     extra["frame_bytes_fp8_mean"] = int(frame_bytes(shape, "fp8", kv_mean))
     extra["prefill_ms_per_token_fp8_p13"] = round(_prefill_ms(ctx, prompt) / len(prompt), 4)
+    if shape.n_layers == 36:
+        extra.update(_prefill_sizes(ctx, shape, "fp8"))
     # roofline of the dominant kernel: the persistent frame kernel is the whole decode step (every
     # weight, scale, gain and the KV once per launch); its average launch duration is the event-timed
     # decode region divided by the frame count (back-to-back launches on the library's stream, so the
@@ -240,6 +244,33 @@ def _traffic(workload: str, shape):
     if t.get("workload") != workload or t.get("source_sha256") != pmc_traffic.source_digest():
         return None
     return t["traffic_bytes_per_launch"]
+
+
+PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16; the FP8 prefill widens e4m3 weights to bf16 for the MFMA
+
+
+def prefill_flops(shape, P: int) -> float:
+    """GEMM flops (2 per weight per token) plus causal attention (QK^T and PV over the P(P+1)/2
+    visible pairs per head) of one cold P-token prefill."""
+    d, hd, F = shape.hidden, shape.head_dim, shape.ffn
+    qd, kvd = shape.q_dim, shape.kv_dim
+    per_layer = (qd + 2 * kvd) * d + d * qd + 2 * F * d + d * F
+    attn = 2 * 2 * shape.n_q_heads * hd * P * (P + 1) / 2
+    return shape.n_layers * (2 * per_layer * P + attn)
+
+
+def _prefill_sizes(ctx, shape, prec: str) -> dict:
+    """ms/token at P = 128 and 512 (seeded prompts) and the MFMA fraction at P = 512."""
+    import synthetic as S
+
+    out = {}
+    for P in (128, 512):
+        ids = S.token_ids(S.SEEDS[f"prefill_{P}"], P, shape.text_vocab)
+        ms = _prefill_ms(ctx, ids, reps=5)
+        out[f"prefill_ms_per_token_{prec}_p{P}"] = round(ms / P, 4)
+        if P == 512:
+            out[f"prefill_mfma_frac_{prec}_p512"] = round(prefill_flops(shape, P) / (ms * 1e-3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4)
+    return out
 
 
 def _prefill_ms(ctx, prompt, reps: int = 20) -> float:

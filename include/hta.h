@@ -148,10 +148,19 @@ int hta_force_codes(hta_ctx* ctx, const int32_t* codes_in);
  * layer of the last decode frame and, last, the final residual;
  * HTA_TAP_PREFILL_LAYER -> float32 [2][P][d], the rows entering and leaving
  * layer HTA_OPT_PREFILL_TAP_LAYER in the last prefill (HTA_E_STATE when the
- * taps are off).  A buffer smaller than the tap gives HTA_E_ARG. */
+ * taps are off).  With HTA_OPT_TRACE on, HTA_TAP_TRACE -> uint32
+ * [blocks][5 * n_layers + 1][8]: for every block of the persistent frame kernel
+ * and every phase of the last frame (per layer: qkv, attention, o_proj,
+ * gate/up, down; then the head), the low 32 bits of the 100 MHz constant clock
+ * at phase start, inputs ready, weights streamed and phase done, then for the
+ * block's first wave during the weight stream: core clock cycles spent waiting
+ * for weight packets, packets consumed, row sums closed, cycles spent issuing
+ * fetches (blocks = one per compute unit; entries of phases a block skips are
+ * left as they were).
+ * A buffer smaller than the tap gives HTA_E_ARG. */
 enum { HTA_TAP_HIDDEN = 0, HTA_TAP_LOGITS = 1, HTA_TAP_STATE = 2, HTA_TAP_KV = 3, HTA_TAP_AMAX = 4,
        HTA_TAP_PREFILL_HIDDEN = 5, HTA_TAP_W_QKV = 6, HTA_TAP_S_QKV = 7, HTA_TAP_W_GU = 8, HTA_TAP_S_GU = 9,
-       HTA_TAP_LAYER_H = 10, HTA_TAP_PREFILL_LAYER = 11 };
+       HTA_TAP_LAYER_H = 10, HTA_TAP_PREFILL_LAYER = 11, HTA_TAP_TRACE = 12 };
 int hta_read_tap(hta_ctx* ctx, int tap, int layer, void* host_out, size_t bytes);
 
 /* FP8 calibration on a BF16 context (FlashRT page, section 8: a short BF16
@@ -195,8 +204,9 @@ int hta_time_kernels(hta_ctx* ctx, int n_frames, float* avg_us_out, int n_classe
  * frames and prefills also write the per-layer residuals read by
  * HTA_TAP_LAYER_H / HTA_TAP_PREFILL_LAYER (frames then launch without the
  * graph); HTA_OPT_PREFILL_TAP_LAYER selects the prefill layer (0..n_layers-1,
- * else HTA_E_ARG). */
-enum { HTA_OPT_USE_GRAPH = 0, HTA_OPT_PERSISTENT = 1, HTA_OPT_TAPS = 2, HTA_OPT_PREFILL_TAP_LAYER = 3 };
+ * else HTA_E_ARG).  HTA_OPT_TRACE (default 0) records the persistent frame
+ * kernel's phase timestamps (HTA_TAP_TRACE). */
+enum { HTA_OPT_USE_GRAPH = 0, HTA_OPT_PERSISTENT = 1, HTA_OPT_TAPS = 2, HTA_OPT_PREFILL_TAP_LAYER = 3, HTA_OPT_TRACE = 4 };
 int hta_set_option(hta_ctx* ctx, int option, int value);
 
 void hta_destroy(hta_ctx* ctx);
