@@ -58,15 +58,30 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
 }
 
 // ---------------------------------------------------------------- reductions
+// Wave-wide sum / max with DPP: row shifts 1, 2, 4, 8 leave each 16-lane row's
+// result in its lane 15, two row broadcasts fold the rows into lane 63, which is
+// returned to every lane.  No LDS round trips.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_src(float x, float fill) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_src<0x111, 0xf>(v, 0.0f);  // row_shr:1
+  v += dpp_src<0x112, 0xf>(v, 0.0f);  // row_shr:2
+  v += dpp_src<0x114, 0xf>(v, 0.0f);  // row_shr:4
+  v += dpp_src<0x118, 0xf>(v, 0.0f);  // row_shr:8
+  v += dpp_src<0x142, 0xa>(v, 0.0f);  // row_bcast:15 into rows 1, 3
+  v += dpp_src<0x143, 0xc>(v, 0.0f);  // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_src<0x111, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_src<0x112, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_src<0x114, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_src<0x118, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_src<0x142, 0xa>(v, -INFINITY));
+  v = fmaxf(v, dpp_src<0x143, 0xc>(v, -INFINITY));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Block-wide sum for blockDim.x <= 1024; `red` needs blockDim.x / 64 floats.

@@ -630,23 +630,6 @@ __device__ __forceinline__ int next_gemv_phase(int phase, int n_layers) {
   return p;
 }
 
-// Sum over the wave's 64 lanes with DPP row shifts and row broadcasts (no LDS
-// round trips); the total is read from lane 63 and returned to every lane.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_add(float x) {
-  const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true);
-  return x + __int_as_float(y);
-}
-__device__ __forceinline__ float wave_total(float x) {
-  x = dpp_add<0x111, 0xf>(x);  // row_shr:1
-  x = dpp_add<0x112, 0xf>(x);  // row_shr:2
-  x = dpp_add<0x114, 0xf>(x);  // row_shr:4
-  x = dpp_add<0x118, 0xf>(x);  // row_shr:8   (lane 15 of each row: the row's sum)
-  x = dpp_add<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
-  x = dpp_add<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3 (lane 63: the total)
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
-
 template <int P>
 struct Issuer {
   const uint8_t* src;   // this lane's address in the next packet to fetch
@@ -702,11 +685,12 @@ __device__ __forceinline__ void issuer_begin(CFA& a, Issuer<P>& is, unsigned cha
 // Wait until every fetch into the ring has landed (before the block leaves the kernel).
 __device__ __forceinline__ void ring_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Consume this wave's piece of `s` from the ring, refilling each freed slot with
-// the wave's next packet.  Each lane follows its own (row, byte-in-row) position;
-// a row's partial sum is closed when the row ends inside the packet just
-// consumed and written to part[row * kFW + wave] (rows local to the block; the
-// caller zeroes part beforehand).  `cslot` is the ring slot of the next packet.
+// Consume this wave's piece of `s` from the ring, two packets per step, refilling
+// each freed slot with the wave's next packet.  Each lane follows its own (row,
+// byte-in-row) position; a row's partial sum is closed when the row ends inside
+// the packets just consumed and written to part[row * kFW + wave] (rows local to
+// the block; the caller zeroes part beforehand).  `cslot` is the ring slot of
+// the next packet.
 template <int P, int HD>
 __device__ __forceinline__ void run_stream(CFA& a, const Stream<P>& s, Issuer<P>& is, int& cslot,
                                            const unsigned char* ring_w, const uint32_t* __restrict__ xs,
@@ -715,7 +699,7 @@ __device__ __forceinline__ void run_stream(CFA& a, const Stream<P>& s, Issuer<P>
   const Piece q = make_piece<P>(s);
   if (q.npk > 0) {
     const int rb = q.rowbytes;
-    int bi = q.b0 + 16 * lane;   // this lane's byte in the piece
+    int bi = q.b0 + 16 * lane;   // this lane's byte in the piece (first packet of the step)
     int lr = bi / rb;            // its row (local)
     int kb = bi - lr * rb;       // its byte within the row
     int cur = q.b0 / rb;         // the open row (uniform)
@@ -725,18 +709,28 @@ __device__ __forceinline__ void run_stream(CFA& a, const Stream<P>& s, Issuer<P>
     const bool tr = a.trace != nullptr && w == 0;
     uint64_t t_wait = 0, t_issue = 0;
     uint32_t n_close = 0;
-    for (int i = 0; i < q.npk; ++i) {
+    for (int i = 0; i < q.npk; i += 2) {
+      const bool two = i + 1 < q.npk;  // uniform
       const uint64_t t0 = tr ? __builtin_amdgcn_s_memtime() : 0;
-      if (is.inflight >= kRD) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // loads land in issue order: with kRD in flight, the oldest two have landed once at
+      // most kRD - 2 younger ones remain outstanding
+      if (is.inflight < kRD) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else if (two) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
       if (tr) t_wait += __builtin_amdgcn_s_memtime() - t0;
-      const uint4 wv = *reinterpret_cast<const uint4*>(ring_w + cslot * 1024 + lane * 16);
-      cslot = cslot + 1 == kRD ? 0 : cslot + 1;
-      --is.inflight;
-      const float d = bi < q.b1 ? packet_dot<P>(wv, xs + kb / Stream<P>::B / 2, 0.0f) : 0.0f;
-      const int pkt_end = min(q.b0 + (i + 1) * 1024, q.b1);
-      while (row_end <= pkt_end) {  // the open row ends in this packet
-        const float v = wave_total(acc + (lr == cur ? d : 0.0f));
+      const int slot_b = cslot + 1 == kRD ? 0 : cslot + 1;
+      const uint4 wa = *reinterpret_cast<const uint4*>(ring_w + cslot * 1024 + lane * 16);
+      const uint4 wb = *reinterpret_cast<const uint4*>(ring_w + slot_b * 1024 + lane * 16);
+      // lane position in the second packet
+      int kb2 = kb + 1024, lr2 = lr;
+      while (kb2 >= rb) { kb2 -= rb; ++lr2; }
+      const float da0 = packet_dot<P>(wa, xs + kb / Stream<P>::B / 2, 0.0f);
+      const float db0 = packet_dot<P>(wb, xs + kb2 / Stream<P>::B / 2, 0.0f);
+      const float da = bi < q.b1 ? da0 : 0.0f;
+      const float db = (two && bi + 1024 < q.b1) ? db0 : 0.0f;
+      const int pkt_end = min(q.b0 + (i + (two ? 2 : 1)) * 1024, q.b1);
+      while (row_end <= pkt_end) {  // the open row ends in these packets
+        const float v = wave_sum(acc + (lr == cur ? da : 0.0f) + (lr2 == cur ? db : 0.0f));
         if (lane == 0) part[cur * kFW + w] = v;
         acc = 0.0f;
         open = false;
@@ -744,19 +738,24 @@ __device__ __forceinline__ void run_stream(CFA& a, const Stream<P>& s, Issuer<P>
         row_end += rb;
         ++n_close;
       }
-      if (row_end - rb < pkt_end) {  // the open row continues into the next packet
-        acc += lr == cur ? d : 0.0f;
+      if (row_end - rb < pkt_end) {  // the open row continues past these packets
+        acc += (lr == cur ? da : 0.0f) + (lr2 == cur ? db : 0.0f);
         open = true;
       }
-      bi += 1024;
-      kb += 1024;
+      const int step = two ? 2 : 1;
+      cslot = two ? (slot_b + 1 == kRD ? 0 : slot_b + 1) : slot_b;
+      is.inflight -= step;
+      bi += 2048;
+      kb = kb2 + 1024;
+      lr = lr2;
       while (kb >= rb) { kb -= rb; ++lr; }
       const uint64_t t1 = tr ? __builtin_amdgcn_s_memtime() : 0;
       issue_one<P, HD>(a, is, n_phases);
+      if (two) issue_one<P, HD>(a, is, n_phases);
       if (tr) t_issue += __builtin_amdgcn_s_memtime() - t1;
     }
     if (open) {
-      const float v = wave_total(acc);
+      const float v = wave_sum(acc);
       if (lane == 0) part[cur * kFW + w] = v;
     }
     if (tr) {
@@ -768,7 +767,7 @@ __device__ __forceinline__ void run_stream(CFA& a, const Stream<P>& s, Issuer<P>
   }
   __syncthreads();
 }
-static_assert(kRD == 12, "run_stream's s_waitcnt immediate is kRD - 1");
+static_assert(kRD == 12, "run_stream's s_waitcnt immediates are kRD - 1 and kRD - 2");
 
 template <int P, int HD>
 __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
