@@ -276,7 +276,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     for (int q = 0; q < kVPL; ++q) {
       const int i = q * kWave + lane;
       const bool allowed = i < a.V && ((i < a.bos) || (k == 0 && i == a.eos));
-      if (allowed && (v[q] > bv || (v[q] == bv && i < bi))) { bv = v[q]; bi = i; }
+      // a NaN logit never wins: with every allowed logit NaN the lowest allowed id is
+      // chosen, so the code stays a valid embedding row
+      const float x = v[q] == v[q] ? v[q] : -INFINITY;
+      if (allowed && (x > bv || (x == bv && i < bi))) { bv = x; bi = i; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {

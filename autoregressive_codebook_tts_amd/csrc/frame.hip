@@ -154,16 +154,25 @@ struct Stream {
   static constexpr int B = (P == kBF16) ? 2 : 1;   // bytes per element
 };
 
+// Rows [r0, r0 + n) of N rows (N / 2 gate/up pairs when pair_rows) for this block.
+__device__ __forceinline__ void block_rows(int N, int pair_rows, int* out) {
+  const unsigned units = pair_rows ? (unsigned)N / 2u : (unsigned)N;
+  const unsigned u0 = units * blockIdx.x / gridDim.x;  // units * gridDim.x < 2^31
+  const unsigned u1 = units * (blockIdx.x + 1u) / gridDim.x;
+  out[0] = (int)(pair_rows ? 2u * u0 : u0);
+  out[1] = (int)(pair_rows ? 2u * (u1 - u0) : (u1 - u0));
+}
+
+// `split` is the block's table of rows per GEMV kind in LDS, [2 * kind] = first row,
+// [2 * kind + 1] = count, filled once per launch with block_rows.
 template <int P>
-__device__ __forceinline__ Stream<P> make_stream(const void* w, int N, int K, int pair_rows) {
+__device__ __forceinline__ Stream<P> make_stream(const int* split, const void* w, int K, int kind) {
   Stream<P> s;
   s.w = static_cast<const uint8_t*>(w);
   s.K = K;
-  const int units = pair_rows ? N / 2 : N;
-  const int u0 = (int)((long)units * blockIdx.x / gridDim.x);
-  const int u1 = (int)((long)units * (blockIdx.x + 1) / gridDim.x);
-  s.r0 = pair_rows ? 2 * u0 : u0;
-  s.nrows = pair_rows ? 2 * (u1 - u0) : (u1 - u0);
+  // LDS reads are not known to be uniform: take lane 0's so that the issue path stays scalar
+  s.r0 = __builtin_amdgcn_readfirstlane(split[2 * kind]);
+  s.nrows = __builtin_amdgcn_readfirstlane(split[2 * kind + 1]);
   return s;
 }
 
@@ -181,26 +190,24 @@ __device__ __forceinline__ Piece make_piece(const Stream<P>& s) {
   Piece q;
   q.rowbytes = s.K * Stream<P>::B;
   q.base = s.w + (size_t)s.r0 * q.rowbytes;
-  const int total = s.nrows * q.rowbytes;  // a multiple of 16
-  q.b0 = (int)(((long)total * w / kFW) & ~15L);
-  q.b1 = w + 1 == kFW ? total : (int)(((long)total * (w + 1) / kFW) & ~15L);
+  const int total = s.nrows * q.rowbytes;  // a multiple of 16, total * kFW < 2^31
+  q.b0 = (total * w / kFW) & ~15;
+  q.b1 = w + 1 == kFW ? total : (total * (w + 1) / kFW) & ~15;
   q.npk = (q.b1 - q.b0 + 1023) >> 10;
   return q;
 }
 
-// bf16-pair dot of one packet with the activations xs (bf16 pairs in LDS)
+// bf16-pair dot of one packet with its activations (bf16 pairs; x1 holds the second
+// 16 bytes of an e4m3 packet's activations)
 template <int P>
-__device__ __forceinline__ float packet_dot(const uint4& wv, const uint32_t* __restrict__ xs, float s) {
+__device__ __forceinline__ float packet_dot(const uint4& wv, const uint4& x0, const uint4& x1, float s) {
   if (P == kBF16) {
-    const uint4 x = *reinterpret_cast<const uint4*>(xs);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.x), __builtin_bit_cast(bf16x2, x.x), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.y), __builtin_bit_cast(bf16x2, x.y), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.z), __builtin_bit_cast(bf16x2, x.z), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.w), __builtin_bit_cast(bf16x2, x.w), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.x), __builtin_bit_cast(bf16x2, x0.x), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.y), __builtin_bit_cast(bf16x2, x0.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.z), __builtin_bit_cast(bf16x2, x0.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.w), __builtin_bit_cast(bf16x2, x0.w), s, false);
     return s;
   } else {
-    const uint4 x0 = *reinterpret_cast<const uint4*>(xs);
-    const uint4 x1 = *reinterpret_cast<const uint4*>(xs + 4);
     const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
     const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
@@ -599,17 +606,17 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
 enum PhaseKind { kQKV = 0, kATTN = 1, kO = 2, kGU = 3, kDOWN = 4, kHEAD = 5 };
 
 template <int P, int HD>
-__device__ __forceinline__ Stream<P> phase_stream(CFA& a, int phase) {
+__device__ __forceinline__ Stream<P> phase_stream(CFA& a, const int* split, int phase) {
   const int layer = phase / 5, kind = phase % 5;
-  const int d = a.d, qd = a.Hq * HD, W = (a.Hq + 2 * a.Hkv) * HD;
-  if (layer >= a.n_layers) return make_stream<P>(a.w_head, a.C * a.V, d, 0);
+  const int d = a.d, qd = a.Hq * HD;
+  if (layer >= a.n_layers) return make_stream<P>(split, a.w_head, d, kHEAD);
   // arithmetic on the argument block only (no dependent load on the issue path)
   const unsigned char* lb = a.wl0 + (size_t)layer * a.lstride;
   switch (kind) {
-    case kQKV: return make_stream<P>(lb + a.off_wqkv, W, d, 0);
-    case kO: return make_stream<P>(lb + a.off_wo, d, qd, 0);
-    case kGU: return make_stream<P>(lb + a.off_wgu, 2 * a.F, d, 1);
-    default: return make_stream<P>(lb + a.off_wd, d, a.F, 0);
+    case kQKV: return make_stream<P>(split, lb + a.off_wqkv, d, kQKV);
+    case kO: return make_stream<P>(split, lb + a.off_wo, qd, kO);
+    case kGU: return make_stream<P>(split, lb + a.off_wgu, d, kGU);
+    default: return make_stream<P>(split, lb + a.off_wd, a.F, kDOWN);
   }
 }
 
@@ -632,142 +639,202 @@ __device__ __forceinline__ int next_gemv_phase(int phase, int n_layers) {
 
 template <int P>
 struct Issuer {
-  const uint8_t* src;   // this lane's address in the next packet to fetch
-  const uint8_t* safe;  // an in-bounds address for lanes past the piece's end
+  const uint8_t* next;  // first byte of the next packet to fetch (uniform)
   int left;             // packets of the current piece still to fetch
-  int tail;             // byte offset of the piece's end from the next packet's start
+  int tail;             // bytes of the current piece's last packet (16 .. 1024)
   int phase;            // phase of the current piece; n_phases once all are issued
   int slot;             // ring slot of the next fetch
   uint32_t m0base;      // LDS byte address of this wave's ring
-  int inflight;         // fetches not yet consumed
+  const int* split;     // the block's rows per GEMV kind (LDS)
 };
 
 template <int P>
 __device__ __forceinline__ void issuer_piece(Issuer<P>& is, const Piece& q) {
-  is.src = q.base + q.b0 + 16 * (int)(threadIdx.x & 63);
-  is.safe = q.base + q.b0;
+  is.next = q.base + q.b0;
   is.left = q.npk;
-  is.tail = q.b1 - q.b0;
+  is.tail = q.b1 - q.b0 - (q.npk - 1) * 1024;
 }
 
+// Fetch the wave's next packet into the next ring slot.  Exactly one fetch per call:
+// once every packet of the frame is issued, the last one is fetched again, so that
+// kRD fetches are always in flight and the ring's waits are constant.
 template <int P, int HD>
 __device__ __forceinline__ void issue_one(CFA& a, Issuer<P>& is, int n_phases) {
   while (is.left == 0 && is.phase < n_phases) {
     is.phase = next_gemv_phase(is.phase, a.n_layers);
-    if (is.phase < n_phases) issuer_piece(is, make_piece<P>(phase_stream<P, HD>(a, is.phase)));
+    if (is.phase < n_phases) issuer_piece(is, make_piece<P>(phase_stream<P, HD>(a, is.split, is.phase)));
   }
-  if (is.left == 0) return;
-  // lanes past the piece's end (last packet only) fetch its first bytes and are ignored
-  const uint8_t* src = 16 * (int)(threadIdx.x & 63) < is.tail ? is.src : is.safe;
+  const int lane16 = 16 * (int)(threadIdx.x & 63);
+  const bool real = is.left > 0;
+  const uint8_t* src = real ? is.next : is.next - 1024;
+  // lanes past the piece's end (its last packet only), and every lane of a repeated
+  // fetch, read the packet's first 16 bytes
+  const int voff = (!real || (is.left == 1 && lane16 >= is.tail)) ? 0 : lane16;
   // Written as inline assembly so that the compiler does not see an LDS write it
   // cannot attribute to a slot (it would wait for every fetch in flight before each
-  // ring read); the ring's waits are the explicit ones in run_stream.  M0 holds the
-  // slot's LDS byte address; each lane's 16 bytes land at M0 + 16 * lane.
-  const uint32_t m0 = is.m0base + (uint32_t)is.slot * 1024u;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
-  is.src += 1024;
-  is.tail -= 1024;
-  --is.left;
+  // ring read); the ring's waits are the explicit ones in run_stream.  The packet's
+  // address is scalar (lane offsets in a VGPR); M0 holds the slot's LDS byte
+  // address, and each lane's 16 bytes land at M0 + 16 * lane.
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(is.m0base + (uint32_t)is.slot * 1024u);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               : : "v"(voff), "s"(src), "s"(m0) : "memory", "m0");
+  if (real) {
+    is.next += 1024;
+    --is.left;
+  }
   is.slot = is.slot + 1 == kRD ? 0 : is.slot + 1;
-  ++is.inflight;
 }
 
 template <int P, int HD>
-__device__ __forceinline__ void issuer_begin(CFA& a, Issuer<P>& is, unsigned char* ring_w, int n_phases) {
+__device__ __forceinline__ void issuer_begin(CFA& a, Issuer<P>& is, unsigned char* ring_w, const int* split,
+                                             int n_phases) {
+  is.split = split;
   is.m0base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)ring_w);
   is.phase = 0;
   is.slot = 0;
-  is.inflight = 0;
-  issuer_piece(is, make_piece<P>(phase_stream<P, HD>(a, 0)));
+  issuer_piece(is, make_piece<P>(phase_stream<P, HD>(a, split, 0)));
   for (int i = 0; i < kRD; ++i) issue_one<P, HD>(a, is, n_phases);
 }
 
 // Wait until every fetch into the ring has landed (before the block leaves the kernel).
 __device__ __forceinline__ void ring_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Consume this wave's piece of `s` from the ring, two packets per step, refilling
-// each freed slot with the wave's next packet.  Each lane follows its own (row,
-// byte-in-row) position; a row's partial sum is closed when the row ends inside
-// the packets just consumed and written to part[row * kFW + wave] (rows local to
-// the block; the caller zeroes part beforehand).  `cslot` is the ring slot of
-// the next packet.
+// Waits for the oldest fetch in flight.  kRD fetches are in flight between packets
+// (one refill per consumed packet) and loads land in issue order: the oldest has
+// landed once at most kRD - 1 younger ones remain (kRD - 2 once it has been waited
+// for and its slot not yet refilled).  Other vector memory operations issued since
+// only make a wait longer.
+__device__ __forceinline__ void wait_first() { asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); }
+__device__ __forceinline__ void wait_next() { asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); }
+static_assert(kRD == 12, "the ring's s_waitcnt immediates are kRD - 1 and kRD - 2");
+
+// Position of the byte `off + lane16` of a packet, counted from the start of the row
+// it falls in, where `off` (< rb) is the packet's first byte within the open row.
+__device__ __forceinline__ int byte_in_row(int off, int lane16, int rb) {
+  int p = off + lane16;
+  if (rb >= 1024) return p >= rb ? p - rb : p;  // at most one row boundary per packet
+  while (p >= rb) p -= rb;
+  return p;
+}
+__device__ __forceinline__ int next_off(int off, int rb) {
+  int o = off + 1024;
+  if (rb >= 1024) return o >= rb ? o - rb : o;
+  while (o >= rb) o -= rb;
+  return o;
+}
+
+// One packet in registers: 16 weight bytes per lane and their activations.
+struct PacketRegs {
+  uint4 w, x0, x1;
+};
+
+template <int P>
+__device__ __forceinline__ void load_packet(PacketRegs& r, const unsigned char* ring_w, int slot, int lane16,
+                                            const uint32_t* __restrict__ xs, int off, int rb) {
+  r.w = *reinterpret_cast<const uint4*>(ring_w + slot * 1024 + lane16);
+  const uint32_t* xp = xs + byte_in_row(off, lane16, rb) / Stream<P>::B / 2;
+  r.x0 = *reinterpret_cast<const uint4*>(xp);
+  if (P == kFP8) r.x1 = *reinterpret_cast<const uint4*>(xp + 4);
+}
+
+// Row bookkeeping of one wave's stream: the open row, the current packet's first byte
+// in it, and this lane's share of it.
+struct RowAcc {
+  int row, off;
+  float acc;
+  uint32_t closes;
+};
+
+// Add packet dv (this lane's dot, zero past the piece's end) to the open row; rows that
+// end inside the packet are summed over the wave and written to part[row * kFW + w].
+__device__ __forceinline__ void add_packet(RowAcc& ra, float dv, int lane, int lane16, int rb, int nrows,
+                                           float* __restrict__ part, int w) {
+  if (ra.off + 1024 < rb) {  // the packet lies inside the open row
+    ra.acc += dv;
+    return;
+  }
+  int lo = 0, hi = rb - ra.off;  // lanes with lo <= lane16 < hi belong to the open row
+  while (hi <= 1024) {
+    const float v = wave_sum(ra.acc + (lane16 >= lo && lane16 < hi ? dv : 0.0f));
+    if (lane == 0 && ra.row < nrows) part[ra.row * kFW + w] = v;
+    ra.acc = 0.0f;
+    ++ra.row;
+    ++ra.closes;
+    lo = hi;
+    hi += rb;
+  }
+  ra.acc = lane16 >= lo ? dv : 0.0f;
+}
+
+// Consume this wave's piece of `s` from the ring, refilling each consumed slot with
+// the wave's next packet; packet i + 1 is read from LDS while packet i is computed.
+// The open row and the packet's offset in it are uniform: a lane's 16 bytes lie in
+// the open row or, where a row ends inside the packet, in a later one.  A row's
+// partial sum is written to part[row * kFW + wave] when the row ends (rows local to
+// the block; the caller zeroes part beforehand).  `cslot` is the ring slot of the
+// next packet.
 template <int P, int HD>
 __device__ __forceinline__ void run_stream(CFA& a, const Stream<P>& s, Issuer<P>& is, int& cslot,
                                            const unsigned char* ring_w, const uint32_t* __restrict__ xs,
                                            float* __restrict__ part, int n_phases, int phase) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane16 = 16 * lane;
   const Piece q = make_piece<P>(s);
   if (q.npk > 0) {
     const int rb = q.rowbytes;
-    int bi = q.b0 + 16 * lane;   // this lane's byte in the piece (first packet of the step)
-    int lr = bi / rb;            // its row (local)
-    int kb = bi - lr * rb;       // its byte within the row
-    int cur = q.b0 / rb;         // the open row (uniform)
-    int row_end = (cur + 1) * rb;
-    float acc = 0.0f;
-    bool open = false;
-    const bool tr = a.trace != nullptr && w == 0;
-    uint64_t t_wait = 0, t_issue = 0;
-    uint32_t n_close = 0;
-    for (int i = 0; i < q.npk; i += 2) {
-      const bool two = i + 1 < q.npk;  // uniform
-      const uint64_t t0 = tr ? __builtin_amdgcn_s_memtime() : 0;
-      // loads land in issue order: with kRD in flight, the oldest two have landed once at
-      // most kRD - 2 younger ones remain outstanding
-      if (is.inflight < kRD) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      else if (two) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
-      if (tr) t_wait += __builtin_amdgcn_s_memtime() - t0;
-      const int slot_b = cslot + 1 == kRD ? 0 : cslot + 1;
-      const uint4 wa = *reinterpret_cast<const uint4*>(ring_w + cslot * 1024 + lane * 16);
-      const uint4 wb = *reinterpret_cast<const uint4*>(ring_w + slot_b * 1024 + lane * 16);
-      // lane position in the second packet
-      int kb2 = kb + 1024, lr2 = lr;
-      while (kb2 >= rb) { kb2 -= rb; ++lr2; }
-      const float da0 = packet_dot<P>(wa, xs + kb / Stream<P>::B / 2, 0.0f);
-      const float db0 = packet_dot<P>(wb, xs + kb2 / Stream<P>::B / 2, 0.0f);
-      const float da = bi < q.b1 ? da0 : 0.0f;
-      const float db = (two && bi + 1024 < q.b1) ? db0 : 0.0f;
-      const int pkt_end = min(q.b0 + (i + (two ? 2 : 1)) * 1024, q.b1);
-      while (row_end <= pkt_end) {  // the open row ends in these packets
-        const float v = wave_sum(acc + (lr == cur ? da : 0.0f) + (lr2 == cur ? db : 0.0f));
-        if (lane == 0) part[cur * kFW + w] = v;
-        acc = 0.0f;
-        open = false;
-        ++cur;
-        row_end += rb;
-        ++n_close;
-      }
-      if (row_end - rb < pkt_end) {  // the open row continues past these packets
-        acc += (lr == cur ? da : 0.0f) + (lr2 == cur ? db : 0.0f);
-        open = true;
-      }
-      const int step = two ? 2 : 1;
-      cslot = two ? (slot_b + 1 == kRD ? 0 : slot_b + 1) : slot_b;
-      is.inflight -= step;
-      bi += 2048;
-      kb = kb2 + 1024;
-      lr = lr2;
-      while (kb >= rb) { kb -= rb; ++lr; }
-      const uint64_t t1 = tr ? __builtin_amdgcn_s_memtime() : 0;
+    const int last_bytes = q.b1 - q.b0 - (q.npk - 1) * 1024;
+    RowAcc ra;
+    ra.row = q.b0 / rb;
+    ra.off = q.b0 - ra.row * rb;
+    ra.acc = 0.0f;
+    ra.closes = 0;
+    PacketRegs A, B;
+    // Every load the compiler knows of has landed here (the prologue's polls are younger
+    // than the ring's fetches, so the ring has landed too).  Saying so with a wait it can
+    // see keeps it from waiting for vector memory inside the loop.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
+    wait_first();
+    load_packet<P>(A, ring_w, cslot, lane16, xs, ra.off, rb);
+    // two packets per iteration, alternating register sets
+    for (int i = 0;; i += 2) {
+      int off1 = next_off(ra.off, rb);
+      const int slot1 = cslot + 1 == kRD ? 0 : cslot + 1;
+      // (after the piece's last packet the next reads are made all the same, and unused,
+      // so that the loop has no branch around them)
+      if (i + 1 < q.npk) wait_next();
+      load_packet<P>(B, ring_w, slot1, lane16, xs, off1, rb);
+      float dv = packet_dot<P>(A.w, A.x0, A.x1, 0.0f);
+      if (i + 1 == q.npk && lane16 >= last_bytes) dv = 0.0f;  // past the piece's end
+      add_packet(ra, dv, lane, lane16, rb, s.nrows, part, w);
+      ra.off = off1;
+      cslot = slot1;
       issue_one<P, HD>(a, is, n_phases);
-      if (two) issue_one<P, HD>(a, is, n_phases);
-      if (tr) t_issue += __builtin_amdgcn_s_memtime() - t1;
+      if (i + 1 >= q.npk) break;
+
+      const int off2 = next_off(ra.off, rb);
+      const int slot2 = cslot + 1 == kRD ? 0 : cslot + 1;
+      if (i + 2 < q.npk) wait_next();
+      load_packet<P>(A, ring_w, slot2, lane16, xs, off2, rb);
+      dv = packet_dot<P>(B.w, B.x0, B.x1, 0.0f);
+      if (i + 2 == q.npk && lane16 >= last_bytes) dv = 0.0f;
+      add_packet(ra, dv, lane, lane16, rb, s.nrows, part, w);
+      ra.off = off2;
+      cslot = slot2;
+      issue_one<P, HD>(a, is, n_phases);
+      if (i + 2 >= q.npk) break;
     }
-    if (open) {
-      const float v = wave_sum(acc);
-      if (lane == 0) part[cur * kFW + w] = v;
+    // the open row's share (zero where the piece ended on a row end)
+    if (ra.row < s.nrows) {
+      const float v = wave_sum(ra.acc);
+      if (lane == 0) part[ra.row * kFW + w] = v;
     }
-    if (tr) {
-      trace_put(a, n_phases, phase, 4, (uint32_t)t_wait);
-      trace_put(a, n_phases, phase, 5, (uint32_t)q.npk);
-      trace_put(a, n_phases, phase, 6, n_close);
-      trace_put(a, n_phases, phase, 7, (uint32_t)t_issue);
+    if (a.trace != nullptr && w == 0) {
+      trace_put(a, n_phases, phase, 4, (uint32_t)q.npk);
+      trace_put(a, n_phases, phase, 5, ra.closes);
     }
   }
   __syncthreads();
 }
-static_assert(kRD == 12, "run_stream's s_waitcnt immediates are kRD - 1 and kRD - 2");
 
 template <int P, int HD>
 __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
@@ -782,6 +849,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
   __shared__ float red[16];
   __shared__ int sh_state[4 + kMaxCodebooks];
   __shared__ int okf;
+  __shared__ int split[12];  // this block's rows per GEMV kind
   const int tid = threadIdx.x;
   unsigned* abort_flag = a.sync + 64;
   const unsigned launch = a.sync[0];
@@ -789,12 +857,20 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
   const unsigned base = (launch + 1u) * (8u + 8u * (unsigned)a.n_layers);
 
   if (tid == 0) {
+    // its own laundered view of the arguments: a load here that the compiler merged with
+    // the same load after the branch would make that value (and the issue path) divergent
+    CFA& a = *launder(ap);
     sh_state[0] = a.st->len;
     sh_state[1] = a.st->t;
     int eoc = a.st->eoc;
     if (eoc < 0 && a.st->t > 0 && a.st->prev[0] == a.eos) eoc = a.st->t - 1;
     sh_state[2] = eoc;
     for (int c = 0; c < a.C; ++c) sh_state[4 + c] = a.st->prev[c];
+    block_rows((a.Hq + 2 * a.Hkv) * HD, 0, split + 2 * kQKV);
+    block_rows(a.d, 0, split + 2 * kO);
+    block_rows(2 * a.F, 1, split + 2 * kGU);
+    block_rows(a.d, 0, split + 2 * kDOWN);
+    block_rows(a.C * a.V, 0, split + 2 * kHEAD);
   }
   __syncthreads();
   const int pos = sh_state[0];
@@ -802,7 +878,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
 
   const int n_phases = 5 * a.n_layers + 1;
   Issuer<P> is;
-  issuer_begin<P, HD>(a, is, ring_w, n_phases);
+  issuer_begin<P, HD>(a, is, ring_w, split, n_phases);
   int cslot = 0;  // ring slot of the next packet to consume
   for (int i = tid; i < kPartMax; i += kFT) part[i] = 0.0f;
 
@@ -811,7 +887,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
   // owned rows (at most one per thread) stay in h_own for the residual updates.
   float h_own = 0.0f;
   {
-    const Stream<P> own = make_stream<P>(nullptr, d, 1, 0);
+    const Stream<P> own = make_stream<P>(split, nullptr, 1, kO);
     constexpr int kMaxPer = 10;  // d <= 10 * kFT
     float hv[kMaxPer];
     float ss = 0.0f;
@@ -821,6 +897,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
       hv[i] = 0.0f;
       if (k < d) {
         float v = 0.0f;
+#pragma unroll 1
         for (int c = 0; c < a.C; ++c) v += bf16_to_f32(*gp(a.e_aud + ((size_t)c * a.V + sh_state[4 + c]) * d + k));
         hv[i] = v;
         ss = fmaf(v, v, ss);
@@ -829,6 +906,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     if (tid < own.nrows) {
       const int k = own.r0 + tid;
       float v = 0.0f;
+#pragma unroll 1
       for (int c = 0; c < a.C; ++c) v += bf16_to_f32(*gp(a.e_aud + ((size_t)c * a.V + sh_state[4 + c]) * d + k));
       h_own = v;
       st64(a.xh + k, v, base);
@@ -865,7 +943,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     const int site = kind == kHEAD ? kSitesPerLayer * a.n_layers
                    : kSitesPerLayer * layer + (kind == kQKV ? 0 : kind == kO ? 1 : kind == kGU ? 2 : 3);
     const float sc_in = P == kFP8 ? a.act_scales[site] : 1.0f;
-    const Stream<P> cur = phase_stream<P, HD>(a, phase);
+    const Stream<P> cur = phase_stream<P, HD>(a, split, phase);
     // FP8 row scales of this block's rows (at most one row, or one gate/up pair, per
     // thread), loaded before the prologue waits so that the epilogue finds them ready
     float ws0 = 1.0f, ws1 = 1.0f;
@@ -966,7 +1044,10 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
         const float v = __uint_as_float((uint32_t)lw[q]);
         *gpw(a.logits_out + (size_t)k * a.V + i) = v;
         const bool allowed = (i < a.bos) || (k == 0 && i == a.eos);
-        if (allowed && (v > bv || (v == bv && i < bi))) { bv = v; bi = i; }
+        // a NaN logit never wins: with every allowed logit NaN the lowest allowed id is
+        // chosen, so the code stays a valid embedding row
+        const float x = v == v ? v : -INFINITY;
+        if (allowed && (x > bv || (x == bv && i < bi))) { bv = x; bi = i; }
       }
     }
 #pragma unroll

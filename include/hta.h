@@ -112,7 +112,8 @@ int hta_prefill(hta_ctx* ctx, const int32_t* tokens, int P);
 
 /* One decode frame (FlashRT page, section 5): embed the previous codes (all
  * BOS for the first frame), run the backbone at position len, the fused head,
- * the greedy argmax under the delay pattern; write the 8 delayed codes of this
+ * the greedy argmax under the delay pattern (lowest id on ties; a NaN logit
+ * never wins, so a code is always a valid id); write the 8 delayed codes of this
  * step to codes_out (host).  Returns HTA_OK, or HTA_DONE when this step
  * completed the utterance; later calls keep returning all-EOS frames with the
  * same work.  HTA_E_CAPACITY when len == max_seq. */
@@ -153,10 +154,9 @@ int hta_force_codes(hta_ctx* ctx, const int32_t* codes_in);
  * and every phase of the last frame (per layer: qkv, attention, o_proj,
  * gate/up, down; then the head), the low 32 bits of the 100 MHz constant clock
  * at phase start, inputs ready, weights streamed and phase done, then for the
- * block's first wave during the weight stream: core clock cycles spent waiting
- * for weight packets, packets consumed, row sums closed, cycles spent issuing
- * fetches (blocks = one per compute unit; entries of phases a block skips are
- * left as they were).
+ * block's first wave: weight packets consumed and row sums closed in the
+ * phase, and two words left as they were (blocks = one per compute unit;
+ * entries of phases a block skips are left as they were).
  * A buffer smaller than the tap gives HTA_E_ARG. */
 enum { HTA_TAP_HIDDEN = 0, HTA_TAP_LOGITS = 1, HTA_TAP_STATE = 2, HTA_TAP_KV = 3, HTA_TAP_AMAX = 4,
        HTA_TAP_PREFILL_HIDDEN = 5, HTA_TAP_W_QKV = 6, HTA_TAP_S_QKV = 7, HTA_TAP_W_GU = 8, HTA_TAP_S_GU = 9,
