@@ -135,7 +135,8 @@ __device__ __forceinline__ bool block_ok(bool ok, int* flag) {
   __syncthreads();
   if (!ok) *flag = 0;
   __syncthreads();
-  return *flag != 0;
+  // every thread reads the same word: take lane 0's, so the branches on it stay uniform
+  return __builtin_amdgcn_readfirstlane(*flag) != 0;
 }
 
 // ---------------------------------------------------------------- the rows of one GEMV phase
@@ -198,15 +199,15 @@ __device__ __forceinline__ Piece make_piece(const Stream<P>& s) {
 }
 
 // bf16-pair dot of one packet with its activations (bf16 pairs; x1 holds the second
-// 16 bytes of an e4m3 packet's activations)
+// 16 bytes of an e4m3 packet's activations), in two partial chains
 template <int P>
-__device__ __forceinline__ float packet_dot(const uint4& wv, const uint4& x0, const uint4& x1, float s) {
+__device__ __forceinline__ float packet_dot(const uint4& wv, const uint4& x0, const uint4& x1) {
+  float s0 = 0.0f, s1 = 0.0f;
   if (P == kBF16) {
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.x), __builtin_bit_cast(bf16x2, x0.x), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.y), __builtin_bit_cast(bf16x2, x0.y), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.z), __builtin_bit_cast(bf16x2, x0.z), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.w), __builtin_bit_cast(bf16x2, x0.w), s, false);
-    return s;
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.x), __builtin_bit_cast(bf16x2, x0.x), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.y), __builtin_bit_cast(bf16x2, x0.y), s1, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.z), __builtin_bit_cast(bf16x2, x0.z), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.w), __builtin_bit_cast(bf16x2, x0.w), s1, false);
   } else {
     const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
     const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -214,11 +215,11 @@ __device__ __forceinline__ float packet_dot(const uint4& wv, const uint4& x0, co
     for (int i = 0; i < 4; ++i) {
       const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ws[i], 1.0f, false);
       const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ws[i], 1.0f, true);
-      s = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2, xw[2 * i]), s, false);
-      s = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, xw[2 * i + 1]), s, false);
+      s0 = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2, xw[2 * i]), s0, false);
+      s1 = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2, xw[2 * i + 1]), s1, false);
     }
-    return s;
   }
+  return s0 + s1;
 }
 
 // Sum of a row's per-wave partials in wave order (deterministic); zeroes them for the next phase.
@@ -343,12 +344,15 @@ __device__ __forceinline__ bool act_to_lds(const uint32_t* x, unsigned tag, int 
 // [0] phase start, [1] inputs ready, [2] weights streamed, [3] phase done; and, for
 // wave 0 of the block during the weight stream (core clock cycles): [4] waiting for
 // ring packets, [5] packets consumed, [6] row sums closed, [7] issuing fetches.
-__device__ __forceinline__ void trace_mark(CFA& a, int n_phases, int phase, int i) {
-  if (a.trace && threadIdx.x == 0)
-    *gpw(a.trace + ((size_t)blockIdx.x * n_phases + phase) * 8 + i) = (uint32_t)__builtin_amdgcn_s_memrealtime();
-}
+// Trace words are written by every lane of wave 0 (the same value to the same word):
+// a branch on the wave index is uniform, where one on the thread index would be a
+// divergent branch that the compiler may thread through the whole phase loop.
 __device__ __forceinline__ void trace_put(CFA& a, int n_phases, int phase, int i, uint32_t v) {
-  if (a.trace && threadIdx.x == 0) *gpw(a.trace + ((size_t)blockIdx.x * n_phases + phase) * 8 + i) = v;
+  if (a.trace != nullptr && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0)
+    *gpw(a.trace + ((size_t)blockIdx.x * n_phases + phase) * 8 + i) = __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ void trace_mark(CFA& a, int n_phases, int phase, int i) {
+  trace_put(a, n_phases, phase, i, (uint32_t)__builtin_amdgcn_s_memrealtime());
 }
 
 // ---------------------------------------------------------------- attention task (split-K, one kv head)
@@ -699,26 +703,50 @@ __device__ __forceinline__ void issuer_begin(CFA& a, Issuer<P>& is, unsigned cha
 // Wait until every fetch into the ring has landed (before the block leaves the kernel).
 __device__ __forceinline__ void ring_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Waits for the oldest fetch in flight.  kRD fetches are in flight between packets
-// (one refill per consumed packet) and loads land in issue order: the oldest has
-// landed once at most kRD - 1 younger ones remain (kRD - 2 once it has been waited
-// for and its slot not yet refilled).  Other vector memory operations issued since
-// only make a wait longer.
-__device__ __forceinline__ void wait_first() { asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); }
-__device__ __forceinline__ void wait_next() { asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); }
+// Fetch the wave's next two packets (one issue_one each, with a shorter path where
+// neither ends a piece).
+template <int P, int HD>
+__device__ __forceinline__ void issue_two(CFA& a, Issuer<P>& is, int n_phases) {
+  if (is.left >= 3) {
+    const int lane16 = 16 * (int)(threadIdx.x & 63);
+    const int s2 = is.slot + 1 == kRD ? 0 : is.slot + 1;
+    const uint32_t m0a = __builtin_amdgcn_readfirstlane(is.m0base + (uint32_t)is.slot * 1024u);
+    const uint32_t m0b = __builtin_amdgcn_readfirstlane(is.m0base + (uint32_t)s2 * 1024u);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 : : "v"(lane16), "s"(is.next), "s"(m0a) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:1024"
+                 : : "v"(lane16), "s"(is.next), "s"(m0b) : "memory", "m0");
+    is.next += 2048;
+    is.left -= 2;
+    is.slot = s2 + 1 == kRD ? 0 : s2 + 1;
+  } else {
+    issue_one<P, HD>(a, is, n_phases);
+    issue_one<P, HD>(a, is, n_phases);
+  }
+}
+
+// Ring waits.  kRD fetches are in flight whenever a step of the stream begins (every
+// consumed packet is replaced by one fetch) and loads land in issue order, so the
+// oldest n have landed once at most kRD - n younger ones remain outstanding.  Other
+// vector memory operations issued since only make a wait longer.
+__device__ __forceinline__ void wait_oldest1() { asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); }
+__device__ __forceinline__ void wait_oldest2() { asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); }
 static_assert(kRD == 12, "the ring's s_waitcnt immediates are kRD - 1 and kRD - 2");
 
 // Position of the byte `off + lane16` of a packet, counted from the start of the row
 // it falls in, where `off` (< rb) is the packet's first byte within the open row.
+// LONG: rows of at least 1 KB, so at most one row boundary per packet.
+template <bool LONG>
 __device__ __forceinline__ int byte_in_row(int off, int lane16, int rb) {
   int p = off + lane16;
-  if (rb >= 1024) return p >= rb ? p - rb : p;  // at most one row boundary per packet
+  if (LONG) return p >= rb ? p - rb : p;
   while (p >= rb) p -= rb;
   return p;
 }
+template <bool LONG>
 __device__ __forceinline__ int next_off(int off, int rb) {
   int o = off + 1024;
-  if (rb >= 1024) return o >= rb ? o - rb : o;
+  if (LONG) return o >= rb ? o - rb : o;
   while (o >= rb) o -= rb;
   return o;
 }
@@ -730,11 +758,27 @@ struct PacketRegs {
 
 template <int P>
 __device__ __forceinline__ void load_packet(PacketRegs& r, const unsigned char* ring_w, int slot, int lane16,
-                                            const uint32_t* __restrict__ xs, int off, int rb) {
+                                            const uint32_t* __restrict__ xs, int p) {
   r.w = *reinterpret_cast<const uint4*>(ring_w + slot * 1024 + lane16);
-  const uint32_t* xp = xs + byte_in_row(off, lane16, rb) / Stream<P>::B / 2;
+  const uint32_t* xp = xs + p / Stream<P>::B / 2;
   r.x0 = *reinterpret_cast<const uint4*>(xp);
   if (P == kFP8) r.x1 = *reinterpret_cast<const uint4*>(xp + 4);
+}
+
+// Store the wave-uniform v to the LDS word p from lane 0 only, without a branch on the
+// lane index: such a branch is divergent control flow, and the compiler may merge code
+// across it in ways that make the (uniform) fetch state look divergent.  The store
+// completes before the statement ends.
+__device__ __forceinline__ void lane0_lds_store(float* p, float v) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(lds_void_t*)p;
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "ds_write_b32 %1, %2\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved) : "v"(addr), "v"(v) : "memory");
 }
 
 // Row bookkeeping of one wave's stream: the open row, the current packet's first byte
@@ -747,91 +791,106 @@ struct RowAcc {
 
 // Add packet dv (this lane's dot, zero past the piece's end) to the open row; rows that
 // end inside the packet are summed over the wave and written to part[row * kFW + w].
+template <bool LONG>
 __device__ __forceinline__ void add_packet(RowAcc& ra, float dv, int lane, int lane16, int rb, int nrows,
                                            float* __restrict__ part, int w) {
-  if (ra.off + 1024 < rb) {  // the packet lies inside the open row
+  const int hi = rb - ra.off;  // lanes with lane16 < hi belong to the open row
+  if (hi > 1024) {             // the packet lies inside the open row
     ra.acc += dv;
+    ra.off += 1024;
     return;
   }
-  int lo = 0, hi = rb - ra.off;  // lanes with lo <= lane16 < hi belong to the open row
-  while (hi <= 1024) {
-    const float v = wave_sum(ra.acc + (lane16 >= lo && lane16 < hi ? dv : 0.0f));
-    if (lane == 0 && ra.row < nrows) part[ra.row * kFW + w] = v;
+  if (LONG) {  // exactly one row ends inside the packet
+    const bool mine = lane16 < hi;
+    const float v = wave_sum(ra.acc + (mine ? dv : 0.0f));
+    if (ra.row < nrows) lane0_lds_store(part + ra.row * kFW + w, v);
+    ra.acc = mine ? 0.0f : dv;
+    ++ra.row;
+    ++ra.closes;
+    ra.off += 1024 - rb;
+    return;
+  }
+  int lo = 0, h = hi;
+  while (h <= 1024) {
+    const float v = wave_sum(ra.acc + (lane16 >= lo && lane16 < h ? dv : 0.0f));
+    if (ra.row < nrows) lane0_lds_store(part + ra.row * kFW + w, v);
     ra.acc = 0.0f;
     ++ra.row;
     ++ra.closes;
-    lo = hi;
-    hi += rb;
+    lo = h;
+    h += rb;
   }
   ra.acc = lane16 >= lo ? dv : 0.0f;
+  ra.off = 1024 - lo;
 }
 
-// Consume this wave's piece of `s` from the ring, refilling each consumed slot with
-// the wave's next packet; packet i + 1 is read from LDS while packet i is computed.
-// The open row and the packet's offset in it are uniform: a lane's 16 bytes lie in
-// the open row or, where a row ends inside the packet, in a later one.  A row's
-// partial sum is written to part[row * kFW + wave] when the row ends (rows local to
-// the block; the caller zeroes part beforehand).  `cslot` is the ring slot of the
-// next packet.
+// Consume this wave's piece q from the ring, two packets per step, refilling each
+// consumed slot with the wave's next packet.  The open row and the packet's offset in
+// it are uniform: a lane's 16 bytes lie in the open row or, where a row ends inside
+// the packet, in a later one.  A row's partial sum is written to part[row * kFW +
+// wave] when the row ends (rows local to the block; the caller zeroes part
+// beforehand).  `cslot` is the ring slot of the next packet.
+template <int P, int HD, bool LONG>
+__device__ __forceinline__ void stream_piece(CFA& a, const Piece& q, int nrows, Issuer<P>& is, int& cslot,
+                                             const unsigned char* ring_w, const uint32_t* __restrict__ xs,
+                                             float* __restrict__ part, int n_phases, uint32_t& closes) {
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane16 = 16 * lane;
+  const int rb = q.rowbytes;
+  const int last_bytes = q.b1 - q.b0 - (q.npk - 1) * 1024;
+  RowAcc ra;
+  ra.row = q.b0 / rb;
+  ra.off = q.b0 - ra.row * rb;
+  ra.acc = 0.0f;
+  ra.closes = 0;
+  // Every load the compiler knows of has landed here (the prologue's polls are younger
+  // than the ring's fetches, so the ring has landed too).  Saying so with a wait it can
+  // see keeps it from waiting for vector memory inside the loop.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
+  int i = 0;
+  for (; i + 2 <= q.npk; i += 2) {
+    wait_oldest2();
+    const int s1 = cslot + 1 == kRD ? 0 : cslot + 1;
+    const int off1 = next_off<LONG>(ra.off, rb);
+    PacketRegs A, B;
+    load_packet<P>(A, ring_w, cslot, lane16, xs, byte_in_row<LONG>(ra.off, lane16, rb));
+    load_packet<P>(B, ring_w, s1, lane16, xs, byte_in_row<LONG>(off1, lane16, rb));
+    const float d0 = packet_dot<P>(A.w, A.x0, A.x1);
+    float d1 = packet_dot<P>(B.w, B.x0, B.x1);
+    if (i + 2 == q.npk && lane16 >= last_bytes) d1 = 0.0f;  // past the piece's end
+    add_packet<LONG>(ra, d0, lane, lane16, rb, nrows, part, w);
+    add_packet<LONG>(ra, d1, lane, lane16, rb, nrows, part, w);
+    cslot = s1 + 1 == kRD ? 0 : s1 + 1;
+    issue_two<P, HD>(a, is, n_phases);
+  }
+  if (i < q.npk) {  // odd count: the piece's last packet
+    wait_oldest1();
+    PacketRegs A;
+    load_packet<P>(A, ring_w, cslot, lane16, xs, byte_in_row<LONG>(ra.off, lane16, rb));
+    float d0 = packet_dot<P>(A.w, A.x0, A.x1);
+    if (lane16 >= last_bytes) d0 = 0.0f;
+    add_packet<LONG>(ra, d0, lane, lane16, rb, nrows, part, w);
+    cslot = cslot + 1 == kRD ? 0 : cslot + 1;
+    issue_one<P, HD>(a, is, n_phases);
+  }
+  // the open row's share (zero where the piece ended on a row end)
+  if (ra.row < nrows) lane0_lds_store(part + ra.row * kFW + w, wave_sum(ra.acc));
+  closes = ra.closes;
+}
+
 template <int P, int HD>
 __device__ __forceinline__ void run_stream(CFA& a, const Stream<P>& s, Issuer<P>& is, int& cslot,
                                            const unsigned char* ring_w, const uint32_t* __restrict__ xs,
                                            float* __restrict__ part, int n_phases, int phase) {
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane16 = 16 * lane;
   const Piece q = make_piece<P>(s);
   if (q.npk > 0) {
-    const int rb = q.rowbytes;
-    const int last_bytes = q.b1 - q.b0 - (q.npk - 1) * 1024;
-    RowAcc ra;
-    ra.row = q.b0 / rb;
-    ra.off = q.b0 - ra.row * rb;
-    ra.acc = 0.0f;
-    ra.closes = 0;
-    PacketRegs A, B;
-    // Every load the compiler knows of has landed here (the prologue's polls are younger
-    // than the ring's fetches, so the ring has landed too).  Saying so with a wait it can
-    // see keeps it from waiting for vector memory inside the loop.
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
-    wait_first();
-    load_packet<P>(A, ring_w, cslot, lane16, xs, ra.off, rb);
-    // two packets per iteration, alternating register sets
-    for (int i = 0;; i += 2) {
-      int off1 = next_off(ra.off, rb);
-      const int slot1 = cslot + 1 == kRD ? 0 : cslot + 1;
-      // (after the piece's last packet the next reads are made all the same, and unused,
-      // so that the loop has no branch around them)
-      if (i + 1 < q.npk) wait_next();
-      load_packet<P>(B, ring_w, slot1, lane16, xs, off1, rb);
-      float dv = packet_dot<P>(A.w, A.x0, A.x1, 0.0f);
-      if (i + 1 == q.npk && lane16 >= last_bytes) dv = 0.0f;  // past the piece's end
-      add_packet(ra, dv, lane, lane16, rb, s.nrows, part, w);
-      ra.off = off1;
-      cslot = slot1;
-      issue_one<P, HD>(a, is, n_phases);
-      if (i + 1 >= q.npk) break;
-
-      const int off2 = next_off(ra.off, rb);
-      const int slot2 = cslot + 1 == kRD ? 0 : cslot + 1;
-      if (i + 2 < q.npk) wait_next();
-      load_packet<P>(A, ring_w, slot2, lane16, xs, off2, rb);
-      dv = packet_dot<P>(B.w, B.x0, B.x1, 0.0f);
-      if (i + 2 == q.npk && lane16 >= last_bytes) dv = 0.0f;
-      add_packet(ra, dv, lane, lane16, rb, s.nrows, part, w);
-      ra.off = off2;
-      cslot = slot2;
-      issue_one<P, HD>(a, is, n_phases);
-      if (i + 2 >= q.npk) break;
-    }
-    // the open row's share (zero where the piece ended on a row end)
-    if (ra.row < s.nrows) {
-      const float v = wave_sum(ra.acc);
-      if (lane == 0) part[ra.row * kFW + w] = v;
-    }
-    if (a.trace != nullptr && w == 0) {
-      trace_put(a, n_phases, phase, 4, (uint32_t)q.npk);
-      trace_put(a, n_phases, phase, 5, ra.closes);
-    }
+    uint32_t closes = 0;
+    if (q.rowbytes >= 1024)
+      stream_piece<P, HD, true>(a, q, s.nrows, is, cslot, ring_w, xs, part, n_phases, closes);
+    else
+      stream_piece<P, HD, false>(a, q, s.nrows, is, cslot, ring_w, xs, part, n_phases, closes);
+    trace_put(a, n_phases, phase, 4, (uint32_t)q.npk);
+    trace_put(a, n_phases, phase, 5, closes);
   }
   __syncthreads();
 }
@@ -873,7 +932,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     block_rows(a.C * a.V, 0, split + 2 * kHEAD);
   }
   __syncthreads();
-  const int pos = sh_state[0];
+  const int pos = __builtin_amdgcn_readfirstlane(sh_state[0]);  // uniform (LDS reads are not known to be)
   const int d = a.d;
 
   const int n_phases = 5 * a.n_layers + 1;
