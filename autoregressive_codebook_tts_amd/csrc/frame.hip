@@ -712,10 +712,11 @@ __device__ __forceinline__ void issue_two(CFA& a, Issuer<P>& is, int n_phases) {
     const int s2 = is.slot + 1 == kRD ? 0 : is.slot + 1;
     const uint32_t m0a = __builtin_amdgcn_readfirstlane(is.m0base + (uint32_t)is.slot * 1024u);
     const uint32_t m0b = __builtin_amdgcn_readfirstlane(is.m0base + (uint32_t)s2 * 1024u);
+    // (two scalar addresses: an instruction offset would move the LDS destination too)
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  : : "v"(lane16), "s"(is.next), "s"(m0a) : "memory", "m0");
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:1024"
-                 : : "v"(lane16), "s"(is.next), "s"(m0b) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 : : "v"(lane16), "s"(is.next + 1024), "s"(m0b) : "memory", "m0");
     is.next += 2048;
     is.left -= 2;
     is.slot = s2 + 1 == kRD ? 0 : s2 + 1;
@@ -768,16 +769,20 @@ __device__ __forceinline__ void load_packet(PacketRegs& r, const unsigned char* 
 // Store the wave-uniform v to the LDS word p from lane 0 only, without a branch on the
 // lane index: such a branch is divergent control flow, and the compiler may merge code
 // across it in ways that make the (uniform) fetch state look divergent.  The store
-// completes before the statement ends.
+// completes before the statement ends.  The compiler does not see the EXEC writes, so
+// each is followed by the wait states that a later DPP or lane-select instruction
+// needs after an SALU write of EXEC (five).
 __device__ __forceinline__ void lane0_lds_store(float* p, float v) {
   const uint32_t addr = (uint32_t)(uintptr_t)(lds_void_t*)p;
   uint64_t saved;
   asm volatile(
       "s_mov_b64 %0, exec\n\t"
       "s_mov_b64 exec, 1\n\t"
+      "s_nop 4\n\t"
       "ds_write_b32 %1, %2\n\t"
       "s_waitcnt lgkmcnt(0)\n\t"
-      "s_mov_b64 exec, %0"
+      "s_mov_b64 exec, %0\n\t"
+      "s_nop 4"
       : "=&s"(saved) : "v"(addr), "v"(v) : "memory");
 }
 

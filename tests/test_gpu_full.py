@@ -317,6 +317,26 @@ def test_full_prefill_end_to_end(request, precision, P):
     assert rel <= E2E_RATIO * rel_s
 
 
+# ----------------------------------------------------------------------------- determinism
+@pytest.mark.parametrize("precision", ["bf16", "fp8"])
+def test_full_decode_is_deterministic(request, precision):
+    """The one-launch frame fixes every reduction order, so the same state decoded twice
+    gives bit-identical hidden states, logits and codes (a stale or misplaced weight
+    fetch into the LDS ring shows up here first)."""
+    ctx, _ = _ctx_and_oracle(request, precision)
+    prompt = S.token_ids(S.SEEDS["full_prompt"], 13, SH.text_vocab)
+    runs = []
+    for _ in range(2):
+        ctx.reset(0)
+        ctx.prefill(prompt)
+        codes, _ = ctx.decode_frames(4)
+        runs.append((codes, ctx.tap_hidden().copy(), ctx.tap_logits().copy()))
+    assert np.array_equal(runs[0][0], runs[1][0]), "codes differ between identical runs"
+    assert np.array_equal(runs[0][1], runs[1][1]), "hidden state differs between identical runs"
+    assert np.array_equal(runs[0][2], runs[1][2]), "logits differ between identical runs"
+    _say(f"[full] {precision} decode: two identical runs bit-identical")
+
+
 # ----------------------------------------------------------------------------- prefix reuse
 @pytest.mark.parametrize("precision", ["bf16", "fp8"])
 def test_full_prefix_reuse(request, precision):
