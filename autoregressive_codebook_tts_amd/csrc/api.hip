@@ -278,6 +278,7 @@ int hta_create(const hta_config* cfg, void* hip_stream, hta_ctx** out) {
     if (hipStreamCreateWithFlags(&c.stream, hipStreamNonBlocking) != hipSuccess) { delete x; return HTA_E_HIP; }
     c.own_stream = true;
   }
+  if (prefill_setup() != hipSuccess) { hta_destroy(x); return HTA_E_HIP; }
   c.lay = make_layout(c.cfg);
   c.layers = new LayerW[c.cfg.n_layers]();
   if (frame_setup(c) == hipSuccess && frame_max_packets(c.cfg, c.frame_blocks) <= frame_part_capacity())

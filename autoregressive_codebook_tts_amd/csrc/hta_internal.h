@@ -169,6 +169,7 @@ int frame_max_packets(const hta_config& f, int blocks);
 int frame_part_capacity();
 
 // ---------------------------------------------------------------- launchers (prefill.hip)
+hipError_t prefill_setup();  // kernel attributes of the prefill GEMM (once per context)
 hipError_t launch_prefill(Ctx& c, int P, bool record);
 
 // ---------------------------------------------------------------- launchers (load.hip)

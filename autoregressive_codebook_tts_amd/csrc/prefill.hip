@@ -19,6 +19,7 @@ namespace hta {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // 8 e4m3 codes (two dwords) -> 8 bf16 values, exactly (hardware pair convert, scale 1).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
@@ -334,6 +335,136 @@ __global__ __launch_bounds__(256) void k_gemm(const void* __restrict__ A, const 
   }
 }
 
+// ============================================================================ LDS-tiled MFMA GEMM
+// For M >= 64.  The products and their order are those of k_gemm (per 16x16 tile:
+// bf16 in 32-wide K chunks of increasing K; e4m3 per 64-wide chunk, the low 8 bytes
+// of every lane's 16-byte unit and then the high 8 bytes) and so is the K split, so a
+// row's result is bit-identical whichever of the two kernels computes it.
+// A block computes 128 rows x 128 columns with 4 waves of 64 x 64.  Per stage, 64
+// bytes of K of each of the 128 A rows and 128 B rows (8 KB + 8 KB) are fetched
+// straight into LDS (global_load_lds_dwordx4) through a ring of kGS stages issued
+// kGS - 1 ahead of the stage being multiplied, so no register holds data in flight
+// and the B tile is shared by the waves.  A stage's 16-byte units are swizzled within
+// each row (unit u of row r at position 4r + (u ^ ((r >> 2) & 3))), so that a fragment
+// read (16 consecutive rows, one unit each) touches 16 different bank groups.
+constexpr int kGemmTileMinM = 64;        // smaller M: k_gemm (weights streamed once per 32 rows)
+constexpr int kGS = 4;                    // LDS stages
+constexpr int kGT = 128;                  // tile rows (A) and columns (B)
+constexpr int kGHalf = kGT * 64;          // bytes of one operand's tile per stage
+constexpr int kGStage = 2 * kGHalf;
+
+size_t gemm_tile_lds_bytes() { return (size_t)kGS * kGStage; }
+
+__device__ __forceinline__ int tile_unit_pos(int row, int u) { return row * 4 + (u ^ ((row >> 2) & 3)); }
+
+template <int P>
+__global__ __launch_bounds__(256) void k_gemm_tile(const void* __restrict__ A, const void* __restrict__ B,
+                                                   float* __restrict__ Cpart, int M, int N, int K, int ksplit) {
+  extern __shared__ __align__(16) unsigned char gsm[];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m0 = blockIdx.x * kGT, n0 = blockIdx.y * kGT, ks = blockIdx.z;
+  constexpr int EB = (P == kBF16) ? 2 : 1;
+  const int rowbytes = K * EB;  // operands below 2^31 bytes
+  const int nsteps = K / 128;   // the split is over 128-element steps, as in k_gemm
+  const int s_beg = (int)((long)nsteps * ks / ksplit), s_end = (int)((long)nsteps * (ks + 1) / ksplit);
+  constexpr int CPS = 128 * EB / 64;  // 64-byte chunks per 128-element step
+  const int c0 = s_beg * CPS, nch = (s_end - s_beg) * CPS;
+
+  // this wave fetches units [64 * (2w + j), +64) of each operand's tile, j = 0, 1
+  int voffA[2], voffB[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = 64 * (2 * w + j) + lane, row = p >> 2, u = (p & 3) ^ ((row >> 2) & 3);
+    const int ra = m0 + row < M ? m0 + row : M - 1;  // rows past M fetch row M - 1 (results unused)
+    voffA[j] = ra * rowbytes + u * 16;
+    voffB[j] = (n0 + row) * rowbytes + u * 16;
+  }
+  const unsigned char* Ab = static_cast<const unsigned char*>(A);
+  const unsigned char* Bb = static_cast<const unsigned char*>(B);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)gsm);
+  auto issue = [&](int c) {  // fetch chunk c into stage c % kGS
+    const uint32_t sb = lds0 + (uint32_t)(c % kGS) * kGStage;
+    const unsigned char* a = Ab + (size_t)(c0 + c) * 64;
+    const unsigned char* b = Bb + (size_t)(c0 + c) * 64;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t ma = __builtin_amdgcn_readfirstlane(sb + (uint32_t)(2 * w + j) * 1024u);
+      const uint32_t mb = __builtin_amdgcn_readfirstlane(sb + kGHalf + (uint32_t)(2 * w + j) * 1024u);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   : : "v"(voffA[j]), "s"(a), "s"(ma) : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   : : "v"(voffB[j]), "s"(b), "s"(mb) : "memory", "m0");
+    }
+  };
+  for (int c = 0; c < kGS - 1 && c < nch; ++c) issue(c);
+
+  const int wm = w >> 1, wn = w & 1, g = lane >> 4, r16 = lane & 15;
+  int fa[4], fb[4];  // byte offsets of this lane's fragment units within a stage
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa[i] = tile_unit_pos(64 * wm + 16 * i + r16, g) * 16;
+    fb[i] = kGHalf + tile_unit_pos(64 * wn + 16 * i + r16, g) * 16;
+  }
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = 0; c < nch; ++c) {
+    // chunk c has landed once at most the fetches of the kGS - 2 younger chunks remain
+    // (4 per chunk and wave; loads land in issue order)
+    if (c + kGS - 2 < nch) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's part of chunk c is in, and chunk c - 1 is consumed
+    if (c + kGS - 1 < nch) issue(c + kGS - 1);
+    const unsigned char* st = gsm + (c % kGS) * kGStage;
+    uint4 av[4], bv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      av[i] = *reinterpret_cast<const uint4*>(st + fa[i]);
+      bv[i] = *reinterpret_cast<const uint4*>(st + fb[i]);
+    }
+    if (P == kBF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i]),
+                                                               __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
+    } else {
+      bf16x8 al[4], ah[4], bl[4], bh[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        al[i] = fp8x8_to_bf16(av[i].x, av[i].y);
+        ah[i] = fp8x8_to_bf16(av[i].z, av[i].w);
+        bl[i] = fp8x8_to_bf16(bv[i].x, bv[i].y);
+        bh[i] = fp8x8_to_bf16(bv[i].z, bv[i].w);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+  // output layout: lane holds rows 4 * g + r of each 16x16 tile, column lane & 15
+  float* Cp = Cpart + (size_t)ks * M * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + 64 * wn + 16 * j + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + 64 * wm + 16 * i + 4 * g + r;
+        if (row < M) Cp[(size_t)row * N + col] = acc[i][j][r];
+      }
+    }
+}
+
 // out = sum over splits (in order) * in_scale * w_scale[n]; mode 0 store, 1 add to out.
 __global__ __launch_bounds__(256) void k_gemm_reduce(const float* __restrict__ Cpart, float* __restrict__ out,
                                                      const float* __restrict__ w_scale, float in_scale, int M, int N,
@@ -363,9 +494,14 @@ template <int P>
 static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scale, float in_scale, float* out, int M,
                        int N, int K, int resid) {
   const int ks = gemm_ksplit(N, K);
-  dim3 grid((M + 31) / 32, (N + 63) / 64, ks);
   float* part = c.pgu + (size_t)c.cfg.max_prefill * 2 * c.cfg.ffn;  // split partials after the gate/up buffer
-  hipLaunchKernelGGL(k_gemm<P>, grid, dim3(256), 0, c.stream, A, B, part, M, N, K, ks);
+  if (M >= kGemmTileMinM && N % kGT == 0 && K % 128 == 0) {
+    dim3 grid((M + kGT - 1) / kGT, N / kGT, ks);
+    hipLaunchKernelGGL(k_gemm_tile<P>, grid, dim3(256), gemm_tile_lds_bytes(), c.stream, A, B, part, M, N, K, ks);
+  } else {
+    dim3 grid((M + 31) / 32, (N + 63) / 64, ks);
+    hipLaunchKernelGGL(k_gemm<P>, grid, dim3(256), 0, c.stream, A, B, part, M, N, K, ks);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t MN = (size_t)M * N;
@@ -429,6 +565,13 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
       return e;
   }
   return hipSuccess;
+}
+
+hipError_t prefill_setup() {
+  const int lds = (int)gemm_tile_lds_bytes();
+  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_tile<kBF16>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)k_gemm_tile<kFP8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }
 
 hipError_t launch_prefill(Ctx& c, int P, bool record) {
