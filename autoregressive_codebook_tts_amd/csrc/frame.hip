@@ -492,14 +492,24 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
       const int kp = t0 + lane;
       float s = -INFINITY;
       if (kp < end) {
-        float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll 8
-        for (int e2 = 0; e2 < HD / 2; ++e2) {
-          const uint32_t kk2 = sm.Kt[lane][e2];
-          d0 = fmaf(sm.qs[w][2 * e2], bf16lo(kk2), d0);
-          d1 = fmaf(sm.qs[w][2 * e2 + 1], bf16hi(kk2), d1);
+        float d0[2] = {0.0f, 0.0f}, d1[2] = {0.0f, 0.0f};
+        for (int eb = 0; eb < HD / 2; eb += 16) {  // 16 key words and 32 query values per batch
+          uint32_t kk[16];
+          float q[32];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) kk[u] = sm.Kt[lane][eb + u];
+#pragma unroll
+          for (int u = 0; u < 32; u += 4) {
+            const float4 q4 = *reinterpret_cast<const float4*>(&sm.qs[w][2 * eb + u]);
+            q[u] = q4.x; q[u + 1] = q4.y; q[u + 2] = q4.z; q[u + 3] = q4.w;
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            d0[u & 1] = fmaf(q[2 * u], bf16lo(kk[u]), d0[u & 1]);
+            d1[u & 1] = fmaf(q[2 * u + 1], bf16hi(kk[u]), d1[u & 1]);
+          }
         }
-        s = (d0 + d1) * inv_sqrt;
+        s = ((d0[0] + d0[1]) + (d1[0] + d1[1])) * inv_sqrt;
       }
       mnew = fmaxf(m, wave_max(s));
       const float p = (kp < end) ? __expf(s - mnew) : 0.0f;
@@ -509,19 +519,30 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
     }
     __syncthreads();
     if (w < G) {
+      // all T keys of the tile (those past the split have p = 0 and zero values), 16 keys
+      // per batch: the batch's LDS reads are issued together, then one FMA chain in key
+      // order (the order of the one-kernel-per-phase frame)
+      const int d0 = lane >> 1, d1 = ((lane + 64) % HD) >> 1;
+      const bool hi0 = lane & 1, hi1 = ((lane + 64) % HD) & 1;
       o0 *= scale;
       o1 *= scale;
-      const int nk = min(T, end - t0);
-      for (int kk = 0; kk < nk; ++kk) {
-        const float p = sm.ps[w][kk];
-        if (lane < HD) {
-          const uint32_t v2 = sm.Vt[kk][lane >> 1];
-          o0 = fmaf(p, (lane & 1) ? bf16hi(v2) : bf16lo(v2), o0);
+      for (int kb = 0; kb < T; kb += 16) {
+        float pp[16];
+        uint32_t v0[16], v1[16];
+#pragma unroll
+        for (int u = 0; u < 16; u += 4) {
+          const float4 p4 = *reinterpret_cast<const float4*>(&sm.ps[w][kb + u]);
+          pp[u] = p4.x; pp[u + 1] = p4.y; pp[u + 2] = p4.z; pp[u + 3] = p4.w;
         }
-        if (HD > 64) {
-          const int dd = (lane + 64) % HD;
-          const uint32_t v2 = sm.Vt[kk][dd >> 1];
-          o1 = fmaf(p, (dd & 1) ? bf16hi(v2) : bf16lo(v2), o1);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          v0[u] = sm.Vt[kb + u][d0];
+          v1[u] = HD > 64 ? sm.Vt[kb + u][d1] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          o0 = fmaf(pp[u], hi0 ? bf16hi(v0[u]) : bf16lo(v0[u]), o0);
+          if (HD > 64) o1 = fmaf(pp[u], hi1 ? bf16hi(v1[u]) : bf16lo(v1[u]), o1);
         }
       }
       m = mnew;
@@ -541,53 +562,57 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
     }
     return true;
   }
-  // split 0: merge with the other active splits (log-sum-exp) and publish the output
+  // split 0: merge with the other active splits (log-sum-exp) and publish the output.
+  // The first round loads every split's (m, l) (lane s holds split s's) together with
+  // the o vectors of the first kMB other splits, so a merge of up to kMB + 1 splits
+  // costs one memory round trip; each word carries its own tag.
+  constexpr int kMB = 8;  // o vectors per round
   Poll pm;
   pm.start(abort_flag);
   if (w < G) {
     const int h = j * G + w;
     const uint64_t* pb = xpart + (size_t)h * a.splits * (HD + 2);
-    // lane s (1 <= s < n_active) holds split s's (m, l); lane 0 holds split 0's own
-    const bool other = lane > 0 && lane < n_active;
-    uint64_t wm = other ? ld64(pb + (size_t)lane * (HD + 2) + HD) : ((uint64_t)tag_part << 32);
-    uint64_t wl = other ? ld64(pb + (size_t)lane * (HD + 2) + HD + 1) : ((uint64_t)tag_part << 32);
-    while (pm.ok && ((unsigned)(wm >> 32) != tag_part || (unsigned)(wl >> 32) != tag_part)) {
-      if (!pm.again()) break;
-      if ((unsigned)(wm >> 32) != tag_part) wm = ld64(pb + (size_t)lane * (HD + 2) + HD);
-      if ((unsigned)(wl >> 32) != tag_part) wl = ld64(pb + (size_t)lane * (HD + 2) + HD + 1);
-    }
-    const float ms = other ? __uint_as_float((uint32_t)wm) : (lane == 0 ? m : -INFINITY);
-    const float ls = other ? __uint_as_float((uint32_t)wl) : (lane == 0 ? lsum : 0.0f);
-    const float M = wave_max(ls > 0.0f ? ms : -INFINITY);
-    const float f = (ls > 0.0f) ? __expf(ms - M) : 0.0f;
-    const float den = wave_sum(f * ls);
-    const float f0 = __shfl(f, 0, kWave);
-    float n0 = f0 * o0, n1 = f0 * o1;
-    // the other splits' o vectors, 8 splits per batch, each word polled by its own tag
     const uint64_t want = (uint64_t)tag_part << 32;
-    for (int sp0 = 1; sp0 < n_active && pm.ok; sp0 += 4) {
-      uint64_t x0[4], x1[4];
+    const bool other = lane > 0 && lane < n_active;
+    uint64_t wm = other ? ld64(pb + (size_t)lane * (HD + 2) + HD) : want;
+    uint64_t wl = other ? ld64(pb + (size_t)lane * (HD + 2) + HD + 1) : want;
+    float n0 = 0.0f, n1 = 0.0f, f = 0.0f;
+    for (int sp0 = 1; sp0 < n_active || sp0 == 1; sp0 += kMB) {
+      uint64_t x0[kMB], x1[kMB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kMB; ++u) {
         const int sp = sp0 + u;
         const uint64_t* q = pb + (size_t)(sp < n_active ? sp : 0) * (HD + 2);
         x0[u] = (sp < n_active && lane < HD) ? ld64(q + lane) : want;
         x1[u] = (sp < n_active && HD > 64) ? ld64(q + lane + 64) : want;
       }
       while (pm.ok) {
-        bool ok = true;
+        bool ok = (unsigned)(wm >> 32) == tag_part && (unsigned)(wl >> 32) == tag_part;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ok = ok && (unsigned)(x0[u] >> 32) == tag_part && (unsigned)(x1[u] >> 32) == tag_part;
+        for (int u = 0; u < kMB; ++u) ok = ok && (unsigned)(x0[u] >> 32) == tag_part && (unsigned)(x1[u] >> 32) == tag_part;
         if (ok || !pm.again()) break;
+        if ((unsigned)(wm >> 32) != tag_part) wm = ld64(pb + (size_t)lane * (HD + 2) + HD);
+        if ((unsigned)(wl >> 32) != tag_part) wl = ld64(pb + (size_t)lane * (HD + 2) + HD + 1);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kMB; ++u) {
           const uint64_t* q = pb + (size_t)(sp0 + u) * (HD + 2);
           if ((unsigned)(x0[u] >> 32) != tag_part) x0[u] = ld64(q + lane);
           if ((unsigned)(x1[u] >> 32) != tag_part) x1[u] = ld64(q + lane + 64);
         }
       }
+      if (!pm.ok) break;
+      if (sp0 == 1) {  // the merge weights, once every (m, l) is in
+        const float ms = other ? __uint_as_float((uint32_t)wm) : (lane == 0 ? m : -INFINITY);
+        const float ls = other ? __uint_as_float((uint32_t)wl) : (lane == 0 ? lsum : 0.0f);
+        const float M = wave_max(ls > 0.0f ? ms : -INFINITY);
+        f = (ls > 0.0f) ? __expf(ms - M) : 0.0f;
+        lsum = wave_sum(f * ls);  // the merged denominator
+        const float f0 = __shfl(f, 0, kWave);
+        n0 = f0 * o0;
+        n1 = f0 * o1;
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kMB; ++u) {
         const int sp = sp0 + u;
         const float fs = __shfl(f, sp < n_active ? sp : 0, kWave);
         if (sp < n_active) {
@@ -596,6 +621,7 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
         }
       }
     }
+    const float den = lsum;
     const float inv = 1.0f / den;
     if (lane < HD) st32(xo + (size_t)h * HD + lane, act_bits<P>(n0 * inv, so), tag_o);
     if (HD > 64) st32(xo + (size_t)h * HD + lane + 64, act_bits<P>(n1 * inv, so), tag_o);
