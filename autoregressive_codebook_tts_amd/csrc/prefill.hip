@@ -253,86 +253,163 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
   }
 }
 
-// ============================================================================ MFMA GEMM
+// ============================================================================ MFMA GEMM, small M
 // C[M][N] (+)= A[M][K] . B[N][K]^T, A = activations (bf16 bits / e4m3 codes),
-// B = packed weights.  A wave computes 32 rows x 16 columns; a block is 4 waves
-// (64 columns); the K range is split into `ksplit` contiguous parts (a function
-// of N and K only) whose partial sums land in Cpart[ksplit][M][N] and are added
-// in split order by k_gemm_reduce.  Each 16x16 MFMA tile accumulates its K
-// range in increasing order, so a row's result does not depend on M.
-template <int P>
+// B = packed weights.  A block computes 16R rows x 64 columns with 4 waves of
+// 16R x 16; the K range is split into `ksplit` contiguous parts (a function of N
+// and K only) whose partial sums land in Cpart[ksplit][M][N] and are added in
+// split order by k_gemm_reduce.  Each 16x16 MFMA tile accumulates its K range in
+// increasing order: bf16 in 32-wide chunks; e4m3 per 64-wide chunk, the low 8
+// bytes of every lane's 16-byte unit and then the high 8 bytes.  A row's result
+// therefore does not depend on M, and the LDS-tiled kernel for larger M computes
+// the same products in the same order.
+//
+// At small M the weights are a stream read once and one block's share of it is
+// short, so the stream is latency-bound unless many bytes are requested ahead.
+// One 128-element step of the block's 64 B rows and 16R A rows is a stage, fetched
+// straight into LDS (global_load_lds_dwordx4) through a ring of NS stages issued
+// NS - 1 ahead; the ring takes at most 80 KB, so two blocks share a CU.  Within a
+// stage, 16-byte unit u of row r sits at position r * NU + (u ^ swz(r)), so a
+// fragment read (16 consecutive rows, one unit each) touches 16 different bank
+// groups.  Rows past M fetch row M - 1 (their results are not stored).
+template <int P, int R>
+struct Skinny {
+  static constexpr int EB = P == kBF16 ? 2 : 1;
+  static constexpr int SK = 128 * EB;                  // bytes of one row per stage
+  static constexpr int NU = SK / 16;                   // 16-byte units per row and stage
+  static constexpr int U = NU / 4;                     // units per lane per 16-row fragment
+  static constexpr int BYTES_B = 64 * SK, BYTES_A = 16 * R * SK, STAGE = BYTES_B + BYTES_A;
+  static constexpr int NS = (80 * 1024) / STAGE;       // bf16: 4 (R = 1), 3 (R = 2); e4m3: 8, 6
+  static constexpr int NB = NU / 4;                    // B fetches per wave and stage
+  static constexpr int NA_ALL = R * NU / 4;            // A fetches per stage
+  static constexpr int AW = NA_ALL >= 4 ? 4 : NA_ALL;  // waves that fetch A
+  static constexpr int NA = NA_ALL / AW;               // A fetches per fetching wave
+  static_assert(NS >= 3 && NA * AW == NA_ALL, "stage shape");
+};
+
+__device__ __forceinline__ int skinny_swz(int row, int nu) { return (row ^ (row >> 3)) & (nu - 1); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory"); }
+
+template <int P, int R>
+size_t skinny_lds_bytes() { return (size_t)Skinny<P, R>::NS * Skinny<P, R>::STAGE; }
+
+template <int P, int R>
 __global__ __launch_bounds__(256) void k_gemm(const void* __restrict__ A, const void* __restrict__ B,
                                               float* __restrict__ Cpart, int M, int N, int K, int ksplit) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int m0 = blockIdx.x * 32;
-  const int n0 = (blockIdx.y * 4 + w) * 16;
-  const int ks = blockIdx.z;
-  if (n0 >= N) return;
-  constexpr int KSTEP = 128;
-  const int nsteps = K / KSTEP;
+  using S = Skinny<P, R>;
+  extern __shared__ __align__(16) unsigned char gsm[];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m0 = blockIdx.x * 16 * R, n0 = blockIdx.y * 64, ks = blockIdx.z;
+  const int rowbytes = K * S::EB;  // operands below 2^31 bytes
+  const int nsteps = K / 128;
   const int s_beg = (int)((long)nsteps * ks / ksplit), s_end = (int)((long)nsteps * (ks + 1) / ksplit);
-  const int rA0 = m0 + (lane & 15), rA1 = m0 + 16 + (lane & 15);
-  const int rB = n0 + (lane & 15);
-  const int grp = lane >> 4;
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  if (P == kBF16) {
-    const uint16_t* Ab = static_cast<const uint16_t*>(A);
-    const uint16_t* Bb = static_cast<const uint16_t*>(B);
-    for (int st = s_beg; st < s_end; ++st) {
-      const int kb = st * KSTEP;
-      uint4 a0[4], a1[4], b[4];
+  const int nst = s_end - s_beg;
+  const bool fetch_a = w < S::AW;
+
+  int voffB[S::NB], voffA[S::NA];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = kb + q * 32 + grp * 8;
-        b[q] = ld_stream16(Bb + (size_t)rB * K + k);
-        a0[q] = rA0 < M ? *reinterpret_cast<const uint4*>(Ab + (size_t)rA0 * K + k) : make_uint4(0, 0, 0, 0);
-        a1[q] = rA1 < M ? *reinterpret_cast<const uint4*>(Ab + (size_t)rA1 * K + k) : make_uint4(0, 0, 0, 0);
-      }
+  for (int j = 0; j < S::NB; ++j) {
+    const int p = 64 * (w * S::NB + j) + lane, row = p / S::NU, u = (p % S::NU) ^ skinny_swz(row, S::NU);
+    voffB[j] = (n0 + row) * rowbytes + u * 16;
+  }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, b[q]);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0[q]), bv, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1[q]), bv, acc1, 0, 0, 0);
+  for (int j = 0; j < S::NA; ++j) {
+    const int p = 64 * (w * S::NA + j) + lane, row = p / S::NU, u = (p % S::NU) ^ skinny_swz(row, S::NU);
+    voffA[j] = min(m0 + row, M - 1) * rowbytes + u * 16;
+  }
+  const unsigned char* Ab = static_cast<const unsigned char*>(A);
+  const unsigned char* Bb = static_cast<const unsigned char*>(B);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)gsm);
+  auto issue = [&](int c) {  // fetch step s_beg + c into stage c % NS
+    const uint32_t sb = lds0 + (uint32_t)(c % S::NS) * S::STAGE;
+    const unsigned char* a = Ab + (size_t)(s_beg + c) * S::SK;
+    const unsigned char* b = Bb + (size_t)(s_beg + c) * S::SK;
+#pragma unroll
+    for (int j = 0; j < S::NB; ++j) {
+      const uint32_t mb = __builtin_amdgcn_readfirstlane(sb + (uint32_t)(w * S::NB + j) * 1024u);
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   : : "v"(voffB[j]), "s"(b), "s"(mb) : "memory", "m0");
+    }
+    if (fetch_a) {
+#pragma unroll
+      for (int j = 0; j < S::NA; ++j) {
+        const uint32_t ma = __builtin_amdgcn_readfirstlane(sb + S::BYTES_B + (uint32_t)(w * S::NA + j) * 1024u);
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     : : "v"(voffA[j]), "s"(a), "s"(ma) : "memory", "m0");
       }
     }
-  } else {
-    // e4m3 operands are widened to bf16 in registers (exact: 4 significant bits)
-    // and multiplied on the bf16 MFMA, which accumulates at full fp32 precision;
-    // the e4m3 MFMA forms accumulate internally with fewer bits.  Each lane's
-    // 16-byte packet covers k = kb + 16*grp .. +16 for both operands; bytes 0-7
-    // feed one MFMA and bytes 8-15 the next (the same permutation of k on both
-    // sides, so the products summed are unchanged).
-    const uint8_t* Ab = static_cast<const uint8_t*>(A);
-    const uint8_t* Bb = static_cast<const uint8_t*>(B);
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    for (int st = s_beg; st < s_end; ++st) {
-      uint4 b[2], a0[2], a1[2];
+  };
+  for (int c = 0; c < S::NS - 1 && c < nst; ++c) issue(c);
+
+  const int g = lane >> 4, r16 = lane & 15;
+  int fb[S::U], fa[R][S::U];  // byte offsets of this lane's fragment units within a stage
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int k = st * KSTEP + q * 64 + grp * 16;
-        b[q] = ld_stream16(Bb + (size_t)rB * K + k);
-        a0[q] = rA0 < M ? *reinterpret_cast<const uint4*>(Ab + (size_t)rA0 * K + k) : z;
-        a1[q] = rA1 < M ? *reinterpret_cast<const uint4*>(Ab + (size_t)rA1 * K + k) : z;
-      }
+  for (int q = 0; q < S::U; ++q) {
+    const int rb = 16 * w + r16;
+    fb[q] = (rb * S::NU + ((4 * q + g) ^ skinny_swz(rb, S::NU))) * 16;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const bf16x8 bl = fp8x8_to_bf16(b[q].x, b[q].y), bh = fp8x8_to_bf16(b[q].z, b[q].w);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(a0[q].x, a0[q].y), bl, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(a1[q].x, a1[q].y), bl, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(a0[q].z, a0[q].w), bh, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(a1[q].z, a1[q].w), bh, acc1, 0, 0, 0);
+    for (int r = 0; r < R; ++r) {
+      const int ra = 16 * r + r16;
+      fa[r][q] = S::BYTES_B + (ra * S::NU + ((4 * q + g) ^ skinny_swz(ra, S::NU))) * 16;
+    }
+  }
+  f32x4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = 0; c < nst; ++c) {
+    // stage c has landed once at most the fetches of the NS - 2 younger stages remain
+    // (loads land in issue order)
+    if (c + S::NS - 2 < nst) {
+      if (S::AW == 4 || fetch_a) wait_vm<(S::NS - 2) * (S::NB + S::NA)>();
+      else wait_vm<(S::NS - 2) * S::NB>();
+    } else {
+      wait_vm<0>();
+    }
+    __syncthreads();  // every wave's part of stage c is in, and stage c - 1 is consumed
+    if (c + S::NS - 1 < nst) issue(c + S::NS - 1);
+    const unsigned char* st = gsm + (c % S::NS) * S::STAGE;
+    uint4 bv[S::U], av[R][S::U];
+#pragma unroll
+    for (int q = 0; q < S::U; ++q) {
+      bv[q] = *reinterpret_cast<const uint4*>(st + fb[q]);
+#pragma unroll
+      for (int r = 0; r < R; ++r) av[r][q] = *reinterpret_cast<const uint4*>(st + fa[r][q]);
+    }
+    if (P == kBF16) {
+#pragma unroll
+      for (int q = 0; q < S::U; ++q)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[r][q]),
+                                                           __builtin_bit_cast(bf16x8, bv[q]), acc[r], 0, 0, 0);
+    } else {
+      // e4m3 operands are widened to bf16 in registers (exact: 4 significant bits) and
+      // multiplied on the bf16 MFMA, which accumulates at full fp32 precision; the e4m3
+      // MFMA forms accumulate internally with fewer bits
+#pragma unroll
+      for (int q = 0; q < S::U; ++q) {
+        const bf16x8 bl = fp8x8_to_bf16(bv[q].x, bv[q].y), bh = fp8x8_to_bf16(bv[q].z, bv[q].w);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(av[r][q].x, av[r][q].y), bl, acc[r], 0, 0, 0);
+          acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(av[r][q].z, av[r][q].w), bh, acc[r], 0, 0, 0);
+        }
       }
     }
   }
-  // output layout: lane holds rows 4*grp + i of the 16x16 tile, column lane & 15
-  const int col = n0 + (lane & 15);
+  // output layout: lane holds rows 4 * g + i of each 16x16 tile, column lane & 15
+  const int col = n0 + 16 * w + r16;
   float* Cp = Cpart + (size_t)ks * M * N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r0 = m0 + grp * 4 + i, r1 = m0 + 16 + grp * 4 + i;
-    if (r0 < M && col < N) Cp[(size_t)r0 * N + col] = acc0[i];
-    if (r1 < M && col < N) Cp[(size_t)r1 * N + col] = acc1[i];
-  }
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + 16 * r + 4 * g + i;
+      if (row < M) Cp[(size_t)row * N + col] = acc[r][i];
+    }
 }
 
 // ============================================================================ LDS-tiled MFMA GEMM
@@ -347,7 +424,7 @@ __global__ __launch_bounds__(256) void k_gemm(const void* __restrict__ A, const 
 // and the B tile is shared by the waves.  A stage's 16-byte units are swizzled within
 // each row (unit u of row r at position 4r + (u ^ ((r >> 2) & 3))), so that a fragment
 // read (16 consecutive rows, one unit each) touches 16 different bank groups.
-constexpr int kGemmTileMinM = 64;        // smaller M: k_gemm (weights streamed once per 32 rows)
+constexpr int kGemmTileMinM = 64;        // smaller M: k_gemm (weights streamed once per 16 or 32 rows)
 constexpr int kGS = 4;                    // LDS stages
 constexpr int kGT = 128;                  // tile rows (A) and columns (B)
 constexpr int kGHalf = kGT * 64;          // bytes of one operand's tile per stage
@@ -493,14 +570,18 @@ static int gemm_ksplit(int N, int K) {
 template <int P>
 static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scale, float in_scale, float* out, int M,
                        int N, int K, int resid) {
+  if (N % 64 != 0 || K % 128 != 0) return hipErrorInvalidValue;  // the kernels' tiling
   const int ks = gemm_ksplit(N, K);
   float* part = c.pgu + (size_t)c.cfg.max_prefill * 2 * c.cfg.ffn;  // split partials after the gate/up buffer
   if (M >= kGemmTileMinM && N % kGT == 0 && K % 128 == 0) {
     dim3 grid((M + kGT - 1) / kGT, N / kGT, ks);
     hipLaunchKernelGGL(k_gemm_tile<P>, grid, dim3(256), gemm_tile_lds_bytes(), c.stream, A, B, part, M, N, K, ks);
+  } else if (M <= 16) {
+    dim3 grid(1, N / 64, ks);
+    hipLaunchKernelGGL((k_gemm<P, 1>), grid, dim3(256), (skinny_lds_bytes<P, 1>()), c.stream, A, B, part, M, N, K, ks);
   } else {
-    dim3 grid((M + 31) / 32, (N + 63) / 64, ks);
-    hipLaunchKernelGGL(k_gemm<P>, grid, dim3(256), 0, c.stream, A, B, part, M, N, K, ks);
+    dim3 grid((M + 31) / 32, N / 64, ks);
+    hipLaunchKernelGGL((k_gemm<P, 2>), grid, dim3(256), (skinny_lds_bytes<P, 2>()), c.stream, A, B, part, M, N, K, ks);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -568,10 +649,19 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
 }
 
 hipError_t prefill_setup() {
-  const int lds = (int)gemm_tile_lds_bytes();
-  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_tile<kBF16>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)k_gemm_tile<kFP8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const struct { const void* f; size_t lds; } kernels[] = {
+      {(const void*)k_gemm_tile<kBF16>, gemm_tile_lds_bytes()},
+      {(const void*)k_gemm_tile<kFP8>, gemm_tile_lds_bytes()},
+      {(const void*)k_gemm<kBF16, 1>, skinny_lds_bytes<kBF16, 1>()},
+      {(const void*)k_gemm<kBF16, 2>, skinny_lds_bytes<kBF16, 2>()},
+      {(const void*)k_gemm<kFP8, 1>, skinny_lds_bytes<kFP8, 1>()},
+      {(const void*)k_gemm<kFP8, 2>, skinny_lds_bytes<kFP8, 2>()},
+  };
+  for (const auto& k : kernels) {
+    const hipError_t e = hipFuncSetAttribute(k.f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)k.lds);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_prefill(Ctx& c, int P, bool record) {

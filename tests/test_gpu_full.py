@@ -337,6 +337,31 @@ def test_full_decode_is_deterministic(request, precision):
     _say(f"[full] {precision} decode: two identical runs bit-identical")
 
 
+# ----------------------------------------------------------------------------- chunked prefill
+@pytest.mark.parametrize("precision", ["bf16", "fp8"])
+def test_full_chunked_prefill_is_bit_identical(request, precision):
+    """A prompt prefilled in chunks of 37, 5, 16 and 42 rows (the GEMM's 32-row and 16-row
+    skinny shapes, whose K splits span many pipelined stages here) leaves the same KV and
+    last rows, bit for bit, as the 100-row prefill in one call (the LDS-tiled GEMM)."""
+    ctx, _ = _ctx_and_oracle(request, precision)
+    ids = S.token_ids(S.SEEDS["prefill_128"], 100, SH.text_vocab)
+    layers = (0, SH.n_layers // 2, SH.n_layers - 1)
+    ctx.reset(0)
+    ctx.prefill(ids)
+    cold_rows = ctx.tap_prefill_hidden(100).copy()
+    cold_kv = [ctx.tap_kv(l, 100) for l in layers]
+    ctx.reset(0)
+    c0 = 0
+    for n in (37, 5, 16, 42):
+        ctx.prefill(ids[c0:c0 + n])
+        c0 += n
+        assert np.array_equal(ctx.tap_prefill_hidden(n), cold_rows[c0 - n:c0]), f"rows {c0 - n}..{c0} differ"
+    for l, (kc, vc) in zip(layers, cold_kv):
+        k, v = ctx.tap_kv(l, 100)
+        assert np.array_equal(k, kc) and np.array_equal(v, vc), f"layer {l}: KV differs"
+    _say(f"[full] {precision} prefill in chunks 37/5/16/42: bit-identical to one 100-row prefill")
+
+
 # ----------------------------------------------------------------------------- prefix reuse
 @pytest.mark.parametrize("precision", ["bf16", "fp8"])
 def test_full_prefix_reuse(request, precision):
