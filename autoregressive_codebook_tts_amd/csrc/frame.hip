@@ -75,6 +75,28 @@ struct FrameArgs {
 // The kernel reads FrameArgs through the constant address space: every field is a
 // scalar (s_load) read that never waits on vector-memory counters.
 typedef const __attribute__((address_space(4))) FrameArgs CFA;
+// The per-layer pointer table is read the same way: a vector load of a pointer
+// would need a vector-memory counter wait before its use, and that wait would also
+// wait for every weight fetch the ring has in flight.
+typedef const __attribute__((address_space(4))) LayerW CLW;
+__device__ __forceinline__ CLW* layer_ptrs(CFA& a, int layer) { return (CLW*)a.layers + layer; }
+// FP8 row-scale pointer i of a layer (0 qkv, 1 o_proj, 2 gate/up, 3 down): the four
+// pointers sit side by side in LayerW, so this is one indexed scalar read (a
+// multi-way select over the fields, lowered to branches, picked the wrong field here)
+static_assert(offsetof(LayerW, s_o) == offsetof(LayerW, s_qkv) + sizeof(float*) &&
+                  offsetof(LayerW, s_gu) == offsetof(LayerW, s_qkv) + 2 * sizeof(float*) &&
+                  offsetof(LayerW, s_d) == offsetof(LayerW, s_qkv) + 3 * sizeof(float*),
+              "LayerW scale pointers must be adjacent");
+__device__ __forceinline__ const float* layer_scales(CFA& a, int layer, int i) {
+  typedef const __attribute__((address_space(4))) uint64_t CU64;
+  const CU64* p = (const CU64*)((const __attribute__((address_space(4))) char*)layer_ptrs(a, layer) +
+                                offsetof(LayerW, s_qkv));
+  return reinterpret_cast<const float*>(p[i]);
+}
+// the static activation scales, likewise (uniform index, scalar read)
+__device__ __forceinline__ float act_scale(CFA& a, int site) {
+  return ((const __attribute__((address_space(4))) float*)a.act_scales)[site];
+}
 
 // ---------------------------------------------------------------- tagged exchange words
 __device__ __forceinline__ uint64_t ld64(const uint64_t* p) {
@@ -223,10 +245,17 @@ __device__ __forceinline__ float packet_dot(const uint4& wv, const uint4& x0, co
 }
 
 // Sum of a row's per-wave partials in wave order (deterministic); zeroes them for the next phase.
-__device__ __forceinline__ float row_sum(float* part, int row) {
+// Sum of a row's per-wave partials, which are cleared for the next phase.  The zeros
+// come from a register quad that lives for the whole kernel (`zero4`, opaque to the
+// compiler): zeros materialised afresh would land in registers that some load on
+// another path also writes, and the compiler would wait for that load first.
+static_assert(kFW % 4 == 0, "partials are cleared four at a time");
+__device__ __forceinline__ float row_sum(float* part, int row, const float4& zero4) {
   float y = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kFW; ++w) { y += part[row * kFW + w]; part[row * kFW + w] = 0.0f; }
+  for (int w = 0; w < kFW; ++w) y += part[row * kFW + w];
+#pragma unroll
+  for (int w = 0; w < kFW; w += 4) *reinterpret_cast<float4*>(part + row * kFW + w) = zero4;
   return y;
 }
 
@@ -237,62 +266,95 @@ __device__ __forceinline__ uint32_t act_bits(float v, float scale) {
   return f32_to_bf16(act_round<P>(v, scale));
 }
 
+// The compiler counts only its own vector loads, not the ring's LDS fetches; where it
+// cannot prove a load of its own has landed it waits for the whole counter, and that
+// wait would also wait for every fetch the ring has in flight.  Right after a poll is
+// satisfied the counter is all but empty (loads land in issue order, and the poll's
+// were the youngest), so an explicit full wait there costs nothing and leaves the
+// compiler nothing pending to guard later in the phase.
+// (The compiler barriers keep loads from being moved across the wait.)
+__device__ __forceinline__ void settle_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  asm volatile("" ::: "memory");
+}
+
 // Tagged words are polled in batches: every load of a batch is issued before any
-// tag is checked (one memory round trip per attempt), and only words that did
-// not yet carry the expected tag are loaded again.
+// tag is checked (one memory round trip per attempt), and a thread that still
+// misses a word loads all of its words again.  No load sits under a condition (a
+// conditional load becomes a basic block of its own with its counter wait inside,
+// which would turn a retry into a chain of round trips): a word past `count`
+// re-reads the thread's word of the first row (callers ignore its value; the batch
+// size is chosen to fit the input, so there are few such words, and they spread
+// over many cache lines rather than piling onto one).  A scheduling barrier after
+// the batch keeps the compiler from pulling the checks in between the loads.
+// The thread index is laundered per call, so that the word offsets are formed at
+// the poll (a few VALU ops) instead of being hoisted out of the phase loop and held
+// in registers for the whole frame; they are 32-bit offsets from the uniform base.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+template <class T>
+__device__ __forceinline__ const T* word_at(const T* base, int i) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + (uint32_t)i * (uint32_t)sizeof(T));
+}
 template <int N>
-__device__ __forceinline__ bool poll_batch64(const uint64_t* base, int stride, int count, unsigned tag,
-                                             uint64_t (&wv)[N], Poll& pl) {
-  const int t = threadIdx.x;
+__device__ __forceinline__ void load_batch64(const uint64_t* base, int stride, int count, uint64_t (&wv)[N]) {
+  const int t = opaque_tid();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const int k = i * stride + t;
-    wv[i] = k < count ? ld64(base + k) : ((uint64_t)tag << 32);
+    wv[i] = ld64(word_at(base, k < count ? k : min(t, count - 1)));
   }
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int N>
+__device__ __forceinline__ bool poll_batch64(const uint64_t* base, int stride, int count, unsigned tag,
+                                             uint64_t (&wv)[N], Poll& pl) {
+  load_batch64<N>(base, stride, count, wv);
   while (true) {
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < N; ++i) ok = ok && ((unsigned)(wv[i] >> 32) == tag);
     if (ok) return true;
     if (!pl.again()) return false;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int k = i * stride + t;
-      if ((unsigned)(wv[i] >> 32) != tag) wv[i] = ld64(base + k);
-    }
+    load_batch64<N>(base, stride, count, wv);
   }
+}
+template <int N>
+__device__ __forceinline__ void load_batch32(const uint32_t* base, int stride, int count, uint32_t (&wv)[N]) {
+  const int t = opaque_tid();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int k = i * stride + t;
+    wv[i] = ld32(word_at(base, k < count ? k : min(t, count - 1)));
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 template <int N>
 __device__ __forceinline__ bool poll_batch32(const uint32_t* base, int stride, int count, unsigned tag,
                                              uint32_t (&wv)[N], Poll& pl) {
-  const int t = threadIdx.x;
   const unsigned t16 = tag & 0xffffu;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int k = i * stride + t;
-    wv[i] = k < count ? ld32(base + k) : (t16 << 16);
-  }
+  load_batch32<N>(base, stride, count, wv);
   while (true) {
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < N; ++i) ok = ok && ((wv[i] >> 16) == t16);
     if (ok) return true;
     if (!pl.again()) return false;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int k = i * stride + t;
-      if ((wv[i] >> 16) != t16) wv[i] = ld32(base + k);
-    }
+    load_batch32<N>(base, stride, count, wv);
   }
 }
 
-// xs = act(rmsnorm(h) * g), h polled from the tagged residual
-template <int P>
-__device__ __forceinline__ bool norm_to_lds(const uint64_t* xh, unsigned tag, const float* g, int K, float eps,
-                                            float scale, uint32_t* xs, float* red, unsigned* abort_flag, int* okf) {
+// xs = act(rmsnorm(h) * g), h polled from the tagged residual; kMaxPer words per thread
+template <int P, int kMaxPer>
+__device__ __forceinline__ bool norm_to_lds_n(const uint64_t* xh, unsigned tag, const float* g, int K, float eps,
+                                              float scale, uint32_t* xs, float* red, unsigned* abort_flag, int* okf,
+                                              uint32_t (&seen)[2]) {
   Poll pl;
   pl.start(abort_flag);
-  constexpr int kMaxPer = 10;  // K <= 10 * kFT
   // the gains do not depend on the frame: their loads travel with the first poll round
   float gv[kMaxPer];
 #pragma unroll
@@ -303,7 +365,10 @@ __device__ __forceinline__ bool norm_to_lds(const uint64_t* xh, unsigned tag, co
   issue_fence();
   uint64_t wv[kMaxPer];
   const bool got = poll_batch64<kMaxPer>(xh, kFT, K, tag, wv, pl);
+  settle_loads();
+  seen[0] = (uint32_t)__builtin_amdgcn_s_memrealtime();
   if (!block_ok(got, okf)) return false;
+  seen[1] = (uint32_t)__builtin_amdgcn_s_memrealtime();
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i) {
@@ -322,28 +387,46 @@ __device__ __forceinline__ bool norm_to_lds(const uint64_t* xh, unsigned tag, co
   __syncthreads();
   return true;
 }
+template <int P>
+__device__ __forceinline__ bool norm_to_lds(const uint64_t* xh, unsigned tag, const float* g, int K, float eps,
+                                            float scale, uint32_t* xs, float* red, unsigned* abort_flag, int* okf,
+                                            uint32_t (&seen)[2]) {
+  // K <= 10 * kFT; hidden sizes up to 5 * kFT (2560 at 512 threads) take the short batch
+  if (K <= 5 * kFT) return norm_to_lds_n<P, 5>(xh, tag, g, K, eps, scale, xs, red, abort_flag, okf, seen);
+  return norm_to_lds_n<P, 10>(xh, tag, g, K, eps, scale, xs, red, abort_flag, okf, seen);
+}
 
-// xs from a tagged exchange buffer already in GEMV units (bf16 bits)
-__device__ __forceinline__ bool act_to_lds(const uint32_t* x, unsigned tag, int K, uint32_t* xs,
-                                           unsigned* abort_flag, int* okf) {
+// xs from a tagged exchange buffer already in GEMV units (bf16 bits); kMaxPer words per thread
+template <int kMaxPer>
+__device__ __forceinline__ bool act_to_lds_n(const uint32_t* x, unsigned tag, int K, uint32_t* xs,
+                                             unsigned* abort_flag, int* okf, uint32_t (&seen)[2]) {
   Poll pl;
   pl.start(abort_flag);
-  constexpr int kMaxPer = 20;  // K <= 20 * kFT
   uint32_t wv[kMaxPer];
   const bool got = poll_batch32<kMaxPer>(x, kFT, K, tag, wv, pl);
+  settle_loads();
+  seen[0] = (uint32_t)__builtin_amdgcn_s_memrealtime();
   uint16_t* xs16 = reinterpret_cast<uint16_t*>(xs);
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i) {
     const int k = i * kFT + threadIdx.x;
     if (k < K) xs16[k] = (uint16_t)(wv[i] & 0xffffu);
   }
-  return block_ok(got, okf);
+  const bool ok = block_ok(got, okf);
+  seen[1] = (uint32_t)__builtin_amdgcn_s_memrealtime();
+  return ok;
+}
+__device__ __forceinline__ bool act_to_lds(const uint32_t* x, unsigned tag, int K, uint32_t* xs,
+                                           unsigned* abort_flag, int* okf, uint32_t (&seen)[2]) {
+  // K <= 20 * kFT; the attention output (Hq * hd = 4096 at 512 threads) takes the short batch
+  if (K <= 8 * kFT) return act_to_lds_n<8>(x, tag, K, xs, abort_flag, okf, seen);
+  return act_to_lds_n<20>(x, tag, K, xs, abort_flag, okf, seen);
 }
 
 // Phase timestamps for profiling the persistent kernel (the constant 100 MHz clock):
-// [0] phase start, [1] inputs ready, [2] weights streamed, [3] phase done; and, for
-// wave 0 of the block during the weight stream (core clock cycles): [4] waiting for
-// ring packets, [5] packets consumed, [6] row sums closed, [7] issuing fetches.
+// [0] phase start, [1] inputs ready, [2] weights streamed, [3] phase done; for wave 0
+// of the block: [4] weight packets consumed and [5] row sums closed in the phase; and
+// (clock again) [6] wave 0's polls of the phase input satisfied, [7] every wave's.
 // Trace words are written by every lane of wave 0 (the same value to the same word):
 // a branch on the wave index is uniform, where one on the thread index would be a
 // divergent branch that the compiler may thread through the whole phase loop.
@@ -970,6 +1053,8 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
   Issuer<P> is;
   issuer_begin<P, HD>(a, is, ring_w, split, n_phases);
   int cslot = 0;  // ring slot of the next packet to consume
+  float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  asm volatile("" : "+v"(zero4.x), "+v"(zero4.y), "+v"(zero4.z), "+v"(zero4.w));
   for (int i = tid; i < kPartMax; i += kFT) part[i] = 0.0f;
 
   // frame input: h = sum_k E_aud[k][prev_k]; every block forms the whole vector for
@@ -1004,8 +1089,8 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     }
     ss = block_sum(ss, red);
     const float rstd = 1.0f / sqrtf(ss / (float)d + a.eps);
-    const float sc = P == kFP8 ? a.act_scales[0] : 1.0f;
-    const float* g = a.layers[0].g_attn;
+    const float sc = P == kFP8 ? act_scale(a, 0) : 1.0f;
+    const float* g = layer_ptrs(a, 0)->g_attn;
     uint16_t* xs16 = reinterpret_cast<uint16_t*>(xs);
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) {
@@ -1014,6 +1099,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     }
     __syncthreads();
   }
+  settle_loads();  // nothing of the prologue's is left pending at the phase loop's entry
 
   unsigned tag_h = base;   // tag of the residual's latest value
   for (int phase = 0; phase < n_phases; ++phase) {
@@ -1032,51 +1118,60 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     }
     const int site = kind == kHEAD ? kSitesPerLayer * a.n_layers
                    : kSitesPerLayer * layer + (kind == kQKV ? 0 : kind == kO ? 1 : kind == kGU ? 2 : 3);
-    const float sc_in = P == kFP8 ? a.act_scales[site] : 1.0f;
+    const float sc_in = P == kFP8 ? act_scale(a, site) : 1.0f;
     const Stream<P> cur = phase_stream<P, HD>(a, split, phase);
     // FP8 row scales of this block's rows (at most one row, or one gate/up pair, per
-    // thread), loaded before the prologue waits so that the epilogue finds them ready
+    // thread), loaded before the prologue's poll and settled right after it (below):
+    // the poll's own wait has landed everything older by then, whereas a first use
+    // in the epilogue would wait for every weight fetch the ring has in flight
+    // Every thread loads (threads past the block's rows load row 0's scale, unused):
+    // a default value written into the register before a conditional load would
+    // make the compiler wait for every load in flight first.
     float ws0 = 1.0f, ws1 = 1.0f;
     if (P == kFP8) {
-      const LayerW* L = a.layers + layer;
-      const float* wsc = kind == kHEAD ? a.s_head
-                       : kind == kQKV ? L->s_qkv : kind == kO ? L->s_o : kind == kGU ? L->s_gu : L->s_d;
-      if (kind == kGU) {
-        if (tid < cur.nrows / 2) { ws0 = *gp(wsc + cur.r0 + 2 * tid); ws1 = *gp(wsc + cur.r0 + 2 * tid + 1); }
-      } else if (tid < cur.nrows) {
-        ws0 = *gp(wsc + cur.r0 + tid);
-      }
+      const float* wsc = kind == kHEAD ? a.s_head : layer_scales(a, layer, kind == kQKV ? 0 : kind - 1);
+      const int n = kind == kGU ? cur.nrows / 2 : cur.nrows;
+      const int i = tid < n ? tid : 0;
+      const int r = tid < n ? cur.r0 + (kind == kGU ? 2 * i : i) : 0;
+      ws0 = *gp(wsc + r);
+      ws1 = *gp(wsc + r + (kind == kGU ? 1 : 0));
       issue_fence();
     }
     // ---- prologue: the phase input in LDS
+    uint32_t seen[2] = {0u, 0u};
     if (kind == kQKV || kind == kGU || kind == kHEAD) {
       if (!(kind == kQKV && layer == 0)) {
-        const float* g = kind == kHEAD ? a.g_final : (kind == kQKV ? a.layers[layer].g_attn : a.layers[layer].g_mlp);
-        if (!norm_to_lds<P>(xh, tag_h, g, d, a.eps, sc_in, xs, red, abort_flag, &okf)) { ring_drain(); return; }
+        const float* g = kind == kHEAD ? a.g_final : (kind == kQKV ? layer_ptrs(a, layer)->g_attn : layer_ptrs(a, layer)->g_mlp);
+        if (!norm_to_lds<P>(xh, tag_h, g, d, a.eps, sc_in, xs, red, abort_flag, &okf, seen)) { ring_drain(); return; }
+      } else {
+        settle_loads();  // layer 0's input was formed in the frame prologue: nothing is in flight
       }
     } else {
       // O reads the attention output (phase tag - 1), DOWN the SiLU*mul output (tag - 1)
       const uint32_t* src = kind == kO ? launder(a.xo) : launder(a.xa);
       const int K = kind == kO ? a.Hq * HD : a.F;
-      if (!act_to_lds(src, tag - 1u, K, xs, abort_flag, &okf)) { ring_drain(); return; }
+      if (!act_to_lds(src, tag - 1u, K, xs, abort_flag, &okf, seen)) { ring_drain(); return; }
     }
+    if (P == kFP8) asm volatile("" : "+v"(ws0), "+v"(ws1));  // the scale loads land here
     trace_mark(a, n_phases, phase, 1);
+    trace_put(a, n_phases, phase, 6, seen[0]);
+    trace_put(a, n_phases, phase, 7, seen[1]);
     // ---- stream the weights from the ring (its fetches run ahead into the next phases)
     run_stream<P, HD>(a, cur, is, cslot, ring_w, xs, part, n_phases, phase);
     trace_mark(a, n_phases, phase, 2);
     // ---- epilogue (rows per block <= 128 < kFT, so one row or pair per thread)
     if (kind == kGU) {
-      const float sc_out = P == kFP8 ? a.act_scales[site + 1] : 1.0f;
+      const float sc_out = P == kFP8 ? act_scale(a, site + 1) : 1.0f;
       if (tid < cur.nrows / 2) {
         const int row = cur.r0 + 2 * tid;
-        const float g = row_sum(part, 2 * tid) * (P == kFP8 ? sc_in * ws0 : 1.0f);
-        const float u = row_sum(part, 2 * tid + 1) * (P == kFP8 ? sc_in * ws1 : 1.0f);
+        const float g = row_sum(part, 2 * tid, zero4) * (P == kFP8 ? sc_in * ws0 : 1.0f);
+        const float u = row_sum(part, 2 * tid + 1, zero4) * (P == kFP8 ? sc_in * ws1 : 1.0f);
         st32(launder(a.xa) + row / 2, act_bits<P>(silu(g) * u, sc_out), tag);
       }
     } else {
       if (tid < cur.nrows) {
         const int row = cur.r0 + tid;
-        const float y = row_sum(part, tid) * (P == kFP8 ? sc_in * ws0 : 1.0f);
+        const float y = row_sum(part, tid, zero4) * (P == kFP8 ? sc_in * ws0 : 1.0f);
         if (kind == kQKV) {
           st64(launder(a.xqkv) + row, y, tag);
         } else if (kind == kHEAD) {
@@ -1116,14 +1211,17 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
       const int i = half * kVPL * kWave + q * kWave + lane;
       lw[q] = i < a.V ? ld64(lg + q * kWave + lane) : want;
     }
-    while (pl.ok) {
+    while (pl.ok) {  // a lane that still misses a logit reloads all of its logits
       bool ok = true;
 #pragma unroll
       for (int q = 0; q < kVPL; ++q) ok = ok && (unsigned)(lw[q] >> 32) == tag_logits;
       if (ok || !pl.again()) break;
 #pragma unroll
-      for (int q = 0; q < kVPL; ++q)
-        if ((unsigned)(lw[q] >> 32) != tag_logits) lw[q] = ld64(lg + q * kWave + lane);
+      for (int q = 0; q < kVPL; ++q) {
+        const int i = half * kVPL * kWave + q * kWave + lane;
+        const uint64_t v = ld64(lg + (i < a.V ? q * kWave + lane : 0));
+        lw[q] = i < a.V ? v : want;
+      }
     }
     float bv = -INFINITY;
     int bi = 0x7fffffff;

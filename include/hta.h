@@ -155,7 +155,9 @@ int hta_force_codes(hta_ctx* ctx, const int32_t* codes_in);
  * gate/up, down; then the head), the low 32 bits of the 100 MHz constant clock
  * at phase start, inputs ready, weights streamed and phase done, then for the
  * block's first wave: weight packets consumed and row sums closed in the
- * phase, and two words left as they were (blocks = one per compute unit;
+ * phase, then the clock when the first wave's polls of the phase input were
+ * satisfied and when every wave's were (zero where a phase has no polled
+ * input; attention phases leave both as they were) (blocks = one per compute unit;
  * entries of phases a block skips are left as they were).
  * A buffer smaller than the tap gives HTA_E_ARG. */
 enum { HTA_TAP_HIDDEN = 0, HTA_TAP_LOGITS = 1, HTA_TAP_STATE = 2, HTA_TAP_KV = 3, HTA_TAP_AMAX = 4,
