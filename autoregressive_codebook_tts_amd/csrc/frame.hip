@@ -266,6 +266,49 @@ __device__ __forceinline__ uint32_t act_bits(float v, float scale) {
   return f32_to_bf16(act_round<P>(v, scale));
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Store the wave-uniform v to the LDS word p from lane 0 only, without a branch on the
+// lane index: such a branch is divergent control flow, and the compiler may merge code
+// across it in ways that make the (uniform) fetch state look divergent.  The store
+// completes before the statement ends.  The compiler does not see the EXEC writes, so
+// each is followed by the wait states that a later DPP or lane-select instruction
+// needs after an SALU write of EXEC (five).
+__device__ __forceinline__ void lane0_lds_store(float* p, float v) {
+  const uint32_t addr = (uint32_t)(uintptr_t)(lds_void_t*)p;
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "s_nop 4\n\t"
+      "ds_write_b32 %1, %2\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_mov_b64 exec, %0\n\t"
+      "s_nop 4"
+      : "=&s"(saved) : "v"(addr), "v"(v) : "memory");
+}
+
+// A block-wide sum and "every thread's poll succeeded" with one barrier: each wave
+// leaves its partial sum and its flag in its own slot of `slots` (2 * kFW floats),
+// then every wave adds the partials in wave order (the order block_sum uses).  The
+// slots are reused phase after phase; the barriers between two uses keep them apart.
+__device__ __forceinline__ bool block_sum_ok(float& v, bool ok, float* slots) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  v = wave_sum(v);
+  const float wok = __all(ok) ? 1.0f : 0.0f;
+  lane0_lds_store(slots + w, v);
+  lane0_lds_store(slots + kFW + w, wok);
+  __syncthreads();
+  float s = 0.0f, all = 1.0f;
+#pragma unroll
+  for (int i = 0; i < kFW; ++i) {
+    s += slots[i];
+    all = fminf(all, slots[kFW + i]);
+  }
+  v = s;
+  return __builtin_amdgcn_readfirstlane(__float_as_uint(all)) != 0u;
+}
+
 // The compiler counts only its own vector loads, not the ring's LDS fetches; where it
 // cannot prove a load of its own has landed it waits for the whole counter, and that
 // wait would also wait for every fetch the ring has in flight.  Right after a poll is
@@ -351,7 +394,7 @@ __device__ __forceinline__ bool poll_batch32(const uint32_t* base, int stride, i
 // xs = act(rmsnorm(h) * g), h polled from the tagged residual; kMaxPer words per thread
 template <int P, int kMaxPer>
 __device__ __forceinline__ bool norm_to_lds_n(const uint64_t* xh, unsigned tag, const float* g, int K, float eps,
-                                              float scale, uint32_t* xs, float* red, unsigned* abort_flag, int* okf,
+                                              float scale, uint32_t* xs, float* red, unsigned* abort_flag,
                                               uint32_t (&seen)[2]) {
   Poll pl;
   pl.start(abort_flag);
@@ -367,8 +410,6 @@ __device__ __forceinline__ bool norm_to_lds_n(const uint64_t* xh, unsigned tag, 
   const bool got = poll_batch64<kMaxPer>(xh, kFT, K, tag, wv, pl);
   settle_loads();
   seen[0] = (uint32_t)__builtin_amdgcn_s_memrealtime();
-  if (!block_ok(got, okf)) return false;
-  seen[1] = (uint32_t)__builtin_amdgcn_s_memrealtime();
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i) {
@@ -376,7 +417,8 @@ __device__ __forceinline__ bool norm_to_lds_n(const uint64_t* xh, unsigned tag, 
     const float v = k < K ? __uint_as_float((uint32_t)wv[i]) : 0.0f;
     ss = fmaf(v, v, ss);
   }
-  ss = block_sum(ss, red);
+  if (!block_sum_ok(ss, got, red)) return false;  // red: 2 * kFW floats
+  seen[1] = (uint32_t)__builtin_amdgcn_s_memrealtime();
   const float rstd = 1.0f / sqrtf(ss / (float)K + eps);
   uint16_t* xs16 = reinterpret_cast<uint16_t*>(xs);
 #pragma unroll
@@ -389,17 +431,17 @@ __device__ __forceinline__ bool norm_to_lds_n(const uint64_t* xh, unsigned tag, 
 }
 template <int P>
 __device__ __forceinline__ bool norm_to_lds(const uint64_t* xh, unsigned tag, const float* g, int K, float eps,
-                                            float scale, uint32_t* xs, float* red, unsigned* abort_flag, int* okf,
+                                            float scale, uint32_t* xs, float* red, unsigned* abort_flag,
                                             uint32_t (&seen)[2]) {
   // K <= 10 * kFT; hidden sizes up to 5 * kFT (2560 at 512 threads) take the short batch
-  if (K <= 5 * kFT) return norm_to_lds_n<P, 5>(xh, tag, g, K, eps, scale, xs, red, abort_flag, okf, seen);
-  return norm_to_lds_n<P, 10>(xh, tag, g, K, eps, scale, xs, red, abort_flag, okf, seen);
+  if (K <= 5 * kFT) return norm_to_lds_n<P, 5>(xh, tag, g, K, eps, scale, xs, red, abort_flag, seen);
+  return norm_to_lds_n<P, 10>(xh, tag, g, K, eps, scale, xs, red, abort_flag, seen);
 }
 
 // xs from a tagged exchange buffer already in GEMV units (bf16 bits); kMaxPer words per thread
 template <int kMaxPer>
 __device__ __forceinline__ bool act_to_lds_n(const uint32_t* x, unsigned tag, int K, uint32_t* xs,
-                                             unsigned* abort_flag, int* okf, uint32_t (&seen)[2]) {
+                                             unsigned* abort_flag, float* slots, uint32_t (&seen)[2]) {
   Poll pl;
   pl.start(abort_flag);
   uint32_t wv[kMaxPer];
@@ -412,15 +454,16 @@ __device__ __forceinline__ bool act_to_lds_n(const uint32_t* x, unsigned tag, in
     const int k = i * kFT + threadIdx.x;
     if (k < K) xs16[k] = (uint16_t)(wv[i] & 0xffffu);
   }
-  const bool ok = block_ok(got, okf);
+  float unused = 0.0f;
+  const bool ok = block_sum_ok(unused, got, slots);  // also makes the xs writes visible
   seen[1] = (uint32_t)__builtin_amdgcn_s_memrealtime();
   return ok;
 }
 __device__ __forceinline__ bool act_to_lds(const uint32_t* x, unsigned tag, int K, uint32_t* xs,
-                                           unsigned* abort_flag, int* okf, uint32_t (&seen)[2]) {
+                                           unsigned* abort_flag, float* slots, uint32_t (&seen)[2]) {
   // K <= 20 * kFT; the attention output (Hq * hd = 4096 at 512 threads) takes the short batch
-  if (K <= 8 * kFT) return act_to_lds_n<8>(x, tag, K, xs, abort_flag, okf, seen);
-  return act_to_lds_n<20>(x, tag, K, xs, abort_flag, okf, seen);
+  if (K <= 8 * kFT) return act_to_lds_n<8>(x, tag, K, xs, abort_flag, slots, seen);
+  return act_to_lds_n<20>(x, tag, K, xs, abort_flag, slots, seen);
 }
 
 // Phase timestamps for profiling the persistent kernel (the constant 100 MHz clock):
@@ -445,7 +488,33 @@ struct AttnLds {
   uint32_t Kt[kAttnTile][65];       // the tile's keys as bf16 pairs (rows padded against bank conflicts)
   uint32_t Vt[kAttnTile][64];       // the tile's values as bf16 pairs
   float ps[4][kAttnTile];
+  float half[8][kAttnTile];         // per (wave, key): the even- or odd-dimension half of a score
+  float scl[4];                     // per query head: the tile's rescale of the running output
+  float ml[4][2];                   // per query head: this split's (max, denominator)
 };
+
+// Half of the dot product of query head qh with key `key` of the tile: the even
+// dimensions (low halves of the key words) or, ODD, the odd ones, as two FMA chains
+// alternating over the key words, added at the end.
+template <int HD, bool ODD>
+__device__ __forceinline__ float half_dot(const AttnLds& sm, int qh, int key) {
+  float d[2] = {0.0f, 0.0f};
+  for (int eb = 0; eb < HD / 2; eb += 16) {  // 16 key words and 32 query values per batch
+    uint32_t kk[16];
+    float q[32];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) kk[u] = sm.Kt[key][eb + u];
+#pragma unroll
+    for (int u = 0; u < 32; u += 4) {
+      const float4 q4 = *reinterpret_cast<const float4*>(&sm.qs[qh][2 * eb + u]);
+      q[u] = q4.x; q[u + 1] = q4.y; q[u + 2] = q4.z; q[u + 3] = q4.w;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      d[u & 1] = ODD ? fmaf(q[2 * u + 1], bf16hi(kk[u]), d[u & 1]) : fmaf(q[2 * u], bf16lo(kk[u]), d[u & 1]);
+  }
+  return d[0] + d[1];
+}
 
 template <int HD>
 __device__ __forceinline__ void attn_norm_rope(const uint64_t* src, unsigned tag, const float* g, const float* cs,
@@ -488,7 +557,7 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
   const int task = blockIdx.x;
   if (task >= ntask) return true;
   const int j = task / a.splits, split = task % a.splits;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nkeys = pos + 1;
   int chunk = (nkeys + a.splits - 1) / a.splits;
   chunk = (chunk + T - 1) / T * T;
@@ -542,12 +611,10 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
   }
   if (!block_ok(pl.ok, okf)) return false;
   trace_mark(a, 5 * a.n_layers + 1, 5 * layer + 1, 1);
-  if (beg <= pos && pos < end && tid < HD) {
-    *gpw(kc + (size_t)pos * HD + tid) = (uint16_t)f32_to_bf16(sm.kn[tid]);
-    *gpw(vc + (size_t)pos * HD + tid) = (uint16_t)f32_to_bf16(sm.vn[tid]);
-  }
   const float inv_sqrt = 1.0f / sqrtf((float)HD);
-  float m = -INFINITY, lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  const bool hi = w >= G;             // the odd-dimension / upper-output wave of a query head
+  const int qh = hi ? w - G : w;      // its query head within the group
+  float m = -INFINITY, lsum = 0.0f, o = 0.0f;  // (m, lsum) live in the lower wave of each head
   for (int t0 = beg; t0 < end; t0 += T) {
     if (t0 != beg) load_tile(t0);
 #pragma unroll
@@ -570,81 +637,77 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
       for (int e = 0; e < 4; ++e) { sm.Kt[key][seg * 4 + e] = kw[e]; sm.Vt[key][seg * 4 + e] = vw[e]; }
     }
     __syncthreads();
-    float scale = 1.0f, mnew = m;
-    if (w < G) {
+    // Every query head is shared by two waves: wave qh takes the even dimensions (the
+    // low halves of the key and value words) and wave qh + G the odd ones of the
+    // scores, and dimensions 0..63 and 64..127 of the output.  The two FMA chains of
+    // each half and their final additions are those of a single wave's dot product,
+    // so the scores and outputs are unchanged.
+    float mnew = m;
+    if (w < 2 * G) {
       const int kp = t0 + lane;
-      float s = -INFINITY;
-      if (kp < end) {
-        float d0[2] = {0.0f, 0.0f}, d1[2] = {0.0f, 0.0f};
-        for (int eb = 0; eb < HD / 2; eb += 16) {  // 16 key words and 32 query values per batch
-          uint32_t kk[16];
-          float q[32];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) kk[u] = sm.Kt[lane][eb + u];
-#pragma unroll
-          for (int u = 0; u < 32; u += 4) {
-            const float4 q4 = *reinterpret_cast<const float4*>(&sm.qs[w][2 * eb + u]);
-            q[u] = q4.x; q[u + 1] = q4.y; q[u + 2] = q4.z; q[u + 3] = q4.w;
-          }
-#pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            d0[u & 1] = fmaf(q[2 * u], bf16lo(kk[u]), d0[u & 1]);
-            d1[u & 1] = fmaf(q[2 * u + 1], bf16hi(kk[u]), d1[u & 1]);
-          }
-        }
-        s = ((d0[0] + d0[1]) + (d1[0] + d1[1])) * inv_sqrt;
-      }
-      mnew = fmaxf(m, wave_max(s));
-      const float p = (kp < end) ? __expf(s - mnew) : 0.0f;
-      scale = __expf(m - mnew);
-      lsum = lsum * scale + wave_sum(p);
-      sm.ps[w][lane] = p;
+      float part = 0.0f;
+      if (kp < end) part = hi ? half_dot<HD, true>(sm, qh, lane) : half_dot<HD, false>(sm, qh, lane);
+      sm.half[w][lane] = part;
     }
     __syncthreads();
     if (w < G) {
+      const int kp = t0 + lane;
+      const float s = (kp < end) ? (sm.half[w][lane] + sm.half[w + G][lane]) * inv_sqrt : -INFINITY;
+      mnew = fmaxf(m, wave_max(s));
+      const float p = (kp < end) ? __expf(s - mnew) : 0.0f;
+      const float scale = __expf(m - mnew);
+      lsum = lsum * scale + wave_sum(p);
+      sm.ps[w][lane] = p;
+      sm.scl[w] = scale;  // every lane writes the same value
+    }
+    __syncthreads();
+    if (w < 2 * G && (HD > 64 || !hi)) {
       // all T keys of the tile (those past the split have p = 0 and zero values), 16 keys
       // per batch: the batch's LDS reads are issued together, then one FMA chain in key
       // order (the order of the one-kernel-per-phase frame)
-      const int d0 = lane >> 1, d1 = ((lane + 64) % HD) >> 1;
-      const bool hi0 = lane & 1, hi1 = ((lane + 64) % HD) & 1;
-      o0 *= scale;
-      o1 *= scale;
+      const int dd = hi ? lane + 64 : lane;  // this lane's output dimension
+      const int dw = dd >> 1;
+      const uint32_t dsh = (dd & 1) ? 0u : 16u;  // bf16 half of the value word: (v << dsh) & hi16
+      o *= sm.scl[qh];
       for (int kb = 0; kb < T; kb += 16) {
         float pp[16];
-        uint32_t v0[16], v1[16];
+        uint32_t v[16];
 #pragma unroll
         for (int u = 0; u < 16; u += 4) {
-          const float4 p4 = *reinterpret_cast<const float4*>(&sm.ps[w][kb + u]);
+          const float4 p4 = *reinterpret_cast<const float4*>(&sm.ps[qh][kb + u]);
           pp[u] = p4.x; pp[u + 1] = p4.y; pp[u + 2] = p4.z; pp[u + 3] = p4.w;
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          v0[u] = sm.Vt[kb + u][d0];
-          v1[u] = HD > 64 ? sm.Vt[kb + u][d1] : 0u;
-        }
+        for (int u = 0; u < 16; ++u) v[u] = sm.Vt[kb + u][dw];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          o0 = fmaf(pp[u], hi0 ? bf16hi(v0[u]) : bf16lo(v0[u]), o0);
-          if (HD > 64) o1 = fmaf(pp[u], hi1 ? bf16hi(v1[u]) : bf16lo(v1[u]), o1);
-        }
+        for (int u = 0; u < 16; ++u) o = fmaf(pp[u], __uint_as_float((v[u] << dsh) & 0xffff0000u), o);
       }
-      m = mnew;
     }
+    m = mnew;
     __syncthreads();
+  }
+  // this frame's key and value into the cache, for the frames to come (this one took
+  // them from LDS): stored after the tiles, so that no tile waits for the stores
+  if (beg <= pos && pos < end && tid < HD) {
+    *gpw(kc + (size_t)pos * HD + tid) = (uint16_t)f32_to_bf16(sm.kn[tid]);
+    *gpw(vc + (size_t)pos * HD + tid) = (uint16_t)f32_to_bf16(sm.vn[tid]);
   }
   trace_mark(a, 5 * a.n_layers + 1, 5 * layer + 1, 2);
   const float so = P == kFP8 ? *gp(a.act_scales + kSitesPerLayer * layer + 1) : 1.0f;
   if (split != 0) {
     // publish this split's (o, m, l)
-    if (w < G) {
-      const int h = j * G + w;
+    if (w < 2 * G && (HD > 64 || !hi)) {
+      const int h = j * G + qh;
       uint64_t* pp = xpart + ((size_t)h * a.splits + split) * (HD + 2);
-      if (lane < HD) st64(pp + lane, o0, tag_part);
-      if (HD > 64) st64(pp + lane + 64, o1, tag_part);
-      if (lane == 0) { st64(pp + HD, m, tag_part); st64(pp + HD + 1, lsum, tag_part); }
+      st64(pp + (hi ? lane + 64 : lane), o, tag_part);
+      if (!hi && lane == 0) { st64(pp + HD, m, tag_part); st64(pp + HD + 1, lsum, tag_part); }
     }
     return true;
   }
+  // the upper wave of each head takes the split's (m, l) from the lower one
+  if (w < G) { sm.ml[w][0] = m; sm.ml[w][1] = lsum; }
+  __syncthreads();
+  if (hi && w < 2 * G) { m = sm.ml[qh][0]; lsum = sm.ml[qh][1]; }
   // split 0: merge with the other active splits (log-sum-exp) and publish the output.
   // The first round loads every split's (m, l) (lane s holds split s's) together with
   // the o vectors of the first kMB other splits, so a merge of up to kMB + 1 splits
@@ -652,35 +715,35 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
   constexpr int kMB = 8;  // o vectors per round
   Poll pm;
   pm.start(abort_flag);
-  if (w < G) {
-    const int h = j * G + w;
+  if (w < 2 * G && (HD > 64 || !hi)) {
+    // both waves of a head form the same merge weights; each merges its half of the output
+    const int h = j * G + qh;
+    const int dd = hi ? lane + 64 : lane;
     const uint64_t* pb = xpart + (size_t)h * a.splits * (HD + 2);
     const uint64_t want = (uint64_t)tag_part << 32;
     const bool other = lane > 0 && lane < n_active;
     uint64_t wm = other ? ld64(pb + (size_t)lane * (HD + 2) + HD) : want;
     uint64_t wl = other ? ld64(pb + (size_t)lane * (HD + 2) + HD + 1) : want;
-    float n0 = 0.0f, n1 = 0.0f, f = 0.0f;
+    float n = 0.0f, f = 0.0f;
     for (int sp0 = 1; sp0 < n_active || sp0 == 1; sp0 += kMB) {
-      uint64_t x0[kMB], x1[kMB];
+      uint64_t x[kMB];
 #pragma unroll
       for (int u = 0; u < kMB; ++u) {
         const int sp = sp0 + u;
         const uint64_t* q = pb + (size_t)(sp < n_active ? sp : 0) * (HD + 2);
-        x0[u] = (sp < n_active && lane < HD) ? ld64(q + lane) : want;
-        x1[u] = (sp < n_active && HD > 64) ? ld64(q + lane + 64) : want;
+        x[u] = sp < n_active ? ld64(q + dd) : want;
       }
       while (pm.ok) {
         bool ok = (unsigned)(wm >> 32) == tag_part && (unsigned)(wl >> 32) == tag_part;
 #pragma unroll
-        for (int u = 0; u < kMB; ++u) ok = ok && (unsigned)(x0[u] >> 32) == tag_part && (unsigned)(x1[u] >> 32) == tag_part;
+        for (int u = 0; u < kMB; ++u) ok = ok && (unsigned)(x[u] >> 32) == tag_part;
         if (ok || !pm.again()) break;
         if ((unsigned)(wm >> 32) != tag_part) wm = ld64(pb + (size_t)lane * (HD + 2) + HD);
         if ((unsigned)(wl >> 32) != tag_part) wl = ld64(pb + (size_t)lane * (HD + 2) + HD + 1);
 #pragma unroll
         for (int u = 0; u < kMB; ++u) {
           const uint64_t* q = pb + (size_t)(sp0 + u) * (HD + 2);
-          if ((unsigned)(x0[u] >> 32) != tag_part) x0[u] = ld64(q + lane);
-          if ((unsigned)(x1[u] >> 32) != tag_part) x1[u] = ld64(q + lane + 64);
+          if ((unsigned)(x[u] >> 32) != tag_part) x[u] = ld64(q + dd);
         }
       }
       if (!pm.ok) break;
@@ -690,24 +753,17 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
         const float M = wave_max(ls > 0.0f ? ms : -INFINITY);
         f = (ls > 0.0f) ? __expf(ms - M) : 0.0f;
         lsum = wave_sum(f * ls);  // the merged denominator
-        const float f0 = __shfl(f, 0, kWave);
-        n0 = f0 * o0;
-        n1 = f0 * o1;
+        n = __shfl(f, 0, kWave) * o;
       }
 #pragma unroll
       for (int u = 0; u < kMB; ++u) {
         const int sp = sp0 + u;
         const float fs = __shfl(f, sp < n_active ? sp : 0, kWave);
-        if (sp < n_active) {
-          n0 = fmaf(fs, __uint_as_float((uint32_t)x0[u]), n0);
-          n1 = fmaf(fs, __uint_as_float((uint32_t)x1[u]), n1);
-        }
+        if (sp < n_active) n = fmaf(fs, __uint_as_float((uint32_t)x[u]), n);
       }
     }
-    const float den = lsum;
-    const float inv = 1.0f / den;
-    if (lane < HD) st32(xo + (size_t)h * HD + lane, act_bits<P>(n0 * inv, so), tag_o);
-    if (HD > 64) st32(xo + (size_t)h * HD + lane + 64, act_bits<P>(n1 * inv, so), tag_o);
+    const float inv = 1.0f / lsum;
+    st32(xo + (size_t)h * HD + dd, act_bits<P>(n * inv, so), tag_o);
   }
   return block_ok(pm.ok, okf);
 }
@@ -741,7 +797,6 @@ __device__ __forceinline__ Stream<P> phase_stream(CFA& a, const int* split, int 
 // for the next phase's inputs and through attention, without holding any
 // registers.  Loads complete in issue order, so "packet k has landed" is
 // "at most issued - k - 1 younger loads are outstanding" (s_waitcnt vmcnt).
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void glb_void_t;
 
 __device__ __forceinline__ int next_gemv_phase(int phase, int n_layers) {
@@ -875,25 +930,6 @@ __device__ __forceinline__ void load_packet(PacketRegs& r, const unsigned char* 
   if (P == kFP8) r.x1 = *reinterpret_cast<const uint4*>(xp + 4);
 }
 
-// Store the wave-uniform v to the LDS word p from lane 0 only, without a branch on the
-// lane index: such a branch is divergent control flow, and the compiler may merge code
-// across it in ways that make the (uniform) fetch state look divergent.  The store
-// completes before the statement ends.  The compiler does not see the EXEC writes, so
-// each is followed by the wait states that a later DPP or lane-select instruction
-// needs after an SALU write of EXEC (five).
-__device__ __forceinline__ void lane0_lds_store(float* p, float v) {
-  const uint32_t addr = (uint32_t)(uintptr_t)(lds_void_t*)p;
-  uint64_t saved;
-  asm volatile(
-      "s_mov_b64 %0, exec\n\t"
-      "s_mov_b64 exec, 1\n\t"
-      "s_nop 4\n\t"
-      "ds_write_b32 %1, %2\n\t"
-      "s_waitcnt lgkmcnt(0)\n\t"
-      "s_mov_b64 exec, %0\n\t"
-      "s_nop 4"
-      : "=&s"(saved) : "v"(addr), "v"(v) : "memory");
-}
 
 // Row bookkeeping of one wave's stream: the open row, the current packet's first byte
 // in it, and this lane's share of it.
@@ -1019,7 +1055,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
   uint32_t* xs = reinterpret_cast<uint32_t*>(lds1);                          // activations, bf16 pairs (<= 10240)
   float* part = reinterpret_cast<float*>(lds1 + 5120 * 4);                   // per-(row, wave) partials
   AttnLds& sm = *reinterpret_cast<AttnLds*>(lds1 + 5120 * 4 + kPartMax * 4);
-  __shared__ float red[16];
+  __shared__ float red[2 * kFW];  // block reductions; (sum, flag) slots of block_sum_ok
   __shared__ int sh_state[4 + kMaxCodebooks];
   __shared__ int okf;
   __shared__ int split[12];  // this block's rows per GEMV kind
@@ -1142,7 +1178,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     if (kind == kQKV || kind == kGU || kind == kHEAD) {
       if (!(kind == kQKV && layer == 0)) {
         const float* g = kind == kHEAD ? a.g_final : (kind == kQKV ? layer_ptrs(a, layer)->g_attn : layer_ptrs(a, layer)->g_mlp);
-        if (!norm_to_lds<P>(xh, tag_h, g, d, a.eps, sc_in, xs, red, abort_flag, &okf, seen)) { ring_drain(); return; }
+        if (!norm_to_lds<P>(xh, tag_h, g, d, a.eps, sc_in, xs, red, abort_flag, seen)) { ring_drain(); return; }
       } else {
         settle_loads();  // layer 0's input was formed in the frame prologue: nothing is in flight
       }
@@ -1150,7 +1186,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
       // O reads the attention output (phase tag - 1), DOWN the SiLU*mul output (tag - 1)
       const uint32_t* src = kind == kO ? launder(a.xo) : launder(a.xa);
       const int K = kind == kO ? a.Hq * HD : a.F;
-      if (!act_to_lds(src, tag - 1u, K, xs, abort_flag, &okf, seen)) { ring_drain(); return; }
+      if (!act_to_lds(src, tag - 1u, K, xs, abort_flag, red, seen)) { ring_drain(); return; }
     }
     if (P == kFP8) asm volatile("" : "+v"(ws0), "+v"(ws1));  // the scale loads land here
     trace_mark(a, n_phases, phase, 1);
