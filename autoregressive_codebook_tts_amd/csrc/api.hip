@@ -93,7 +93,7 @@ Layout make_layout(const hta_config& c) {
   if (2 * F > nmax) nmax = 2 * F;
   if (d > nmax) nmax = d;
   L.off_pgu = take(Pm * 2 * F * 4 + 8 * Pm * nmax * 4);  // gate/up rows, then GEMM split partials
-  L.off_pa = 0;
+  L.off_pa = take(Pm * F * 2);  // SiLU * mul rows (the down projection's input)
   L.off_taps = take(((size_t)c.n_layers + 1) * d * 4);
   L.off_ptaps = take(2 * Pm * d * 4);
   L.off_trace = take((size_t)kTraceBlocks * (5 * c.n_layers + 1) * 8 * 4);
@@ -198,6 +198,7 @@ static void set_pointers(Ctx& c) {
   c.pq = reinterpret_cast<float*>(w + L.off_pq);
   c.po = w + L.off_po;
   c.pgu = reinterpret_cast<float*>(w + L.off_pgu);
+  c.pa = w + L.off_pa;
 }
 
 static void drop_graph(Ctx& c) {

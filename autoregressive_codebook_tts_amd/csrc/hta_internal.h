@@ -126,6 +126,7 @@ struct Ctx {
   float* pq = nullptr;          // [Pmax][qd] rotated q (bf16-rounded values)
   void* po = nullptr;           // [Pmax][qd] act
   float* pgu = nullptr;         // [Pmax][2F]
+  void* pa = nullptr;           // [Pmax][F] SiLU * mul rows (act)
   int last_prefill_P = 0;
   // test taps: the residual entering every layer of each decode frame (and the final one),
   // and the rows entering / leaving layer prefill_tap_layer of each prefill

@@ -272,6 +272,42 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
 // stage, 16-byte unit u of row r sits at position r * NU + (u ^ swz(r)), so a
 // fragment read (16 consecutive rows, one unit each) touches 16 different bank
 // groups.  Rows past M fetch row M - 1 (their results are not stored).
+// What the small-M GEMM does with a finished output tile when K is not split (the work
+// k_gemm_reduce and k_silu_mul_rows do otherwise): mode 0 stores, mode 1 adds to `out`
+// (the residual), mode 2 forms SiLU(gate) * up of the interleaved gate/up columns
+// and stores it in GEMV units (bf16 bits / e4m3 codes of x / act_scale) into `act`
+// [M][N / 2], recording |x| maxima in *amax when amax is set.
+struct GemmEpi {
+  float* out;
+  const float* w_scale;  // e4m3 per-row weight scales, or null
+  float in_scale;
+  int mode;
+  void* act;
+  float act_scale;
+  float* amax;
+};
+
+// the sum of a column's splits, as k_gemm_reduce scales it
+__device__ __forceinline__ float epi_scale(const GemmEpi& e, float s, int col) {
+  if (e.w_scale) s *= e.in_scale * e.w_scale[col];
+  return s;
+}
+template <int P>
+__device__ __forceinline__ float epi_store(const GemmEpi& e, int N, int row, int col, float s) {
+  const size_t idx = (size_t)row * N + col;
+  if (e.mode == 1) e.out[idx] += s;
+  else e.out[idx] = s;
+  return 0.0f;
+}
+template <int P>
+__device__ __forceinline__ float epi_silu(const GemmEpi& e, int N, int row, int pair, float g, float u) {
+  const float v = silu(g) * u;
+  const size_t idx = (size_t)row * (N / 2) + pair;
+  if (P == kBF16) static_cast<uint16_t*>(e.act)[idx] = (uint16_t)act_encode<P>(v, e.act_scale);
+  else static_cast<uint8_t*>(e.act)[idx] = (uint8_t)act_encode<P>(v, e.act_scale);
+  return fabsf(v);
+}
+
 template <int P, int R>
 struct Skinny {
   static constexpr int EB = P == kBF16 ? 2 : 1;
@@ -297,7 +333,8 @@ size_t skinny_lds_bytes() { return (size_t)Skinny<P, R>::NS * Skinny<P, R>::STAG
 
 template <int P, int R>
 __global__ __launch_bounds__(256) void k_gemm(const void* __restrict__ A, const void* __restrict__ B,
-                                              float* __restrict__ Cpart, int M, int N, int K, int ksplit) {
+                                              float* __restrict__ Cpart, int M, int N, int K, int ksplit,
+                                              GemmEpi epi) {
   using S = Skinny<P, R>;
   extern __shared__ __align__(16) unsigned char gsm[];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -402,14 +439,45 @@ __global__ __launch_bounds__(256) void k_gemm(const void* __restrict__ A, const 
   }
   // output layout: lane holds rows 4 * g + i of each 16x16 tile, column lane & 15
   const int col = n0 + 16 * w + r16;
-  float* Cp = Cpart + (size_t)ks * M * N;
+  // the ring is idle once every stage is consumed: its first bytes hold the amax slots
+  // (behind block_max's barriers), so the block stays within 80 KB
+  float* red = reinterpret_cast<float*>(gsm);
+  float mx = 0.0f;
+  if (ksplit == 1) {
+    // the whole K range is here: the epilogue works from the registers (0 + acc, as the
+    // split sum starts from zero)
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + 16 * r + 4 * g + i;
-      if (row < M) Cp[(size_t)row * N + col] = acc[r][i];
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + 16 * r + 4 * g + i;
+        float sum = 0.0f;
+        sum += acc[r][i];
+        const float v = epi_scale(epi, sum, col);
+        if (epi.mode == 2) {
+          const float up = __shfl_xor(v, 1, kWave);  // the neighbouring lane holds the pair's up column
+          if (row < M && (r16 & 1) == 0) mx = fmaxf(mx, epi_silu<P>(epi, N, row, col / 2, v, up));
+        } else if (row < M) {
+          epi_store<P>(epi, N, row, col, v);
+        }
+      }
+  } else {
+    // a split's partial, for k_gemm_reduce (a last-arriving block adding the splits here
+    // would put three memory round trips on the kernel's tail, more than the reduce's launch)
+    float* Cp = Cpart + (size_t)ks * M * N;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + 16 * r + 4 * g + i;
+        if (row < M) Cp[(size_t)row * N + col] = acc[r][i];
+      }
+    return;
+  }
+  if (epi.mode == 2 && epi.amax) {
+    mx = block_max(mx, red);
+    if (threadIdx.x == 0) record_amax(epi.amax, mx);
+  }
 }
 
 // ============================================================================ LDS-tiled MFMA GEMM
@@ -569,25 +637,34 @@ static int gemm_ksplit(int N, int K) {
 
 template <int P>
 static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scale, float in_scale, float* out, int M,
-                       int N, int K, int resid) {
+                       int N, int K, int resid, void* act = nullptr, float act_scale = 1.0f, float* amax = nullptr) {
   if (N % 64 != 0 || K % 128 != 0) return hipErrorInvalidValue;  // the kernels' tiling
   const int ks = gemm_ksplit(N, K);
   float* part = c.pgu + (size_t)c.cfg.max_prefill * 2 * c.cfg.ffn;  // split partials after the gate/up buffer
-  if (M >= kGemmTileMinM && N % kGT == 0 && K % 128 == 0) {
+  const GemmEpi epi{out, P == kFP8 ? w_scale : nullptr, in_scale, act ? 2 : (resid ? 1 : 0), act, act_scale, amax};
+  hipError_t e;
+  if (M < kGemmTileMinM) {
+    const int R = M <= 16 ? 1 : 2;
+    dim3 grid((M + 16 * R - 1) / (16 * R), N / 64, ks);
+    if (R == 1)
+      hipLaunchKernelGGL((k_gemm<P, 1>), grid, dim3(256), (skinny_lds_bytes<P, 1>()), c.stream, A, B, part, M, N,
+                         K, ks, epi);
+    else
+      hipLaunchKernelGGL((k_gemm<P, 2>), grid, dim3(256), (skinny_lds_bytes<P, 2>()), c.stream, A, B, part, M, N,
+                         K, ks, epi);
+    if ((e = hipGetLastError()) != hipSuccess || ks == 1) return e;  // one split: the epilogue ran in the GEMM
+  } else {
     dim3 grid((M + kGT - 1) / kGT, N / kGT, ks);
     hipLaunchKernelGGL(k_gemm_tile<P>, grid, dim3(256), gemm_tile_lds_bytes(), c.stream, A, B, part, M, N, K, ks);
-  } else if (M <= 16) {
-    dim3 grid(1, N / 64, ks);
-    hipLaunchKernelGGL((k_gemm<P, 1>), grid, dim3(256), (skinny_lds_bytes<P, 1>()), c.stream, A, B, part, M, N, K, ks);
-  } else {
-    dim3 grid((M + 31) / 32, N / 64, ks);
-    hipLaunchKernelGGL((k_gemm<P, 2>), grid, dim3(256), (skinny_lds_bytes<P, 2>()), c.stream, A, B, part, M, N, K, ks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const size_t MN = (size_t)M * N;
   hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, c.stream, part, out,
                      P == kFP8 ? w_scale : nullptr, in_scale, M, N, ks, resid);
+  if ((e = hipGetLastError()) != hipSuccess || !act) return e;
+  const int F = N / 2;
+  hipLaunchKernelGGL((k_silu_mul_rows<P>), dim3((F + 255) / 256, M), dim3(256), 0, c.stream, out, act, F, act_scale,
+                     amax);
   return hipGetLastError();
 }
 
@@ -635,12 +712,10 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
     hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, L.g_mlp, f.rms_eps, c.pu, d,
                        host_act_scale(c, s0 + 2), amax ? amax + s0 + 2 : nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = gemm<P>(c, c.pu, L.w_gu, L.s_gu, host_act_scale(c, s0 + 2), c.pgu, Pn, 2 * F, d, 0)) != hipSuccess)
+    if ((e = gemm<P>(c, c.pu, L.w_gu, L.s_gu, host_act_scale(c, s0 + 2), c.pgu, Pn, 2 * F, d, 0, c.pa,
+                     host_act_scale(c, s0 + 3), amax ? amax + s0 + 3 : nullptr)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL((k_silu_mul_rows<P>), dim3((F + 255) / 256, Pn), dim3(256), 0, c.stream, c.pgu, c.pu, F,
-                       host_act_scale(c, s0 + 3), amax ? amax + s0 + 3 : nullptr);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = gemm<P>(c, c.pu, L.w_d, L.s_d, host_act_scale(c, s0 + 3), c.px, Pn, d, F, 1)) != hipSuccess) return e;
+    if ((e = gemm<P>(c, c.pa, L.w_d, L.s_d, host_act_scale(c, s0 + 3), c.px, Pn, d, F, 1)) != hipSuccess) return e;
     if (tap && (e = hipMemcpyAsync(c.taps_p + (size_t)f.max_prefill * d, c.px, tap_bytes, hipMemcpyDeviceToDevice,
                                    c.stream)) != hipSuccess)
       return e;
