@@ -43,6 +43,11 @@ __global__ __launch_bounds__(256) void k_embed_rows(const int32_t* __restrict__ 
   for (int k = threadIdx.x; k < d; k += blockDim.x) X[(size_t)i * d + k] = bf16_to_f32(e_text[t * d + k]);
 }
 
+// The row kernels issue all of a thread's loads before using any (clamped addresses,
+// no load under a condition): a loop that loads and uses one element per step waits
+// a memory round trip per element.
+constexpr int kRowPer = 16;  // row elements per thread (rows up to 16 * 256)
+
 template <int P>
 __global__ __launch_bounds__(256) void k_rmsnorm_act_rows(const float* __restrict__ X, const float* __restrict__ g,
                                                           float eps, void* __restrict__ U, int d, float scale,
@@ -50,16 +55,28 @@ __global__ __launch_bounds__(256) void k_rmsnorm_act_rows(const float* __restric
   __shared__ float red[16];
   const int i = blockIdx.x;
   const float* x = X + (size_t)i * d;
-  float ss = 0.0f;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) ss = fmaf(x[k], x[k], ss);
+  float xv[kRowPer], gv[kRowPer];
+#pragma unroll
+  for (int u = 0; u < kRowPer; ++u) {
+    const int k = u * 256 + threadIdx.x, kc = min(k, d - 1);
+    xv[u] = x[kc];
+    gv[u] = g[kc];
+  }
+  float ss = 0.0f;  // over k = tid, tid + 256, ... in increasing order
+#pragma unroll
+  for (int u = 0; u < kRowPer; ++u)
+    if (u * 256 + threadIdx.x < d) ss = fmaf(xv[u], xv[u], ss);
   ss = block_sum(ss, red);
   const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
   float mx = 0.0f;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    const float u = x[k] * rstd * g[k];
-    mx = fmaxf(mx, fabsf(u));
-    if (P == kBF16) static_cast<uint16_t*>(U)[(size_t)i * d + k] = (uint16_t)act_encode<P>(u, scale);
-    else static_cast<uint8_t*>(U)[(size_t)i * d + k] = (uint8_t)act_encode<P>(u, scale);
+#pragma unroll
+  for (int u = 0; u < kRowPer; ++u) {
+    const int k = u * 256 + threadIdx.x;
+    if (k >= d) continue;
+    const float v = xv[u] * rstd * gv[u];
+    mx = fmaxf(mx, fabsf(v));
+    if (P == kBF16) static_cast<uint16_t*>(U)[(size_t)i * d + k] = (uint16_t)act_encode<P>(v, scale);
+    else static_cast<uint8_t*>(U)[(size_t)i * d + k] = (uint8_t)act_encode<P>(v, scale);
   }
   if (amax) {
     mx = block_max(mx, red);
@@ -88,19 +105,18 @@ __global__ __launch_bounds__(256) void k_silu_mul_rows(const float* __restrict__
 }
 
 // q/k RMSNorm + RoPE for one row of heads; rotated values rounded to bf16.
+// (x0, x1: the lane's two elements of the head, lane < HD / 2; g0, g1 their gains;
+// c, s the rotation of the lane's pair)
 template <int HD>
-__device__ __forceinline__ void norm_rope_row(const float* __restrict__ src, const float* __restrict__ g,
-                                              const float* __restrict__ cs, const float* __restrict__ sn, float eps,
-                                              int lane, float* a_out, float* b_out) {
+__device__ __forceinline__ void norm_rope_vals(float x0, float x1, float g0, float g1, float c_, float s_, float eps,
+                                               int lane, float* a_out, float* b_out) {
   constexpr int H2 = HD / 2;
   const bool act = lane < H2;
-  const float x0 = act ? src[lane] : 0.0f;
-  const float x1 = act ? src[lane + H2] : 0.0f;
   const float ss = wave_sum(x0 * x0 + x1 * x1);
   const float rstd = 1.0f / sqrtf(ss / (float)HD + eps);
-  const float a = x0 * rstd * (act ? g[lane] : 0.0f);
-  const float b = x1 * rstd * (act ? g[lane + H2] : 0.0f);
-  const float c = act ? cs[lane] : 0.0f, s = act ? sn[lane] : 0.0f;
+  const float a = x0 * rstd * (act ? g0 : 0.0f);
+  const float b = x1 * rstd * (act ? g1 : 0.0f);
+  const float c = act ? c_ : 0.0f, s = act ? s_ : 0.0f;
   *a_out = round_bf16(a * c - b * s);
   *b_out = round_bf16(b * c + a * s);
 }
@@ -118,26 +134,49 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
   const float* row = QKV + (size_t)i * W;
   const float* cs = rope_cos + (size_t)pos * H2;
   const float* sn = rope_sin + (size_t)pos * H2;
-  for (int h = w; h < Hq + Hkv; h += nw) {
+  // this wave's heads' values, all loaded before the first is used
+  constexpr int kHeadsPerWave = 16;  // Hq + Hkv <= 16 * waves
+  const bool act = lane < H2;
+  const int la = act ? lane : 0;
+  float x0[kHeadsPerWave], x1[kHeadsPerWave];
+#pragma unroll
+  for (int t = 0; t < kHeadsPerWave; ++t) {
+    const int h = min(w + t * nw, Hq + Hkv - 1);
+    x0[t] = row[(size_t)h * HD + la];
+    x1[t] = row[(size_t)h * HD + la + H2];
+  }
+  const float gq0 = g_q[la], gq1 = g_q[la + H2], gk0 = g_k[la], gk1 = g_k[la + H2];
+  const float c_ = cs[la], s_ = sn[la];
+#pragma unroll
+  for (int t = 0; t < kHeadsPerWave; ++t) {
+    const int h = w + t * nw;
+    if (h >= Hq + Hkv) break;
     float a, b;
     if (h < Hq) {
-      norm_rope_row<HD>(row + (size_t)h * HD, g_q, cs, sn, eps, lane, &a, &b);
+      norm_rope_vals<HD>(act ? x0[t] : 0.0f, act ? x1[t] : 0.0f, gq0, gq1, c_, s_, eps, lane, &a, &b);
       if (lane < H2) {
         Q[(size_t)i * Hq * HD + (size_t)h * HD + lane] = a;
         Q[(size_t)i * Hq * HD + (size_t)h * HD + lane + H2] = b;
       }
     } else {
       const int j = h - Hq;
-      norm_rope_row<HD>(row + (size_t)h * HD, g_k, cs, sn, eps, lane, &a, &b);
+      norm_rope_vals<HD>(act ? x0[t] : 0.0f, act ? x1[t] : 0.0f, gk0, gk1, c_, s_, eps, lane, &a, &b);
       if (lane < H2) {
         kc[((size_t)j * max_seq + pos) * HD + lane] = (uint16_t)f32_to_bf16(a);
         kc[((size_t)j * max_seq + pos) * HD + lane + H2] = (uint16_t)f32_to_bf16(b);
       }
     }
   }
-  for (int e = threadIdx.x; e < Hkv * HD; e += blockDim.x) {
+  constexpr int kVPer = 8;  // Hkv * HD <= 8 * 256
+  float vv[kVPer];
+#pragma unroll
+  for (int u = 0; u < kVPer; ++u) vv[u] = row[(size_t)(Hq + Hkv) * HD + min(u * 256 + (int)threadIdx.x, Hkv * HD - 1)];
+#pragma unroll
+  for (int u = 0; u < kVPer; ++u) {
+    const int e = u * 256 + threadIdx.x;
+    if (e >= Hkv * HD) break;
     const int j = e / HD, dd = e % HD;
-    vc[((size_t)j * max_seq + pos) * HD + dd] = (uint16_t)f32_to_bf16(row[(size_t)(Hq + Hkv) * HD + e]);
+    vc[((size_t)j * max_seq + pos) * HD + dd] = (uint16_t)f32_to_bf16(vv[u]);
   }
 }
 
@@ -617,8 +656,13 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(const float* __restrict__ C
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t MN = (size_t)M * N;
   if (idx >= MN) return;
+  float pv[8];  // ksplit <= 8
+#pragma unroll
+  for (int k = 0; k < 8; ++k) pv[k] = Cpart[(size_t)min(k, ksplit - 1) * MN + idx];
   float s = 0.0f;
-  for (int k = 0; k < ksplit; ++k) s += Cpart[(size_t)k * MN + idx];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (k < ksplit) s += pv[k];
   if (w_scale) s *= in_scale * w_scale[idx % N];
   if (resid) out[idx] += s;
   else out[idx] = s;
@@ -675,6 +719,8 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
   const int qd = Hq * hd, kvd = Hkv * hd, F = f.ffn, W = qd + 2 * kvd;
   const int len0 = c.len;
   float* amax = record ? c.amax : nullptr;
+  // the row kernels' per-thread register batches (k_rmsnorm_act_rows, k_qk_rope_rows)
+  if (d > kRowPer * 256 || Hq + Hkv > 16 * 4 || kvd > 8 * 256) return hipErrorInvalidValue;
   hipError_t e;
   hipLaunchKernelGGL(k_embed_rows, dim3(Pn), dim3(256), 0, c.stream, c.tok, c.e_text, c.px, d);
   if ((e = hipGetLastError()) != hipSuccess) return e;
