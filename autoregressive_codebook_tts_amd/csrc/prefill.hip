@@ -202,9 +202,21 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
   const int qi = i0 + r;
   const bool qvalid = qi < n_rows;
   const int qpos = len0 + qi;
-  for (int e = tid; e < QT * HD; e += blockDim.x) {
-    const int rr = e / HD, dd = e % HD;
-    qs[rr][dd] = (i0 + rr < n_rows) ? Q[((size_t)(i0 + rr) * Hq + h) * HD + dd] : 0.0f;
+  // every load of a thread is issued before the first use (a loop that loads and uses
+  // one element per step waits a memory round trip per step); the next key tile is
+  // fetched into registers while the current one is used
+  constexpr int NQ = QT * HD / 256;
+  static_assert(NQ * 256 == QT * HD, "query tile");
+  float qv[NQ];
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const int e = u * 256 + tid, rr = e / HD, dd = e % HD;
+    qv[u] = Q[((size_t)min(i0 + rr, n_rows - 1) * Hq + h) * HD + dd];
+  }
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const int e = u * 256 + tid, rr = e / HD, dd = e % HD;
+    qs[rr][dd] = (i0 + rr < n_rows) ? qv[u] : 0.0f;
   }
   const int last_pos = len0 + min(i0 + QT, n_rows) - 1;
   const int n_tiles = last_pos / T + 1;
@@ -215,27 +227,37 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
   float o[DPT];
 #pragma unroll
   for (int e = 0; e < DPT; ++e) o[e] = 0.0f;
+  constexpr int SEG = HD / 8;
+  constexpr int NKV = T * SEG / 256;
+  static_assert(NKV * 256 == T * SEG, "key tile");
+  uint4 kr[NKV], vr[NKV];
+  auto load_kv = [&](int t0) {
+#pragma unroll
+    for (int u = 0; u < NKV; ++u) {
+      const int idx = u * 256 + tid, key = idx / SEG, seg = idx % SEG;
+      const int kp = min(t0 + key, last_pos);
+      kr[u] = *reinterpret_cast<const uint4*>(kb + (size_t)kp * HD + seg * 8);
+      vr[u] = *reinterpret_cast<const uint4*>(vb + (size_t)kp * HD + seg * 8);
+    }
+  };
+  load_kv(0);
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int t0 = tile * T;
     __syncthreads();
-    constexpr int SEG = HD / 8;
-    for (int idx = tid; idx < T * SEG; idx += blockDim.x) {
-      const int key = idx / SEG, seg = idx % SEG;
-      const int kp = t0 + key;
-      if (kp <= last_pos) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(kb + (size_t)kp * HD + seg * 8);
-        const uint4 vw = *reinterpret_cast<const uint4*>(vb + (size_t)kp * HD + seg * 8);
-        const uint32_t ks[4] = {kw.x, kw.y, kw.z, kw.w}, vs[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          Kt[key][seg * 8 + 2 * q] = bf16lo(ks[q]); Kt[key][seg * 8 + 2 * q + 1] = bf16hi(ks[q]);
-          Vt[key][seg * 8 + 2 * q] = bf16lo(vs[q]); Vt[key][seg * 8 + 2 * q + 1] = bf16hi(vs[q]);
-        }
-      } else {
+    for (int u = 0; u < NKV; ++u) {
+      const int idx = u * 256 + tid, key = idx / SEG, seg = idx % SEG;
+      const bool valid = t0 + key <= last_pos;  // keys past the block's last query are zero
+      const uint32_t ks[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w}, vs[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
 #pragma unroll
-        for (int q = 0; q < 8; ++q) { Kt[key][seg * 8 + q] = 0.0f; Vt[key][seg * 8 + q] = 0.0f; }
+      for (int q = 0; q < 4; ++q) {
+        Kt[key][seg * 8 + 2 * q] = valid ? bf16lo(ks[q]) : 0.0f;
+        Kt[key][seg * 8 + 2 * q + 1] = valid ? bf16hi(ks[q]) : 0.0f;
+        Vt[key][seg * 8 + 2 * q] = valid ? bf16lo(vs[q]) : 0.0f;
+        Vt[key][seg * 8 + 2 * q + 1] = valid ? bf16hi(vs[q]) : 0.0f;
       }
     }
+    if (tile + 1 < n_tiles) load_kv(t0 + T);
     __syncthreads();
     // scores: thread (r, sub) takes keys sub, sub+16, sub+32, sub+48
     float s[4];
