@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
 // stage, 16-byte unit u of row r sits at position r * NU + (u ^ swz(r)), so a
 // fragment read (16 consecutive rows, one unit each) touches 16 different bank
 // groups.  Rows past M fetch row M - 1 (their results are not stored).
-// What the small-M GEMM does with a finished output tile when K is not split (the work
+// What a GEMM does with a finished output tile when K is not split (the work
 // k_gemm_reduce and k_silu_mul_rows do otherwise): mode 0 stores, mode 1 adds to `out`
 // (the residual), mode 2 forms SiLU(gate) * up of the interleaved gate/up columns
 // and stores it in GEMV units (bf16 bits / e4m3 codes of x / act_scale) into `act`
@@ -565,7 +565,8 @@ __device__ __forceinline__ int tile_unit_pos(int row, int u) { return row * 4 + 
 
 template <int P>
 __global__ __launch_bounds__(256) void k_gemm_tile(const void* __restrict__ A, const void* __restrict__ B,
-                                                   float* __restrict__ Cpart, int M, int N, int K, int ksplit) {
+                                                   float* __restrict__ Cpart, int M, int N, int K, int ksplit,
+                                                   GemmEpi epi) {
   extern __shared__ __align__(16) unsigned char gsm[];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m0 = blockIdx.x * kGT, n0 = blockIdx.y * kGT, ks = blockIdx.z;
@@ -657,6 +658,34 @@ __global__ __launch_bounds__(256) void k_gemm_tile(const void* __restrict__ A, c
     }
   }
   // output layout: lane holds rows 4 * g + r of each 16x16 tile, column lane & 15
+  if (ksplit == 1) {
+    // the whole K range is here: the epilogue works from the registers, as in k_gemm
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + 64 * wn + 16 * j + r16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + 64 * wm + 16 * i + 4 * g + r;
+          float sum = 0.0f;
+          sum += acc[i][j][r];
+          const float v = epi_scale(epi, sum, col);
+          if (epi.mode == 2) {
+            const float up = __shfl_xor(v, 1, kWave);  // the neighbouring lane holds the pair's up column
+            if (row < M && (r16 & 1) == 0) mx = fmaxf(mx, epi_silu<P>(epi, N, row, col / 2, v, up));
+          } else if (row < M) {
+            epi_store<P>(epi, N, row, col, v);
+          }
+        }
+      }
+    if (epi.mode == 2 && epi.amax) {
+      mx = block_max(mx, reinterpret_cast<float*>(gsm));  // the ring is idle: its first bytes
+      if (threadIdx.x == 0) record_amax(epi.amax, mx);
+    }
+    return;
+  }
   float* Cp = Cpart + (size_t)ks * M * N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -718,12 +747,12 @@ static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scal
     else
       hipLaunchKernelGGL((k_gemm<P, 2>), grid, dim3(256), (skinny_lds_bytes<P, 2>()), c.stream, A, B, part, M, N,
                          K, ks, epi);
-    if ((e = hipGetLastError()) != hipSuccess || ks == 1) return e;  // one split: the epilogue ran in the GEMM
   } else {
     dim3 grid((M + kGT - 1) / kGT, N / kGT, ks);
-    hipLaunchKernelGGL(k_gemm_tile<P>, grid, dim3(256), gemm_tile_lds_bytes(), c.stream, A, B, part, M, N, K, ks);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gemm_tile<P>, grid, dim3(256), gemm_tile_lds_bytes(), c.stream, A, B, part, M, N, K, ks,
+                       epi);
   }
+  if ((e = hipGetLastError()) != hipSuccess || ks == 1) return e;  // one split: the epilogue ran in the GEMM
   const size_t MN = (size_t)M * N;
   hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, c.stream, part, out,
                      P == kFP8 ? w_scale : nullptr, in_scale, M, N, ks, resid);
