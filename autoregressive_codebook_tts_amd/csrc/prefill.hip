@@ -181,60 +181,82 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
 }
 
 // ============================================================================ causal attention
-// One block: 16 queries of one q head; keys in 64-wide tiles at absolute
-// positions 0, 64, 128, ... up to the last query's position.
-template <int P, int HD>
-__global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ Q, const uint16_t* __restrict__ kc,
+// One block: 16 query rows of one kv head's group of G <= 4 query heads, one wave per
+// head; keys in 64-wide tiles at absolute positions 0, 64, 128, ... up to the last
+// query's position, shared by the group's waves through LDS.  Per tile and wave:
+// S = Q K^T on the bf16 MFMA (q values are bf16-rounded and k is bf16, so the products
+// are exact; fp32 accumulation), the online softmax per row in fp32, and O += P V on
+// the MFMA with P split into three bf16 parts (P = hi + mid + lo up to 2^-24 of P,
+// the precision of the fp32 value; all three are multiplied).  Every row is computed on its own (MFMA rows
+// do not mix), so a row's result does not depend on which rows share its block.
+// Lane layout of a 16x16x32 MFMA: the A operand row is lane & 15 with k = 8 (lane >> 4)
+// .. + 8; the B operand column is lane & 15 with the same k; the result holds rows
+// 4 (lane >> 4) + i, column lane & 15.
+constexpr int kAttnQT = 16;
+template <int HD>
+struct __align__(16) PrefillAttnLds {
+  uint16_t K[kAttnTile][HD + 8];   // [key][dim] (rows padded against bank conflicts)
+  uint16_t V[HD][kAttnTile + 8];   // [dim][key], transposed for the P V operand
+  float Pm[4][kAttnQT][kAttnTile + 4];  // per wave: the tile's probabilities, [row][key]
+};
+
+__device__ __forceinline__ uint32_t pack_bf16_trunc(float a, float b) {  // exact for bf16 values
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
+template <int P, int HD, int G>
+__global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict__ Q, const uint16_t* __restrict__ kc,
                                                       const uint16_t* __restrict__ vc, void* __restrict__ O, int len0,
                                                       int n_rows, int Hq, int Hkv, int max_seq, float scale,
                                                       float* amax) {
-  constexpr int T = kAttnTile;
-  constexpr int QT = 16;
-  constexpr int DPT = HD / 16;  // output dims per thread
-  __shared__ float qs[QT][HD];
-  __shared__ float Kt[T][HD + 1];
-  __shared__ float Vt[T][HD];
-  __shared__ float ps[QT][T + 1];
+  constexpr int T = kAttnTile, QT = kAttnQT;
+  constexpr int KC = HD / 32;   // 32-wide k chunks of a q row
+  constexpr int NT = HD / 16;   // 16-wide output column tiles
+  static_assert(T == 64, "four 16-key blocks per tile");
+  __shared__ PrefillAttnLds<HD> sm;
   __shared__ float red[16];
-  const int h = blockIdx.x, i0 = blockIdx.y * QT;
-  const int G = Hq / Hkv, j = h / G;
-  const int tid = threadIdx.x, r = tid / 16, sub = tid % 16;
-  const int qi = i0 + r;
-  const bool qvalid = qi < n_rows;
-  const int qpos = len0 + qi;
-  // every load of a thread is issued before the first use (a loop that loads and uses
-  // one element per step waits a memory round trip per step); the next key tile is
-  // fetched into registers while the current one is used
-  constexpr int NQ = QT * HD / 256;
-  static_assert(NQ * 256 == QT * HD, "query tile");
-  float qv[NQ];
-#pragma unroll
-  for (int u = 0; u < NQ; ++u) {
-    const int e = u * 256 + tid, rr = e / HD, dd = e % HD;
-    qv[u] = Q[((size_t)min(i0 + rr, n_rows - 1) * Hq + h) * HD + dd];
-  }
-#pragma unroll
-  for (int u = 0; u < NQ; ++u) {
-    const int e = u * 256 + tid, rr = e / HD, dd = e % HD;
-    qs[rr][dd] = (i0 + rr < n_rows) ? qv[u] : 0.0f;
-  }
+  constexpr int nthr = 64 * G;  // one wave per query head of the kv group
+  const int j = blockIdx.x, i0 = blockIdx.y * QT;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = j * G + w;
+  const int r16 = lane & 15, g4 = lane >> 4;
   const int last_pos = len0 + min(i0 + QT, n_rows) - 1;
   const int n_tiles = last_pos / T + 1;
   const uint16_t* kb = kc + (size_t)j * max_seq * HD;
   const uint16_t* vb = vc + (size_t)j * max_seq * HD;
   const float inv_sqrt = 1.0f / sqrtf((float)HD);
-  float m = -INFINITY, l = 0.0f;
-  float o[DPT];
+
+  // this lane's A fragments of the 16 query rows (row r16; clamped rows are unused)
+  bf16x8 qa[KC];
+  {
+    const float* qrow = Q + ((size_t)min(i0 + r16, n_rows - 1) * Hq + h) * HD;
 #pragma unroll
-  for (int e = 0; e < DPT; ++e) o[e] = 0.0f;
+    for (int c = 0; c < KC; ++c) {
+      const float4 a = *reinterpret_cast<const float4*>(qrow + c * 32 + 8 * g4);
+      const float4 b = *reinterpret_cast<const float4*>(qrow + c * 32 + 8 * g4 + 4);
+      const uint4 u = make_uint4(pack_bf16_trunc(a.x, a.y), pack_bf16_trunc(a.z, a.w), pack_bf16_trunc(b.x, b.y),
+                                 pack_bf16_trunc(b.z, b.w));
+      qa[c] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+  f32x4 oacc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
+
+  // key/value tile loads: 16-byte segments, every load of a thread issued before its use;
+  // the next tile is fetched while the current one is used
   constexpr int SEG = HD / 8;
-  constexpr int NKV = T * SEG / 256;
-  static_assert(NKV * 256 == T * SEG, "key tile");
+  constexpr int NKV = T * SEG / nthr;
+  static_assert(NKV * nthr == T * SEG, "key tile segments per thread");
   uint4 kr[NKV], vr[NKV];
   auto load_kv = [&](int t0) {
 #pragma unroll
     for (int u = 0; u < NKV; ++u) {
-      const int idx = u * 256 + tid, key = idx / SEG, seg = idx % SEG;
+      const int idx = u * nthr + tid;
+      const int key = idx / SEG, seg = idx % SEG;
       const int kp = min(t0 + key, last_pos);
       kr[u] = *reinterpret_cast<const uint4*>(kb + (size_t)kp * HD + seg * 8);
       vr[u] = *reinterpret_cast<const uint4*>(vb + (size_t)kp * HD + seg * 8);
@@ -243,67 +265,115 @@ __global__ __launch_bounds__(256) void k_attn_prefill(const float* __restrict__ 
   load_kv(0);
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int t0 = tile * T;
-    __syncthreads();
+    __syncthreads();  // the previous tile is consumed
 #pragma unroll
     for (int u = 0; u < NKV; ++u) {
-      const int idx = u * 256 + tid, key = idx / SEG, seg = idx % SEG;
+      const int idx = u * nthr + tid;
+      const int key = idx / SEG, seg = idx % SEG;
       const bool valid = t0 + key <= last_pos;  // keys past the block's last query are zero
-      const uint32_t ks[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w}, vs[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+      const uint4 kw = valid ? kr[u] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 vw = valid ? vr[u] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&sm.K[key][seg * 8]) = kw;
+      const uint32_t vs[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        Kt[key][seg * 8 + 2 * q] = valid ? bf16lo(ks[q]) : 0.0f;
-        Kt[key][seg * 8 + 2 * q + 1] = valid ? bf16hi(ks[q]) : 0.0f;
-        Vt[key][seg * 8 + 2 * q] = valid ? bf16lo(vs[q]) : 0.0f;
-        Vt[key][seg * 8 + 2 * q + 1] = valid ? bf16hi(vs[q]) : 0.0f;
+        sm.V[seg * 8 + 2 * q][key] = (uint16_t)(vs[q] & 0xffffu);
+        sm.V[seg * 8 + 2 * q + 1][key] = (uint16_t)(vs[q] >> 16);
       }
     }
     if (tile + 1 < n_tiles) load_kv(t0 + T);
     __syncthreads();
-    // scores: thread (r, sub) takes keys sub, sub+16, sub+32, sub+48
-    float s[4];
-    float tmax = -INFINITY;
+    // scores of the 16 rows against the tile's 64 keys (four 16-key blocks)
+    f32x4 sc[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int kk = sub + 16 * q;
-      const int kp = t0 + kk;
-      float d = 0.0f;
-#pragma unroll 8
-      for (int e = 0; e < HD; ++e) d = fmaf(qs[r][e], Kt[kk][e], d);
-      s[q] = (qvalid && kp <= qpos) ? d * inv_sqrt : -INFINITY;
-      tmax = fmaxf(tmax, s[q]);
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const uint4 b = *reinterpret_cast<const uint4*>(&sm.K[kb4 * 16 + r16][c * 32 + 8 * g4]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+      }
+      sc[kb4] = acc;
+    }
+    float mnew[4], fs[4], psum[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * g4 + i, qi = i0 + row, qpos = len0 + qi;
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        const int kp = t0 + kb4 * 16 + r16;
+        const float v = (qi < n_rows && kp <= qpos) ? sc[kb4][i] * inv_sqrt : -INFINITY;
+        sc[kb4][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+#pragma unroll
+      for (int o2 = 8; o2 > 0; o2 >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o2, 16));
+      mnew[i] = fmaxf(m[i], tmax);
+      float ps = 0.0f;
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        const float v = sc[kb4][i];
+        const float p = (v == -INFINITY) ? 0.0f : __expf(v - mnew[i]);
+        sm.Pm[w][row][kb4 * 16 + r16] = p;
+        ps += p;
+      }
+#pragma unroll
+      for (int o2 = 8; o2 > 0; o2 >>= 1) ps += __shfl_xor(ps, o2, 16);
+      psum[i] = ps;
+      fs[i] = (m[i] == -INFINITY) ? 0.0f : __expf(m[i] - mnew[i]);
+      l[i] = l[i] * fs[i] + psum[i];
+      m[i] = mnew[i];
     }
 #pragma unroll
-    for (int o2 = 8; o2 > 0; o2 >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o2, 16));
-    const float mnew = fmaxf(m, tmax);
-    float psum = 0.0f;
+    for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float p = (s[q] == -INFINITY) ? 0.0f : __expf(s[q] - mnew);
-      ps[r][sub + 16 * q] = p;
-      psum += p;
-    }
+      for (int i = 0; i < 4; ++i) oacc[n][i] *= fs[i];
+    // the wave reads back its probabilities in the other lane order: its LDS writes first
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // O += P V: the probabilities (this wave's own LDS rows) as A, in two 32-key chunks
 #pragma unroll
-    for (int o2 = 8; o2 > 0; o2 >>= 1) psum += __shfl_xor(psum, o2, 16);
-    const float sc = (m == -INFINITY) ? 0.0f : __expf(m - mnew);
-    l = l * sc + psum;
-    m = mnew;
-    __syncthreads();
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const float4 pa = *reinterpret_cast<const float4*>(&sm.Pm[w][r16][c2 * 32 + 8 * g4]);
+      const float4 pb = *reinterpret_cast<const float4*>(&sm.Pm[w][r16][c2 * 32 + 8 * g4 + 4]);
+      const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+      // each part is the bf16 truncation of what the parts before it leave (the
+      // differences are exact in fp32)
+      uint32_t hi[4], mid[4], lo[4];
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) o[e] *= sc;
-    for (int kk = 0; kk < T; ++kk) {
-      const float p = ps[r][kk];
+      for (int q = 0; q < 4; ++q) {
+        const float a = pv[2 * q], b = pv[2 * q + 1];
+        const float ah = __uint_as_float(__float_as_uint(a) & 0xffff0000u), bh = __uint_as_float(__float_as_uint(b) & 0xffff0000u);
+        const float ar = a - ah, br = b - bh;
+        const float am = __uint_as_float(__float_as_uint(ar) & 0xffff0000u), bm = __uint_as_float(__float_as_uint(br) & 0xffff0000u);
+        hi[q] = pack_bf16_trunc(ah, bh);
+        mid[q] = pack_bf16_trunc(am, bm);
+        lo[q] = pack_bf16_trunc(ar - am, br - bm);
+      }
+      const bf16x8 ahi = __builtin_bit_cast(bf16x8, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      const bf16x8 amid = __builtin_bit_cast(bf16x8, make_uint4(mid[0], mid[1], mid[2], mid[3]));
+      const bf16x8 alo = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
 #pragma unroll
-      for (int e = 0; e < DPT; ++e) o[e] = fmaf(p, Vt[kk][sub * DPT + e], o[e]);
+      for (int n = 0; n < NT; ++n) {
+        const uint4 b = *reinterpret_cast<const uint4*>(&sm.V[n * 16 + r16][c2 * 32 + 8 * g4]);
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+        oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, oacc[n], 0, 0, 0);
+        oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(amid, bv, oacc[n], 0, 0, 0);
+        oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bv, oacc[n], 0, 0, 0);
+      }
     }
   }
   float mx = 0.0f;
-  if (qvalid) {
-    const float inv = 1.0f / l;
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) {
-      const float v = o[e] * inv;
+  for (int i = 0; i < 4; ++i) {
+    const int qi = i0 + 4 * g4 + i;
+    if (qi >= n_rows) continue;
+    const float inv = 1.0f / l[i];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const float v = oacc[n][i] * inv;
       mx = fmaxf(mx, fabsf(v));
-      const size_t idx = ((size_t)qi * Hq + h) * HD + sub * DPT + e;
+      const size_t idx = ((size_t)qi * Hq + h) * HD + n * 16 + r16;
       if (P == kBF16) static_cast<uint16_t*>(O)[idx] = (uint16_t)act_encode<P>(v, scale);
       else static_cast<uint8_t*>(O)[idx] = (uint8_t)act_encode<P>(v, scale);
     }
@@ -772,6 +842,7 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
   float* amax = record ? c.amax : nullptr;
   // the row kernels' per-thread register batches (k_rmsnorm_act_rows, k_qk_rope_rows)
   if (d > kRowPer * 256 || Hq + Hkv > 16 * 4 || kvd > 8 * 256) return hipErrorInvalidValue;
+  if (Hq % Hkv != 0 || (Hq / Hkv != 1 && Hq / Hkv != 2 && Hq / Hkv != 4)) return hipErrorInvalidValue;
   hipError_t e;
   hipLaunchKernelGGL(k_embed_rows, dim3(Pn), dim3(256), 0, c.stream, c.tok, c.e_text, c.px, d);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -794,15 +865,21 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
                          c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
-      dim3 grid(Hq, (Pn + 15) / 16);
+      const int G = Hq / Hkv;
+      dim3 grid(Hkv, (Pn + kAttnQT - 1) / kAttnQT);
       const float so = host_act_scale(c, s0 + 1);
       float* am = amax ? amax + s0 + 1 : nullptr;
-      if (hd == 128)
-        hipLaunchKernelGGL((k_attn_prefill<P, 128>), grid, dim3(256), 0, c.stream, c.pq, L.k_cache, L.v_cache, c.po,
-                           len0, Pn, Hq, Hkv, f.max_seq, so, am);
-      else
-        hipLaunchKernelGGL((k_attn_prefill<P, 64>), grid, dim3(256), 0, c.stream, c.pq, L.k_cache, L.v_cache, c.po,
-                           len0, Pn, Hq, Hkv, f.max_seq, so, am);
+#define HTA_ATTN(HDV, GV)                                                                                        \
+  hipLaunchKernelGGL((k_attn_prefill<P, HDV, GV>), grid, dim3(64 * GV), 0, c.stream, c.pq, L.k_cache, L.v_cache, c.po, \
+                     len0, Pn, Hq, Hkv, f.max_seq, so, am)
+      if (hd == 128 && G == 4) HTA_ATTN(128, 4);
+      else if (hd == 128 && G == 2) HTA_ATTN(128, 2);
+      else if (hd == 128 && G == 1) HTA_ATTN(128, 1);
+      else if (hd == 64 && G == 4) HTA_ATTN(64, 4);
+      else if (hd == 64 && G == 2) HTA_ATTN(64, 2);
+      else if (hd == 64 && G == 1) HTA_ATTN(64, 1);
+      else return hipErrorInvalidValue;
+#undef HTA_ATTN
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if ((e = gemm<P>(c, c.po, L.w_o, L.s_o, host_act_scale(c, s0 + 1), c.px, Pn, d, qd, 1)) != hipSuccess) return e;
