@@ -1,6 +1,6 @@
 // Persistent decode-frame kernel for gfx950: the whole frame (embedding,
 // n_layers x [qkv GEMV, attention, o_proj GEMV, gate/up GEMV, down GEMV],
-// head, argmax + delay bookkeeping) in one cooperative launch, one block per
+// head, argmax + delay bookkeeping) in one launch of one resident block per
 // compute unit.
 //
 // Reference: FlashRT "Higgs Audio v3 TTS-4B" page, section 5 (the per-frame
@@ -1357,7 +1357,11 @@ hipError_t launch_frame_persistent(Ctx& c) {
   if (f.precision == HTA_FP8_E4M3) fn = f.head_dim == 128 ? (void*)k_frame<kFP8, 128> : (void*)k_frame<kFP8, 64>;
   else fn = f.head_dim == 128 ? (void*)k_frame<kBF16, 128> : (void*)k_frame<kBF16, 64>;
   time_begin(c, HTA_K_FRAME);
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(c.frame_blocks), dim3(kFT), args, lds, c.stream);
+  // One block per CU, each CU able to hold one (checked at set-up), and nothing else on
+  // the stream: the blocks are all resident.  An ordinary launch: a cooperative one,
+  // which would guarantee it, adds about 20 us per frame; should a block ever not be
+  // placed, the bounded waits end the frame with HTA_E_TIMEOUT instead of a hang.
+  hipError_t e = hipLaunchKernel(fn, dim3(c.frame_blocks), dim3(kFT), args, lds, c.stream);
   time_end(c);
   return e;
 }

@@ -200,9 +200,10 @@ int hta_time_kernels(hta_ctx* ctx, int n_frames, float* avg_us_out, int n_classe
 /* Options: HTA_OPT_USE_GRAPH (default 1) replays the captured position-agnostic
  * frame graph; 0 launches the same kernels one by one (for tests that compare
  * the two).  HTA_OPT_PERSISTENT (default 1 where the device fits it) decodes
- * each frame with one cooperative persistent kernel (one block per compute
+ * each frame with one persistent kernel (one resident block per compute
  * unit; blocks hand values to each other through phase-tagged words, no grid
- * barrier); 0 uses one kernel per phase.  HTA_OPT_TAPS (default 0) makes decode
+ * barrier; a wait that runs out ends the frame with HTA_E_TIMEOUT); 0 uses one
+ * kernel per phase.  HTA_OPT_TAPS (default 0) makes decode
  * frames and prefills also write the per-layer residuals read by
  * HTA_TAP_LAYER_H / HTA_TAP_PREFILL_LAYER (frames then launch without the
  * graph); HTA_OPT_PREFILL_TAP_LAYER selects the prefill layer (0..n_layers-1,
