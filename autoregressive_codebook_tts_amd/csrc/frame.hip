@@ -39,7 +39,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kFT = 512;            // threads per block
 constexpr int kFW = kFT / kWave;    // waves per block
-constexpr int kRD = 12;             // LDS ring slots (1 KB packets) per wave
+constexpr int kRD = 15;             // LDS ring slots (1 KB packets) per wave
 constexpr int kPartMax = 1024;      // packet partial sums per block per phase
 constexpr uint64_t kSpinLimit = 50000000ull;  // 0.5 s at the 100 MHz constant clock
 
@@ -492,6 +492,9 @@ struct AttnLds {
   float scl[4];                     // per query head: the tile's rescale of the running output
   float ml[4][2];                   // per query head: this split's (max, denominator)
 };
+// bytes of the region the GEMV input vector (5120 words) and the attention scratch share
+constexpr size_t kFrameShared = ((sizeof(AttnLds) > 5120 * 4 + kPartMax * 4 ? sizeof(AttnLds) : 5120 * 4 + kPartMax * 4) + 15) / 16 * 16;
+static_assert(kFW * kRD * 1024 + kFrameShared + 1024 <= 160 * 1024, "frame LDS");
 
 // Half of the dot product of query head qh with key `key` of the tile: the even
 // dimensions (low halves of the key words) or, ODD, the odd ones, as two FMA chains
@@ -894,9 +897,9 @@ __device__ __forceinline__ void issue_two(CFA& a, Issuer<P>& is, int n_phases) {
 // consumed packet is replaced by one fetch) and loads land in issue order, so the
 // oldest n have landed once at most kRD - n younger ones remain outstanding.  Other
 // vector memory operations issued since only make a wait longer.
-__device__ __forceinline__ void wait_oldest1() { asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); }
-__device__ __forceinline__ void wait_oldest2() { asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); }
-static_assert(kRD == 12, "the ring's s_waitcnt immediates are kRD - 1 and kRD - 2");
+__device__ __forceinline__ void wait_oldest1() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kRD - 1) : "memory"); }
+__device__ __forceinline__ void wait_oldest2() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kRD - 2) : "memory"); }
+static_assert(kRD >= 3 && kRD <= 63, "the ring's waits are s_waitcnt vmcnt immediates");
 
 // Position of the byte `off + lane16` of a packet, counted from the start of the row
 // it falls in, where `off` (< rb) is the packet's first byte within the open row.
@@ -1052,9 +1055,12 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   unsigned char* ring_w = smem_raw + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kRD * 1024;  // this wave's ring
   unsigned char* lds1 = smem_raw + kFW * kRD * 1024;
+  // the attention task's scratch shares its bytes with the GEMV input vector: the QKV
+  // stream ends on a barrier before attention starts, and a barrier follows the task
+  // before the o_proj input is written
   uint32_t* xs = reinterpret_cast<uint32_t*>(lds1);                          // activations, bf16 pairs (<= 10240)
+  AttnLds& sm = *reinterpret_cast<AttnLds*>(lds1);
   float* part = reinterpret_cast<float*>(lds1 + 5120 * 4);                   // per-(row, wave) partials
-  AttnLds& sm = *reinterpret_cast<AttnLds*>(lds1 + 5120 * 4 + kPartMax * 4);
   __shared__ float red[2 * kFW];  // block reductions; (sum, flag) slots of block_sum_ok
   __shared__ int sh_state[4 + kMaxCodebooks];
   __shared__ int okf;
@@ -1149,6 +1155,8 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
       const LayerW L = a.layers[layer];
       // inputs: the QKV phase (tag - 1); partials and output carry this phase's tag
       if (!attn_task<P, HD>(a, L, layer, pos, tag - 1u, tag, tag, sm, abort_flag, &okf)) { ring_drain(); return; }
+      __syncthreads();  // the task's scratch is the next phase's input vector and partials
+      if (tid < kPartMax / 4) reinterpret_cast<float4*>(part)[tid] = zero4;
       trace_mark(a, n_phases, phase, 3);
       continue;
     }
@@ -1317,7 +1325,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
 }
 
 // ---------------------------------------------------------------- launcher
-size_t frame_lds_bytes() { return (size_t)kFW * kRD * 1024 + 5120 * 4 + kPartMax * 4 + sizeof(AttnLds); }
+size_t frame_lds_bytes() { return (size_t)kFW * kRD * 1024 + kFrameShared; }
 
 // The kernel reads its arguments from device memory (fields are re-read where
 // they are used instead of pinning dozens of scalar registers for the whole
