@@ -273,6 +273,7 @@ int hta_create(const hta_config* cfg, void* hip_stream, hta_ctx** out) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, c.device) != hipSuccess) { delete x; return HTA_E_HIP; }
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) { delete x; return HTA_E_UNSUPPORTED; }
+  c.num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
   if (hip_stream) {
     c.stream = static_cast<hipStream_t>(hip_stream);
   } else {

@@ -90,6 +90,7 @@ struct Ctx {
   bool use_persistent = true;
   bool frame_ok = false;      // the persistent frame kernel fits this device and shape
   int frame_blocks = 0, frame_splits = 0;
+  int num_cus = 256;          // compute units of the device (prefill block-width choice)
   // derived device pointers
   LayerW* layers = nullptr;  // host array of n_layers
   uint16_t* e_text = nullptr;

@@ -439,17 +439,19 @@ __device__ __forceinline__ float epi_silu(const GemmEpi& e, int N, int row, int 
   return fabsf(v);
 }
 
-template <int P, int R>
+// NW waves per block, each computing 16R x 16 (16 NW columns per block).  The ring's
+// budget keeps two blocks per CU at NW = 4 and three at NW = 2.
+template <int P, int R, int NW>
 struct Skinny {
   static constexpr int EB = P == kBF16 ? 2 : 1;
   static constexpr int SK = 128 * EB;                  // bytes of one row per stage
   static constexpr int NU = SK / 16;                   // 16-byte units per row and stage
   static constexpr int U = NU / 4;                     // units per lane per 16-row fragment
-  static constexpr int BYTES_B = 64 * SK, BYTES_A = 16 * R * SK, STAGE = BYTES_B + BYTES_A;
-  static constexpr int NS = (80 * 1024) / STAGE;       // bf16: 4 (R = 1), 3 (R = 2); e4m3: 8, 6
+  static constexpr int BYTES_B = 16 * NW * SK, BYTES_A = 16 * R * SK, STAGE = BYTES_B + BYTES_A;
+  static constexpr int NS = ((NW == 4 ? 80 : 52) * 1024) / STAGE;  // NW = 4: bf16 4 (R = 1), 3 (R = 2); e4m3 8, 6
   static constexpr int NB = NU / 4;                    // B fetches per wave and stage
   static constexpr int NA_ALL = R * NU / 4;            // A fetches per stage
-  static constexpr int AW = NA_ALL >= 4 ? 4 : NA_ALL;  // waves that fetch A
+  static constexpr int AW = NA_ALL >= NW ? NW : NA_ALL;  // waves that fetch A
   static constexpr int NA = NA_ALL / AW;               // A fetches per fetching wave
   static_assert(NS >= 3 && NA * AW == NA_ALL, "stage shape");
 };
@@ -459,17 +461,17 @@ __device__ __forceinline__ int skinny_swz(int row, int nu) { return (row ^ (row 
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory"); }
 
-template <int P, int R>
-size_t skinny_lds_bytes() { return (size_t)Skinny<P, R>::NS * Skinny<P, R>::STAGE; }
+template <int P, int R, int NW>
+size_t skinny_lds_bytes() { return (size_t)Skinny<P, R, NW>::NS * Skinny<P, R, NW>::STAGE; }
 
-template <int P, int R>
-__global__ __launch_bounds__(256) void k_gemm(const void* __restrict__ A, const void* __restrict__ B,
-                                              float* __restrict__ Cpart, int M, int N, int K, int ksplit,
-                                              GemmEpi epi) {
-  using S = Skinny<P, R>;
+template <int P, int R, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, const void* __restrict__ B,
+                                                  float* __restrict__ Cpart, int M, int N, int K, int ksplit,
+                                                  GemmEpi epi) {
+  using S = Skinny<P, R, NW>;
   extern __shared__ __align__(16) unsigned char gsm[];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int m0 = blockIdx.x * 16 * R, n0 = blockIdx.y * 64, ks = blockIdx.z;
+  const int m0 = blockIdx.x * 16 * R, n0 = blockIdx.y * 16 * NW, ks = blockIdx.z;
   const int rowbytes = K * S::EB;  // operands below 2^31 bytes
   const int nsteps = K / 128;
   const int s_beg = (int)((long)nsteps * ks / ksplit), s_end = (int)((long)nsteps * (ks + 1) / ksplit);
@@ -531,7 +533,7 @@ __global__ __launch_bounds__(256) void k_gemm(const void* __restrict__ A, const 
     // stage c has landed once at most the fetches of the NS - 2 younger stages remain
     // (loads land in issue order)
     if (c + S::NS - 2 < nst) {
-      if (S::AW == 4 || fetch_a) wait_vm<(S::NS - 2) * (S::NB + S::NA)>();
+      if (S::AW == NW || fetch_a) wait_vm<(S::NS - 2) * (S::NB + S::NA)>();
       else wait_vm<(S::NS - 2) * S::NB>();
     } else {
       wait_vm<0>();
@@ -810,13 +812,34 @@ static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scal
   hipError_t e;
   if (M < kGemmTileMinM) {
     const int R = M <= 16 ? 1 : 2;
-    dim3 grid((M + 16 * R - 1) / (16 * R), N / 64, ks);
-    if (R == 1)
-      hipLaunchKernelGGL((k_gemm<P, 1>), grid, dim3(256), (skinny_lds_bytes<P, 1>()), c.stream, A, B, part, M, N,
-                         K, ks, epi);
-    else
-      hipLaunchKernelGGL((k_gemm<P, 2>), grid, dim3(256), (skinny_lds_bytes<P, 2>()), c.stream, A, B, part, M, N,
-                         K, ks, epi);
+    const int mt = (M + 16 * R - 1) / (16 * R);
+    // Block width: the weight stream is dealt to the CUs in whole blocks, so the
+    // kernel lasts about as long as the CU with the most columns.  Two-wave blocks
+    // (32 columns, three resident per CU) are taken when they lower that maximum.
+    // Which block computes a column does not change its arithmetic.
+    const long cus = c.num_cus;
+    auto max_cols = [&](long width) {
+      const long blocks = (long)mt * (N / width) * ks;
+      return (blocks + cus - 1) / cus * width;  // columns x splits on the busiest CU
+    };
+    const bool narrow = max_cols(32) < max_cols(64);
+    if (!narrow) {
+      dim3 grid(mt, N / 64, ks);
+      if (R == 1)
+        hipLaunchKernelGGL((k_gemm<P, 1, 4>), grid, dim3(256), (skinny_lds_bytes<P, 1, 4>()), c.stream, A, B, part,
+                           M, N, K, ks, epi);
+      else
+        hipLaunchKernelGGL((k_gemm<P, 2, 4>), grid, dim3(256), (skinny_lds_bytes<P, 2, 4>()), c.stream, A, B, part,
+                           M, N, K, ks, epi);
+    } else {
+      dim3 grid(mt, N / 32, ks);
+      if (R == 1)
+        hipLaunchKernelGGL((k_gemm<P, 1, 2>), grid, dim3(128), (skinny_lds_bytes<P, 1, 2>()), c.stream, A, B, part,
+                           M, N, K, ks, epi);
+      else
+        hipLaunchKernelGGL((k_gemm<P, 2, 2>), grid, dim3(128), (skinny_lds_bytes<P, 2, 2>()), c.stream, A, B, part,
+                           M, N, K, ks, epi);
+    }
   } else {
     dim3 grid((M + kGT - 1) / kGT, N / kGT, ks);
     hipLaunchKernelGGL(k_gemm_tile<P>, grid, dim3(256), gemm_tile_lds_bytes(), c.stream, A, B, part, M, N, K, ks,
@@ -901,10 +924,14 @@ hipError_t prefill_setup() {
   const struct { const void* f; size_t lds; } kernels[] = {
       {(const void*)k_gemm_tile<kBF16>, gemm_tile_lds_bytes()},
       {(const void*)k_gemm_tile<kFP8>, gemm_tile_lds_bytes()},
-      {(const void*)k_gemm<kBF16, 1>, skinny_lds_bytes<kBF16, 1>()},
-      {(const void*)k_gemm<kBF16, 2>, skinny_lds_bytes<kBF16, 2>()},
-      {(const void*)k_gemm<kFP8, 1>, skinny_lds_bytes<kFP8, 1>()},
-      {(const void*)k_gemm<kFP8, 2>, skinny_lds_bytes<kFP8, 2>()},
+      {(const void*)k_gemm<kBF16, 1, 4>, skinny_lds_bytes<kBF16, 1, 4>()},
+      {(const void*)k_gemm<kBF16, 2, 4>, skinny_lds_bytes<kBF16, 2, 4>()},
+      {(const void*)k_gemm<kFP8, 1, 4>, skinny_lds_bytes<kFP8, 1, 4>()},
+      {(const void*)k_gemm<kFP8, 2, 4>, skinny_lds_bytes<kFP8, 2, 4>()},
+      {(const void*)k_gemm<kBF16, 1, 2>, skinny_lds_bytes<kBF16, 1, 2>()},
+      {(const void*)k_gemm<kBF16, 2, 2>, skinny_lds_bytes<kBF16, 2, 2>()},
+      {(const void*)k_gemm<kFP8, 1, 2>, skinny_lds_bytes<kFP8, 1, 2>()},
+      {(const void*)k_gemm<kFP8, 2, 2>, skinny_lds_bytes<kFP8, 2, 2>()},
   };
   for (const auto& k : kernels) {
     const hipError_t e = hipFuncSetAttribute(k.f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)k.lds);
