@@ -92,6 +92,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--layers", type=int, default=36, help="backbone depth (36 = the benchmark model)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the prefix-reuse and KV-4096 decode measurements")
     ap.add_argument("--no-kernel-classes", action="store_true",
                     help="skip the per-kernel-class event timing that follows the timed region")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -153,7 +155,11 @@ def main() -> int:
 
     # ---------------------------------------------------------------- FP8 context: the timed workload
     log("FP8 context: load")
-    ctx = hta.Hta(shape, "fp8", max_seq=max_seq, max_prefill=min(512, max_seq))
+    # room for the long-context measurement (4095 prompt keys + the timed frames); the KV
+    # length a frame attends, not the cache's capacity, sets the frame's work
+    long_kv = shape.n_layers == 36 and not args.no_long
+    f_seq = max(max_seq, LONG_PROMPT + LONG_FRAMES + 8) if long_kv else max_seq
+    ctx = hta.Hta(shape, "fp8", max_seq=f_seq, max_prefill=min(512, f_seq))
     ctx.load_weights(tensors, src, act_scales=scales)
     del tensors
     if args.copy_probe_mib:
@@ -203,6 +209,10 @@ def main() -> int:
                 "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": _traffic(workload, shape),
                 "bytes_per_launch": int(k_bytes), "avg_launch_us": round(k_us, 3)}
+    if long_kv:
+        log("prefix reuse and long-context decode (FP8)")
+        extra.update(_prefix_reuse(ctx, shape))
+        extra.update(_long_decode(ctx, shape))
     if not args.no_kernel_classes:
         log("per-kernel timing (FP8)")
         ctx.reset(0)
@@ -271,6 +281,67 @@ def _prefill_sizes(ctx, shape, prec: str) -> dict:
         if P == 512:
             out[f"prefill_mfma_frac_{prec}_p512"] = round(prefill_flops(shape, P) / (ms * 1e-3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4)
     return out
+
+
+LONG_PROMPT, LONG_FRAMES = 4095, 64
+
+
+def _prefix_reuse(ctx, shape, reps: int = 5) -> dict:
+    """A 64-token preamble prefilled once and kept (hta_reset(64)), then 8 different
+    16-token suffixes, against cold 80-token prefills of the same ids: device ms per
+    suffix (median over suffixes of the median over reps)."""
+    import torch
+    import synthetic as S
+
+    pre = S.token_ids(S.SEEDS["preamble"], 64, shape.text_vocab)
+    sufs = [S.token_ids(S.SEEDS["suffix_base"] + i, 16, shape.text_vocab) for i in range(8)]
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(ctx.stream)
+        fn()
+        e1.record(ctx.stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1)
+
+    ctx.reset(0)
+    ctx.prefill(pre)
+    reuse, cold = [], []
+    for suf in sufs:
+        r = [timed(lambda: (ctx.reset(64), ctx.prefill(suf))) for _ in range(reps + 1)][1:]
+        reuse.append(statistics.median(r))
+    for suf in sufs:
+        full = np.concatenate([pre, suf]).astype(np.int32)
+        c = [timed(lambda: (ctx.reset(0), ctx.prefill(full))) for _ in range(reps + 1)][1:]
+        cold.append(statistics.median(c))
+    r_ms, c_ms = statistics.median(reuse), statistics.median(cold)
+    return {"prefix_reuse_fp8": {"preamble": 64, "suffix": 16, "suffixes": 8, "reuse_ms": round(r_ms, 4),
+                                 "cold_80_ms": round(c_ms, 4), "saved_frac": round(1.0 - r_ms / c_ms, 4)}}
+
+
+def _long_decode(ctx, shape) -> dict:
+    """FP8 decode with 4096 keys: a 4095-token prompt prefilled in chunks of 512, then
+    LONG_FRAMES frames timed (KV 4096 -> 4096 + LONG_FRAMES - 1)."""
+    import torch
+    import synthetic as S
+
+    ids = S.token_ids(S.SEEDS["long_prompt"], LONG_PROMPT, shape.text_vocab)
+    ctx.reset(0)
+    for i in range(0, LONG_PROMPT, 512):
+        ctx.prefill(ids[i:i + 512])
+    ctx.decode_frames(1)  # warm: the first frame attends 4096 keys
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(ctx.stream)
+    _, done = ctx.decode_frames(LONG_FRAMES)
+    e1.record(ctx.stream)
+    e1.synchronize()
+    # every requested frame runs the whole step; `done` only says an end-of-audio code
+    # appeared among them (random weights)
+    ms = e0.elapsed_time(e1) / LONG_FRAMES
+    kv_mean = LONG_PROMPT + 1 + (LONG_FRAMES + 1) / 2
+    frac = frame_bytes(shape, "fp8", kv_mean) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS
+    return {"decode_ms_per_frame_fp8_kv4096": round(ms, 4), "frame_hbm_frac_fp8_kv4096": round(frac, 4),
+            "kv4096_end_of_audio_seen": bool(done)}
 
 
 def _prefill_ms(ctx, prompt, reps: int = 20) -> float:
