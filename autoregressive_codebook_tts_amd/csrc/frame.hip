@@ -619,7 +619,6 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
   const int qh = hi ? w - G : w;      // its query head within the group
   float m = -INFINITY, lsum = 0.0f, o = 0.0f;  // (m, lsum) live in the lower wave of each head
   for (int t0 = beg; t0 < end; t0 += T) {
-    if (t0 != beg) load_tile(t0);
 #pragma unroll
     for (int u = 0; u < NPT; ++u) {
       const int idx = u * kFT + tid;
@@ -639,6 +638,8 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) { sm.Kt[key][seg * 4 + e] = kw[e]; sm.Vt[key][seg * 4 + e] = vw[e]; }
     }
+    // the next tile's loads (into the registers just stored) overlap this tile's work
+    if (t0 + T < end) load_tile(t0 + T);
     __syncthreads();
     // Every query head is shared by two waves: wave qh takes the even dimensions (the
     // low halves of the key and value words) and wave qh + G the odd ones of the
