@@ -690,6 +690,11 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
     m = mnew;
     __syncthreads();
   }
+  // The last tile issues no prefetch, but the compiler cannot tell: it would take the
+  // tile registers for in flight and wait for all vector memory (the ring's fetches
+  // too) wherever it reuses them.  Nothing is in flight here by now (the ring's last
+  // fetches went out before the QKV epilogue), so a full wait costs nothing.
+  settle_loads();
   // this frame's key and value into the cache, for the frames to come (this one took
   // them from LDS): stored after the tiles, so that no tile waits for the stores
   if (beg <= pos && pos < end && tid < HD) {
