@@ -17,11 +17,20 @@ Parity status of each function (what pins it, in the CPU test suite):
                                   split-K/LSE combine equals the one-pass form
 * model.OracleModel            -- batched prefill equals step-by-step decode
                                   (causal-mask equivalence), GQA equals MHA with
-                                  repeated K/V, mode S equals mode E with a
-                                  precision-free format; whole-model values:
-                                  parity unpinned (no page prints a worked example)
+                                  repeated K/V; mode E equals a torch library
+                                  formulation (F.linear, F.rms_norm, complex RoPE,
+                                  scaled_dot_product_attention) to 1e-10; mode S
+                                  (BF16 and FP8) equals the same formulation with
+                                  torch.bfloat16 / torch.float8_e4m3fn casts at
+                                  the storage points to 1e-10 (rounding placement
+                                  and the scale of each activation site);
+                                  whole-model values beyond these: parity
+                                  unpinned (no page prints a worked example)
 * delay.*                      -- brute-force enumeration over every EOC step
                                   against an independent restatement; undelay
                                   inverts delay
-* model.calibrate              -- the quantised site maximum lands exactly on 448
+* model.calibrate              -- the per-site maxima equal those the torch
+                                  formulation records on the same rows before
+                                  rounding (1e-12; float32 scales bit-equal), and
+                                  the quantised site maximum lands exactly on 448
 """

@@ -27,16 +27,80 @@ def tiny_weights():
 
 
 # ----------------------------------------------------------------------------- independent torch formulation
-def torch_forward(shape, w, ids_frames):
-    """Causal forward over an input sequence given as a list of ("text", id) / ("audio", codes[8])."""
+SITES = 4  # per layer: attention input, attention output, MLP input, down input; then the head input
+
+
+class TorchStorage:
+    """Rounding at the storage points of one precision, written with torch's own casts.
+
+    ``None``: no rounding (the exact model).  ``"bf16"``: weights, embeddings, the five
+    GEMV inputs and q/k/v through ``torch.bfloat16``.  ``"fp8"``: projection and head
+    weights through ``torch.float8_e4m3fn`` with per-row float32 scales amax/448, and
+    the five GEMV inputs as float8_e4m3fn codes of fp32(x) / s (clamped to +-448, the
+    saturating reading of FlashRT section 8), dequantised before the product; embeddings
+    bf16; q/k/v bf16 in both.  ``record`` (a float64 array) receives max |x| of every
+    GEMV input before rounding."""
+
+    def __init__(self, kind=None, scales=None, record=None):
+        self.kind, self.record = kind, record
+        self.scales = None if scales is None else torch.from_numpy(np.asarray(scales, np.float32))
+
+    @staticmethod
+    def bf16(t):
+        """float64 -> bfloat16 with one correct rounding.  torch converts float64 to bfloat16
+        through float32, and that double rounding lands on a bf16 tie for about one value in
+        2^16.  Rounding to odd at the float32 step (truncate, then set the last bit when
+        inexact; Boldo and Melquiond, IEEE Trans. Computers 57(4), 2008) makes the second
+        rounding (torch's RNE float32 -> bfloat16) the correctly rounded result."""
+        f = t.to(torch.float32)
+        f = torch.where(f.to(torch.float64).abs() > t.abs(), torch.nextafter(f, torch.zeros_like(f)), f)
+        inexact = (f.to(torch.float64) != t).to(torch.int32)
+        f = (f.view(torch.int32) | inexact).view(torch.float32)
+        return f.to(torch.bfloat16).to(torch.float64)
+
+    def embedding(self, t):
+        return t if self.kind is None else self.bf16(t)
+
+    def weight(self, t):
+        if self.kind is None:
+            return t
+        if self.kind == "bf16":
+            return self.bf16(t)
+        w32 = t.to(torch.float32)
+        amax = w32.abs().amax(dim=-1)
+        s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        codes = (w32 / s[:, None]).to(torch.float8_e4m3fn)
+        return codes.to(torch.float64) * s.to(torch.float64)[:, None]
+
+    def act(self, t, site):
+        if self.record is not None:
+            self.record[site] = max(self.record[site], float(t.abs().max()))
+        if self.kind is None:
+            return t
+        if self.kind == "bf16":
+            return self.bf16(t)
+        s = self.scales[site]
+        codes = (t.to(torch.float32) / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        return codes.to(torch.float64) * s.to(torch.float64)
+
+    def kv(self, t):
+        return t if self.kind is None else self.bf16(t)
+
+
+def torch_forward(shape, w, ids_frames, store=None):
+    """Causal forward over an input sequence given as a list of ("text", id) / ("audio", codes[8]);
+    ``store`` (a TorchStorage) rounds at the storage points.  Returns the final residual of every
+    row and the head's logits of every row."""
+    store = store or TorchStorage()
     d, hd, Hq, Hkv = shape.hidden, shape.head_dim, shape.n_q_heads, shape.n_kv_heads
     T = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    e_text, e_aud = store.embedding(T(w["e_text"])), store.embedding(T(w["e_aud"]))
     rows = []
     for kind, val in ids_frames:
         if kind == "text":
-            rows.append(T(w["e_text"][val]))
+            rows.append(e_text[val])
         else:
-            rows.append(sum(T(w["e_aud"][k, int(c)]) for k, c in enumerate(val)))
+            rows.append(sum(e_aud[k, int(c)] for k, c in enumerate(val)))
     x = torch.stack(rows)  # [N, d]
     N = x.shape[0]
     pos = torch.arange(N, dtype=torch.float64)
@@ -49,21 +113,30 @@ def torch_forward(shape, w, ids_frames):
 
     for layer in range(shape.n_layers):
         p = f"layers.{layer}."
-        Wt = lambda n: T(w[p + n])
-        u = F.rms_norm(x, (d,), Wt("g_attn"), eps=shape.rms_eps)
+        G = lambda n: T(w[p + n])
+        Wt = lambda n: store.weight(T(w[p + n]))
+        s0 = SITES * layer
+        u = store.act(F.rms_norm(x, (d,), G("g_attn"), eps=shape.rms_eps), s0)
         q = F.linear(u, Wt("wq")).view(N, Hq, hd)
         k = F.linear(u, Wt("wk")).view(N, Hkv, hd)
-        v = F.linear(u, Wt("wv")).view(N, Hkv, hd)
-        q = rope(F.rms_norm(q, (hd,), Wt("g_q"), eps=shape.rms_eps))
-        k = rope(F.rms_norm(k, (hd,), Wt("g_k"), eps=shape.rms_eps))
+        v = store.kv(F.linear(u, Wt("wv")).view(N, Hkv, hd))
+        q = store.kv(rope(F.rms_norm(q, (hd,), G("g_q"), eps=shape.rms_eps)))
+        k = store.kv(rope(F.rms_norm(k, (hd,), G("g_k"), eps=shape.rms_eps)))
         o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None], v.transpose(0, 1)[None],
                                            is_causal=True, enable_gqa=True)[0].transpose(0, 1).reshape(N, Hq * hd)
-        x = x + F.linear(o, Wt("wo"))
-        u2 = F.rms_norm(x, (d,), Wt("g_mlp"), eps=shape.rms_eps)
-        x = x + F.linear(F.silu(F.linear(u2, Wt("wg"))) * F.linear(u2, Wt("wu")), Wt("wd"))
-    z = F.rms_norm(x, (d,), T(w["g_final"]), eps=shape.rms_eps)
-    logits = F.linear(z, T(w["w_head"])).view(N, shape.n_codebooks, shape.codebook_size)
-    return x.numpy(), logits.numpy()
+        x = x + F.linear(store.act(o, s0 + 1), Wt("wo"))
+        u2 = store.act(F.rms_norm(x, (d,), G("g_mlp"), eps=shape.rms_eps), s0 + 2)
+        a = store.act(F.silu(F.linear(u2, Wt("wg"))) * F.linear(u2, Wt("wu")), s0 + 3)
+        x = x + F.linear(a, Wt("wd"))
+    return x.numpy(), x
+
+
+def torch_head(shape, w, x_rows, store=None):
+    """Logits [rows][C][V] of the fused head for final residual rows (torch tensor)."""
+    store = store or TorchStorage()
+    T = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    z = store.act(F.rms_norm(x_rows, (shape.hidden,), T(w["g_final"]), eps=shape.rms_eps), SITES * shape.n_layers)
+    return F.linear(z, store.weight(T(w["w_head"]))).view(-1, shape.n_codebooks, shape.codebook_size).numpy()
 
 
 def test_oracle_matches_torch_formulation(tiny_weights):
@@ -80,11 +153,70 @@ def test_oracle_matches_torch_formulation(tiny_weights):
         logit_list.append(m.last_logits.copy())
         seq.append(("audio", np.full(8, 1024) if f == 0 else forced[f - 1]))
         m.force_codes(forced[f])
-    x_ref, lg_ref = torch_forward(TINY, w, seq)
+    x_ref, xt = torch_forward(TINY, w, seq)
+    lg_ref = torch_head(TINY, w, xt)
     P = len(ids)
     for f in range(6):
         assert np.allclose(hid[f], x_ref[P + f], rtol=1e-10, atol=1e-13)
         assert np.allclose(logit_list[f], lg_ref[P + f], rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp8"])
+def test_mode_s_matches_torch_storage_formulation(tiny_weights, precision):
+    """Mode S rounds exactly at the storage points: the same teacher-forced run through the
+    torch formulation that casts with torch.bfloat16 / torch.float8_e4m3fn at the five GEMV
+    inputs, q/k/v and the weights (FP8: dequantised weights and activations, where the
+    oracle scales the code products) agrees to 1e-10.  A rounding moved to another point, a
+    dropped rounding or an activation scale taken from the wrong site moves the result by
+    far more (at least one bf16 / e4m3 rounding step of some element)."""
+    w = tiny_weights
+    calib_ids = S.token_ids(S.SEEDS["calib_prompt"], 16, TINY.text_vocab)
+    scales = calibrate(TINY, w, calib_ids, 8)[0] if precision == "fp8" else None
+    ids = S.token_ids(S.SEEDS["tiny_prompt"], 8, TINY.text_vocab)
+    m = OracleModel(TINY, w, precision, "S", act_scales=scales, max_seq=64)
+    m.prefill(ids)
+    seq = [("text", int(i)) for i in ids]
+    forced = S.code_frames(78, 6)
+    hid, lgs = [], []
+    for f in range(6):
+        m.decode_frame()
+        hid.append(m.last_hidden.copy())
+        lgs.append(m.last_logits.copy())
+        seq.append(("audio", np.full(8, 1024) if f == 0 else forced[f - 1]))
+        m.force_codes(forced[f])
+    store = TorchStorage(precision, scales)
+    x_ref, xt = torch_forward(TINY, w, seq, store)
+    lg_ref = torch_head(TINY, w, xt[len(ids):], store)
+    P = len(ids)
+    for f in range(6):
+        assert np.max(np.abs(hid[f] - x_ref[P + f])) <= 1e-10 * np.max(np.abs(x_ref[P + f])), f
+        assert np.max(np.abs(lgs[f] - lg_ref[f])) <= 1e-10 * np.max(np.abs(lg_ref[f])), f
+    # the formulation is sharp: without the storage rounding it lands far away
+    x_e, _ = torch_forward(TINY, w, seq)
+    assert np.max(np.abs(x_e[P:] - x_ref[P:])) > 1e-4 * np.max(np.abs(x_ref[P:]))
+
+
+def test_calibration_records_each_site_before_rounding(tiny_weights):
+    """calibrate() records max |x| of every GEMV input before its bf16 rounding, over every
+    prefill row and every decode frame (the head input over the frames only, as a prefill
+    evaluates no head), at the site index the activation-scale table uses.  The torch
+    formulation records the same maxima on the same rows independently; both agree to
+    1e-12 and give bit-identical float32 scales."""
+    w = tiny_weights
+    calib_ids = S.token_ids(S.SEEDS["calib_prompt"], 16, TINY.text_vocab)
+    n = 8
+    scales, amax, codes = calibrate(TINY, w, calib_ids, n)
+    seq = [("text", int(i)) for i in calib_ids]
+    seq += [("audio", np.full(8, 1024) if f == 0 else codes[f - 1]) for f in range(n)]
+    rec = np.zeros(SITES * TINY.n_layers + 1)
+    store = TorchStorage("bf16", record=rec)
+    _, xt = torch_forward(TINY, w, seq, store)
+    torch_head(TINY, w, xt[len(calib_ids):], store)
+    assert np.all(rec > 0)
+    assert np.allclose(amax, rec, rtol=1e-12, atol=0.0), np.abs(amax / rec - 1).max()
+    assert np.array_equal(scales, np.array([nx.act_scale(a) for a in rec], np.float32))
+    # the sites are distinct enough that a permuted table would not pass
+    assert len(np.unique(np.round(rec, 6))) == len(rec)
 
 
 def test_prefill_equals_step_by_step(tiny_weights):
