@@ -499,7 +499,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, co
 #pragma unroll
     for (int j = 0; j < S::NB; ++j) {
       const uint32_t mb = __builtin_amdgcn_readfirstlane(sb + (uint32_t)(w * S::NB + j) * 1024u);
-      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+      // weight rows, read once per call: non-temporal, past the caches
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                    : : "v"(voffB[j]), "s"(b), "s"(mb) : "memory", "m0");
     }
     if (fetch_a) {

@@ -123,7 +123,7 @@ def main() -> int:
 
     # ---------------------------------------------------------------- BF16 context: calibration + BF16 numbers
     log("BF16 context: load + FP8 calibration")
-    b_seq = max(max_seq, args.prompt + args.bf16_frames + 8)
+    b_seq = max(max_seq, args.prompt + args.bf16_frames + 8, 520)  # room for the P = 512 prefill
     bctx = hta.Hta(shape, "bf16", max_seq=b_seq, max_prefill=min(512, b_seq))
     bctx.load_weights(tensors, src)
     scales = bctx.calibrate(calib, 16)
@@ -158,7 +158,7 @@ def main() -> int:
     # room for the long-context measurement (4095 prompt keys + the timed frames); the KV
     # length a frame attends, not the cache's capacity, sets the frame's work
     long_kv = shape.n_layers == 36 and not args.no_long
-    f_seq = max(max_seq, LONG_PROMPT + LONG_FRAMES + 8) if long_kv else max_seq
+    f_seq = max(max_seq, LONG_PROMPT + LONG_FRAMES + 8) if long_kv else max(max_seq, 520)
     ctx = hta.Hta(shape, "fp8", max_seq=f_seq, max_prefill=min(512, f_seq))
     ctx.load_weights(tensors, src, act_scales=scales)
     del tensors
