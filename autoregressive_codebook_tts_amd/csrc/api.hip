@@ -96,6 +96,8 @@ Layout make_layout(const hta_config& c) {
   L.off_pa = take(Pm * F * 2);  // SiLU * mul rows (the down projection's input)
   L.off_taps = take(((size_t)c.n_layers + 1) * d * 4);
   L.off_ptaps = take(2 * Pm * d * 4);
+  L.off_tact = take((5 * (size_t)c.n_layers + 1) * kActsWidth * 2);
+  L.off_tq = take((size_t)c.n_layers * qd * 2);
   L.off_trace = take((size_t)kTraceBlocks * (5 * c.n_layers + 1) * 8 * 4);
   L.off_fargs = take(kFrameArgsBytes);
   L.total = o;
@@ -124,8 +126,13 @@ static bool shape_ok(const hta_config& f, std::string* why) {
   if (f.n_layers < 1 || f.hidden < 64 || f.n_q_heads < 1 || f.n_kv_heads < 1) return bad("non-positive shape");
   if (f.head_dim != 64 && f.head_dim != 128) return bad("head_dim must be 64 or 128");
   if (f.n_q_heads % f.n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
-  if (f.n_q_heads / f.n_kv_heads > 4) return bad("GQA group size above 4 is not supported");
+  {
+    const int g = f.n_q_heads / f.n_kv_heads;
+    if (g != 1 && g != 2 && g != 4) return bad("GQA group size must be 1, 2 or 4");
+  }
   if (f.n_kv_heads > 32) return bad("n_kv_heads above 32 is not supported");
+  if (f.n_q_heads + f.n_kv_heads > 64 || f.n_kv_heads * f.head_dim > 2048)
+    return bad("n_q_heads + n_kv_heads above 64 or kv width above 2048 exceed the prefill row kernels");
   if (f.hidden % 128 || f.ffn % 128 || (f.n_q_heads * f.head_dim) % 128) return bad("hidden, ffn and q width must be multiples of 128");
   if (f.n_codebooks < 1 || f.n_codebooks > kMaxCodebooks) return bad("n_codebooks must be in 1..16");
   if (f.codebook_size < 2 || f.codebook_size > 2048) return bad("codebook_size must be in 2..2048");
@@ -189,6 +196,8 @@ static void set_pointers(Ctx& c) {
   c.sync = reinterpret_cast<unsigned*>(w + L.off_sync);
   c.taps_h = reinterpret_cast<float*>(w + L.off_taps);
   c.taps_p = reinterpret_cast<float*>(w + L.off_ptaps);
+  c.taps_act = reinterpret_cast<uint16_t*>(w + L.off_tact);
+  c.taps_q = reinterpret_cast<uint16_t*>(w + L.off_tq);
   c.trace_buf = reinterpret_cast<uint32_t*>(w + L.off_trace);
   c.fargs = w + L.off_fargs;
   c.tok = reinterpret_cast<int32_t*>(w + L.off_tok);
@@ -215,25 +224,10 @@ static hipError_t clear_exchange(Ctx& c) {
   return launch_fill_u32(c.ws + L.off_xh, 0u, n, c.stream);
 }
 
-static hipError_t enqueue_frame(Ctx& c, bool record) {
-  if (!record && c.use_persistent && c.frame_ok) return launch_frame_persistent(c);
-  const size_t hb = (size_t)c.cfg.hidden * 4;
-  hipError_t e = launch_frame_begin(c);
-  if (e != hipSuccess) return e;
-  if (c.taps && (e = hipMemcpyAsync(c.taps_h, c.h, hb, hipMemcpyDeviceToDevice, c.stream)) != hipSuccess) return e;
-  for (int l = 0; l < c.cfg.n_layers; ++l) {
-    if ((e = launch_layer_decode(c, l, c.h, record)) != hipSuccess) return e;
-    if (c.taps && (e = hipMemcpyAsync(c.taps_h + (size_t)(l + 1) * c.cfg.hidden, c.h, hb, hipMemcpyDeviceToDevice,
-                                      c.stream)) != hipSuccess)
-      return e;
-  }
-  return launch_head(c, record);
-}
-
 static int ensure_graph(Ctx& c) {
   if (c.frame_exec) return HTA_OK;
   HIPCK(hipStreamBeginCapture(c.stream, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
-  hipError_t e = enqueue_frame(c, false);
+  hipError_t e = launch_frame_persistent(c);
   hipGraph_t g = nullptr;
   hipError_t e2 = hipStreamEndCapture(c.stream, &g);
   if (e != hipSuccess) { if (g) (void)hipGraphDestroy(g); return hip_fail(c, e, "frame capture"); }
@@ -286,6 +280,20 @@ int hta_create(const hta_config* cfg, void* hip_stream, hta_ctx** out) {
   if (frame_setup(c) == hipSuccess && frame_max_packets(c.cfg, c.frame_blocks) <= frame_part_capacity())
     c.frame_ok = true;
   (void)hipGetLastError();
+  {
+    // The frame kernel runs one resident block per compute unit, and every block must own
+    // rows in every GEMV phase: a block that owned none would not hold back the phase's
+    // producers, which could then rewrite an exchange buffer before that block has read it.
+    const hta_config& f = c.cfg;
+    const long units[5] = {(long)(f.n_q_heads + 2 * f.n_kv_heads) * f.head_dim, f.hidden, f.ffn, f.hidden,
+                           (long)f.n_codebooks * f.codebook_size};
+    bool rows_ok = true;
+    for (long u : units) rows_ok = rows_ok && u >= c.frame_blocks;
+    if (!c.frame_ok || !rows_ok) {
+      hta_destroy(x);
+      return HTA_E_UNSUPPORTED;
+    }
+  }
   c.h_stage_elems = (size_t)c.cfg.max_seq * c.cfg.n_codebooks;
   if ((size_t)c.cfg.max_prefill > c.h_stage_elems) c.h_stage_elems = c.cfg.max_prefill;
   if (hipHostMalloc((void**)&c.h_stage, c.h_stage_elems * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
@@ -418,6 +426,14 @@ int hta_prefill(hta_ctx* x, const int32_t* tokens, int P) {
   return HTA_OK;
 }
 
+// A bounded wait of the frame kernel expired (every block left the kernel early): clear
+// the exchange words so that the next launch starts clean.
+static int frame_timed_out(Ctx& c) {
+  HIPCK(clear_exchange(c), "fill");
+  HIPCK(hipStreamSynchronize(c.stream), "sync");
+  return fail(c, HTA_E_TIMEOUT, "a bounded wait of the frame kernel expired; the utterance must be reset");
+}
+
 static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out) {
   int r = ready(c);
   if (r) return r;
@@ -427,22 +443,16 @@ static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out) {
     if ((r = ensure_graph(c)) != HTA_OK) return r;
     for (int i = 0; i < n; ++i) HIPCK(hipGraphLaunch(c.frame_exec, c.stream), "hipGraphLaunch");
   } else {
-    for (int i = 0; i < n; ++i) HIPCK(enqueue_frame(c, false), "frame");
+    for (int i = 0; i < n; ++i) HIPCK(launch_frame_persistent(c), "frame");
   }
   const int C = c.cfg.n_codebooks;
   const int t0 = c.t;
   HIPCK(hipMemcpyAsync(c.h_stage, c.hist + (size_t)t0 * C, (size_t)n * C * 4, hipMemcpyDeviceToHost, c.stream), "codes");
   HIPCK(hipMemcpyAsync(c.h_state, c.state, sizeof(DevState), hipMemcpyDeviceToHost, c.stream), "state");
   unsigned aborted = 0;
-  if (c.use_persistent && c.frame_ok)
-    HIPCK(hipMemcpyAsync(&aborted, c.sync + 64, sizeof(unsigned), hipMemcpyDeviceToHost, c.stream), "status");
+  HIPCK(hipMemcpyAsync(&aborted, c.sync + 64, sizeof(unsigned), hipMemcpyDeviceToHost, c.stream), "status");
   HIPCK(hipStreamSynchronize(c.stream), "decode sync");
-  if (aborted) {
-    // a bounded wait expired: clear the exchange words so the next launch starts clean
-    HIPCK(clear_exchange(c), "fill");
-    HIPCK(hipStreamSynchronize(c.stream), "sync");
-    return fail(c, HTA_E_TIMEOUT, "a bounded wait of the frame kernel expired; the utterance must be reset");
-  }
+  if (aborted) return frame_timed_out(c);
   std::memcpy(codes_out, c.h_stage, (size_t)n * C * 4);
   c.len += n;
   c.t += n;
@@ -563,6 +573,20 @@ int hta_read_tap(hta_ctx* x, int tap, int layer, void* host_out, size_t bytes) {
       }
       return HTA_OK;
     }
+    case HTA_TAP_ACT: {
+      const size_t nb = (5 * (size_t)f.n_layers + 1) * kActsWidth * 2;
+      if (!c.taps) return fail(c, HTA_E_STATE, "taps are off");
+      if (bytes < nb) return fail(c, HTA_E_ARG, "buffer too small");
+      HIPCK(hipMemcpy(host_out, c.taps_act, nb, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    }
+    case HTA_TAP_Q: {
+      const size_t nb = (size_t)f.n_layers * f.n_q_heads * f.head_dim * 2;
+      if (!c.taps) return fail(c, HTA_E_STATE, "taps are off");
+      if (bytes < nb) return fail(c, HTA_E_ARG, "buffer too small");
+      HIPCK(hipMemcpy(host_out, c.taps_q, nb, hipMemcpyDeviceToHost), "tap");
+      return HTA_OK;
+    }
     case HTA_TAP_TRACE: {
       const size_t nb = (size_t)c.frame_blocks * (5 * f.n_layers + 1) * 8 * 4;
       if (!c.trace) return fail(c, HTA_E_STATE, "trace is off");
@@ -598,15 +622,24 @@ int hta_calibrate(hta_ctx* x, const int32_t* tokens, int P, int n_frames, const 
   HIPCK(hipMemcpyAsync(c.tok, c.h_stage, (size_t)P * 4, hipMemcpyHostToDevice, c.stream), "tokens");
   HIPCK(launch_prefill(c, P, true), "calibration prefill");
   HIPCK(launch_set_len(c, P), "set len");
-  for (int fr = 0; fr < n_frames; ++fr) {
-    HIPCK(enqueue_frame(c, true), "calibration frame");
-    if (forced) HIPCK(launch_set_prev(c, forced + (size_t)fr * f.n_codebooks), "force");
+  // the frames run on the decode frame kernel itself, recording each site's maximum
+  c.frame_record = true;
+  HIPCK(frame_write_args(c), "frame arguments");
+  hipError_t e = hipSuccess;
+  for (int fr = 0; fr < n_frames && e == hipSuccess; ++fr) {
+    e = launch_frame_persistent(c);
+    if (e == hipSuccess && forced) e = launch_set_prev(c, forced + (size_t)fr * f.n_codebooks);
   }
+  c.frame_record = false;
+  const hipError_t e2 = frame_write_args(c);  // synchronises the stream first
+  if (e != hipSuccess) return hip_fail(c, e, "calibration frame");
+  if (e2 != hipSuccess) return hip_fail(c, e2, "frame arguments");
+  unsigned aborted = 0;
+  HIPCK(hipMemcpy(&aborted, c.sync + 64, sizeof(unsigned), hipMemcpyDeviceToHost), "status");
+  if (aborted) return frame_timed_out(c);
   std::vector<float> amax(nsites);
-  HIPCK(hipStreamSynchronize(c.stream), "sync");
   HIPCK(hipMemcpy(amax.data(), c.amax, nsites * 4, hipMemcpyDeviceToHost), "amax");
   for (int i = 0; i < nsites; ++i) scales_out[i] = amax[i] > 0.0f ? amax[i] / 448.0f : 1.0f;
-  c.len = P + n_frames;
   c.last_prefill_P = P;
   HIPCK(launch_reset_state(c, 0), "reset");
   HIPCK(hipStreamSynchronize(c.stream), "sync");
@@ -622,15 +655,30 @@ int hta_layer_step(hta_ctx* x, int layer, int kv_len, const void* k_init, const 
   const hta_config& f = c.cfg;
   int r = ready(c);
   if (r) return r;
-  if (layer < 0 || layer >= f.n_layers) return fail(c, HTA_E_ARG, "bad layer");
+  if (f.n_layers != 1 || layer != 0) return fail(c, HTA_E_UNSUPPORTED, "a layer step runs layer 0 of a one-layer context");
   if (kv_len < 1 || kv_len > f.max_seq) return fail(c, HTA_E_CAPACITY, "kv_len out of range");
   if (!h_io) return fail(c, HTA_E_ARG, "null hidden state");
   if ((k_init == nullptr) != (v_init == nullptr)) return fail(c, HTA_E_ARG, "k_init and v_init go together");
+  if (!k_init && kv_len - 1 > c.len) return fail(c, HTA_E_STATE, "the cache holds fewer than kv_len - 1 positions");
   if (k_init)
-    HIPCK(launch_kv_init(c.layers[layer].k_cache, c.layers[layer].v_cache, k_init, v_init, f.n_kv_heads, kv_len - 1,
+    HIPCK(launch_kv_init(c.layers[0].k_cache, c.layers[0].v_cache, k_init, v_init, f.n_kv_heads, kv_len - 1,
                          f.max_seq, f.head_dim, c.stream), "kv init");
-  HIPCK(launch_layer_decode_at(c, layer, static_cast<float*>(h_io), false, kv_len - 1), "layer step");
-  HIPCK(hipStreamSynchronize(c.stream), "sync");
+  // one frame of the decode frame kernel at position kv_len - 1 with h_io as its input
+  HIPCK(launch_reset_state(c, kv_len - 1), "reset");
+  c.frame_h_in = static_cast<const float*>(h_io);
+  hipError_t e = frame_write_args(c);
+  if (e == hipSuccess) e = launch_frame_persistent(c);
+  c.frame_h_in = nullptr;
+  const hipError_t e2 = frame_write_args(c);  // synchronises the stream first
+  if (e != hipSuccess) return hip_fail(c, e, "layer step");
+  if (e2 != hipSuccess) return hip_fail(c, e2, "frame arguments");
+  unsigned aborted = 0;
+  HIPCK(hipMemcpy(&aborted, c.sync + 64, sizeof(unsigned), hipMemcpyDeviceToHost), "status");
+  if (aborted) return frame_timed_out(c);
+  HIPCK(hipMemcpy(h_io, c.h, (size_t)f.hidden * 4, hipMemcpyDeviceToDevice), "layer output");
+  c.len = kv_len;
+  c.t = 1;
+  c.done = false;
   return HTA_OK;
 }
 
@@ -655,35 +703,32 @@ int hta_time_kernels(hta_ctx* x, int n_frames, float* avg_us, int n_classes) {
   if (r) return r;
   if (n_frames <= 0 || !avg_us || n_classes <= 0) return fail(c, HTA_E_ARG, "bad arguments");
   if (c.len + n_frames > c.cfg.max_seq) return fail(c, HTA_E_CAPACITY, "KV cache full");
-  const int per_frame = 2 * (3 + 5 * c.cfg.n_layers);
-  std::vector<hipEvent_t> ev(per_frame);
-  std::vector<int> cls(per_frame / 2);
-  for (auto& e : ev) HIPCK(hipEventCreate(&e), "hipEventCreate");
-  double sum[HTA_K_COUNT] = {0};
-  long cnt[HTA_K_COUNT] = {0};
+  hipEvent_t ev[2];
+  HIPCK(hipEventCreate(&ev[0]), "hipEventCreate");
+  if (hipEventCreate(&ev[1]) != hipSuccess) {
+    (void)hipEventDestroy(ev[0]);
+    return fail(c, HTA_E_HIP, "hipEventCreate");
+  }
+  int cls = -1;
+  double sum = 0.0;
   int rc = HTA_OK;
   for (int fr = 0; fr < n_frames && rc == HTA_OK; ++fr) {
-    c.tev = ev.data();
-    c.tev_cap = per_frame;
+    c.tev = ev;
+    c.tev_cap = 2;
     c.tev_next = 0;
-    c.tev_class = cls.data();
-    hipError_t e = enqueue_frame(c, false);
-    const int used = c.tev_next;
+    c.tev_class = &cls;
+    hipError_t e = launch_frame_persistent(c);
     c.tev = nullptr;
     if (e != hipSuccess) { rc = hip_fail(c, e, "timed frame"); break; }
     if ((e = hipStreamSynchronize(c.stream)) != hipSuccess) { rc = hip_fail(c, e, "sync"); break; }
-    for (int i = 0; i < used / 2; ++i) {
-      float ms = 0.0f;
-      if (hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) == hipSuccess && cls[i] >= 0 && cls[i] < HTA_K_COUNT) {
-        sum[cls[i]] += ms * 1000.0;
-        cnt[cls[i]] += 1;
-      }
-    }
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, ev[0], ev[1]) == hipSuccess) sum += ms * 1000.0;
     c.len += 1;
     c.t += 1;
   }
-  for (auto& e : ev) (void)hipEventDestroy(e);
-  for (int k = 0; k < n_classes; ++k) avg_us[k] = (k < HTA_K_COUNT && cnt[k]) ? (float)(sum[k] / cnt[k]) : 0.0f;
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
+  for (int k = 0; k < n_classes; ++k) avg_us[k] = (k == HTA_K_FRAME && rc == HTA_OK) ? (float)(sum / n_frames) : 0.0f;
   return rc;
 }
 
@@ -692,13 +737,6 @@ int hta_set_option(hta_ctx* x, int option, int value) {
   Ctx& c = x->c;
   if (option == HTA_OPT_USE_GRAPH) {
     c.use_graph = value != 0;
-    return HTA_OK;
-  }
-  if (option == HTA_OPT_PERSISTENT) {
-    const bool v = value != 0;
-    if (v && !c.frame_ok) return fail(c, HTA_E_UNSUPPORTED, "the persistent frame kernel does not fit this device");
-    if (v != c.use_persistent) drop_graph(c);
-    c.use_persistent = v;
     return HTA_OK;
   }
   if (option == HTA_OPT_TAPS) {

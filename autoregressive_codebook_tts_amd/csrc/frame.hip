@@ -66,6 +66,10 @@ struct FrameArgs {
   float* h_out;              // [d]    final residual (plain, for taps)
   float* logits_out;         // [C*V]  logits (plain, for taps)
   float* taps;               // [n_layers + 1][d] residual entering each layer, or null
+  uint16_t* acts;            // [5 * n_layers + 1][kActsWidth] GEMV input of each phase (block 0), or null
+  uint16_t* q_tap;           // [n_layers][Hq * hd] rotated queries (bf16), or null
+  const float* h_in;         // [d] frame input in place of the codebook embedding sum, or null
+  float* amax;               // [4L + 1] max |x| of each activation site before rounding, or null
   uint32_t* trace;           // [blocks][5 * n_layers + 1][8] phase timestamps and counters, or null
   unsigned* sync;            // [0] launch count, [64] abort flag
   DevState* st;
@@ -395,7 +399,7 @@ __device__ __forceinline__ bool poll_batch32(const uint32_t* base, int stride, i
 template <int P, int kMaxPer>
 __device__ __forceinline__ bool norm_to_lds_n(const uint64_t* xh, unsigned tag, const float* g, int K, float eps,
                                               float scale, uint32_t* xs, float* red, unsigned* abort_flag,
-                                              uint32_t (&seen)[2]) {
+                                              uint32_t (&seen)[2], float* rec) {
   Poll pl;
   pl.start(abort_flag);
   // the gains do not depend on the frame: their loads travel with the first poll round
@@ -421,10 +425,19 @@ __device__ __forceinline__ bool norm_to_lds_n(const uint64_t* xh, unsigned tag, 
   seen[1] = (uint32_t)__builtin_amdgcn_s_memrealtime();
   const float rstd = 1.0f / sqrtf(ss / (float)K + eps);
   uint16_t* xs16 = reinterpret_cast<uint16_t*>(xs);
+  float mx = 0.0f;
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i) {
     const int k = i * kFT + threadIdx.x;
-    if (k < K) xs16[k] = (uint16_t)act_bits<P>(__uint_as_float((uint32_t)wv[i]) * rstd * gv[i], scale);
+    const float u = __uint_as_float((uint32_t)wv[i]) * rstd * gv[i];
+    if (k < K) {
+      xs16[k] = (uint16_t)act_bits<P>(u, scale);
+      mx = fmaxf(mx, fabsf(u));
+    }
+  }
+  if (rec != nullptr) {  // calibration: the site's maximum before rounding (uniform branch)
+    mx = block_max(mx, red);
+    if (threadIdx.x == 0) record_amax(rec, mx);
   }
   __syncthreads();
   return true;
@@ -432,10 +445,10 @@ __device__ __forceinline__ bool norm_to_lds_n(const uint64_t* xh, unsigned tag, 
 template <int P>
 __device__ __forceinline__ bool norm_to_lds(const uint64_t* xh, unsigned tag, const float* g, int K, float eps,
                                             float scale, uint32_t* xs, float* red, unsigned* abort_flag,
-                                            uint32_t (&seen)[2]) {
+                                            uint32_t (&seen)[2], float* rec) {
   // K <= 10 * kFT; hidden sizes up to 5 * kFT (2560 at 512 threads) take the short batch
-  if (K <= 5 * kFT) return norm_to_lds_n<P, 5>(xh, tag, g, K, eps, scale, xs, red, abort_flag, seen);
-  return norm_to_lds_n<P, 10>(xh, tag, g, K, eps, scale, xs, red, abort_flag, seen);
+  if (K <= 5 * kFT) return norm_to_lds_n<P, 5>(xh, tag, g, K, eps, scale, xs, red, abort_flag, seen, rec);
+  return norm_to_lds_n<P, 10>(xh, tag, g, K, eps, scale, xs, red, abort_flag, seen, rec);
 }
 
 // xs from a tagged exchange buffer already in GEMV units (bf16 bits); kMaxPer words per thread
@@ -613,6 +626,8 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
     if (HD > 64) sm.vn[lane + 64] = round_bf16(__uint_as_float((uint32_t)v1));
   }
   if (!block_ok(pl.ok, okf)) return false;
+  if (a.q_tap != nullptr && split == 0 && tid < G * HD)  // taps: this kv group's rotated queries
+    *gpw(a.q_tap + (size_t)layer * a.Hq * HD + (size_t)j * G * HD + tid) = (uint16_t)f32_to_bf16(sm.qs[tid / HD][tid % HD]);
   trace_mark(a, 5 * a.n_layers + 1, 5 * layer + 1, 1);
   const float inv_sqrt = 1.0f / sqrtf((float)HD);
   const bool hi = w >= G;             // the odd-dimension / upper-output wave of a query head
@@ -773,6 +788,10 @@ __device__ __forceinline__ bool attn_task(CFA& a, const LayerW L, int layer, int
     }
     const float inv = 1.0f / lsum;
     st32(xo + (size_t)h * HD + dd, act_bits<P>(n * inv, so), tag_o);
+    if (a.amax != nullptr) {  // calibration: the attention-output site's maximum before rounding
+      const float mx = wave_max(fabsf(n * inv));
+      if (lane == 0) record_amax(a.amax + kSitesPerLayer * layer + 1, mx);
+    }
   }
   return block_ok(pm.ok, okf);
 }
@@ -1107,13 +1126,22 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
   asm volatile("" : "+v"(zero4.x), "+v"(zero4.y), "+v"(zero4.z), "+v"(zero4.w));
   for (int i = tid; i < kPartMax; i += kFT) part[i] = 0.0f;
 
-  // frame input: h = sum_k E_aud[k][prev_k]; every block forms the whole vector for
-  // the first norm and publishes the rows it owns (the O/DOWN row split of d).  The
-  // owned rows (at most one per thread) stay in h_own for the residual updates.
+  // frame input: h = sum_k E_aud[k][prev_k] (or, for a one-layer step, the given h_in);
+  // every block forms the whole vector for the first norm and publishes the rows it owns
+  // (the O/DOWN row split of d).  The owned rows (at most one per thread) stay in h_own
+  // for the residual updates.
   float h_own = 0.0f;
   {
     const Stream<P> own = make_stream<P>(split, nullptr, 1, kO);
     constexpr int kMaxPer = 10;  // d <= 10 * kFT
+    const float* h_in = a.h_in;
+    auto input = [&](int k) {
+      if (h_in != nullptr) return *gp(h_in + k);
+      float v = 0.0f;
+#pragma unroll 1
+      for (int c = 0; c < a.C; ++c) v += bf16_to_f32(*gp(a.e_aud + ((size_t)c * a.V + sh_state[4 + c]) * d + k));
+      return v;
+    };
     float hv[kMaxPer];
     float ss = 0.0f;
 #pragma unroll
@@ -1121,18 +1149,14 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
       const int k = i * kFT + tid;
       hv[i] = 0.0f;
       if (k < d) {
-        float v = 0.0f;
-#pragma unroll 1
-        for (int c = 0; c < a.C; ++c) v += bf16_to_f32(*gp(a.e_aud + ((size_t)c * a.V + sh_state[4 + c]) * d + k));
+        const float v = input(k);
         hv[i] = v;
         ss = fmaf(v, v, ss);
       }
     }
     if (tid < own.nrows) {
       const int k = own.r0 + tid;
-      float v = 0.0f;
-#pragma unroll 1
-      for (int c = 0; c < a.C; ++c) v += bf16_to_f32(*gp(a.e_aud + ((size_t)c * a.V + sh_state[4 + c]) * d + k));
+      const float v = input(k);
       h_own = v;
       st64(a.xh + k, v, base);
       if (a.taps) *gpw(a.taps + k) = v;
@@ -1142,10 +1166,19 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     const float sc = P == kFP8 ? act_scale(a, 0) : 1.0f;
     const float* g = layer_ptrs(a, 0)->g_attn;
     uint16_t* xs16 = reinterpret_cast<uint16_t*>(xs);
+    float mx = 0.0f;
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i) {
       const int k = i * kFT + tid;
-      if (k < d) xs16[k] = (uint16_t)act_bits<P>(hv[i] * rstd * *gp(g + k), sc);
+      if (k < d) {
+        const float u = hv[i] * rstd * *gp(g + k);
+        xs16[k] = (uint16_t)act_bits<P>(u, sc);
+        mx = fmaxf(mx, fabsf(u));
+      }
+    }
+    if (a.amax != nullptr && blockIdx.x == 0) {  // calibration: layer 0's attention-input site
+      mx = block_max(mx, red);
+      if (tid == 0) record_amax(a.amax, mx);
     }
     __syncthreads();
   }
@@ -1194,7 +1227,8 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     if (kind == kQKV || kind == kGU || kind == kHEAD) {
       if (!(kind == kQKV && layer == 0)) {
         const float* g = kind == kHEAD ? a.g_final : (kind == kQKV ? layer_ptrs(a, layer)->g_attn : layer_ptrs(a, layer)->g_mlp);
-        if (!norm_to_lds<P>(xh, tag_h, g, d, a.eps, sc_in, xs, red, abort_flag, seen)) { ring_drain(); return; }
+        float* rec = (a.amax != nullptr && blockIdx.x == 0) ? a.amax + site : nullptr;
+        if (!norm_to_lds<P>(xh, tag_h, g, d, a.eps, sc_in, xs, red, abort_flag, seen, rec)) { ring_drain(); return; }
       } else {
         settle_loads();  // layer 0's input was formed in the frame prologue: nothing is in flight
       }
@@ -1205,6 +1239,11 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
       if (!act_to_lds(src, tag - 1u, K, xs, abort_flag, red, seen)) { ring_drain(); return; }
     }
     if (P == kFP8) asm volatile("" : "+v"(ws0), "+v"(ws1));  // the scale loads land here
+    if (a.acts != nullptr && blockIdx.x == 0) {  // taps: this phase's GEMV input vector
+      const int K = kind == kO ? a.Hq * HD : (kind == kDOWN ? a.F : d);
+      const uint16_t* xs16 = reinterpret_cast<const uint16_t*>(xs);
+      for (int k = tid; k < K; k += kFT) *gpw(a.acts + (size_t)phase * kActsWidth + k) = xs16[k];
+    }
     trace_mark(a, n_phases, phase, 1);
     trace_put(a, n_phases, phase, 6, seen[0]);
     trace_put(a, n_phases, phase, 7, seen[1]);
@@ -1214,11 +1253,18 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     // ---- epilogue (rows per block <= 128 < kFT, so one row or pair per thread)
     if (kind == kGU) {
       const float sc_out = P == kFP8 ? act_scale(a, site + 1) : 1.0f;
+      float mx = 0.0f;
       if (tid < cur.nrows / 2) {
         const int row = cur.r0 + 2 * tid;
         const float g = row_sum(part, 2 * tid, zero4) * (P == kFP8 ? sc_in * ws0 : 1.0f);
         const float u = row_sum(part, 2 * tid + 1, zero4) * (P == kFP8 ? sc_in * ws1 : 1.0f);
-        st32(launder(a.xa) + row / 2, act_bits<P>(silu(g) * u, sc_out), tag);
+        const float v = silu(g) * u;
+        st32(launder(a.xa) + row / 2, act_bits<P>(v, sc_out), tag);
+        mx = fabsf(v);
+      }
+      if (a.amax != nullptr) {  // calibration: the down-input site's maximum before rounding
+        mx = wave_max(mx);
+        if ((tid & 63) == 0) record_amax(a.amax + site + 1, mx);
       }
     } else {
       if (tid < cur.nrows) {
@@ -1356,6 +1402,10 @@ hipError_t frame_write_args(Ctx& c) {
   a.xh = c.x_h; a.xqkv = c.x_qkv; a.xo = c.x_o; a.xa = c.x_a; a.xpart = c.x_part; a.xlogits = c.x_logits;
   a.h_out = c.h; a.logits_out = c.logits;
   a.taps = c.taps ? c.taps_h : nullptr;
+  a.acts = c.taps ? c.taps_act : nullptr;
+  a.q_tap = c.taps ? c.taps_q : nullptr;
+  a.h_in = c.frame_h_in;
+  a.amax = c.frame_record ? c.amax : nullptr;
   a.trace = c.trace ? c.trace_buf : nullptr;
   a.sync = c.sync; a.st = c.state; a.hist = c.hist;
   a.splits = c.frame_splits;

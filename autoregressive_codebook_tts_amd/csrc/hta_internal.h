@@ -14,6 +14,7 @@ constexpr int kAttnTile = 64;       // keys per attention tile (aligned to absol
 constexpr int kMaxCodebooks = 16;
 constexpr int kTraceBlocks = 1024;  // most blocks the persistent kernel's trace records
 constexpr size_t kFrameArgsBytes = 1024;  // device slot of the persistent kernel's arguments
+constexpr int kActsWidth = 10240;   // widest GEMV input (hidden <= 5120, q width and ffn <= 10240)
 
 // Decode state kept on the device (one per context).
 struct DevState {
@@ -58,7 +59,7 @@ struct Layout {
   size_t off_layer_table, off_xh, off_xqkv, off_xo, off_xa, off_xpart, off_xlogits, off_sync;
   // prefill scratch
   size_t off_tok, off_x, off_u, off_pqkv, off_pq, off_po, off_pgu, off_pa;
-  size_t off_taps, off_ptaps, off_trace, off_fargs;
+  size_t off_taps, off_ptaps, off_tact, off_tq, off_trace, off_fargs;
   int attn_splits;
 };
 
@@ -87,8 +88,9 @@ struct Ctx {
   int tev_next = 0, tev_cap = 0;
   int* tev_class = nullptr;
   bool own_stream = false;
-  bool use_persistent = true;
   bool frame_ok = false;      // the persistent frame kernel fits this device and shape
+  const float* frame_h_in = nullptr;  // frame input override (one-layer steps), or null
+  bool frame_record = false;  // the frame records activation maxima (calibration)
   int frame_blocks = 0, frame_splits = 0;
   int num_cus = 256;          // compute units of the device (prefill block-width choice)
   // derived device pointers
@@ -135,6 +137,8 @@ struct Ctx {
   int prefill_tap_layer = 0;
   float* taps_h = nullptr;      // [n_layers + 1][d]
   float* taps_p = nullptr;      // [2][Pmax][d]
+  uint16_t* taps_act = nullptr; // [5 * n_layers + 1][kActsWidth] GEMV inputs of the last frame (block 0)
+  uint16_t* taps_q = nullptr;   // [n_layers][Hq * hd] rotated queries of the last frame
   bool trace = false;           // persistent frame kernel phase timestamps
   uint32_t* trace_buf = nullptr;  // [kTraceBlocks][5 * n_layers + 1][4]
   void* fargs = nullptr;          // the persistent kernel's arguments (device)
@@ -154,11 +158,7 @@ inline void time_end(Ctx& c) {
   }
 }
 
-// ---------------------------------------------------------------- launchers (decode.hip)
-hipError_t launch_frame_begin(Ctx& c);
-hipError_t launch_layer_decode(Ctx& c, int layer, float* h, bool record);
-hipError_t launch_layer_decode_at(Ctx& c, int layer, float* h, bool record, int pos_override);
-hipError_t launch_head(Ctx& c, bool record);
+// ---------------------------------------------------------------- decode state (load.hip)
 hipError_t launch_set_prev(Ctx& c, const int32_t* codes);
 hipError_t launch_reset_state(Ctx& c, int keep_len);
 hipError_t launch_set_len(Ctx& c, int len);

@@ -2,7 +2,7 @@
 // e4m3 codes with per-row scales max|row| / 448 (FlashRT "Higgs Audio v3
 // TTS-4B" page, section 8: FP8 W8A8 with per-output-channel weight scales),
 // written at a row stride so that gate and up rows interleave and q/k/v rows
-// concatenate.  Plus small fill and KV-initialisation kernels.
+// concatenate.  Plus small fill, KV-initialisation and decode-state kernels.
 #include "device_common.h"
 #include "hta_internal.h"
 
@@ -87,6 +87,51 @@ hipError_t launch_kv_init(uint16_t* k_cache, uint16_t* v_cache, const void* k_in
   dim3 grid(64, n_kv);
   hipLaunchKernelGGL(k_kv_init, grid, dim3(256), 0, s, k_cache, v_cache, static_cast<const uint16_t*>(k_init),
                      static_cast<const uint16_t*>(v_init), n, max_seq, hd);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- decode state
+__global__ void k_set_prev(DevState* st, int c0, int c1, int c2, int c3, int c4, int c5, int c6, int c7,
+                           int c8, int c9, int c10, int c11, int c12, int c13, int c14, int c15, int C) {
+  const int cs[16] = {c0, c1, c2, c3, c4, c5, c6, c7, c8, c9, c10, c11, c12, c13, c14, c15};
+  if (threadIdx.x < C) st->prev[threadIdx.x] = cs[threadIdx.x];
+}
+
+// a new utterance at length len: step 0, no EOC yet, all-BOS codes fed into the first frame
+__global__ void k_reset_state(DevState* st, int len, int C, int bos) {
+  if (threadIdx.x == 0) {
+    st->len = len;
+    st->t = 0;
+    st->eoc = -1;
+    st->done = 0;
+    st->n_done = 0;
+  }
+  if (threadIdx.x < C) {
+    st->prev[threadIdx.x] = bos;
+    st->codes[threadIdx.x] = bos;
+  }
+}
+
+__global__ void k_set_len(DevState* st, int len) {
+  if (threadIdx.x == 0) st->len = len;
+}
+
+hipError_t launch_set_prev(Ctx& c, const int32_t* v) {
+  int cs[16] = {0};
+  for (int i = 0; i < c.cfg.n_codebooks; ++i) cs[i] = v[i];
+  hipLaunchKernelGGL(k_set_prev, dim3(1), dim3(64), 0, c.stream, c.state, cs[0], cs[1], cs[2], cs[3], cs[4], cs[5],
+                     cs[6], cs[7], cs[8], cs[9], cs[10], cs[11], cs[12], cs[13], cs[14], cs[15], c.cfg.n_codebooks);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset_state(Ctx& c, int keep_len) {
+  hipLaunchKernelGGL(k_reset_state, dim3(1), dim3(64), 0, c.stream, c.state, keep_len, c.cfg.n_codebooks,
+                     c.cfg.bos_id);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_len(Ctx& c, int len) {
+  hipLaunchKernelGGL(k_set_len, dim3(1), dim3(64), 0, c.stream, c.state, len);
   return hipGetLastError();
 }
 

@@ -9,6 +9,8 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
+import weakref
 
 import numpy as np
 
@@ -21,9 +23,9 @@ ERRORS = {-1: "HTA_E_ARG", -2: "HTA_E_STATE", -3: "HTA_E_CAPACITY", -4: "HTA_E_R
 HTA_BF16, HTA_FP8_E4M3 = 0, 1
 HTA_SRC_F32, HTA_SRC_BF16 = 0, 1
 (TAP_HIDDEN, TAP_LOGITS, TAP_STATE, TAP_KV, TAP_AMAX, TAP_PREFILL_HIDDEN, TAP_W_QKV, TAP_S_QKV, TAP_W_GU, TAP_S_GU,
- TAP_LAYER_H, TAP_PREFILL_LAYER, TAP_TRACE) = range(13)
+ TAP_LAYER_H, TAP_PREFILL_LAYER, TAP_TRACE, TAP_ACT, TAP_Q) = range(15)
+ACTS_WIDTH = 10240  # row width of TAP_ACT
 OPT_USE_GRAPH = 0
-OPT_PERSISTENT = 1
 OPT_TAPS = 2
 OPT_PREFILL_TAP_LAYER = 3
 OPT_TRACE = 4
@@ -117,8 +119,22 @@ def undelay(step_codes: np.ndarray, eos: int = 1025) -> np.ndarray:
     return out[: n.value].copy()
 
 
+_open = weakref.WeakSet()  # live contexts, closed by close_all()
+
+
+def close_all() -> None:
+    """Destroy every open context (tests and the benchmark call this before exiting, so
+    that no graph or stream is destroyed during interpreter teardown)."""
+    for ctx in list(_open):
+        ctx.close()
+
+
 class Hta:
-    """One decode context on the current GPU with a torch-allocated workspace."""
+    """One decode context on the current GPU with a torch-allocated workspace.
+
+    Close it explicitly (close(), or use it as a context manager): hta_destroy waits for
+    the stream and destroys the captured frame graph, which must happen while the HIP
+    runtime is still up and before torch frees the workspace the graph references."""
 
     def __init__(self, shape, precision: str = "bf16", max_seq: int = 2048, max_prefill: int = 512, stream=None,
                  fill_byte: int | None = None):
@@ -143,6 +159,7 @@ class Hta:
         self._check(lib().hta_bind_workspace(self.ctx, ctypes.c_void_p(aligned), nbytes), "hta_bind_workspace")
         self.C = shape.n_codebooks
         self.V = shape.codebook_size
+        _open.add(self)
 
     # ------------------------------------------------------------------ plumbing
     def _check(self, rc: int, what: str) -> int:
@@ -155,8 +172,21 @@ class Hta:
             lib().hta_destroy(self.ctx)
             self.ctx = ctypes.c_void_p()
         self.ws = None
+        _open.discard(self)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False
 
     def __del__(self):
+        # During interpreter teardown the HIP runtime (and a profiler's tool library)
+        # may already be gone: a context still open then is left to process exit
+        # rather than destroyed through a runtime that no longer exists.
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
@@ -258,6 +288,16 @@ class Hta:
         counters of the last persistent frame (needs OPT_TRACE on)."""
         return self._tap(TAP_TRACE, 0, np.zeros((blocks, 5 * self.shape.n_layers + 1, 8), np.uint32))
 
+    def tap_acts(self) -> np.ndarray:
+        """[5 * n_layers + 1][ACTS_WIDTH] uint16: the GEMV input of every phase of the last
+        frame as bf16 bits (needs OPT_TAPS on)."""
+        return self._tap(TAP_ACT, 0, np.zeros((5 * self.shape.n_layers + 1, ACTS_WIDTH), np.uint16))
+
+    def tap_q(self) -> np.ndarray:
+        """[n_layers][Hq][hd] uint16: bf16 bits of the rotated queries of the last frame (OPT_TAPS on)."""
+        sh = self.shape
+        return self._tap(TAP_Q, 0, np.zeros((sh.n_layers, sh.n_q_heads, sh.head_dim), np.uint16))
+
     def tap_prefill_hidden(self, P: int) -> np.ndarray:
         return self._tap(TAP_PREFILL_HIDDEN, 0, np.zeros((P, self.shape.hidden), np.float32))
 
@@ -272,7 +312,8 @@ class Hta:
         return out
 
     def layer_step(self, layer: int, kv_len: int, k_init, v_init, h) -> None:
-        """Run layer ``layer`` on device tensor ``h`` (float32 [d], in place) at position kv_len - 1."""
+        """One-layer context: run the frame kernel's layer 0 on device tensor ``h`` (float32 [d],
+        in place) at position kv_len - 1, after filling KV positions [0, kv_len - 1)."""
         self.torch.cuda.synchronize()
         kp = ctypes.c_void_p(k_init.data_ptr()) if k_init is not None else None
         vp = ctypes.c_void_p(v_init.data_ptr()) if v_init is not None else None

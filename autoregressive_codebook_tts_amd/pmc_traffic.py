@@ -12,7 +12,8 @@ reports the figure only while the kernel is unchanged.
 
 Usage:
   python -m autoregressive_codebook_tts_amd.pmc_traffic FETCH.csv WRITE.csv \
-      --copy-mib 1024 --first 1017 --kernel "k_frame<1, 128>" --workload "..." --out traffic.json
+      --copy-mib 1024 --first 1017 --kernel "k_frame<1, 128>" --workload "..." \
+      --out profiles/k_frame_fp8_decode_p13_f1017_traffic.json
 """
 from __future__ import annotations
 
@@ -24,6 +25,7 @@ import os
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_JSON = os.path.join(os.path.dirname(HERE), "profiles", "k_frame_fp8_decode_p13_f1017_traffic.json")
 KERNEL_SOURCES = ("csrc/frame.hip", "csrc/device_common.h", "csrc/hta_internal.h")
 
 
@@ -64,7 +66,7 @@ def main(argv=None) -> int:
     ap.add_argument("--first", type=int, required=True)
     ap.add_argument("--kernel", default="k_frame<1, 128>")
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--out", default=os.path.join(HERE, "traffic.json"))
+    ap.add_argument("--out", default=TRAFFIC_JSON)
     a = ap.parse_args(argv)
     known = a.copy_mib * 1024 * 1024
     f_kib, f_copy, n = per_dispatch(a.fetch_csv, "FETCH_SIZE", a.kernel, a.first)

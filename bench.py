@@ -238,6 +238,7 @@ def main() -> int:
     }
     line.update(extra)
     print(json.dumps(line), flush=True)
+    hta.close_all()
     return 0
 
 
@@ -246,7 +247,7 @@ def _traffic(workload: str, shape):
     or None when they were taken on another workload or before the kernel's sources last changed."""
     from autoregressive_codebook_tts_amd import pmc_traffic
 
-    path = os.path.join(ROOT, "autoregressive_codebook_tts_amd", "traffic.json")
+    path = pmc_traffic.TRAFFIC_JSON
     if shape.n_layers != 36 or not os.path.exists(path):
         return None
     with open(path) as f:
@@ -362,6 +363,12 @@ def _prefill_ms(ctx, prompt, reps: int = 20) -> float:
 
 
 if __name__ == "__main__":
-    rc = main()
+    try:
+        rc = main()
+    finally:
+        # contexts are destroyed while the HIP runtime is up, also after an error
+        _hta = sys.modules.get("autoregressive_codebook_tts_amd.hta")
+        if _hta is not None:
+            _hta.close_all()
     if rc:  # a clean run returns from the script instead of raising SystemExit
         sys.exit(rc)

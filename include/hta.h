@@ -70,14 +70,20 @@ typedef struct {
 
 typedef struct hta_ctx hta_ctx;
 
-/* Shape limits the kernels support: head_dim 64 or 128; hidden, q and kv widths
- * multiples of 64; ffn a multiple of 64; n_codebooks <= 16; codebook_size <= 2048;
- * n_q_heads a multiple of n_kv_heads with group size <= 8. */
+/* Shape limits the kernels support (hta_create returns HTA_E_UNSUPPORTED otherwise):
+ * head_dim 64 or 128; hidden, ffn and the q width (n_q_heads * head_dim) multiples of
+ * 128, with hidden <= 5120 and ffn, q width <= 10240; GQA group n_q_heads / n_kv_heads
+ * of 1, 2 or 4; n_kv_heads <= 32, n_q_heads + n_kv_heads <= 64, kv width <= 2048;
+ * n_codebooks <= 16; codebook_size <= 2048.  The decode frame kernel runs one resident
+ * block per compute unit (256 on MI355X), and each of its GEMV phases needs at least one
+ * row unit per block: q + 2 kv widths, hidden, ffn (gate/up pairs) and n_codebooks *
+ * codebook_size must each be at least the compute-unit count. */
 
 /* Create a context for cfg on the current HIP device, enqueueing on hip_stream
- * (a hipStream_t, e.g. torch.cuda.current_stream().cuda_stream; NULL = the null
- * stream).  Fails with HTA_E_UNSUPPORTED on a device other than gfx950 or an
- * unsupported shape.  *out receives the context. */
+ * (a hipStream_t, e.g. torch.cuda.current_stream().cuda_stream; NULL makes the
+ * library create a non-blocking stream of its own, destroyed by hta_destroy).  Fails
+ * with HTA_E_UNSUPPORTED on a device other than gfx950 or an unsupported shape.
+ * *out receives the context. */
 int hta_create(const hta_config* cfg, void* hip_stream, hta_ctx** out);
 
 /* Bytes of device workspace the context needs: packed weights, KV cache
@@ -159,26 +165,35 @@ int hta_force_codes(hta_ctx* ctx, const int32_t* codes_in);
  * satisfied and when every wave's were (zero where a phase has no polled
  * input; attention phases leave both as they were) (blocks = one per compute unit;
  * entries of phases a block skips are left as they were).
+ * With HTA_OPT_TAPS on, HTA_TAP_ACT -> uint16 [5 * n_layers + 1][10240]: for every
+ * GEMV phase of the last decode frame (per layer qkv, -, o_proj, gate/up, down; then the
+ * head), the input vector the phase multiplies with, as bf16 bits of the rounded values
+ * (BF16) or of the e4m3 code values (FP8; every e4m3 value is exact in bf16), in the
+ * first hidden / q width / ffn entries of its row (attention rows unused); HTA_TAP_Q ->
+ * uint16 [n_layers][Hq][hd]: the bf16 bits of the queries after q-norm and RoPE that the
+ * last frame's attention used.
  * A buffer smaller than the tap gives HTA_E_ARG. */
 enum { HTA_TAP_HIDDEN = 0, HTA_TAP_LOGITS = 1, HTA_TAP_STATE = 2, HTA_TAP_KV = 3, HTA_TAP_AMAX = 4,
        HTA_TAP_PREFILL_HIDDEN = 5, HTA_TAP_W_QKV = 6, HTA_TAP_S_QKV = 7, HTA_TAP_W_GU = 8, HTA_TAP_S_GU = 9,
-       HTA_TAP_LAYER_H = 10, HTA_TAP_PREFILL_LAYER = 11, HTA_TAP_TRACE = 12 };
+       HTA_TAP_LAYER_H = 10, HTA_TAP_PREFILL_LAYER = 11, HTA_TAP_TRACE = 12, HTA_TAP_ACT = 13, HTA_TAP_Q = 14 };
 int hta_read_tap(hta_ctx* ctx, int tap, int layer, void* host_out, size_t bytes);
 
 /* FP8 calibration on a BF16 context (FlashRT page, section 8: a short BF16
  * free run of a fixed prompt, scale = amax / 448): reset, prefill the P
- * calibration tokens, decode n_frames frames (fed with forced_codes
- * [n_frames][C] when not NULL, else greedy), recording max |x| at every
- * activation site; writes 4*n_layers+1 scales (host) and leaves the context
- * reset to length 0. */
+ * calibration tokens, decode n_frames frames with the decode frame kernel (fed
+ * with forced_codes [n_frames][C] when not NULL, else greedy), recording max |x|
+ * at every activation site before its rounding; writes 4*n_layers+1 scales
+ * (host) and leaves the context reset to length 0. */
 int hta_calibrate(hta_ctx* ctx, const int32_t* tokens, int P, int n_frames, const int32_t* forced_codes,
                   float* scales_out);
 
-/* One decoder layer for tests and per-layer timing: set layer `layer`'s KV
- * length to kv_len - 1 from k_init/v_init (device bf16 [Hkv][kv_len-1][hd],
- * NULL to keep the cache), then run the decode step of that layer on h_io
- * (device float32 [d], updated in place) at position kv_len - 1.  Uses the
- * same kernels as the frame. */
+/* One decoder layer (the one-layer configuration of the benchmark): on a context with
+ * n_layers == 1 (layer must be 0, else HTA_E_UNSUPPORTED), fill the KV cache's positions
+ * [0, kv_len - 1) from k_init/v_init (device bf16 [Hkv][kv_len-1][hd], NULL to keep the
+ * cache), then run one frame of the decode frame kernel at position kv_len - 1 with
+ * h_io (device float32 [d]) as its input in place of the codebook embedding sum, and
+ * write the residual leaving the layer back to h_io.  The new key and value land in
+ * slot kv_len - 1; the context is left at length kv_len, one step into an utterance. */
 int hta_layer_step(hta_ctx* ctx, int layer, int kv_len, const void* k_init, const void* v_init, void* h_io);
 
 /* Un-delay (host only): frames[f][k] = step_codes[f+k][k] for f < n, with
@@ -186,30 +201,27 @@ int hta_layer_step(hta_ctx* ctx, int layer, int kv_len, const void* k_init, cons
  * room for T*C codes; *n_frames receives n. */
 int hta_undelay(const int32_t* step_codes, int T, int n_codebooks, int eos_id, int32_t* frames_out, int* n_frames);
 
-/* Per-kernel timing for the benchmark: decode n_frames frames launching the
- * frame's kernels one by one with a HIP event pair around each launch on the
- * context's stream; avg_us_out (host, n_classes floats) receives the average
- * device time per launch of each kernel class: HTA_K_EMBED, HTA_K_QKV,
- * HTA_K_ATTN, HTA_K_O, HTA_K_GATEUP, HTA_K_DOWN, HTA_K_HEAD for the per-kernel
- * frame, HTA_K_FRAME for the persistent frame kernel (whichever the context
- * decodes with).  The frames are real decode steps (the state advances). */
+/* Kernel timing for the benchmark: decode n_frames frames, each one launch of the
+ * decode frame kernel bracketed by a HIP event pair on the context's stream;
+ * avg_us_out (host, n_classes floats) receives the average device time per launch
+ * at index HTA_K_FRAME and zero for the other classes (kept for the ABI).  The
+ * frames are real decode steps (the state advances). */
 enum { HTA_K_EMBED = 0, HTA_K_QKV = 1, HTA_K_ATTN = 2, HTA_K_O = 3, HTA_K_GATEUP = 4, HTA_K_DOWN = 5, HTA_K_HEAD = 6,
        HTA_K_FRAME = 7, HTA_K_COUNT = 8 };
 int hta_time_kernels(hta_ctx* ctx, int n_frames, float* avg_us_out, int n_classes);
 
 /* Options: HTA_OPT_USE_GRAPH (default 1) replays the captured position-agnostic
- * frame graph; 0 launches the same kernels one by one (for tests that compare
- * the two).  HTA_OPT_PERSISTENT (default 1 where the device fits it) decodes
- * each frame with one persistent kernel (one resident block per compute
- * unit; blocks hand values to each other through phase-tagged words, no grid
- * barrier; a wait that runs out ends the frame with HTA_E_TIMEOUT); 0 uses one
- * kernel per phase.  HTA_OPT_TAPS (default 0) makes decode
- * frames and prefills also write the per-layer residuals read by
- * HTA_TAP_LAYER_H / HTA_TAP_PREFILL_LAYER (frames then launch without the
- * graph); HTA_OPT_PREFILL_TAP_LAYER selects the prefill layer (0..n_layers-1,
- * else HTA_E_ARG).  HTA_OPT_TRACE (default 0) records the persistent frame
- * kernel's phase timestamps (HTA_TAP_TRACE). */
-enum { HTA_OPT_USE_GRAPH = 0, HTA_OPT_PERSISTENT = 1, HTA_OPT_TAPS = 2, HTA_OPT_PREFILL_TAP_LAYER = 3, HTA_OPT_TRACE = 4 };
+ * frame graph; 0 launches the frame kernel directly (for tests that compare the
+ * two).  Every frame is one launch of the persistent decode frame kernel (one
+ * resident block per compute unit; blocks hand values to each other through
+ * phase-tagged words, no grid barrier; a wait that runs out ends the frame with
+ * HTA_E_TIMEOUT).  HTA_OPT_TAPS (default 0) makes decode frames and prefills also
+ * write the per-layer residuals and GEMV inputs read by HTA_TAP_LAYER_H,
+ * HTA_TAP_ACT and HTA_TAP_PREFILL_LAYER (frames then launch without the graph);
+ * HTA_OPT_PREFILL_TAP_LAYER selects the prefill layer (0..n_layers-1, else
+ * HTA_E_ARG).  HTA_OPT_TRACE (default 0) records the frame kernel's phase
+ * timestamps (HTA_TAP_TRACE).  Value 1 is unused. */
+enum { HTA_OPT_USE_GRAPH = 0, HTA_OPT_TAPS = 2, HTA_OPT_PREFILL_TAP_LAYER = 3, HTA_OPT_TRACE = 4 };
 int hta_set_option(hta_ctx* ctx, int option, int value);
 
 void hta_destroy(hta_ctx* ctx);

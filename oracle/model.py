@@ -227,6 +227,74 @@ class OracleModel:
         """Teacher forcing: the next frame embeds ``codes`` instead of the last choice."""
         self.state.prev = np.asarray(codes, dtype=np.int64).copy()
 
+    # ------------------------------------------------------------------ site-anchored checks
+    def layer_anchored(self, layer: int, h, site_vals, qkv=None):
+        """One decode step of ``layer`` for a single row ``h`` at position ``length`` in which
+        each GEMV multiplies with the given rounded input instead of the oracle's own:
+        ``site_vals`` holds the four GEMV inputs (attention input, attention output, MLP
+        input, down input) in GEMV units -- bfloat16 values (BF16) or e4m3 code values
+        (FP8).  This is how an implementation is checked rounding decision by rounding
+        decision: every rounding point then starts from the same values on both sides.
+
+        ``qkv`` (optional): the rounded rotated queries [Hq][hd], key and value [Hkv][hd]
+        to attend with and append to the cache in place of the oracle's own (the
+        implementation's, so that its attention output is checked on its own inputs).
+
+        Returns (pre, k, v, h_out, qkv_pre): the four sites' values before rounding
+        (float64), the key and value row appended to the cache (rounded as stored), the
+        layer output computed from the given site values, and the oracle's own q, k and v
+        rows before their rounding."""
+        sh, Lw = self.shape, self.layers[layer]
+        hd, Hq, Hkv = sh.head_dim, sh.n_q_heads, sh.n_kv_heads
+        s0 = SITES_PER_LAYER * layer
+        pos = self.length
+        h = np.asarray(h, np.float64)[None, :]
+        x = [np.asarray(v, np.float64)[None, :] for v in site_vals]
+        pre = [nx.rmsnorm(h, Lw["g_attn"], sh.rms_eps)]
+        q = self._linear(x[0], Lw["wq"], s0).reshape(1, Hq, hd)
+        k = self._linear(x[0], Lw["wk"], s0).reshape(1, Hkv, hd)
+        v = self._linear(x[0], Lw["wv"], s0).reshape(1, Hkv, hd)
+        p = np.array([pos])
+        q_pre = nx.rope(nx.rmsnorm(q, Lw["g_q"], sh.rms_eps), p, sh.rope_theta)
+        k_pre = nx.rope(nx.rmsnorm(k, Lw["g_k"], sh.rms_eps), p, sh.rope_theta)
+        v_pre = v
+        if qkv is None:
+            q, k, v = self._kv_round(q_pre), self._kv_round(k_pre), self._kv_round(v_pre)
+        else:
+            q, k, v = (np.asarray(a, np.float64)[None] for a in qkv)
+        self.k_cache[layer, pos] = k[0]
+        self.v_cache[layer, pos] = v[0]
+        group = Hq // Hkv
+        o = np.empty((Hq, hd))
+        for hh in range(Hq):
+            j = hh // group
+            o[hh] = nx.attention_one(q[0, hh], self.k_cache[layer, :pos + 1, j], self.v_cache[layer, :pos + 1, j])
+        pre.append(o.reshape(1, Hq * hd))
+        h_mid = h + self._linear(x[1], Lw["wo"], s0 + 1)
+        pre.append(nx.rmsnorm(h_mid, Lw["g_mlp"], sh.rms_eps))
+        g = self._linear(x[2], Lw["wg"], s0 + 2)
+        up = self._linear(x[2], Lw["wu"], s0 + 2)
+        pre.append(nx.silu(g) * up)
+        h_out = h_mid + self._linear(x[3], Lw["wd"], s0 + 3)
+        self.length += 1
+        return [a[0] for a in pre], k[0], v[0], h_out[0], (q_pre[0], k_pre[0], v_pre[0])
+
+    def head_anchored(self, h, z_val):
+        """The head for final residual ``h`` with the given rounded head input ``z_val`` (GEMV
+        units): (the head input before rounding, logits [C][V])."""
+        sh = self.shape
+        site = SITES_PER_LAYER * sh.n_layers
+        pre = nx.rmsnorm(np.asarray(h, np.float64)[None, :], self.g_final, sh.rms_eps)[0]
+        lg = self._linear(np.asarray(z_val, np.float64)[None, :], self.w_head, site)[0]
+        return pre, lg.reshape(sh.n_codebooks, sh.codebook_size)
+
+    def round_site(self, x, site: int):
+        """The oracle's rounding of GEMV input values ``x`` at activation site ``site``, in GEMV
+        units (bfloat16 value, or e4m3 code value of fp32(x) / scale)."""
+        if self.precision == "bf16":
+            return nx.round_bf16(x)
+        return nx.quantize_static(x, self.scales[site])
+
     # ------------------------------------------------------------------ one layer at a preset KV
     def set_kv(self, layer: int, k, v) -> None:
         """Fill positions [0, n) of ``layer`` with given K/V rows [n][Hkv][hd] (as stored) and set length n."""

@@ -11,3 +11,11 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long CPU-only oracle run")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # destroy every decode context while the HIP runtime is still up (not during interpreter
+    # teardown, where hta_destroy would call into a runtime that is being unloaded)
+    hta = sys.modules.get("autoregressive_codebook_tts_amd.hta")
+    if hta is not None:
+        hta.close_all()

@@ -1,7 +1,14 @@
 """One decoder layer at the Qwen3-4B shape (hidden 2560, 32q/8kv heads, head_dim
-128, FFN 9728) on the GPU against the CPU oracle: a single M = 1 decode step
-at KV length 512, 2048 and 4096 with N(0,1) cache contents and a N(0,1) input
-hidden state, in BF16 and FP8."""
+128, FFN 9728) on the GPU against the CPU oracle: a single M = 1 decode step at
+KV length 512, 2048 and 4096 with N(0,1) cache contents and a N(0,1) input
+hidden state, in BF16 and FP8, run by the decode frame kernel itself (a
+one-layer context; hta_layer_step feeds the hidden state in place of the
+codebook embedding sum).
+
+Checked site by site (every rounding decision of the step, see
+gpu_common.check_layer_sites) and, as a whole, against the storage-faithful
+oracle: BF16 update rel <= 2e-3, output rel vs the exact model <= 2e-2; FP8
+update rel <= 6e-2."""
 import dataclasses
 
 import numpy as np
@@ -9,7 +16,8 @@ import pytest
 import torch
 
 import synthetic as S
-from gpu_common import gpu_context, rel_l2
+from autoregressive_codebook_tts_amd import hta
+from gpu_common import check_layer_sites, gpu_context, rel_l2
 from oracle import numerics as nx
 from oracle.model import OracleModel
 
@@ -40,13 +48,22 @@ def _oracle(w, precision, mode, L, h, kb, vb, scales=None):
 
 
 def _gpu(w, precision, L, h, kb, vb, scales=None):
+    """One layer step on the frame kernel with the taps on: (output, input residual tap,
+    output residual tap, GEMV-input taps, context)."""
     ctx = gpu_context(SH, w, precision, max_seq=4096, max_prefill=16, act_scales=scales)
+    ctx.set_option(hta.OPT_TAPS, 1)
     ht = torch.from_numpy(h.astype(np.float32)).cuda()
     ctx.layer_step(0, L, torch.from_numpy(kb.view(np.int16)).cuda(), torch.from_numpy(vb.view(np.int16)).cuda(), ht)
     torch.cuda.synchronize()
-    k_new, v_new = ctx.tap_kv(0, L)
-    ctx.close()
-    return ht.cpu().numpy().astype(np.float64), k_new[:, L - 1], v_new[:, L - 1]
+    taps = ctx.tap_layers().astype(np.float64)
+    return ht.cpu().numpy().astype(np.float64), taps, ctx.tap_acts(), ctx
+
+
+def _site_check(ctx, w, precision, L, taps, acts, scales=None):
+    oracle = OracleModel(SH, w, precision, "S", act_scales=scales, max_seq=L + 1, layers_only=True)
+    flips, kv_flips, upd = check_layer_sites(ctx, oracle, 0, taps[0], taps[1], acts, ctx.tap_q(), L - 1,
+                                             f"{precision} L={L}")
+    print(f"layer {precision} L={L} site-anchored: flips per site {flips}, K/V flips {kv_flips}, output rel {upd:.2e}")
 
 
 @pytest.mark.parametrize("L", [512, 2048, 4096])
@@ -54,7 +71,13 @@ def test_layer_bf16(layer_weights, L):
     h, kb, vb = _inputs(L)
     ref_s, ms = _oracle(layer_weights, "bf16", "S", L, h, kb, vb)
     ref_e, _ = _oracle(layer_weights, "bf16", "E", L, h, kb, vb)
-    out, k_new, v_new = _gpu(layer_weights, "bf16", L, h, kb, vb)
+    out, taps, acts, ctx = _gpu(layer_weights, "bf16", L, h, kb, vb)
+    try:
+        assert np.array_equal(taps[0], h.astype(np.float32)) and np.array_equal(taps[1], out)
+        _site_check(ctx, layer_weights, "bf16", L, taps, acts)
+        k_new, v_new = ctx.tap_kv(0, L)
+    finally:
+        ctx.close()
     d_s = rel_l2(out - h, ref_s - h)
     d_e = rel_l2(out - h, ref_e - h)
     print(f"layer bf16 L={L}: update rel vs storage-faithful {d_s:.3e}, vs exact {d_e:.3e}, output rel vs exact "
@@ -63,7 +86,7 @@ def test_layer_bf16(layer_weights, L):
     assert rel_l2(out, ref_e) <= 2e-2
     # the new key/value landed in slot L-1 as the oracle's bf16 values (up to rounding flips)
     k_ref = ms.k_cache[0, L - 1]
-    k_gpu = nx.bf16_bits_to_float(k_new)
+    k_gpu = nx.bf16_bits_to_float(k_new[:, L - 1])
     assert np.mean(k_gpu == k_ref) > 0.99 and rel_l2(k_gpu, k_ref) < 1e-2
 
 
@@ -74,7 +97,11 @@ def test_layer_fp8(layer_weights, L):
     scales = np.array([nx.act_scale(a) for a in me.record], dtype=np.float32)
     scales[4] = 1.0
     ref_s, _ = _oracle(layer_weights, "fp8", "S", L, h, kb, vb, scales=scales)
-    out, _, _ = _gpu(layer_weights, "fp8", L, h, kb, vb, scales=scales)
+    out, taps, acts, ctx = _gpu(layer_weights, "fp8", L, h, kb, vb, scales=scales)
+    try:
+        _site_check(ctx, layer_weights, "fp8", L, taps, acts, scales=scales)
+    finally:
+        ctx.close()
     d_s = rel_l2(out - h, ref_s - h)
     q = rel_l2(ref_s - h, ref_e - h)
     print(f"layer fp8 L={L}: update rel vs fp8 oracle {d_s:.3e}; fp8 oracle vs exact {q:.3e}; "

@@ -416,3 +416,48 @@ def test_forced_eos_weight_set_stops_at_step_zero(tiny_weights):
         codes, done = m.decode_frame()
         assert np.all(codes[: t + 1] == 1025) and np.all(codes[t + 1:] == 1024)
         assert done == (t == 7)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp8"])
+def test_layer_anchored_equals_layer_on_own_site_values(tiny_weights, precision):
+    """Fed the oracle's own rounded GEMV inputs, the site-anchored step reproduces the plain
+    layer: the same pre-rounding values at the four sites, the same K/V row and the same
+    output; fed values moved by one rounding step at one site, its output moves."""
+    w = tiny_weights
+    calib_ids = S.token_ids(S.SEEDS["calib_prompt"], 16, TINY.text_vocab)
+    scales = calibrate(TINY, w, calib_ids, 4)[0] if precision == "fp8" else None
+    ids = S.token_ids(S.SEEDS["tiny_prompt"], 8, TINY.text_vocab)
+    a = OracleModel(TINY, w, precision, "S", act_scales=scales, max_seq=32)
+    b = OracleModel(TINY, w, precision, "S", act_scales=scales, max_seq=32)
+    a.prefill(ids)
+    b.prefill(ids)
+    h = a.frame_input()
+    seen = {}
+    orig = a._act
+
+    def capture(x, site):
+        seen[site] = (np.array(x, copy=True), orig(x, site))
+        return seen[site][1]
+
+    a._act = capture
+    out_a = a.layer(0, h[None, :], np.array([a.length]))[0]
+    vals = [seen[s][1][0] for s in range(4)]
+    pre, k, v, out_b, (q_pre, k_pre, v_pre) = b.layer_anchored(0, h, vals)
+    assert np.array_equal(nx.round_bf16(k_pre), k) and np.array_equal(nx.round_bf16(v_pre), v)
+    # given the oracle's own rounded q, k, v explicitly, the step is the same
+    b2 = OracleModel(TINY, w, precision, "S", act_scales=scales, max_seq=32)
+    b2.prefill(ids)
+    out_b2 = b2.layer_anchored(0, h, vals, qkv=(nx.round_bf16(q_pre), k, v))[3]
+    assert np.array_equal(out_b2, out_b)
+    for s in range(4):
+        assert np.allclose(pre[s], seen[s][0][0], rtol=1e-12, atol=1e-14), s
+        assert np.array_equal(b.round_site(pre[s], s), vals[s]), s
+    assert np.array_equal(k, a.k_cache[0, 8]) and np.array_equal(v, a.v_cache[0, 8])
+    assert np.allclose(out_b, out_a, rtol=1e-12, atol=1e-14)
+    # one site value moved to its neighbour on the grid changes the output
+    moved = [x.copy() for x in vals]
+    moved[3][0] = vals[3][0] * (1 + 2.0 ** -6) if vals[3][0] != 0 else 2.0 ** -9
+    c = OracleModel(TINY, w, precision, "S", act_scales=scales, max_seq=32)
+    c.prefill(ids)
+    out_c = c.layer_anchored(0, h, moved)[3]
+    assert not np.allclose(out_c, out_a, rtol=1e-9, atol=0)
