@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -14,6 +15,37 @@ using namespace hta;
 struct hta_ctx {
   Ctx c;
 };
+
+// Exchange words of hta_decode_frames_noalloc: one array per GPU, held until the process
+// ends and shared by every context on that GPU (overlapping calls on one GPU race).  2 MiB
+// covers every shape hta_create accepts at 256 frame blocks: at most 1 MiB of attention
+// partials (n_q_heads * splits <= 1024 rows of head_dim + 2 words), 256 KiB of logits and
+// under 256 KiB for the rest.
+constexpr size_t kStaticScratchBytes = 2u << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch` on each GPU, once looked up
+
+// The array's device address on the current device (`device`), looked up once per device.
+// The host-side name `scratch` is only a handle for the lookup, never a device address.
+hipError_t static_scratch(int device, char** out) {
+  *out = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[device] = static_cast<char*>(p);
+  }
+  *out = g_scratch_dev[device];
+  return hipSuccess;
+}
+}  // namespace
 
 namespace hta {
 
@@ -100,6 +132,7 @@ Layout make_layout(const hta_config& c) {
   L.off_tq = take((size_t)c.n_layers * qd * 2);
   L.off_trace = take((size_t)kTraceBlocks * (5 * c.n_layers + 1) * 8 * 4);
   L.off_fargs = take(kFrameArgsBytes);
+  L.off_fargs_s = take(kFrameArgsBytes);
   L.total = o;
   return L;
 }
@@ -200,6 +233,7 @@ static void set_pointers(Ctx& c) {
   c.taps_q = reinterpret_cast<uint16_t*>(w + L.off_tq);
   c.trace_buf = reinterpret_cast<uint32_t*>(w + L.off_trace);
   c.fargs = w + L.off_fargs;
+  c.fargs_s = w + L.off_fargs_s;
   c.tok = reinterpret_cast<int32_t*>(w + L.off_tok);
   c.px = reinterpret_cast<float*>(w + L.off_x);
   c.pu = w + L.off_u;
@@ -297,10 +331,17 @@ int hta_create(const hta_config* cfg, void* hip_stream, hta_ctx** out) {
   c.h_stage_elems = (size_t)c.cfg.max_seq * c.cfg.n_codebooks;
   if ((size_t)c.cfg.max_prefill > c.h_stage_elems) c.h_stage_elems = c.cfg.max_prefill;
   if (hipHostMalloc((void**)&c.h_stage, c.h_stage_elems * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
-      hipHostMalloc((void**)&c.h_state, sizeof(DevState), hipHostMallocDefault) != hipSuccess) {
+      hipHostMalloc((void**)&c.h_state, sizeof(DevState), hipHostMallocDefault) != hipSuccess ||
+      hipHostMalloc((void**)&c.h_status, sizeof(unsigned), hipHostMallocDefault) != hipSuccess) {
     hta_destroy(x);
     return HTA_E_HIP;
   }
+  // the static exchange array's address on this device (the current one)
+  if (static_scratch(c.device, &c.scratch_dev) != hipSuccess) {
+    hta_destroy(x);
+    return HTA_E_HIP;
+  }
+  c.static_exch_bytes = exchange_layout(c.cfg, c.frame_splits, nullptr, nullptr);
   *out = x;
   return HTA_OK;
 }
@@ -434,12 +475,26 @@ static int frame_timed_out(Ctx& c) {
   return fail(c, HTA_E_TIMEOUT, "a bounded wait of the frame kernel expired; the utterance must be reset");
 }
 
-static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out) {
+// n frames; with `no_alloc` the frame kernel exchanges through the static per-device array
+// (cleared first, launch counter included) and is launched directly, never through the graph.
+static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out, bool no_alloc) {
   int r = ready(c);
   if (r) return r;
   if (n <= 0 || !codes_out) return fail(c, HTA_E_ARG, "bad frame count or output");
   if (c.len + n > c.cfg.max_seq) return fail(c, HTA_E_CAPACITY, "KV cache full");
-  if (c.use_graph && !c.taps) {
+  const unsigned* abort_word = c.sync + 64;
+  if (no_alloc) {
+    if (!c.scratch_dev) return fail(c, HTA_E_STATE, "static scratch address not looked up");
+    if (c.static_exch_bytes > kStaticScratchBytes)
+      return fail(c, HTA_E_CAPACITY, "this shape's exchange words need " + std::to_string(c.static_exch_bytes) +
+                                         " bytes; the static scratch array holds " + std::to_string(kStaticScratchBytes));
+    Exchange xs;
+    exchange_layout(c.cfg, c.frame_splits, c.scratch_dev, &xs);
+    abort_word = xs.sync + 64;
+    // the previous call on this GPU (any context, any shape) left its tags there
+    HIPCK(launch_fill_u32(c.scratch_dev, 0u, c.static_exch_bytes / 4, c.stream), "fill");
+    for (int i = 0; i < n; ++i) HIPCK(launch_frame_args(c, c.fargs_s), "frame");
+  } else if (c.use_graph && !c.taps) {
     if ((r = ensure_graph(c)) != HTA_OK) return r;
     for (int i = 0; i < n; ++i) HIPCK(hipGraphLaunch(c.frame_exec, c.stream), "hipGraphLaunch");
   } else {
@@ -449,10 +504,9 @@ static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out) {
   const int t0 = c.t;
   HIPCK(hipMemcpyAsync(c.h_stage, c.hist + (size_t)t0 * C, (size_t)n * C * 4, hipMemcpyDeviceToHost, c.stream), "codes");
   HIPCK(hipMemcpyAsync(c.h_state, c.state, sizeof(DevState), hipMemcpyDeviceToHost, c.stream), "state");
-  unsigned aborted = 0;
-  HIPCK(hipMemcpyAsync(&aborted, c.sync + 64, sizeof(unsigned), hipMemcpyDeviceToHost, c.stream), "status");
+  HIPCK(hipMemcpyAsync(c.h_status, abort_word, sizeof(unsigned), hipMemcpyDeviceToHost, c.stream), "status");
   HIPCK(hipStreamSynchronize(c.stream), "decode sync");
-  if (aborted) return frame_timed_out(c);
+  if (*c.h_status) return frame_timed_out(c);
   std::memcpy(codes_out, c.h_stage, (size_t)n * C * 4);
   c.len += n;
   c.t += n;
@@ -464,12 +518,17 @@ static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out) {
 
 int hta_decode_frame(hta_ctx* x, int32_t* codes_out) {
   if (!x) return HTA_E_ARG;
-  return decode_n(x->c, 1, codes_out, nullptr);
+  return decode_n(x->c, 1, codes_out, nullptr, false);
 }
 
 int hta_decode_frames(hta_ctx* x, int n, int32_t* codes_out, int* n_done) {
   if (!x) return HTA_E_ARG;
-  return decode_n(x->c, n, codes_out, n_done);
+  return decode_n(x->c, n, codes_out, n_done, false);
+}
+
+int hta_decode_frames_noalloc(hta_ctx* x, int n, int32_t* codes_out, int* n_done) {
+  if (!x) return HTA_E_ARG;
+  return decode_n(x->c, n, codes_out, n_done, true);
 }
 
 int hta_force_codes(hta_ctx* x, const int32_t* codes) {
@@ -768,6 +827,7 @@ void hta_destroy(hta_ctx* x) {
   drop_graph(c);
   if (c.h_stage) (void)hipHostFree(c.h_stage);
   if (c.h_state) (void)hipHostFree(c.h_state);
+  if (c.h_status) (void)hipHostFree(c.h_status);
   if (c.own_stream && c.stream) (void)hipStreamDestroy(c.stream);
   delete[] c.layers;
   delete x;

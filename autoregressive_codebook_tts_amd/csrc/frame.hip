@@ -1411,13 +1411,22 @@ hipError_t frame_write_args(Ctx& c) {
   a.splits = c.frame_splits;
   hipError_t e = hipStreamSynchronize(c.stream);
   if (e != hipSuccess) return e;
-  return hipMemcpy(c.fargs, &a, sizeof(a), hipMemcpyHostToDevice);
+  if ((e = hipMemcpy(c.fargs, &a, sizeof(a), hipMemcpyHostToDevice)) != hipSuccess) return e;
+  if (!c.scratch_dev || !c.fargs_s) return hipSuccess;
+  // the same arguments with the exchange words in the static per-device array
+  Exchange x;
+  exchange_layout(f, c.frame_splits, c.scratch_dev, &x);
+  a.xh = x.xh; a.xqkv = x.xqkv; a.xo = x.xo; a.xa = x.xa; a.xpart = x.xpart; a.xlogits = x.xlogits;
+  a.sync = x.sync;
+  return hipMemcpy(c.fargs_s, &a, sizeof(a), hipMemcpyHostToDevice);
 }
 
-hipError_t launch_frame_persistent(Ctx& c) {
+hipError_t launch_frame_persistent(Ctx& c) { return launch_frame_args(c, c.fargs); }
+
+hipError_t launch_frame_args(Ctx& c, void* fargs) {
   const hta_config& f = c.cfg;
   const size_t lds = frame_lds_bytes();
-  void* ap = c.fargs;
+  void* ap = fargs;
   void* args[] = {&ap};
   void* fn;
   if (f.precision == HTA_FP8_E4M3) fn = f.head_dim == 128 ? (void*)k_frame<kFP8, 128> : (void*)k_frame<kFP8, 64>;

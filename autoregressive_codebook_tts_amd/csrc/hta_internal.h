@@ -59,7 +59,7 @@ struct Layout {
   size_t off_layer_table, off_xh, off_xqkv, off_xo, off_xa, off_xpart, off_xlogits, off_sync;
   // prefill scratch
   size_t off_tok, off_x, off_u, off_pqkv, off_pq, off_po, off_pgu, off_pa;
-  size_t off_taps, off_ptaps, off_tact, off_tq, off_trace, off_fargs;
+  size_t off_taps, off_ptaps, off_tact, off_tq, off_trace, off_fargs, off_fargs_s;
   int attn_splits;
 };
 
@@ -142,6 +142,12 @@ struct Ctx {
   bool trace = false;           // persistent frame kernel phase timestamps
   uint32_t* trace_buf = nullptr;  // [kTraceBlocks][5 * n_layers + 1][4]
   void* fargs = nullptr;          // the persistent kernel's arguments (device)
+  // hta_decode_frames_noalloc: the frame kernel's exchange words in the library's static
+  // per-device array (its address on this context's device) instead of the workspace
+  char* scratch_dev = nullptr;
+  size_t static_exch_bytes = 0;   // bytes of that array this shape's exchange words take
+  void* fargs_s = nullptr;        // kernel arguments pointing at it (device)
+  unsigned* h_status = nullptr;   // pinned host word: the abort flag read back after a decode
 };
 
 // Event pair around one kernel launch when per-kernel timing is on (kernel class k).
@@ -166,6 +172,7 @@ hipError_t launch_set_len(Ctx& c, int len);
 // ---------------------------------------------------------------- persistent frame (frame.hip)
 hipError_t frame_setup(Ctx& c);
 hipError_t launch_frame_persistent(Ctx& c);
+hipError_t launch_frame_args(Ctx& c, void* fargs);  // the same kernel with another argument slot
 hipError_t frame_write_args(Ctx& c);
 int frame_max_packets(const hta_config& f, int blocks);
 int frame_part_capacity();
@@ -183,5 +190,33 @@ hipError_t launch_kv_init(uint16_t* k_cache, uint16_t* v_cache, const void* k_in
                           int n_kv, int n, int max_seq, int hd, hipStream_t s);
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The frame kernel's tagged exchange words and launch counter / abort flag laid out from
+// `base`: residual, q/k/v, attention output, SiLU*mul output, attention partials (for the
+// kernel's split count), logits, then 1024 words of sync.  Returns the bytes taken.
+struct Exchange {
+  uint64_t* xh; uint64_t* xqkv; uint32_t* xo; uint32_t* xa; uint64_t* xpart; uint64_t* xlogits;
+  unsigned* sync;
+};
+inline size_t exchange_layout(const hta_config& f, int splits, char* base, Exchange* x) {
+  const size_t d = f.hidden, hd = f.head_dim, qd = (size_t)f.n_q_heads * hd, W = qd + 2 * (size_t)f.n_kv_heads * hd;
+  const size_t CV = (size_t)f.n_codebooks * f.codebook_size;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { char* r = base + o; o = align256(o + bytes); return r; };
+  char* xh = take(d * 8);
+  char* xqkv = take(W * 8);
+  char* xo = take(qd * 4);
+  char* xa = take((size_t)f.ffn * 4);
+  char* xpart = take((size_t)f.n_q_heads * splits * (hd + 2) * 8);
+  char* xlogits = take(CV * 8);
+  char* sync = take(1024 * 4);
+  if (x) {
+    x->xh = reinterpret_cast<uint64_t*>(xh); x->xqkv = reinterpret_cast<uint64_t*>(xqkv);
+    x->xo = reinterpret_cast<uint32_t*>(xo); x->xa = reinterpret_cast<uint32_t*>(xa);
+    x->xpart = reinterpret_cast<uint64_t*>(xpart); x->xlogits = reinterpret_cast<uint64_t*>(xlogits);
+    x->sync = reinterpret_cast<unsigned*>(sync);
+  }
+  return o;
+}
 
 }  // namespace hta

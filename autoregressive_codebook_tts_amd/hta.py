@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhta.so")
 
 HTA_OK, HTA_DONE = 0, 1
+HTA_E_ARG, HTA_E_STATE, HTA_E_CAPACITY, HTA_E_RANGE, HTA_E_UNSUPPORTED, HTA_E_HIP, HTA_E_TIMEOUT = range(-1, -8, -1)
 ERRORS = {-1: "HTA_E_ARG", -2: "HTA_E_STATE", -3: "HTA_E_CAPACITY", -4: "HTA_E_RANGE", -5: "HTA_E_UNSUPPORTED",
           -6: "HTA_E_HIP", -7: "HTA_E_TIMEOUT"}
 HTA_BF16, HTA_FP8_E4M3 = 0, 1
@@ -65,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "hta_prefill": (I, [P, P, I]),
             "hta_decode_frame": (I, [P, P]),
             "hta_decode_frames": (I, [P, I, P, P]),
+            "hta_decode_frames_noalloc": (I, [P, I, P, P]),
             "hta_reset": (I, [P, I]),
             "hta_force_codes": (I, [P, P]),
             "hta_read_tap": (I, [P, I, I, P, S]),
@@ -216,6 +218,18 @@ class Hta:
         out = np.zeros((n, self.C), dtype=np.int32)
         nd = ctypes.c_int(0)
         rc = self._check(lib().hta_decode_frames(self.ctx, n, _ptr(out), ctypes.byref(nd)), "hta_decode_frames")
+        return out, rc == HTA_DONE
+
+    def decode_frames_noalloc(self, n: int, out=None):
+        """hta_decode_frames_noalloc: the exchange words in the library's static per-GPU array.
+        `out` (int32 [n][C], C-contiguous) is filled in place when given."""
+        if out is None:
+            out = np.zeros((n, self.C), dtype=np.int32)
+        if out.dtype != np.int32 or out.shape != (n, self.C) or not out.flags.c_contiguous:
+            raise ValueError("out must be a C-contiguous int32 array of shape (n, C)")
+        nd = ctypes.c_int(0)
+        rc = self._check(lib().hta_decode_frames_noalloc(self.ctx, n, _ptr(out), ctypes.byref(nd)),
+                         "hta_decode_frames_noalloc")
         return out, rc == HTA_DONE
 
     def reset(self, keep_len: int = 0) -> None:

@@ -130,6 +130,19 @@ int hta_decode_frame(hta_ctx* ctx, int32_t* codes_out);
  * number of steps that ended in the done state. */
 int hta_decode_frames(hta_ctx* ctx, int n, int32_t* codes_out, int* n_done);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): hta_decode_frames with the same arguments, results
+ * and errors, allocating nothing.  The decode frame kernel's exchange words (tagged
+ * residual, q/k/v, attention output and partials, SiLU*mul output, logits) and its launch
+ * counter / abort flag live in a static device array of the library, 2 MiB per GPU, held
+ * until the process ends, instead of the workspace; each call first clears the part its
+ * shape uses, then launches the kernel directly (no graph is instantiated).  Every context
+ * on one GPU shares that array: calls that overlap in time on one GPU (two streams, two
+ * threads) race and must be serialised by the caller.  HTA_E_CAPACITY when the shape's
+ * exchange words exceed the array (no shape hta_create accepts on a 256-CU device does);
+ * HTA_E_TIMEOUT as for hta_decode_frames. */
+int hta_decode_frames_noalloc(hta_ctx* ctx, int n, int32_t* codes_out, int* n_done);
+
 /* Start a new utterance: keep the KV of positions [0, keep_len) (prefix reuse,
  * FlashRT page, section 4) and reset the delay state.  keep_len = 0 is a cold
  * start; keep_len must not exceed the current length. */
