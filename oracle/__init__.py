@@ -29,6 +29,13 @@ Parity status of each function (what pins it, in the CPU test suite):
 * delay.*                      -- brute-force enumeration over every EOC step
                                   against an independent restatement; undelay
                                   inverts delay
+* sampling.philox4x32_10       -- the generator's published known-answer vectors;
+                                  array form equals the scalar form
+* sampling.uniform / draw      -- 60000 draws per case follow torch.softmax over the
+                                  allowed ids (chi-square, three temperatures, EOS
+                                  allowed or not); a hand-worked inversion including
+                                  an exact boundary; tiny-temperature argmax, NaN and
+                                  single-id limits; the delay rule's forced codes
 * model.calibrate              -- the per-site maxima equal those the torch
                                   formulation records on the same rows before
                                   rounding (1e-12; float32 scales bit-equal), and
