@@ -531,6 +531,19 @@ int hta_decode_frames_noalloc(hta_ctx* x, int n, int32_t* codes_out, int* n_done
   return decode_n(x->c, n, codes_out, n_done, true);
 }
 
+int hta_set_sampling(hta_ctx* x, float temperature, uint64_t seed) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  if (!(temperature >= 0.0f) || !std::isfinite(temperature)) return fail(c, HTA_E_ARG, "temperature must be finite and >= 0");
+  const size_t logit_bytes = (size_t)c.cfg.n_codebooks * c.cfg.codebook_size * sizeof(float);
+  if (temperature > 0.0f && logit_bytes > frame_sample_capacity())
+    return fail(c, HTA_E_UNSUPPORTED, "n_codebooks * codebook_size logits exceed the sampling head's LDS");
+  c.temperature = temperature;
+  c.seed = seed;
+  if (c.ws) HIPCK(frame_write_args(c), "frame arguments");
+  return HTA_OK;
+}
+
 int hta_force_codes(hta_ctx* x, const int32_t* codes) {
   if (!x) return HTA_E_ARG;
   Ctx& c = x->c;
@@ -683,6 +696,8 @@ int hta_calibrate(hta_ctx* x, const int32_t* tokens, int P, int n_frames, const 
   HIPCK(launch_set_len(c, P), "set len");
   // the frames run on the decode frame kernel itself, recording each site's maximum
   c.frame_record = true;
+  const float temperature = c.temperature;  // calibration is a greedy run
+  c.temperature = 0.0f;
   HIPCK(frame_write_args(c), "frame arguments");
   hipError_t e = hipSuccess;
   for (int fr = 0; fr < n_frames && e == hipSuccess; ++fr) {
@@ -690,6 +705,7 @@ int hta_calibrate(hta_ctx* x, const int32_t* tokens, int P, int n_frames, const 
     if (e == hipSuccess && forced) e = launch_set_prev(c, forced + (size_t)fr * f.n_codebooks);
   }
   c.frame_record = false;
+  c.temperature = temperature;
   const hipError_t e2 = frame_write_args(c);  // synchronises the stream first
   if (e != hipSuccess) return hip_fail(c, e, "calibration frame");
   if (e2 != hipSuccess) return hip_fail(c, e2, "frame arguments");

@@ -74,6 +74,8 @@ struct FrameArgs {
   unsigned* sync;            // [0] launch count, [64] abort flag
   DevState* st;
   int32_t* hist;
+  float temperature;         // 0: greedy argmax; > 0: categorical draw at this temperature
+  uint32_t seed_lo, seed_hi; // the draw's 64-bit seed
 };
 
 // The kernel reads FrameArgs through the constant address space: every field is a
@@ -100,6 +102,83 @@ __device__ __forceinline__ const float* layer_scales(CFA& a, int layer, int i) {
 // the static activation scales, likewise (uniform index, scalar read)
 __device__ __forceinline__ float act_scale(CFA& a, int site) {
   return ((const __attribute__((address_space(4))) float*)a.act_scales)[site];
+}
+
+// ---------------------------------------------------------------- sampling head
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds over the counter
+// (c0, c1, 0, 0) with the key (k0, k1) advanced by the two Weyl constants between rounds;
+// each round multiplies words 0 and 2 by the round constants into 64-bit products.  The
+// draw's uniform is the top 24 bits of output word 0, exact in fp32, in [0, 1).
+__device__ __forceinline__ float philox_uniform(uint32_t k0, uint32_t k1, uint32_t c0, uint32_t c1) {
+  uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, x0), lo0 = 0xD2511F53u * x0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, x2), lo1 = 0xCD9E8D57u * x2;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+  }
+  return (float)(x0 >> 8) * (1.0f / 16777216.0f);
+}
+
+// One wave draws codebook k's code from its fp32 logits z[V] (LDS): weights
+// exp((z_i - m) / T) over the allowed finite logits, m their maximum; the draw is the
+// first id whose running weight (in id order) exceeds u times the total.  Lane l holds
+// the contiguous ids [l * c, l * c + c); the running weight is the lane's sequential sum
+// added to an inclusive scan of the lane sums.  Returns the id in every lane.
+__device__ __forceinline__ int sample_codebook(const float* z, int V, int k, int bos, int eos, float T, float u) {
+  const int lane = threadIdx.x & 63;
+  const int c = (V + kWave - 1) / kWave;
+  const int i0 = lane * c, i1 = min(i0 + c, V);
+  auto weight_ok = [&](int i, float v) { return ((i < bos) || (k == 0 && i == eos)) && v == v; };
+  float mx = -INFINITY;
+  for (int i = i0; i < i1; ++i) {
+    const float v = z[i];
+    if (weight_ok(i, v)) mx = fmaxf(mx, v);
+  }
+  mx = wave_max(mx);
+  if (!(mx > -INFINITY)) return 0;  // no allowed finite logit: the lowest allowed id, as the greedy path
+  float s = 0.0f;
+  for (int i = i0; i < i1; ++i) {
+    const float v = z[i];
+    if (weight_ok(i, v)) s += expf((v - mx) / T);
+  }
+  float incl = s;
+#pragma unroll
+  for (int dd = 1; dd < kWave; dd <<= 1) {
+    const float o = __shfl_up(incl, dd, kWave);
+    if (lane >= dd) incl += o;
+  }
+  // (the shuffle runs in every lane: a lane left out of it would read as zero to its neighbour)
+  const float prev = __shfl_up(incl, 1, kWave);
+  const float excl = lane == 0 ? 0.0f : prev;
+  const float target = u * __shfl(incl, kWave - 1, kWave);
+  const uint64_t hit = __ballot(incl > target);
+  // the lane whose share holds the target; past the end (rounding), the last lane with weight
+  const int owner = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(__ballot(s > 0.0f));
+  int pick = -1, last = -1;
+  if (lane == owner) {
+    float acc = excl;
+    for (int i = i0; i < i1; ++i) {
+      const float v = z[i];
+      if (!weight_ok(i, v)) continue;
+      const float e = expf((v - mx) / T);
+      if (e > 0.0f) last = i;
+      acc += e;
+      if (acc > target && e > 0.0f) {
+        pick = i;
+        break;
+      }
+    }
+    if (pick < 0) pick = last;
+  }
+  return __shfl(pick, owner, kWave);
 }
 
 // ---------------------------------------------------------------- tagged exchange words
@@ -1290,6 +1369,10 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
   ring_drain();  // every packet was consumed by the head phase; nothing is left in flight
   const unsigned tag_logits = base + (unsigned)n_phases;
   if (blockIdx.x != 0) return;
+  // every wave of the block has drained its ring: a sampling run keeps the logits there
+  __syncthreads();
+  const bool sampling = a.temperature > 0.0f;
+  float* lgs = reinterpret_cast<float*>(smem_raw);  // [C][V] logits (sampling)
 
   // ---- block 0: per-codebook argmax over the allowed ids, delay rule, state advance
   __shared__ int sh_arg[kMaxCodebooks];
@@ -1329,6 +1412,7 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
       if (i < a.V) {
         const float v = __uint_as_float((uint32_t)lw[q]);
         *gpw(a.logits_out + (size_t)k * a.V + i) = v;
+        if (sampling) lgs[(size_t)k * a.V + i] = v;
         const bool allowed = (i < a.bos) || (k == 0 && i == a.eos);
         // a NaN logit never wins: with every allowed logit NaN the lowest allowed id is
         // chosen, so the code stays a valid embedding row
@@ -1352,6 +1436,15 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     sh_arg[tid] = (v1 > v0 || (v1 == v0 && i1 < i0)) ? i1 : i0;
   }
   if (!block_ok(pl.ok, &okf)) return;
+  if (sampling) {  // the draw replaces the argmax (block_ok's barriers ordered the LDS logits)
+    const int t = sh_state[1];
+    for (int k = wv; k < a.C; k += kFW) {
+      const float u = philox_uniform(a.seed_lo, a.seed_hi, (uint32_t)t, (uint32_t)k);
+      const int id = sample_codebook(lgs + (size_t)k * a.V, a.V, k, a.bos, a.eos, a.temperature, u);
+      if (lane == 0) sh_arg[k] = id;
+    }
+    __syncthreads();
+  }
   if (tid == 0) {
     DevState* st = a.st;
     const int t = sh_state[1], eoc = sh_state[2];
@@ -1409,6 +1502,9 @@ hipError_t frame_write_args(Ctx& c) {
   a.trace = c.trace ? c.trace_buf : nullptr;
   a.sync = c.sync; a.st = c.state; a.hist = c.hist;
   a.splits = c.frame_splits;
+  a.temperature = c.temperature;
+  a.seed_lo = (uint32_t)c.seed;
+  a.seed_hi = (uint32_t)(c.seed >> 32);
   hipError_t e = hipStreamSynchronize(c.stream);
   if (e != hipSuccess) return e;
   if ((e = hipMemcpy(c.fargs, &a, sizeof(a), hipMemcpyHostToDevice)) != hipSuccess) return e;
@@ -1480,5 +1576,6 @@ int frame_max_packets(const hta_config& f, int blocks) {
   return (int)m;
 }
 int frame_part_capacity() { return kPartMax; }
+size_t frame_sample_capacity() { return (size_t)kFW * kRD * 1024; }
 
 }  // namespace hta

@@ -148,6 +148,8 @@ struct Ctx {
   size_t static_exch_bytes = 0;   // bytes of that array this shape's exchange words take
   void* fargs_s = nullptr;        // kernel arguments pointing at it (device)
   unsigned* h_status = nullptr;   // pinned host word: the abort flag read back after a decode
+  float temperature = 0.0f;       // 0: greedy; > 0: the head draws at this temperature
+  uint64_t seed = 0;              // the draw's seed
 };
 
 // Event pair around one kernel launch when per-kernel timing is on (kernel class k).
@@ -176,6 +178,7 @@ hipError_t launch_frame_args(Ctx& c, void* fargs);  // the same kernel with anot
 hipError_t frame_write_args(Ctx& c);
 int frame_max_packets(const hta_config& f, int blocks);
 int frame_part_capacity();
+size_t frame_sample_capacity();  // bytes of LDS that hold a sampling frame's logits
 
 // ---------------------------------------------------------------- launchers (prefill.hip)
 hipError_t prefill_setup();  // kernel attributes of the prefill GEMM (once per context)

@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "hta_decode_frames_noalloc": (I, [P, I, P, P]),
             "hta_reset": (I, [P, I]),
             "hta_force_codes": (I, [P, P]),
+            "hta_set_sampling": (I, [P, ctypes.c_float, ctypes.c_uint64]),
             "hta_read_tap": (I, [P, I, I, P, S]),
             "hta_calibrate": (I, [P, P, I, I, P, P]),
             "hta_layer_step": (I, [P, I, I, P, P, P]),
@@ -234,6 +235,11 @@ class Hta:
 
     def reset(self, keep_len: int = 0) -> None:
         self._check(lib().hta_reset(self.ctx, keep_len), "hta_reset")
+
+    def set_sampling(self, temperature: float, seed: int = 0) -> None:
+        """hta_set_sampling: 0 = greedy argmax; > 0 = categorical draw keyed by (seed, step, codebook)."""
+        self._check(lib().hta_set_sampling(self.ctx, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF),
+                    "hta_set_sampling")
 
     def force_codes(self, codes) -> None:
         c = np.ascontiguousarray(codes, dtype=np.int32)

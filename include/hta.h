@@ -143,6 +143,20 @@ int hta_decode_frames(hta_ctx* ctx, int n, int32_t* codes_out, int* n_done);
  * HTA_E_TIMEOUT as for hta_decode_frames. */
 int hta_decode_frames_noalloc(hta_ctx* ctx, int n, int32_t* codes_out, int* n_done);
 
+/* Decode policy of the head (FlashRT page, section 4 "Sampling policy", section 5 and
+ * section 8 "Decode policy"): temperature 0 (the default) is the greedy argmax;
+ * temperature > 0 replaces the argmax of every codebook not forced by the delay rule with
+ * a categorical draw: weights exp((z_i - m) / temperature) over the codebook's allowed ids
+ * (the greedy path's set; NaN logits weigh nothing), m their largest fp32 logit, and the
+ * first id (in id order) whose running weight exceeds u times the total.  u is a uniform
+ * in [0, 1): the top 24 bits of word 0 of Philox4x32-10 (Salmon et al., SC'11) keyed by
+ * `seed` (low 32 bits first) at counter (step t of the utterance, codebook k, 0, 0), so a
+ * fixed seed repeats the same draws.  The draw runs in the frame kernel's head epilogue,
+ * in the same launch and graph as the argmax; no top-p or top-k.  Holds until changed;
+ * hta_calibrate always runs greedy.  HTA_E_ARG for a negative or non-finite temperature;
+ * HTA_E_UNSUPPORTED when n_codebooks * codebook_size fp32 logits exceed 120 KiB. */
+int hta_set_sampling(hta_ctx* ctx, float temperature, uint64_t seed);
+
 /* Start a new utterance: keep the KV of positions [0, keep_len) (prefix reuse,
  * FlashRT page, section 4) and reset the delay state.  keep_len = 0 is a cold
  * start; keep_len must not exceed the current length. */

@@ -16,6 +16,8 @@ import numpy as np
 import synthetic as S
 from autoregressive_codebook_tts_amd import hta
 from oracle import numerics as nx
+from oracle import sampling as smp
+from oracle.delay import DelayState
 from oracle.model import OracleModel
 
 HIDDEN_TOL = {"bf16": 2e-2, "fp8": 6e-2}
@@ -231,3 +233,48 @@ def check_layer_sites(ctx, oracle, layer, h_in, h_out, acts, q_tap, pos, what):
     upd = rel_l2(h_out - h_in, h_o - h_in)
     assert upd <= 1e-5, f"{what} layer {layer}: output from the GPU's own site values off by {upd:.3e}"
     return flips, qkv_flips, upd
+
+
+# ----------------------------------------------------------------------------- sampling head
+# The kernel's fp32 error relative to the total weight: a lane's sequential sum of at most
+# 17 weights, six scan additions, the exponentials and the product u * total, each within
+# 2^-24 relative.  A draw whose target lies within this of a cumulative boundary may fall
+# on either side of it.
+SAMPLE_BAND = 2e-6
+
+
+def sample_neighbours(z, allowed, T, u):
+    """Ids on both sides of the cumulative boundary nearest to u * total."""
+    wts = smp.weights(z, allowed, T)
+    c = np.cumsum(wts)
+    target = u * c[-1]
+    pos = np.nonzero(wts > 0)[0]
+    j = int(np.argmin(np.abs(c[pos[:-1]] - target)))
+    return {int(pos[j]), int(pos[j + 1])}
+
+
+def sampled_run(ctx, SH, n, T, seed):
+    """Decode n frames one at a time; check every draw against the oracle on the GPU's logits."""
+    st = DelayState(SH.n_codebooks, SH.codebook_size, SH.bos_id, SH.eos_id)
+    codes_all, n_band, n_draws = [], 0, 0
+    for f in range(n):
+        st.begin_frame()
+        codes, _ = ctx.decode_frame()
+        z = ctx.tap_logits().reshape(SH.n_codebooks, SH.codebook_size).astype(np.float64)
+        want, margins = smp.choose_sampled(st, z, T, seed)
+        for k in range(SH.n_codebooks):
+            if np.isinf(margins[k]):  # forced by the delay rule (or no finite logit)
+                assert codes[k] == want[k], (f, k, codes[k], want[k])
+                continue
+            n_draws += 1
+            if margins[k] > SAMPLE_BAND:
+                assert codes[k] == want[k], (f, k, int(codes[k]), int(want[k]), float(margins[k]))
+            else:
+                n_band += 1
+                u = float(smp.uniform(seed, st.t, k))
+                assert int(codes[k]) in sample_neighbours(z[k], st.allowed_mask(k), T, u), (f, k)
+        st.finish(codes)
+        codes_all.append(codes.copy())
+    return np.array(codes_all), n_draws, n_band
+
+

@@ -39,7 +39,8 @@ import pytest
 import synthetic as S
 from autoregressive_codebook_tts_amd import hta
 from gpu_common import (COS_MIN, FLIP_LOG, HEAD_BAND, HIDDEN_TOL, MARGIN, allowed_mask, bf16_values,
-                        check_layer_sites, check_site, cosines, gpu_context, kv_rows as _kv_rows, rel_l2, top2_margin)
+                        check_layer_sites, check_site, cosines, gpu_context, kv_rows as _kv_rows, rel_l2, sampled_run,
+                        top2_margin)
 from oracle import numerics as nx
 from oracle.model import OracleModel, calibrate
 
@@ -363,6 +364,21 @@ def test_full_decode_is_deterministic(request, precision):
     assert np.array_equal(runs[0][1], runs[1][1]), "hidden state differs between identical runs"
     assert np.array_equal(runs[0][2], runs[1][2]), "logits differ between identical runs"
     _say(f"[full] {precision} decode: two identical runs bit-identical")
+
+
+def test_full_fp8_sampling_head(gpu_fp8):
+    """The sampling head at the 36-layer shape: every draw of 12 frames equals the sampling
+    oracle's on the GPU's own logits (a neighbour within the fp32 band)."""
+    prompt = S.token_ids(S.SEEDS["full_prompt"], 13, SH.text_vocab)
+    try:
+        gpu_fp8.reset(0)
+        gpu_fp8.set_sampling(1.0, 0xFEEDFACECAFEBEEF)
+        gpu_fp8.prefill(prompt)
+        _, n_draws, n_band = sampled_run(gpu_fp8, SH, 12, 1.0, 0xFEEDFACECAFEBEEF)
+    finally:
+        gpu_fp8.set_sampling(0.0, 0)
+    _say(f"[full] fp8 sampling: {n_draws} draws checked, {n_band} within the fp32 band")
+    assert n_draws >= 12 * 8 - 28 - 8 and n_band <= 3
 
 
 # ----------------------------------------------------------------------------- chunked prefill
