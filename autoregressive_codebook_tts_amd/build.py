@@ -6,7 +6,7 @@ import shutil
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["api.hip", "prefill.hip", "load.hip", "frame.hip"]
+SOURCES = ["api.hip", "prefill.hip", "load.hip", "frame.hip", "stream.hip"]
 HEADERS = ["device_common.h", "hta_internal.h"]
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
          # keep hipcc from emitting packed fp32 VALU ops

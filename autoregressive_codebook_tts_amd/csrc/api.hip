@@ -828,6 +828,11 @@ int hta_set_option(hta_ctx* x, int option, int value) {
     HIPCK(frame_write_args(c), "frame arguments");
     return HTA_OK;
   }
+  if (option == HTA_OPT_FORCE_TIMEOUT) {
+    c.force_timeout = value != 0;
+    HIPCK(frame_write_args(c), "frame arguments");
+    return HTA_OK;
+  }
   if (option == HTA_OPT_PREFILL_TAP_LAYER) {
     if (value < 0 || value >= c.cfg.n_layers) return fail(c, HTA_E_ARG, "tap layer out of range");
     c.prefill_tap_layer = value;

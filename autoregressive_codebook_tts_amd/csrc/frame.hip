@@ -76,6 +76,7 @@ struct FrameArgs {
   int32_t* hist;
   float temperature;         // 0: greedy argmax; > 0: categorical draw at this temperature
   uint32_t seed_lo, seed_hi; // the draw's 64-bit seed
+  uint32_t input_tag_skew;   // 0; otherwise added to layer 0's attention input tag (a wait that cannot end)
 };
 
 // The kernel reads FrameArgs through the constant address space: every field is a
@@ -1273,8 +1274,11 @@ __global__ __launch_bounds__(kFT) void k_frame(const FrameArgs* ap_generic) {
     uint64_t* xh = launder(a.xh);
     if (kind == kATTN) {
       const LayerW L = a.layers[layer];
-      // inputs: the QKV phase (tag - 1); partials and output carry this phase's tag
-      if (!attn_task<P, HD>(a, L, layer, pos, tag - 1u, tag, tag, sm, abort_flag, &okf)) { ring_drain(); return; }
+      // inputs: the QKV phase (tag - 1); partials and output carry this phase's tag.  (A
+      // forced-timeout run skews layer 0's input tag, the frame's first polled one: no
+      // block writes it.)
+      const unsigned tag_in = layer == 0 ? tag - 1u + a.input_tag_skew : tag - 1u;
+      if (!attn_task<P, HD>(a, L, layer, pos, tag_in, tag, tag, sm, abort_flag, &okf)) { ring_drain(); return; }
       __syncthreads();  // the task's scratch is the next phase's input vector and partials
       if (tid < kPartMax / 4) reinterpret_cast<float4*>(part)[tid] = zero4;
       trace_mark(a, n_phases, phase, 3);
@@ -1503,6 +1507,7 @@ hipError_t frame_write_args(Ctx& c) {
   a.sync = c.sync; a.st = c.state; a.hist = c.hist;
   a.splits = c.frame_splits;
   a.temperature = c.temperature;
+  a.input_tag_skew = c.force_timeout ? 0x40000000u : 0u;
   a.seed_lo = (uint32_t)c.seed;
   a.seed_hi = (uint32_t)(c.seed >> 32);
   hipError_t e = hipStreamSynchronize(c.stream);

@@ -149,6 +149,7 @@ struct Ctx {
   void* fargs_s = nullptr;        // kernel arguments pointing at it (device)
   unsigned* h_status = nullptr;   // pinned host word: the abort flag read back after a decode
   float temperature = 0.0f;       // 0: greedy; > 0: the head draws at this temperature
+  bool force_timeout = false;     // frames wait for an input no block writes (recovery tests)
   uint64_t seed = 0;              // the draw's seed
 };
 

@@ -30,6 +30,7 @@ OPT_USE_GRAPH = 0
 OPT_TAPS = 2
 OPT_PREFILL_TAP_LAYER = 3
 OPT_TRACE = 4
+OPT_FORCE_TIMEOUT = 5
 SITES_PER_LAYER = 4
 
 LAYER_TENSORS = ("g_attn", "wq", "wk", "wv", "g_q", "g_k", "wo", "g_mlp", "wg", "wu", "wd")
@@ -74,6 +75,10 @@ def lib() -> ctypes.CDLL:
             "hta_calibrate": (I, [P, P, I, I, P, P]),
             "hta_layer_step": (I, [P, I, I, P, P, P]),
             "hta_undelay": (I, [P, I, I, I, P, P]),
+            "hta_stream_create": (I, [I, I, I, I, I, I, ctypes.POINTER(P)]),
+            "hta_stream_push": (I, [P, P, I, P, I, P, P]),
+            "hta_stream_finish": (I, [P, P, I, P]),
+            "hta_stream_destroy": (None, [P]),
             "hta_set_option": (I, [P, I, I]),
             "hta_time_kernels": (I, [P, I, P, I]),
             "hta_destroy": (None, [P]),
@@ -123,6 +128,56 @@ def undelay(step_codes: np.ndarray, eos: int = 1025) -> np.ndarray:
 
 
 _open = weakref.WeakSet()  # live contexts, closed by close_all()
+
+
+STREAM_RUNNING, STREAM_DONE, STREAM_STOPPED, STREAM_CAPPED = 0, 1, 2, 3
+
+
+class Streamer:
+    """hta_stream_*: incremental un-delay, chunked hand-off and the repeated-code stop guard."""
+
+    def __init__(self, n_codebooks: int = 8, bos: int = 1024, eos: int = 1025, chunk_frames: int = 25,
+                 guard_window: int = 50, guard_max_period: int = 4):
+        self.C = n_codebooks
+        self.s = ctypes.c_void_p()
+        rc = lib().hta_stream_create(n_codebooks, bos, eos, chunk_frames, guard_window, guard_max_period,
+                                     ctypes.byref(self.s))
+        if rc != HTA_OK:
+            raise HtaError(rc, "hta_stream_create")
+        self.status = STREAM_RUNNING
+
+    def push(self, step_codes, max_frames: int = 1 << 16) -> np.ndarray:
+        steps = np.ascontiguousarray(step_codes, dtype=np.int32).reshape(-1, self.C)
+        out = np.zeros((max_frames, self.C), dtype=np.int32)
+        n, st = ctypes.c_int(0), ctypes.c_int(0)
+        rc = lib().hta_stream_push(self.s, _ptr(steps), steps.shape[0], _ptr(out), max_frames, ctypes.byref(n),
+                                   ctypes.byref(st))
+        if rc != HTA_OK:
+            raise HtaError(rc, "hta_stream_push")
+        self.status = st.value
+        return out[: n.value].copy()
+
+    def finish(self, max_frames: int = 1 << 16) -> np.ndarray:
+        out = np.zeros((max_frames, self.C), dtype=np.int32)
+        n = ctypes.c_int(0)
+        rc = lib().hta_stream_finish(self.s, _ptr(out), max_frames, ctypes.byref(n))
+        if rc != HTA_OK:
+            raise HtaError(rc, "hta_stream_finish")
+        if self.status == STREAM_RUNNING:
+            self.status = STREAM_CAPPED
+        return out[: n.value].copy()
+
+    def close(self) -> None:
+        if self.s:
+            lib().hta_stream_destroy(self.s)
+            self.s = ctypes.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False
 
 
 def close_all() -> None:

@@ -228,6 +228,34 @@ int hta_layer_step(hta_ctx* ctx, int layer, int kv_len, const void* k_init, cons
  * room for T*C codes; *n_frames receives n. */
 int hta_undelay(const int32_t* step_codes, int T, int n_codebooks, int eos_id, int32_t* frames_out, int* n_frames);
 
+/* Streaming hand-off of one utterance (host only; FlashRT page, section 4: a streaming
+ * generator whose output equals the one-shot output; Performance section: a deterministic
+ * repeated-code stop guard ends runs that never emit EOC before the generation cap).
+ * The caller pushes the delayed step codes as it decodes them; the stream un-delays them
+ * (frame f is complete once step f + C - 1 is in; with EOC at step e the frames are
+ * 0..e-1) and hands out complete frames in whole chunks of chunk_frames while the
+ * utterance runs, and all remaining complete frames once it has ended.  The frames handed
+ * out, concatenated, equal hta_undelay of every pushed step.
+ * Stop guard (the page gives no rule; this reading): after frame f completes, if the
+ * last guard_window frames repeat with a period p <= guard_max_period (frame g equals
+ * frame g - p for every g of the window after its first p), the stream stops with frames
+ * 0..f; guard_window 0 disables it.  Steps pushed after the end are ignored. */
+typedef struct hta_stream hta_stream;
+enum { HTA_STREAM_RUNNING = 0, HTA_STREAM_DONE = 1, HTA_STREAM_STOPPED = 2, HTA_STREAM_CAPPED = 3 };
+/* HTA_E_ARG for n_codebooks outside 1..64, chunk_frames < 1 or negative guard values. */
+int hta_stream_create(int n_codebooks, int bos_id, int eos_id, int chunk_frames, int guard_window,
+                      int guard_max_period, hta_stream** out);
+/* Push n_steps steps (host int32 [n_steps][C]); writes up to max_frames frames (host int32
+ * [max_frames][C]) to frames_out and their count to *n_frames; frames beyond max_frames stay
+ * queued for the next call (push 0 steps to drain).  *status (may be NULL) receives
+ * HTA_STREAM_RUNNING, _DONE (EOC: every frame before it is complete) or _STOPPED (guard). */
+int hta_stream_push(hta_stream* s, const int32_t* step_codes, int n_steps, int32_t* frames_out, int max_frames,
+                    int* n_frames, int* status);
+/* The caller ends a running utterance (its generation cap): the stream becomes
+ * HTA_STREAM_CAPPED and hands out every remaining complete frame. */
+int hta_stream_finish(hta_stream* s, int32_t* frames_out, int max_frames, int* n_frames);
+void hta_stream_destroy(hta_stream* s);
+
 /* Kernel timing for the benchmark: decode n_frames frames, each one launch of the
  * decode frame kernel bracketed by a HIP event pair on the context's stream;
  * avg_us_out (host, n_classes floats) receives the average device time per launch
@@ -247,8 +275,13 @@ int hta_time_kernels(hta_ctx* ctx, int n_frames, float* avg_us_out, int n_classe
  * HTA_TAP_ACT and HTA_TAP_PREFILL_LAYER (frames then launch without the graph);
  * HTA_OPT_PREFILL_TAP_LAYER selects the prefill layer (0..n_layers-1, else
  * HTA_E_ARG).  HTA_OPT_TRACE (default 0) records the frame kernel's phase
- * timestamps (HTA_TAP_TRACE).  Value 1 is unused. */
-enum { HTA_OPT_USE_GRAPH = 0, HTA_OPT_TAPS = 2, HTA_OPT_PREFILL_TAP_LAYER = 3, HTA_OPT_TRACE = 4 };
+ * timestamps (HTA_TAP_TRACE).  HTA_OPT_FORCE_TIMEOUT (default 0; for tests of the
+ * recovery path) makes every frame's first input wait for a tag no block writes: the
+ * bounded wait runs out (0.5 s), every block leaves the kernel, and the decode call
+ * returns HTA_E_TIMEOUT with the exchange words cleared; after setting it back to 0,
+ * hta_reset starts a clean utterance.  Value 1 is unused. */
+enum { HTA_OPT_USE_GRAPH = 0, HTA_OPT_TAPS = 2, HTA_OPT_PREFILL_TAP_LAYER = 3, HTA_OPT_TRACE = 4,
+       HTA_OPT_FORCE_TIMEOUT = 5 };
 int hta_set_option(hta_ctx* ctx, int option, int value);
 
 void hta_destroy(hta_ctx* ctx);

@@ -18,6 +18,15 @@ reading:
 * the utterance is done once codebook 7 has emitted EOS, i.e. after step e + 7;
 * e is taken from the code of codebook 0 that is fed back into the next
   frame, so forcing codes (teacher forcing) drives the same bookkeeping.
+
+The same page's Performance section mentions a deterministic repeated-code stop guard that
+ends pathological runs without EOC before the generation cap, and section 4 a streaming
+generator whose output equals the one-shot output; neither gives a rule.  The reading
+taken here (``repeat_guard``): the guard watches the complete (un-delayed) frames and fires
+at the first frame f that ends a window of ``window`` frames repeating with some period
+p <= ``max_period`` (frame g equals frame g - p for every g of the window after its first
+p); the frames up to and including f are the output.  Streaming emits the un-delayed frames
+in chunks as they complete; the chunks concatenated equal ``undelay`` of all the steps.
 """
 from __future__ import annotations
 
@@ -103,3 +112,15 @@ def find_eoc(step_codes, eos: int = 1025):
     col = np.asarray(step_codes)[:, 0]
     hits = np.nonzero(col == eos)[0]
     return int(hits[0]) if hits.size else None
+
+
+def repeat_guard(frames, window: int, max_period: int):
+    """First frame index f at which the last ``window`` complete frames repeat with some
+    period p in 1..max_period, or None."""
+    frames = np.asarray(frames, dtype=np.int64)
+    for f in range(window - 1, frames.shape[0]):
+        w = frames[f - window + 1: f + 1]
+        for p in range(1, max_period + 1):
+            if p < window and all(np.array_equal(w[g], w[g - p]) for g in range(p, window)):
+                return f
+    return None

@@ -335,3 +335,72 @@ def test_layer_step_needs_a_one_layer_context(w):
         assert e.value.code == -5  # HTA_E_UNSUPPORTED: two layers
     finally:
         ctx.close()
+
+
+def test_streamed_utterance_equals_one_shot(w, prompt):
+    """Steps decoded on the GPU in chunks of 5 and pushed through the host streamer come out
+    as the one-shot un-delay of the whole run, in whole chunks of 4 frames."""
+    from oracle.delay import find_eoc, undelay
+    with gpu_context(SH, w, "bf16") as ctx, hta.Streamer(SH.n_codebooks, SH.bos_id, SH.eos_id, 4, 50, 4) as st:
+        ctx.prefill(prompt)
+        steps, out = [], []
+        for _ in range(8):
+            codes, _ = ctx.decode_frames(5)
+            steps.append(codes)
+            out.append(st.push(codes))
+            assert len(out[-1]) % 4 == 0
+        out.append(st.finish())
+        steps = np.concatenate(steps)
+        assert np.array_equal(np.concatenate(out), undelay(steps, find_eoc(steps)))
+
+
+def test_forced_timeout_returns_timeout_and_reset_recovers(w, prompt):
+    """Every bounded wait of the frame kernel ends: with the first input of each frame made
+    unreachable from the host, the graph path, the direct launch and the allocation-free
+    entry point each return HTA_E_TIMEOUT (after the 0.5 s bound); once the option is off,
+    a reset and a fresh utterance are bit-identical to a clean context's."""
+    ref = gpu_context(SH, w, "bf16")
+    ctx = gpu_context(SH, w, "bf16")
+    try:
+        ref.prefill(prompt)
+        want = ref.decode_frames(6)[0]
+        h_want = ref.tap_hidden()
+        ctx.prefill(prompt)
+        ctx.decode_frames(2)
+        ctx.set_option(hta.OPT_FORCE_TIMEOUT, 1)
+        for use_graph, call in ((1, lambda: ctx.decode_frames(1)), (0, lambda: ctx.decode_frame()),
+                                (1, lambda: ctx.decode_frames_noalloc(1))):
+            ctx.set_option(hta.OPT_USE_GRAPH, use_graph)
+            with pytest.raises(hta.HtaError) as e:
+                call()
+            assert e.value.code == hta.HTA_E_TIMEOUT
+        ctx.set_option(hta.OPT_FORCE_TIMEOUT, 0)
+        ctx.set_option(hta.OPT_USE_GRAPH, 1)
+        ctx.reset(0)
+        ctx.prefill(prompt)
+        got = ctx.decode_frames(6)[0]
+        assert np.array_equal(got, want)
+        assert np.array_equal(ctx.tap_hidden().view(np.uint32), h_want.view(np.uint32))
+    finally:
+        ref.close()
+        ctx.close()
+
+
+def test_create_run_destroy_twenty_times(w, prompt):
+    """Contexts created, run through the captured graph and destroyed 20 times, the
+    workspace freed by torch after each hta_destroy: the same codes every time."""
+    import torch
+    first = None
+    for i in range(20):
+        ctx = gpu_context(SH, w, "fp8" if i % 2 else "bf16", act_scales=np.full(4 * SH.n_layers + 1, 0.05, np.float32)
+                          if i % 2 else None)
+        ctx.prefill(prompt)
+        codes = ctx.decode_frames(3)[0]
+        ctx.close()
+        torch.cuda.synchronize()
+        if i % 5 == 4:
+            torch.cuda.empty_cache()
+        if i < 2:
+            first = codes if i == 0 else (first, codes)
+        else:
+            assert np.array_equal(codes, first[i % 2]), f"iteration {i}"
