@@ -51,34 +51,35 @@ def frame_bytes(shape, precision: str, kv_len: float) -> float:
     return (per_layer * L + head) * wb + scales + gains + emb + kv
 
 
-def cpu_oracle_baseline(shape, weights, scales, prompt, n_layers_sample=4, n_frames=3):
-    """The CPU oracle (FP8 storage-faithful mode, float32 weight storage) on a sample of
-    the workload: the first n_layers_sample layers plus the head, prefill of the prompt,
-    then n_frames decode frames; ms/frame scaled by 36 / n_layers_sample."""
-    from oracle.model import OracleModel, SITES_PER_LAYER
+def cpu_oracle_baseline(shape, weights, scales, prompt, n_frames=2):
+    """The CPU oracle (FP8 storage-faithful mode, float32 weight storage) on the whole
+    36-layer model: the prompt prefilled, then n_frames decode frames with the BLAS on every
+    host thread, then one more frame on one thread.  Building the oracle (the float32 copies
+    and the e4m3 weight quantisation) is not timed."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    sub = shape.with_layers(n_layers_sample)
-    keep = {k: v for k, v in weights.items()
-            if not k.startswith("layers.") or int(k.split(".")[1]) < n_layers_sample}
-    sc = np.concatenate([scales[: SITES_PER_LAYER * n_layers_sample], scales[-1:]])
+    from oracle.model import OracleModel
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     t0 = time.perf_counter()
-    m = OracleModel(sub, keep, "fp8", "S", act_scales=sc, storage=np.float32, max_seq=len(prompt) + n_frames + 1)
+    m = OracleModel(shape, weights, "fp8", "S", act_scales=scales, storage=np.float32,
+                    max_seq=len(prompt) + n_frames + 2)
     t_build = time.perf_counter() - t0
     m.prefill(prompt)
     t1 = time.perf_counter()
     for _ in range(n_frames):
         m.decode_frame()
     t2 = time.perf_counter()
-    ms = (t2 - t1) / n_frames * 1e3 * shape.n_layers / n_layers_sample
-    return {"value": round(ms, 2), "unit": "ms/frame", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_frames} FP8 decode frames of the first {n_layers_sample} of 36 layers (+ head) after a "
-                      f"P={len(prompt)} prefill, scaled x{shape.n_layers / n_layers_sample:g}; weight quantisation "
-                      f"({t_build:.1f} s) excluded"}
+    with threadpool_limits(1):
+        t3 = time.perf_counter()
+        m.decode_frame()
+        t4 = time.perf_counter()
+    ms = (t2 - t1) / n_frames * 1e3
+    return {"value": round(ms, 1), "unit": "ms/frame", "cores": int(threads), "kind": "oracle",
+            "cpu_count": os.cpu_count(), "one_thread_ms_per_frame": round((t4 - t3) * 1e3, 1),
+            "sample": f"whole {shape.n_layers}-layer FP8 decode frames (KV {len(prompt) + 1}..{len(prompt) + n_frames}) "
+                      f"after a P={len(prompt)} prefill: {n_frames} frames on {threads} BLAS threads, then one frame "
+                      f"on 1 thread; building the oracle ({t_build:.0f} s) not timed"}
 
 
 def main() -> int:
@@ -94,6 +95,10 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=36, help="backbone depth (36 = the benchmark model)")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the prefix-reuse and KV-4096 decode measurements")
+    ap.add_argument("--no-kv-slope", action="store_true",
+                    help="skip the chunked utterance that measures frame time against KV length")
+    ap.add_argument("--no-one-layer", action="store_true",
+                    help="skip the one-layer decode step with one and rotated weight copies")
     ap.add_argument("--no-kernel-classes", action="store_true",
                     help="skip the per-kernel-class event timing that follows the timed region")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -209,6 +214,9 @@ def main() -> int:
                 "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": _traffic(workload, shape),
                 "bytes_per_launch": int(k_bytes), "avg_launch_us": round(k_us, 3)}
+    if shape.n_layers == 36 and not args.no_kv_slope:
+        log("per-frame time against KV length (FP8)")
+        extra.update(_frame_vs_kv(ctx, prompt, args.frames))
     if long_kv:
         log("prefix reuse and long-context decode (FP8)")
         extra.update(_prefix_reuse(ctx, shape))
@@ -220,6 +228,9 @@ def main() -> int:
         extra["kernel_us_fp8"] = {k: round(v, 2) for k, v in ctx.time_kernels(32).items() if v > 0}
     ctx.close()
 
+    if shape.n_layers == 36 and not args.no_one_layer:
+        log("one-layer decode step at KV 512 / 2048, one weight copy and rotated copies")
+        extra["one_layer"] = _one_layer(shape, w, scales)
     cpu = None
     if not args.no_cpu_baseline:
         log("CPU oracle baseline (bounded sample)")
@@ -285,6 +296,74 @@ def _prefill_sizes(ctx, shape, prec: str) -> dict:
 
 
 LONG_PROMPT, LONG_FRAMES = 4095, 64
+
+
+def _frame_vs_kv(ctx, prompt, n_frames: int, chunk: int = 64) -> dict:
+    """One utterance decoded in chunks of `chunk` frames, each chunk event-timed: device us
+    per frame against the mean number of keys attended, and the least-squares slope."""
+    import torch
+
+    ctx.reset(0)
+    ctx.prefill(prompt)
+    kv, us = [], []
+    done = 0
+    while done + chunk <= n_frames:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(ctx.stream)
+        ctx.decode_frames(chunk)
+        e1.record(ctx.stream)
+        e1.synchronize()
+        kv.append(len(prompt) + done + (chunk + 1) / 2)
+        us.append(e0.elapsed_time(e1) * 1e3 / chunk)
+        done += chunk
+    slope, icpt = np.polyfit(np.array(kv), np.array(us), 1)
+    return {"frame_us_vs_kv_fp8": {"kv": [round(k, 1) for k in kv], "us": [round(u, 2) for u in us],
+                                   "slope_ns_per_key": round(slope * 1e3, 3), "intercept_us": round(icpt, 2)}}
+
+
+def _one_layer(shape, w, scales, kvs=(512, 2048), rounds: int = 8) -> dict:
+    """The one-layer decode step (one 4B layer plus the head, on the decode frame kernel) at
+    KV length L: the mean kernel time over `rounds` frames of one context (its weights stay
+    in the 256 MB memory-side cache between frames) and over rounds of frames rotated
+    across enough contexts that their weight copies exceed 800 MB (each frame then reads
+    its weights from HBM).  Each context holds its own copy; all share one stream."""
+    import dataclasses
+
+    import torch
+    import synthetic as S
+    from autoregressive_codebook_tts_amd import hta
+
+    sh1 = dataclasses.replace(shape.with_layers(1), text_vocab=1024)
+    w1 = {k: v for k, v in w.items() if not k.startswith("layers.") or k.startswith("layers.0.")}
+    w1["e_text"] = w["e_text"][:1024]
+    tensors, src = hta.weights_to_device(w1, 1)
+    sc1 = np.concatenate([scales[:4], scales[-1:]]).astype(np.float32)
+    stream = torch.cuda.Stream()
+    out = {}
+    for prec in ("bf16", "fp8"):
+        copy_bytes = frame_bytes(sh1, prec, 0)
+        n_copies = max(4, int(np.ceil(800e6 / copy_bytes)))
+        for L in kvs:
+            ids = S.token_ids(S.SEEDS["full_prompt"], L - 1, sh1.text_vocab)
+            ctxs = []
+            for _ in range(n_copies):
+                c = hta.Hta(sh1, prec, max_seq=L + 2 * rounds * n_copies + 4, max_prefill=512, stream=stream)
+                c.load_weights(tensors, src, act_scales=sc1 if prec == "fp8" else None)
+                for i in range(0, L - 1, 512):
+                    c.prefill(ids[i:i + 512])
+                c.time_kernels(1)  # warm
+                ctxs.append(c)
+            one = [ctxs[0].time_kernels(1)["frame"] for _ in range(rounds)]
+            rot = [c.time_kernels(1)["frame"] for _ in range(rounds) for c in ctxs]
+            b = frame_bytes(sh1, prec, L)
+            out[f"{prec}_kv{L}"] = {
+                "one_copy_us": round(statistics.mean(one), 2), "rotated_us": round(statistics.mean(rot), 2),
+                "copies": n_copies, "bytes_per_frame": int(b),
+                "rotated_frac_of_8TBs": round(b / (statistics.mean(rot) * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            for c in ctxs:
+                c.close()
+    del tensors
+    return out
 
 
 def _prefix_reuse(ctx, shape, reps: int = 5) -> dict:
