@@ -245,6 +245,8 @@ static void set_pointers(Ctx& c) {
 }
 
 static void drop_graph(Ctx& c) {
+  for (auto& g : c.prefill_graphs) (void)hipGraphExecDestroy(g.exec);
+  c.prefill_graphs.clear();
   if (c.frame_exec) (void)hipGraphExecDestroy(c.frame_exec);
   if (c.frame_graph) (void)hipGraphDestroy(c.frame_graph);
   c.frame_exec = nullptr;
@@ -268,6 +270,31 @@ static int ensure_graph(Ctx& c) {
   if (e2 != hipSuccess) return hip_fail(c, e2, "hipStreamEndCapture");
   c.frame_graph = g;
   HIPCK(hipGraphInstantiate(&c.frame_exec, g, nullptr, nullptr, 0), "hipGraphInstantiate");
+  return HTA_OK;
+}
+
+// The prefill of P rows as one graph, captured on first use; at most kMaxPrefillGraphs
+// prompt lengths are kept (the oldest is dropped).
+constexpr size_t kMaxPrefillGraphs = 16;
+static int prefill_graph(Ctx& c, int P, hipGraphExec_t* out) {
+  for (const auto& g : c.prefill_graphs)
+    if (g.P == P) { *out = g.exec; return HTA_OK; }
+  HIPCK(hipStreamBeginCapture(c.stream, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
+  hipError_t e = launch_prefill(c, P, false);
+  hipGraph_t g = nullptr;
+  hipError_t e2 = hipStreamEndCapture(c.stream, &g);
+  if (e != hipSuccess) { if (g) (void)hipGraphDestroy(g); return hip_fail(c, e, "prefill capture"); }
+  if (e2 != hipSuccess) return hip_fail(c, e2, "hipStreamEndCapture");
+  hipGraphExec_t x = nullptr;
+  e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return hip_fail(c, e, "hipGraphInstantiate");
+  if (c.prefill_graphs.size() >= kMaxPrefillGraphs) {
+    (void)hipGraphExecDestroy(c.prefill_graphs.front().exec);
+    c.prefill_graphs.erase(c.prefill_graphs.begin());
+  }
+  c.prefill_graphs.push_back({P, x});
+  *out = x;
   return HTA_OK;
 }
 
@@ -459,7 +486,14 @@ int hta_prefill(hta_ctx* x, const int32_t* tokens, int P) {
   HIPCK(hipStreamSynchronize(c.stream), "sync");
   std::memcpy(c.h_stage, tokens, (size_t)P * 4);
   HIPCK(hipMemcpyAsync(c.tok, c.h_stage, (size_t)P * 4, hipMemcpyHostToDevice, c.stream), "tokens");
-  HIPCK(launch_prefill(c, P, false), "prefill");
+  if (c.use_graph && !c.taps) {
+    hipGraphExec_t x = nullptr;
+    int r2 = prefill_graph(c, P, &x);
+    if (r2 != HTA_OK) return r2;
+    HIPCK(hipGraphLaunch(x, c.stream), "hipGraphLaunch");
+  } else {
+    HIPCK(launch_prefill(c, P, false), "prefill");
+  }
   HIPCK(launch_set_len(c, c.len + P), "set len");
   HIPCK(hipStreamSynchronize(c.stream), "prefill sync");
   c.len += P;

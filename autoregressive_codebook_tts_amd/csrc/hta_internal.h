@@ -142,6 +142,9 @@ struct Ctx {
   bool trace = false;           // persistent frame kernel phase timestamps
   uint32_t* trace_buf = nullptr;  // [kTraceBlocks][5 * n_layers + 1][4]
   void* fargs = nullptr;          // the persistent kernel's arguments (device)
+  // captured prefills, one per prompt length P (positions come from the device state)
+  struct PrefillGraph { int P; hipGraphExec_t exec; };
+  std::vector<PrefillGraph> prefill_graphs;
   // hta_decode_frames_noalloc: the frame kernel's exchange words in the library's static
   // per-device array (its address on this context's device) instead of the workspace
   char* scratch_dev = nullptr;

@@ -125,9 +125,10 @@ template <int HD>
 __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ QKV, const float* __restrict__ g_q,
                                                       const float* __restrict__ g_k, const float* __restrict__ rope_cos,
                                                       const float* __restrict__ rope_sin, float* __restrict__ Q,
-                                                      uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int len0,
+                                                      uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int* __restrict__ len_at,
                                                       int Hq, int Hkv, int max_seq, float eps) {
   constexpr int H2 = HD / 2;
+  const int len0 = *len_at;  // the first prompt position: the KV length before this prefill
   const int i = blockIdx.x, pos = len0 + i;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int W = (Hq + 2 * Hkv) * HD;
@@ -206,9 +207,9 @@ __device__ __forceinline__ uint32_t pack_bf16_trunc(float a, float b) {  // exac
 
 template <int P, int HD, int G>
 __global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict__ Q, const uint16_t* __restrict__ kc,
-                                                      const uint16_t* __restrict__ vc, void* __restrict__ O, int len0,
-                                                      int n_rows, int Hq, int Hkv, int max_seq, float scale,
-                                                      float* amax) {
+                                                      const uint16_t* __restrict__ vc, void* __restrict__ O,
+                                                      const int* __restrict__ len_at, int n_rows, int Hq, int Hkv,
+                                                      int max_seq, float scale, float* amax) {
   constexpr int T = kAttnTile, QT = kAttnQT;
   constexpr int KC = HD / 32;   // 32-wide k chunks of a q row
   constexpr int NT = HD / 16;   // 16-wide output column tiles
@@ -220,6 +221,7 @@ __global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = j * G + w;
   const int r16 = lane & 15, g4 = lane >> 4;
+  const int len0 = *len_at;  // the first prompt position: the KV length before this prefill
   const int last_pos = len0 + min(i0 + QT, n_rows) - 1;
   const int n_tiles = last_pos / T + 1;
   const uint16_t* kb = kc + (size_t)j * max_seq * HD;
@@ -862,7 +864,9 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
   const auto& f = c.cfg;
   const int d = f.hidden, hd = f.head_dim, Hq = f.n_q_heads, Hkv = f.n_kv_heads;
   const int qd = Hq * hd, kvd = Hkv * hd, F = f.ffn, W = qd + 2 * kvd;
-  const int len0 = c.len;
+  // the kernels read the first position from the device state (the KV length before this
+  // prefill), so a captured prefill of Pn rows serves every position
+  const int* len0 = &c.state->len;
   float* amax = record ? c.amax : nullptr;
   // the row kernels' per-thread register batches (k_rmsnorm_act_rows, k_qk_rope_rows)
   if (d > kRowPer * 256 || Hq + Hkv > 16 * 4 || kvd > 8 * 256) return hipErrorInvalidValue;
