@@ -440,7 +440,7 @@ def test_full_prefix_reuse(request, precision):
 
 
 # ----------------------------------------------------------------------------- FP8 decode at KV 4096
-def test_full_fp8_decode_kv4096(gpu_fp8, oracle_s8, oracle_e):
+def test_full_fp8_decode_kv4096(request, gpu_fp8, oracle_s8, oracle_e):
     ids = S.token_ids(S.SEEDS["long_prompt"], MAX_SEQ - 1, SH.text_vocab)
     ctx = gpu_fp8
     ctx.reset(0)
@@ -457,11 +457,18 @@ def test_full_fp8_decode_kv4096(gpu_fp8, oracle_s8, oracle_e):
     # the FP8 storage-faithful mode and exactly; as for every 36-layer end-to-end comparison the
     # gate is the oracle's own FP8 run's distance to the exact model (one flipped e4m3 rounding
     # cascades through the remaining layers)
-    for o in (oracle_s8, oracle_e):
+    # a second faithful FP8 oracle that differs only in accumulation precision (float64 instead
+    # of float32 products): its distance from the first is the scale at which a handful of
+    # rounding-boundary flips, cascading through 36 layers, moves the end result
+    twin = OracleModel(SH, request.getfixturevalue("w"), "fp8", "S", act_scales=oracle_s8.scales,
+                       storage=np.float64, max_seq=MAX_SEQ)
+    for o in (oracle_s8, oracle_e, twin):
         o.reset(0)
         for layer in range(SH.n_layers):
             o.set_kv(layer, *_kv_rows(ctx, layer, MAX_SEQ - 1))
         o.decode_frame()
+    n_s = rel_l2(twin.last_hidden, oracle_s8.last_hidden)
+    del twin
     ctx.reset(MAX_SEQ - 1)
     ctx.decode_frame()
     d_s = rel_l2(ctx.tap_hidden(), oracle_s8.last_hidden)
@@ -469,9 +476,10 @@ def test_full_fp8_decode_kv4096(gpu_fp8, oracle_s8, oracle_e):
     q_e = rel_l2(oracle_s8.last_hidden, oracle_e.last_hidden)
     cos_e = cosines(ctx.tap_logits(), oracle_e.last_logits).min()
     cos_q = cosines(oracle_s8.last_logits, oracle_e.last_logits).min()
-    _say(f"[full] fp8 frame at KV 4096 end to end from the same cache: hidden rel vs fp8 oracle {d_s:.3e}, vs exact "
-         f"{d_e:.3e} (fp8 oracle vs exact {q_e:.3e}); logits cos vs exact {cos_e:.6f} (fp8 oracle {cos_q:.6f})")
-    assert d_s <= HIDDEN_TOL["fp8"]
+    _say(f"[full] fp8 frame at KV 4096 end to end from the same cache: hidden rel vs fp8 oracle {d_s:.3e} (the float64 "
+         f"fp8 oracle vs the float32 one {n_s:.3e}), vs exact {d_e:.3e} (fp8 oracle vs exact {q_e:.3e}); logits cos "
+         f"vs exact {cos_e:.6f} (fp8 oracle {cos_q:.6f})")
+    assert d_s <= max(HIDDEN_TOL["fp8"], 2.0 * n_s)
     assert d_e <= E2E_RATIO * q_e
     assert cos_e >= cos_q - 0.02
     # a full cache refuses another frame
