@@ -62,6 +62,10 @@ Layout make_layout(const hta_config& c) {
   const size_t F = c.ffn, W = qd + 2 * kvd, wb = wbytes(c), ms = c.max_seq, Pm = c.max_prefill;
   const size_t CV = (size_t)c.n_codebooks * c.codebook_size;
   const bool fp8 = c.precision == HTA_FP8_E4M3;
+  const size_t M = c.n_streams > 1 ? (size_t)c.n_streams : 1;
+  const size_t CVp = (CV + 63) / 64 * 64;  // head rows padded for the batched step's GEMM tiles
+  L.cv_pad = (int)CVp;
+  L.n_streams = (int)M;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
   // one layer block
@@ -79,22 +83,23 @@ Layout make_layout(const hta_config& c) {
   L.off_gq = ltake(hd * 4);
   L.off_gk = ltake(hd * 4);
   L.off_gmlp = ltake(d * 4);
-  L.off_k = ltake((size_t)c.n_kv_heads * ms * hd * 2);
-  L.off_v = ltake((size_t)c.n_kv_heads * ms * hd * 2);
+  L.kv_stream_bytes = (size_t)c.n_kv_heads * ms * hd * 2;
+  L.off_k = ltake(M * L.kv_stream_bytes);  // stream m's cache at + m * kv_stream_bytes
+  L.off_v = ltake(M * L.kv_stream_bytes);
   L.layer_stride = lo;
   L.layer_base = take(lo * c.n_layers);
   L.off_etext = take((size_t)c.text_vocab * d * 2);
   L.off_eaud = take(CV * d * 2);
   L.off_gfinal = take(d * 4);
-  L.off_whead = take(CV * d * wb);
-  L.off_shead = take(fp8 ? CV * 4 : 0);
+  L.off_whead = take(CVp * d * wb);
+  L.off_shead = take(fp8 ? CVp * 4 : 0);
   L.off_rope_cos = take(ms * (hd / 2) * 4);
   L.off_rope_sin = take(ms * (hd / 2) * 4);
   const size_t nsites = (size_t)kSitesPerLayer * c.n_layers + 1;
   L.off_act_scales = take(nsites * 4);
   L.off_amax = take(nsites * 4);
-  L.off_state = take(sizeof(DevState));
-  L.off_hist = take(ms * c.n_codebooks * 4);
+  L.off_state = take(M * sizeof(DevState));
+  L.off_hist = take(M * ms * c.n_codebooks * 4);
   L.off_counters = take(64 * 4);
   int splits = 256 / c.n_kv_heads;
   if (splits > 64) splits = 64;
@@ -124,6 +129,7 @@ Layout make_layout(const hta_config& c) {
   size_t nmax = W;
   if (2 * F > nmax) nmax = 2 * F;
   if (d > nmax) nmax = d;
+  if (M > 1 && CVp > nmax) nmax = CVp;  // the batched step's head GEMM
   L.off_pgu = take(Pm * 2 * F * 4 + 8 * Pm * nmax * 4);  // gate/up rows, then GEMM split partials
   L.off_pa = take(Pm * F * 2);  // SiLU * mul rows (the down projection's input)
   L.off_taps = take(((size_t)c.n_layers + 1) * d * 4);
@@ -133,6 +139,12 @@ Layout make_layout(const hta_config& c) {
   L.off_trace = take((size_t)kTraceBlocks * (5 * c.n_layers + 1) * 8 * 4);
   L.off_fargs = take(kFrameArgsBytes);
   L.off_fargs_s = take(kFrameArgsBytes);
+  {
+    int S = M > 1 ? (int)(256 / ((size_t)c.n_kv_heads * M)) : 1;  // about one block per CU
+    L.batch_splits = S < 1 ? 1 : (S > 16 ? 16 : S);
+  }
+  L.off_blogits = take(M > 1 ? M * CVp * 4 : 0);
+  L.off_bpart = take(M > 1 ? M * (size_t)c.n_q_heads * L.batch_splits * (hd + 2) * 4 : 0);
   L.total = o;
   return L;
 }
@@ -173,9 +185,23 @@ static bool shape_ok(const hta_config& f, std::string* why) {
   if (f.text_vocab < 1) return bad("text_vocab must be positive");
   if (f.max_seq < 2 || f.max_prefill < 1 || f.max_prefill > f.max_seq) return bad("bad max_seq / max_prefill");
   if (f.precision != HTA_BF16 && f.precision != HTA_FP8_E4M3) return bad("unknown precision");
+  if (f.n_streams < 0 || f.n_streams > 16) return bad("n_streams must be in 0..16");
+  if (f.n_streams > 1 && f.n_streams > f.max_prefill) return bad("n_streams must not exceed max_prefill");
   if (f.hidden > 5120 || f.ffn > 10240 || f.n_q_heads * f.head_dim > 10240)
     return bad("hidden above 5120 or ffn / q width above 10240 exceed the GEMV prologue budget");
   return true;
+}
+
+// Point `state`, `hist` and every layer's K/V cache at the selected stream's.
+static void point_stream(Ctx& c) {
+  const int m = c.sel;
+  c.state = c.state_base + m;
+  c.hist = c.hist_base + (size_t)m * c.cfg.max_seq * c.cfg.n_codebooks;
+  const size_t ke = c.lay.kv_stream_bytes / 2;  // elements
+  for (int l = 0; l < c.cfg.n_layers; ++l) {
+    c.layers[l].k_cache = c.k_base[l] + (size_t)m * ke;
+    c.layers[l].v_cache = c.v_base[l] + (size_t)m * ke;
+  }
 }
 
 static void set_pointers(Ctx& c) {
@@ -210,8 +236,17 @@ static void set_pointers(Ctx& c) {
   c.rope_sin = reinterpret_cast<float*>(w + L.off_rope_sin);
   c.act_scales = reinterpret_cast<float*>(w + L.off_act_scales);
   c.amax = reinterpret_cast<float*>(w + L.off_amax);
-  c.state = reinterpret_cast<DevState*>(w + L.off_state);
-  c.hist = reinterpret_cast<int32_t*>(w + L.off_hist);
+  c.state_base = reinterpret_cast<DevState*>(w + L.off_state);
+  c.hist_base = reinterpret_cast<int32_t*>(w + L.off_hist);
+  c.b_logits = reinterpret_cast<float*>(w + L.off_blogits);
+  c.b_part = reinterpret_cast<float*>(w + L.off_bpart);
+  c.k_base.assign(f.n_layers, nullptr);
+  c.v_base.assign(f.n_layers, nullptr);
+  for (int l = 0; l < f.n_layers; ++l) {
+    c.k_base[l] = c.layers[l].k_cache;
+    c.v_base[l] = c.layers[l].v_cache;
+  }
+  point_stream(c);
   c.counters = reinterpret_cast<unsigned*>(w + L.off_counters);
   c.h = reinterpret_cast<float*>(w + L.off_h);
   c.qkv = reinterpret_cast<float*>(w + L.off_qkv);
@@ -245,6 +280,10 @@ static void set_pointers(Ctx& c) {
 }
 
 static void drop_graph(Ctx& c) {
+  if (c.batch_exec) (void)hipGraphExecDestroy(c.batch_exec);
+  if (c.batch_graph) (void)hipGraphDestroy(c.batch_graph);
+  c.batch_exec = nullptr;
+  c.batch_graph = nullptr;
   for (auto& g : c.prefill_graphs) (void)hipGraphExecDestroy(g.exec);
   c.prefill_graphs.clear();
   if (c.frame_exec) (void)hipGraphExecDestroy(c.frame_exec);
@@ -278,7 +317,7 @@ static int ensure_graph(Ctx& c) {
 constexpr size_t kMaxPrefillGraphs = 16;
 static int prefill_graph(Ctx& c, int P, hipGraphExec_t* out) {
   for (const auto& g : c.prefill_graphs)
-    if (g.P == P) { *out = g.exec; return HTA_OK; }
+    if (g.P == P && g.stream == c.sel) { *out = g.exec; return HTA_OK; }
   HIPCK(hipStreamBeginCapture(c.stream, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
   hipError_t e = launch_prefill(c, P, false);
   hipGraph_t g = nullptr;
@@ -293,7 +332,7 @@ static int prefill_graph(Ctx& c, int P, hipGraphExec_t* out) {
     (void)hipGraphExecDestroy(c.prefill_graphs.front().exec);
     c.prefill_graphs.erase(c.prefill_graphs.begin());
   }
-  c.prefill_graphs.push_back({P, x});
+  c.prefill_graphs.push_back({P, c.sel, x});
   *out = x;
   return HTA_OK;
 }
@@ -355,7 +394,7 @@ int hta_create(const hta_config* cfg, void* hip_stream, hta_ctx** out) {
       return HTA_E_UNSUPPORTED;
     }
   }
-  c.h_stage_elems = (size_t)c.cfg.max_seq * c.cfg.n_codebooks;
+  c.h_stage_elems = (size_t)c.cfg.max_seq * c.cfg.n_codebooks * (c.cfg.n_streams > 1 ? c.cfg.n_streams : 1);
   if ((size_t)c.cfg.max_prefill > c.h_stage_elems) c.h_stage_elems = c.cfg.max_prefill;
   if (hipHostMalloc((void**)&c.h_stage, c.h_stage_elems * sizeof(int32_t), hipHostMallocDefault) != hipSuccess ||
       hipHostMalloc((void**)&c.h_state, sizeof(DevState), hipHostMallocDefault) != hipSuccess ||
@@ -382,6 +421,7 @@ int hta_bind_workspace(hta_ctx* x, void* dev_ptr, size_t bytes) {
   drop_graph(c);
   c.ws = static_cast<char*>(dev_ptr);
   c.weights_loaded = false;
+  c.sel = 0;
   set_pointers(c);
   const hta_config& f = c.cfg;
   // RoPE table: phi = p * theta^(-2i/hd) in double, stored as float cos / sin
@@ -401,13 +441,21 @@ int hta_bind_workspace(hta_ctx* x, void* dev_ptr, size_t bytes) {
   HIPCK(launch_fill_u32(c.counters, 0u, 64, c.stream), "fill");
   HIPCK(launch_fill_u32(c.amax, 0u, nsites, c.stream), "fill");
   HIPCK(launch_fill_u32(c.act_scales, 0x3f800000u, nsites, c.stream), "fill");
-  HIPCK(launch_fill_u32(c.state, 0u, sizeof(DevState) / 4, c.stream), "fill");
+  const int M = c.lay.n_streams;
+  HIPCK(launch_fill_u32(c.state_base, 0u, (size_t)M * sizeof(DevState) / 4, c.stream), "fill");
   HIPCK(clear_exchange(c), "fill");
-  HIPCK(launch_reset_state(c, 0), "reset");
+  for (int m = M - 1; m >= 0; --m) {  // every stream's state; stream 0 stays selected
+    c.sel = m;
+    point_stream(c);
+    HIPCK(launch_reset_state(c, 0), "reset");
+  }
   HIPCK(hipStreamSynchronize(c.stream), "sync");
   HIPCK(frame_write_args(c), "frame arguments");
   c.len = 0;
   c.t = 0;
+  c.s_len.assign(M, 0);
+  c.s_t.assign(M, 0);
+  c.s_done.assign(M, 0);
   return HTA_OK;
 }
 
@@ -454,6 +502,12 @@ int hta_load_weights(hta_ctx* x, const void* const* t, int n, int src_dtype, con
   const void* const* T = t + 2 + 11 * f.n_layers;
   HIPCK(launch_copy_f32(c.g_final, T[0], src_dtype, d, s), "gain");
   HIPCK(launch_pack_rows(c.w_head, 0, 1, T[1], src_dtype, CV, d, q8, c.s_head, s), "pack head");
+  if (c.lay.cv_pad > CV) {  // the padded head rows of the batched step's GEMM: zero weights
+    const size_t wbh = fp8 ? 1 : 2;
+    HIPCK(launch_fill_u32(static_cast<char*>(c.w_head) + (size_t)CV * d * wbh, 0u,
+                          (size_t)(c.lay.cv_pad - CV) * d * wbh / 4, s), "fill");
+    if (fp8) HIPCK(launch_fill_u32(c.s_head + CV, 0x3f800000u, (size_t)(c.lay.cv_pad - CV), s), "fill");
+  }
   HIPCK(hipMemcpyAsync(c.act_scales, c.h_scales.data(), nsites * 4, hipMemcpyHostToDevice, s), "scales");
   HIPCK(hipMemcpyAsync(c.d_layers, c.layers, (size_t)f.n_layers * sizeof(LayerW), hipMemcpyHostToDevice, s), "layer table");
   HIPCK(hipStreamSynchronize(s), "load sync");
@@ -470,6 +524,22 @@ int hta_reset(hta_ctx* x, int keep_len) {
   c.len = keep_len;
   c.t = 0;
   c.done = false;
+  return HTA_OK;
+}
+
+int hta_select_stream(hta_ctx* x, int m) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  if (!c.ws) return fail(c, HTA_E_STATE, "no workspace bound");
+  if (m < 0 || m >= c.lay.n_streams) return fail(c, HTA_E_ARG, "stream out of range");
+  c.s_len[c.sel] = c.len;
+  c.s_t[c.sel] = c.t;
+  c.s_done[c.sel] = c.done ? 1 : 0;
+  c.sel = m;
+  point_stream(c);
+  c.len = c.s_len[m];
+  c.t = c.s_t[m];
+  c.done = c.s_done[m] != 0;
   return HTA_OK;
 }
 
@@ -511,10 +581,57 @@ static int frame_timed_out(Ctx& c) {
 
 // n frames; with `no_alloc` the frame kernel exchanges through the static per-device array
 // (cleared first, launch counter included) and is launched directly, never through the graph.
+// n batched steps of every stream (n_streams > 1): the step graph replayed n times, then
+// each stream's n codes from its history into codes_out[frame][stream][codebook].
+static int decode_batch(Ctx& c, int n, int32_t* codes_out, int* n_done_out) {
+  const int M = c.lay.n_streams, C = c.cfg.n_codebooks;
+  c.s_len[c.sel] = c.len;
+  c.s_t[c.sel] = c.t;
+  for (int m = 0; m < M; ++m)
+    if (c.s_len[m] + n > c.cfg.max_seq) return fail(c, HTA_E_CAPACITY, "KV cache of a stream full");
+  if ((size_t)n * M * C > c.h_stage_elems) return fail(c, HTA_E_ARG, "too many frames for one call");
+  if (!c.batch_exec) {
+    HIPCK(hipStreamBeginCapture(c.stream, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
+    hipError_t e = launch_batch_step(c);
+    hipGraph_t g = nullptr;
+    hipError_t e2 = hipStreamEndCapture(c.stream, &g);
+    if (e != hipSuccess) { if (g) (void)hipGraphDestroy(g); return hip_fail(c, e, "batch step capture"); }
+    if (e2 != hipSuccess) return hip_fail(c, e2, "hipStreamEndCapture");
+    c.batch_graph = g;
+    HIPCK(hipGraphInstantiate(&c.batch_exec, g, nullptr, nullptr, 0), "hipGraphInstantiate");
+  }
+  for (int i = 0; i < n; ++i) HIPCK(hipGraphLaunch(c.batch_exec, c.stream), "hipGraphLaunch");
+  for (int m = 0; m < M; ++m)  // stream m's steps t_m .. t_m + n - 1
+    HIPCK(hipMemcpy2DAsync(c.h_stage + (size_t)m * C, (size_t)M * C * 4,
+                           c.hist_base + ((size_t)m * c.cfg.max_seq + c.s_t[m]) * C, (size_t)C * 4, (size_t)C * 4, n,
+                           hipMemcpyDeviceToHost, c.stream), "codes");
+  HIPCK(hipStreamSynchronize(c.stream), "decode sync");
+  std::vector<DevState> st(M);
+  HIPCK(hipMemcpy(st.data(), c.state_base, (size_t)M * sizeof(DevState), hipMemcpyDeviceToHost), "state");
+  std::memcpy(codes_out, c.h_stage, (size_t)n * M * C * 4);
+  int done = 0;
+  for (int m = 0; m < M; ++m) {
+    c.s_len[m] += n;
+    c.s_t[m] += n;
+    c.s_done[m] = st[m].done ? 1 : 0;
+    done += c.s_done[m];
+    if (st[m].len != c.s_len[m] || st[m].t != c.s_t[m]) return fail(c, HTA_E_STATE, "device state out of step with host");
+  }
+  c.len = c.s_len[c.sel];
+  c.t = c.s_t[c.sel];
+  c.done = c.s_done[c.sel] != 0;
+  if (n_done_out) *n_done_out = done;
+  return done == M ? HTA_DONE : HTA_OK;
+}
+
 static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out, bool no_alloc) {
   int r = ready(c);
   if (r) return r;
   if (n <= 0 || !codes_out) return fail(c, HTA_E_ARG, "bad frame count or output");
+  if (c.lay.n_streams > 1) {
+    if (no_alloc) return fail(c, HTA_E_UNSUPPORTED, "the allocation-free decode serves single-stream contexts");
+    return decode_batch(c, n, codes_out, n_done_out);
+  }
   if (c.len + n > c.cfg.max_seq) return fail(c, HTA_E_CAPACITY, "KV cache full");
   const unsigned* abort_word = c.sync + 64;
   if (no_alloc) {
@@ -568,6 +685,7 @@ int hta_decode_frames_noalloc(hta_ctx* x, int n, int32_t* codes_out, int* n_done
 int hta_set_sampling(hta_ctx* x, float temperature, uint64_t seed) {
   if (!x) return HTA_E_ARG;
   Ctx& c = x->c;
+  if (c.lay.n_streams > 1 && temperature != 0.0f) return fail(c, HTA_E_UNSUPPORTED, "batched decode is greedy");
   if (!(temperature >= 0.0f) || !std::isfinite(temperature)) return fail(c, HTA_E_ARG, "temperature must be finite and >= 0");
   const size_t logit_bytes = (size_t)c.cfg.n_codebooks * c.cfg.codebook_size * sizeof(float);
   if (temperature > 0.0f && logit_bytes > frame_sample_capacity())
@@ -598,14 +716,18 @@ int hta_read_tap(hta_ctx* x, int tap, int layer, void* host_out, size_t bytes) {
   HIPCK(hipStreamSynchronize(c.stream), "sync");
   const int C = f.n_codebooks;
   switch (tap) {
-    case HTA_TAP_HIDDEN:
+    case HTA_TAP_HIDDEN: {
       if (bytes < (size_t)f.hidden * 4) return fail(c, HTA_E_ARG, "buffer too small");
-      HIPCK(hipMemcpy(host_out, c.h, (size_t)f.hidden * 4, hipMemcpyDeviceToHost), "tap");
+      // batched: the selected stream's final residual row of the last step
+      const float* src = c.lay.n_streams > 1 ? c.px + (size_t)c.sel * f.hidden : c.h;
+      HIPCK(hipMemcpy(host_out, src, (size_t)f.hidden * 4, hipMemcpyDeviceToHost), "tap");
       return HTA_OK;
+    }
     case HTA_TAP_LOGITS: {
       const size_t nb = (size_t)C * f.codebook_size * 4;
       if (bytes < nb) return fail(c, HTA_E_ARG, "buffer too small");
-      HIPCK(hipMemcpy(host_out, c.logits, nb, hipMemcpyDeviceToHost), "tap");
+      const float* src = c.lay.n_streams > 1 ? c.b_logits + (size_t)c.sel * c.lay.cv_pad : c.logits;
+      HIPCK(hipMemcpy(host_out, src, nb, hipMemcpyDeviceToHost), "tap");
       return HTA_OK;
     }
     case HTA_TAP_STATE: {
@@ -712,6 +834,7 @@ int hta_calibrate(hta_ctx* x, const int32_t* tokens, int P, int n_frames, const 
   int r = ready(c);
   if (r) return r;
   if (f.precision != HTA_BF16) return fail(c, HTA_E_STATE, "calibration runs on a BF16 context");
+  if (c.lay.n_streams > 1) return fail(c, HTA_E_UNSUPPORTED, "calibration runs on a single-stream context");
   if (!tokens || P <= 0 || P > f.max_prefill || n_frames < 0 || !scales_out) return fail(c, HTA_E_ARG, "bad calibration arguments");
   if (P + n_frames > f.max_seq) return fail(c, HTA_E_CAPACITY, "calibration run exceeds max_seq");
   for (int i = 0; i < P; ++i)
@@ -764,6 +887,7 @@ int hta_layer_step(hta_ctx* x, int layer, int kv_len, const void* k_init, const 
   const hta_config& f = c.cfg;
   int r = ready(c);
   if (r) return r;
+  if (c.lay.n_streams > 1) return fail(c, HTA_E_UNSUPPORTED, "a single-stream call");
   if (f.n_layers != 1 || layer != 0) return fail(c, HTA_E_UNSUPPORTED, "a layer step runs layer 0 of a one-layer context");
   if (kv_len < 1 || kv_len > f.max_seq) return fail(c, HTA_E_CAPACITY, "kv_len out of range");
   if (!h_io) return fail(c, HTA_E_ARG, "null hidden state");
@@ -810,6 +934,7 @@ int hta_time_kernels(hta_ctx* x, int n_frames, float* avg_us, int n_classes) {
   Ctx& c = x->c;
   int r = ready(c);
   if (r) return r;
+  if (c.lay.n_streams > 1) return fail(c, HTA_E_UNSUPPORTED, "a single-stream call");
   if (n_frames <= 0 || !avg_us || n_classes <= 0) return fail(c, HTA_E_ARG, "bad arguments");
   if (c.len + n_frames > c.cfg.max_seq) return fail(c, HTA_E_CAPACITY, "KV cache full");
   hipEvent_t ev[2];
@@ -848,6 +973,9 @@ int hta_set_option(hta_ctx* x, int option, int value) {
     c.use_graph = value != 0;
     return HTA_OK;
   }
+  if ((option == HTA_OPT_TAPS || option == HTA_OPT_TRACE || option == HTA_OPT_FORCE_TIMEOUT) && value != 0 &&
+      c.lay.n_streams > 1)
+    return fail(c, HTA_E_UNSUPPORTED, "a single-stream option");
   if (option == HTA_OPT_TAPS) {
     const bool v = value != 0;
     if (v != c.taps) drop_graph(c);

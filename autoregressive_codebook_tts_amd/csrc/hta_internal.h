@@ -60,6 +60,11 @@ struct Layout {
   // prefill scratch
   size_t off_tok, off_x, off_u, off_pqkv, off_pq, off_po, off_pgu, off_pa;
   size_t off_taps, off_ptaps, off_tact, off_tq, off_trace, off_fargs, off_fargs_s;
+  // batched decode: logits [M][CVp] and attention split partials [M][Hq][splits][hd + 2]
+  size_t off_blogits, off_bpart;
+  size_t kv_stream_bytes;   // bytes of one stream's K (or V) cache within a layer
+  int cv_pad;               // head rows padded to a multiple of 64 (the GEMM's column tile)
+  int n_streams, batch_splits;
   int attn_splits;
 };
 
@@ -143,7 +148,7 @@ struct Ctx {
   uint32_t* trace_buf = nullptr;  // [kTraceBlocks][5 * n_layers + 1][4]
   void* fargs = nullptr;          // the persistent kernel's arguments (device)
   // captured prefills, one per prompt length P (positions come from the device state)
-  struct PrefillGraph { int P; hipGraphExec_t exec; };
+  struct PrefillGraph { int P; int stream; hipGraphExec_t exec; };  // (prompt length, stream)
   std::vector<PrefillGraph> prefill_graphs;
   // hta_decode_frames_noalloc: the frame kernel's exchange words in the library's static
   // per-device array (its address on this context's device) instead of the workspace
@@ -151,6 +156,19 @@ struct Ctx {
   size_t static_exch_bytes = 0;   // bytes of that array this shape's exchange words take
   void* fargs_s = nullptr;        // kernel arguments pointing at it (device)
   unsigned* h_status = nullptr;   // pinned host word: the abort flag read back after a decode
+  // batched decode (n_streams > 1): the selected stream's state / history / caches are
+  // what `state`, `hist` and layers[].k_cache / v_cache point at; the others' host-side
+  // lengths and steps are kept here
+  int sel = 0;
+  std::vector<int> s_len, s_t;
+  std::vector<char> s_done;
+  DevState* state_base = nullptr;
+  int32_t* hist_base = nullptr;
+  std::vector<uint16_t*> k_base, v_base;   // stream 0's cache of each layer
+  hipGraph_t batch_graph = nullptr;
+  hipGraphExec_t batch_exec = nullptr;
+  float* b_logits = nullptr;
+  float* b_part = nullptr;
   float temperature = 0.0f;       // 0: greedy; > 0: the head draws at this temperature
   bool force_timeout = false;     // frames wait for an input no block writes (recovery tests)
   uint64_t seed = 0;              // the draw's seed
@@ -187,6 +205,7 @@ size_t frame_sample_capacity();  // bytes of LDS that hold a sampling frame's lo
 // ---------------------------------------------------------------- launchers (prefill.hip)
 hipError_t prefill_setup();  // kernel attributes of the prefill GEMM (once per context)
 hipError_t launch_prefill(Ctx& c, int P, bool record);
+hipError_t launch_batch_step(Ctx& c);  // one batched decode step of all n_streams streams
 
 // ---------------------------------------------------------------- launchers (load.hip)
 hipError_t launch_pack_rows(void* dst, int dst_row0, int dst_row_stride, const void* src, int src_dtype,

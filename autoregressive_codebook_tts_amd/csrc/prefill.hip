@@ -126,10 +126,16 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
                                                       const float* __restrict__ g_k, const float* __restrict__ rope_cos,
                                                       const float* __restrict__ rope_sin, float* __restrict__ Q,
                                                       uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int* __restrict__ len_at,
-                                                      int Hq, int Hkv, int max_seq, float eps) {
+                                                      int Hq, int Hkv, int max_seq, float eps, int len_stride,
+                                                      long kv_stride) {
   constexpr int H2 = HD / 2;
-  const int len0 = *len_at;  // the first prompt position: the KV length before this prefill
-  const int i = blockIdx.x, pos = len0 + i;
+  // prefill (len_stride 0): row i of a prompt sits at the KV length before the prefill
+  // plus i.  Batched decode: row i is stream i, at its own KV length (len_at[i *
+  // len_stride]), with its own cache (kv_stride elements after the previous stream's).
+  const int i = blockIdx.x;
+  const int pos = len_stride ? len_at[(long)i * len_stride] : *len_at + i;
+  kc += (long)i * kv_stride;
+  vc += (long)i * kv_stride;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int W = (Hq + 2 * Hkv) * HD;
   const float* row = QKV + (size_t)i * W;
@@ -887,10 +893,10 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
     if ((e = gemm<P>(c, c.pu, L.w_qkv, L.s_qkv, host_act_scale(c, s0), c.pqkv, Pn, W, d, 0)) != hipSuccess) return e;
     if (hd == 128)
       hipLaunchKernelGGL(k_qk_rope_rows<128>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
-                         c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps);
+                         c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L);
     else
       hipLaunchKernelGGL(k_qk_rope_rows<64>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
-                         c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps);
+                         c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
       const int G = Hq / Hkv;
@@ -923,6 +929,248 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
       return e;
   }
   return hipSuccess;
+}
+
+// ============================================================================ batched decode step
+// M independent streams (utterances) advance one step together: row m of every row
+// buffer is stream m.  The GEMMs are the prefill's (M rows share one weight stream); the
+// kernels below are the per-stream parts.
+
+// Row m = the sum of the codebook embeddings of stream m's previous codes (codebooks in
+// order, fp32).
+__global__ __launch_bounds__(256) void k_embed_codes_rows(const DevState* __restrict__ st,
+                                                          const uint16_t* __restrict__ e_aud, float* __restrict__ X,
+                                                          int d, int C, int V) {
+  const int m = blockIdx.x;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    float v = 0.0f;
+    for (int c = 0; c < C; ++c) v += bf16_to_f32(e_aud[((size_t)c * V + st[m].prev[c]) * d + k]);
+    X[(size_t)m * d + k] = v;
+  }
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Decode attention of the batched step: one block per (key split s, kv head j, stream m),
+// one wave per query head of the group.  Stream m's query is at position p = its KV
+// length (its key and value were just written there); split s takes keys
+// [s * chunk, min(p + 1, (s + 1) * chunk)) with chunk = ceil((p + 1) / S) in whole 64-key
+// tiles.  Lane l scores key kb + l of a tile (fp32 dot of the bf16 key with the
+// bf16-rounded query, scale 1/sqrt(hd)); the wave keeps the online softmax (running
+// max and denominator, fp32) and lane l accumulates output dimensions l and l + 64.
+// The split's (o[hd], max, denominator) go to part[((m * Hq + h) * S + s) * (hd + 2)].
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_rows(const float* __restrict__ Q, const uint16_t* __restrict__ kc,
+                                                   const uint16_t* __restrict__ vc, long kv_stride,
+                                                   const DevState* __restrict__ st, int Hq, int Hkv, int max_seq,
+                                                   float* __restrict__ part) {
+  const int S = gridDim.x, s = blockIdx.x, j = blockIdx.y, m = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int h = j * G + w;
+  const int L = st[m].len + 1;
+  int chunk = (L + S - 1) / S;
+  chunk = (chunk + 63) / 64 * 64;
+  const int k0 = s * chunk, k1 = min(L, k0 + chunk);
+  __shared__ __align__(16) float sq[4][HD];
+  __shared__ float sp[4][64];
+  const float* q = Q + ((size_t)m * Hq + h) * HD;
+  for (int dd = lane; dd < HD; dd += 64) sq[w][dd] = q[dd];
+  __syncthreads();
+  const uint16_t* K = kc + (long)m * kv_stride + (size_t)j * max_seq * HD;
+  const uint16_t* V = vc + (long)m * kv_stride + (size_t)j * max_seq * HD;
+  const float inv_sqrt = 1.0f / sqrtf((float)HD);
+  float mrun = -INFINITY, lrun = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int kb = k0; kb < k1; kb += 64) {  // the same trip count in every wave of the block
+    const int key = kb + lane;
+    const bool ok = key < k1;
+    const uint4* kr = reinterpret_cast<const uint4*>(K + (size_t)(ok ? key : k0) * HD);
+    float sc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < HD / 8; ++u) {
+      const uint4 k4 = kr[u];
+      const float4 qa = *reinterpret_cast<const float4*>(&sq[w][8 * u]);
+      const float4 qb = *reinterpret_cast<const float4*>(&sq[w][8 * u + 4]);
+      sc = fmaf(qa.x, bf16_lo(k4.x), sc);
+      sc = fmaf(qa.y, bf16_hi(k4.x), sc);
+      sc = fmaf(qa.z, bf16_lo(k4.y), sc);
+      sc = fmaf(qa.w, bf16_hi(k4.y), sc);
+      sc = fmaf(qb.x, bf16_lo(k4.z), sc);
+      sc = fmaf(qb.y, bf16_hi(k4.z), sc);
+      sc = fmaf(qb.z, bf16_lo(k4.w), sc);
+      sc = fmaf(qb.w, bf16_hi(k4.w), sc);
+    }
+    sc = ok ? sc * inv_sqrt : -INFINITY;
+    const float mnew = fmaxf(mrun, wave_max(sc));
+    const float p = ok ? __expf(sc - mnew) : 0.0f;
+    const float scale = __expf(mrun - mnew);
+    lrun = lrun * scale + wave_sum(p);
+    o0 *= scale;
+    o1 *= scale;
+    sp[w][lane] = p;
+    __syncthreads();
+    const int nk = min(64, k1 - kb);
+    for (int kk = 0; kk < nk; ++kk) {
+      const float pk = sp[w][kk];
+      const uint16_t* vr = V + (size_t)(kb + kk) * HD;
+      o0 = fmaf(pk, bf16_to_f32(vr[lane]), o0);
+      if (HD > 64) o1 = fmaf(pk, bf16_to_f32(vr[lane + 64]), o1);
+    }
+    mrun = mnew;
+    __syncthreads();
+  }
+  float* pp = part + (((size_t)m * Hq + h) * S + s) * (HD + 2);
+  pp[lane] = o0;
+  if (HD > 64) pp[lane + 64] = o1;
+  if (lane == 0) {
+    pp[HD] = mrun;
+    pp[HD + 1] = lrun;
+  }
+}
+
+// Log-sum-exp combine of the splits (those holding keys), then the attention output in
+// GEMM units (bf16 bits, or e4m3 codes at the site's static scale): one block per
+// (query head, stream), one thread per output dimension.
+template <int P, int HD>
+__global__ __launch_bounds__(HD) void k_attn_combine(const float* __restrict__ part, int S, int Hq,
+                                                      void* __restrict__ O, float scale) {
+  const int h = blockIdx.x, m = blockIdx.y, dd = threadIdx.x;
+  const float* pp = part + ((size_t)m * Hq + h) * S * (HD + 2);
+  float mx = -INFINITY;
+  for (int s = 0; s < S; ++s)
+    if (pp[s * (HD + 2) + HD + 1] > 0.0f) mx = fmaxf(mx, pp[s * (HD + 2) + HD]);
+  float num = 0.0f, den = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const float l = pp[s * (HD + 2) + HD + 1];
+    if (l > 0.0f) {
+      const float f = __expf(pp[s * (HD + 2) + HD] - mx);
+      num = fmaf(f, pp[s * (HD + 2) + dd], num);
+      den = fmaf(f, l, den);
+    }
+  }
+  const float v = num / den;
+  const size_t idx = ((size_t)m * Hq + h) * HD + dd;
+  if (P == kBF16) static_cast<uint16_t*>(O)[idx] = (uint16_t)act_encode<P>(v, scale);
+  else static_cast<uint8_t*>(O)[idx] = (uint8_t)act_encode<P>(v, scale);
+}
+
+// Each stream's codes of the step: per codebook the greedy argmax over the allowed ids
+// (codebook 0: codes and EOS; the others: codes; ties to the lowest id; a NaN logit never
+// wins), then the delay rule and the state advance, as in the decode frame kernel.
+__global__ __launch_bounds__(256) void k_head_select(const float* __restrict__ logits, int ld,
+                                                     DevState* __restrict__ st, int32_t* __restrict__ hist,
+                                                     int max_seq, int C, int V, int bos, int eos) {
+  const int m = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const float* z = logits + (size_t)m * ld;
+  __shared__ int arg[kMaxCodebooks];
+  for (int k = w; k < C; k += nw) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = lane; i < V; i += 64) {
+      const float v = z[(size_t)k * V + i];
+      const bool allowed = (i < bos) || (k == 0 && i == eos);
+      const float x = v == v ? v : -INFINITY;
+      if (allowed && (x > bv || (x == bv && i < bi))) { bv = x; bi = i; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0) arg[k] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    DevState* s = st + m;
+    const int t = s->t;
+    int eoc = s->eoc;
+    if (eoc < 0 && t > 0 && s->prev[0] == eos) eoc = t - 1;  // EOC from the fed-back code
+    int codes[kMaxCodebooks];
+    for (int k = 0; k < C; ++k) codes[k] = t < k ? bos : ((eoc >= 0 && t >= eoc + k) ? eos : arg[k]);
+    const int eoc2 = eoc >= 0 ? eoc : (codes[0] == eos ? t : -1);
+    const int done = (eoc2 >= 0 && t >= eoc2 + C - 1) ? 1 : 0;
+    for (int k = 0; k < C; ++k) {
+      s->codes[k] = codes[k];
+      s->prev[k] = codes[k];
+      hist[((size_t)m * max_seq + t) * C + k] = codes[k];
+    }
+    s->eoc = eoc;
+    s->t = t + 1;
+    s->len = s->len + 1;
+    s->done = done;
+    s->n_done += done;
+  }
+}
+
+template <int P>
+static hipError_t batch_step_p(Ctx& c) {
+  const auto& f = c.cfg;
+  const int M = c.lay.n_streams, S = c.lay.batch_splits;
+  const int d = f.hidden, hd = f.head_dim, Hq = f.n_q_heads, Hkv = f.n_kv_heads, G = Hq / Hkv;
+  const int qd = Hq * hd, kvd = Hkv * hd, F = f.ffn, W = qd + 2 * kvd;
+  const long kvs = (long)(c.lay.kv_stream_bytes / 2);
+  const int len_stride = (int)(sizeof(DevState) / sizeof(int));
+  hipError_t e;
+  hipLaunchKernelGGL(k_embed_codes_rows, dim3(M), dim3(256), 0, c.stream, c.state_base, c.e_aud, c.px, d,
+                     f.n_codebooks, f.codebook_size);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int layer = 0; layer < f.n_layers; ++layer) {
+    const LayerW& L = c.layers[layer];
+    const int s0 = kSitesPerLayer * layer;
+    hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px, L.g_attn, f.rms_eps, c.pu, d,
+                       host_act_scale(c, s0), nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = gemm<P>(c, c.pu, L.w_qkv, L.s_qkv, host_act_scale(c, s0), c.pqkv, M, W, d, 0)) != hipSuccess) return e;
+    if (hd == 128)
+      hipLaunchKernelGGL(k_qk_rope_rows<128>, dim3(M), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
+                         c.rope_sin, c.pq, c.k_base[layer], c.v_base[layer], &c.state_base->len, Hq, Hkv, f.max_seq,
+                         f.rms_eps, len_stride, kvs);
+    else
+      hipLaunchKernelGGL(k_qk_rope_rows<64>, dim3(M), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
+                         c.rope_sin, c.pq, c.k_base[layer], c.v_base[layer], &c.state_base->len, Hq, Hkv, f.max_seq,
+                         f.rms_eps, len_stride, kvs);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (hd == 128)
+      hipLaunchKernelGGL(k_attn_rows<128>, dim3(S, Hkv, M), dim3(64 * G), 0, c.stream, c.pq, c.k_base[layer],
+                         c.v_base[layer], kvs, c.state_base, Hq, Hkv, f.max_seq, c.b_part);
+    else
+      hipLaunchKernelGGL(k_attn_rows<64>, dim3(S, Hkv, M), dim3(64 * G), 0, c.stream, c.pq, c.k_base[layer],
+                         c.v_base[layer], kvs, c.state_base, Hq, Hkv, f.max_seq, c.b_part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (hd == 128)
+      hipLaunchKernelGGL((k_attn_combine<P, 128>), dim3(Hq, M), dim3(128), 0, c.stream, c.b_part, S, Hq, c.po,
+                         host_act_scale(c, s0 + 1));
+    else
+      hipLaunchKernelGGL((k_attn_combine<P, 64>), dim3(Hq, M), dim3(64), 0, c.stream, c.b_part, S, Hq, c.po,
+                         host_act_scale(c, s0 + 1));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = gemm<P>(c, c.po, L.w_o, L.s_o, host_act_scale(c, s0 + 1), c.px, M, d, qd, 1)) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px, L.g_mlp, f.rms_eps, c.pu, d,
+                       host_act_scale(c, s0 + 2), nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = gemm<P>(c, c.pu, L.w_gu, L.s_gu, host_act_scale(c, s0 + 2), c.pgu, M, 2 * F, d, 0, c.pa,
+                     host_act_scale(c, s0 + 3), nullptr)) != hipSuccess)
+      return e;
+    if ((e = gemm<P>(c, c.pa, L.w_d, L.s_d, host_act_scale(c, s0 + 3), c.px, M, d, F, 1)) != hipSuccess) return e;
+  }
+  const int hs = kSitesPerLayer * f.n_layers;  // the head input's site
+  hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px, c.g_final, f.rms_eps, c.pu, d,
+                     host_act_scale(c, hs), nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = gemm<P>(c, c.pu, c.w_head, c.s_head, host_act_scale(c, hs), c.b_logits, M, c.lay.cv_pad, d, 0)) !=
+      hipSuccess)
+    return e;
+  hipLaunchKernelGGL(k_head_select, dim3(M), dim3(256), 0, c.stream, c.b_logits, c.lay.cv_pad, c.state_base,
+                     c.hist_base, f.max_seq, f.n_codebooks, f.codebook_size, f.bos_id, f.eos_id);
+  return hipGetLastError();
+}
+
+hipError_t launch_batch_step(Ctx& c) {
+  if (c.cfg.n_q_heads / c.cfg.n_kv_heads > 4) return hipErrorInvalidValue;  // one wave per head, 256 threads
+  if (c.cfg.precision == HTA_FP8_E4M3) return batch_step_p<kFP8>(c);
+  return batch_step_p<kBF16>(c);
 }
 
 hipError_t prefill_setup() {

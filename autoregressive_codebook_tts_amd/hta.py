@@ -40,7 +40,8 @@ class HtaConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn",
                                              "text_vocab", "n_codebooks", "codebook_size", "bos_id", "eos_id")] + [
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
-        ("max_seq", ctypes.c_int), ("max_prefill", ctypes.c_int), ("precision", ctypes.c_int)]
+        ("max_seq", ctypes.c_int), ("max_prefill", ctypes.c_int), ("precision", ctypes.c_int),
+        ("n_streams", ctypes.c_int)]
 
 
 class HtaError(RuntimeError):
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "hta_decode_frames": (I, [P, I, P, P]),
             "hta_decode_frames_noalloc": (I, [P, I, P, P]),
             "hta_reset": (I, [P, I]),
+            "hta_select_stream": (I, [P, I]),
             "hta_force_codes": (I, [P, P]),
             "hta_set_sampling": (I, [P, ctypes.c_float, ctypes.c_uint64]),
             "hta_read_tap": (I, [P, I, I, P, S]),
@@ -97,10 +99,10 @@ def _ptr(a: np.ndarray) -> ctypes.c_void_p:
     return ctypes.c_void_p(a.ctypes.data)
 
 
-def make_config(shape, precision: int, max_seq: int, max_prefill: int) -> HtaConfig:
+def make_config(shape, precision: int, max_seq: int, max_prefill: int, n_streams: int = 1) -> HtaConfig:
     return HtaConfig(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
                      shape.text_vocab, shape.n_codebooks, shape.codebook_size, shape.bos_id, shape.eos_id,
-                     float(shape.rope_theta), float(shape.rms_eps), max_seq, max_prefill, precision)
+                     float(shape.rope_theta), float(shape.rms_eps), max_seq, max_prefill, precision, n_streams)
 
 
 def workspace_bytes(cfg: HtaConfig) -> int:
@@ -195,13 +197,14 @@ class Hta:
     runtime is still up and before torch frees the workspace the graph references."""
 
     def __init__(self, shape, precision: str = "bf16", max_seq: int = 2048, max_prefill: int = 512, stream=None,
-                 fill_byte: int | None = None):
+                 fill_byte: int | None = None, n_streams: int = 1):
         import torch
 
         self.torch = torch
         self.shape = shape
         self.precision = precision
-        self.cfg = make_config(shape, HTA_FP8_E4M3 if precision == "fp8" else HTA_BF16, max_seq, max_prefill)
+        self.cfg = make_config(shape, HTA_FP8_E4M3 if precision == "fp8" else HTA_BF16, max_seq, max_prefill, n_streams)
+        self.M = max(1, n_streams)
         self.stream = stream if stream is not None else torch.cuda.Stream()
         self.ctx = ctypes.c_void_p()
         rc = lib().hta_create(ctypes.byref(self.cfg), ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(self.ctx))
@@ -266,15 +269,21 @@ class Hta:
         self._check(lib().hta_prefill(self.ctx, _ptr(t), t.shape[0]), "hta_prefill")
 
     def decode_frame(self):
-        out = np.zeros(self.C, dtype=np.int32)
+        """One step: codes [C] (single stream) or [M][C] (batched)."""
+        out = np.zeros((self.M, self.C) if self.M > 1 else self.C, dtype=np.int32)
         rc = self._check(lib().hta_decode_frame(self.ctx, _ptr(out)), "hta_decode_frame")
         return out, rc == HTA_DONE
 
     def decode_frames(self, n: int):
-        out = np.zeros((n, self.C), dtype=np.int32)
+        """n steps: codes [n][C] (single stream) or [n][M][C] (batched)."""
+        out = np.zeros((n, self.M, self.C) if self.M > 1 else (n, self.C), dtype=np.int32)
         nd = ctypes.c_int(0)
         rc = self._check(lib().hta_decode_frames(self.ctx, n, _ptr(out), ctypes.byref(nd)), "hta_decode_frames")
         return out, rc == HTA_DONE
+
+    def select_stream(self, m: int) -> None:
+        """hta_select_stream: the stream that prefill, reset, force_codes and the taps act on."""
+        self._check(lib().hta_select_stream(self.ctx, m), "hta_select_stream")
 
     def decode_frames_noalloc(self, n: int, out=None):
         """hta_decode_frames_noalloc: the exchange words in the library's static per-GPU array.

@@ -97,6 +97,8 @@ def main() -> int:
                     help="skip the prefix-reuse and KV-4096 decode measurements")
     ap.add_argument("--no-kv-slope", action="store_true",
                     help="skip the chunked utterance that measures frame time against KV length")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip batched multi-stream decode (M = 2, 4, 8, 16 utterances per step)")
     ap.add_argument("--no-one-layer", action="store_true",
                     help="skip the one-layer decode step with one and rotated weight copies")
     ap.add_argument("--no-kernel-classes", action="store_true",
@@ -228,6 +230,9 @@ def main() -> int:
         extra["kernel_us_fp8"] = {k: round(v, 2) for k, v in ctx.time_kernels(32).items() if v > 0}
     ctx.close()
 
+    if shape.n_layers == 36 and not args.no_batched:
+        log("batched multi-stream decode (FP8), M = 2, 4, 8, 16")
+        extra["batched_decode_fp8"] = _batched(shape, w, scales, prompt, ms_frame)
     if shape.n_layers == 36 and not args.no_one_layer:
         log("one-layer decode step at KV 512 / 2048, one weight copy and rotated copies")
         extra["one_layer"] = _one_layer(shape, w, scales)
@@ -296,6 +301,36 @@ def _prefill_sizes(ctx, shape, prec: str) -> dict:
 
 
 LONG_PROMPT, LONG_FRAMES = 4095, 64
+
+
+def _batched(shape, w, scales, prompt, ms_single, Ms=(2, 4, 8, 16), warm: int = 8, frames: int = 64) -> dict:
+    """Batched decode: M utterances (the P=13 prompt's seed plus m) prefilled into one
+    FP8 context, then `warm` steps and `frames` timed steps of all M together (one
+    captured step graph each); aggregate frames/s against the single-stream frame kernel."""
+    import torch
+    import synthetic as S
+    from autoregressive_codebook_tts_amd import hta
+
+    tensors, src = hta.weights_to_device(w, shape.n_layers)
+    out = {"single_stream_frames_per_s": round(1e3 / ms_single, 1)}
+    for M in Ms:
+        ctx = hta.Hta(shape, "fp8", max_seq=len(prompt) + warm + frames + 8, max_prefill=max(16, len(prompt)),
+                      n_streams=M)
+        ctx.load_weights(tensors, src, act_scales=scales)
+        for m in range(M):
+            ctx.select_stream(m)
+            ctx.prefill(S.token_ids(S.SEEDS["full_prompt"] + m, len(prompt), shape.text_vocab))
+        ctx.decode_frames(warm)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(ctx.stream)
+        ctx.decode_frames(frames)
+        e1.record(ctx.stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / frames
+        out[f"M{M}"] = {"ms_per_step": round(ms, 4), "frames_per_s": round(M * 1e3 / ms, 1)}
+        ctx.close()
+    del tensors
+    return out
 
 
 def _frame_vs_kv(ctx, prompt, n_frames: int, chunk: int = 64) -> dict:

@@ -66,9 +66,26 @@ typedef struct {
   int max_seq;       /* KV capacity in positions */
   int max_prefill;   /* largest P accepted by one hta_prefill call */
   int precision;     /* hta_precision */
+  int n_streams;     /* utterances decoded together (batched decode); 0 reads as 1 */
 } hta_config;
 
 typedef struct hta_ctx hta_ctx;
+
+/* Batched decode (SGLang-Omni Higgs Audio v3 page, performance section: requests decoded
+ * concurrently on one GPU).  A context with n_streams = M > 1 holds M independent
+ * utterances, each with its own KV cache, delay state and code history, over one copy of
+ * the weights.  hta_select_stream picks the stream that hta_prefill, hta_reset,
+ * hta_force_codes and hta_read_tap (HIDDEN, LOGITS, STATE, KV) act on.  hta_decode_frame(s)
+ * advance every stream by one step per frame in one batched step: the embedding of each
+ * stream's previous codes, then per layer the M rows through the same GEMMs (one weight
+ * stream shared by all streams), q/k-norm + RoPE + KV write at each stream's own position,
+ * decode attention of each row over its own cache (key splits, log-sum-exp combine), and
+ * the head with each stream's greedy argmax and delay rule; the whole step is one captured
+ * graph.  codes_out then receives n * M * C codes ([frame][stream][codebook]); *n_done
+ * the number of streams whose utterance is done; HTA_DONE when all are.  Limits: 2 <= M
+ * <= 16 and M <= max_prefill; greedy only (hta_set_sampling gives HTA_E_UNSUPPORTED);
+ * hta_calibrate, hta_layer_step, HTA_OPT_TAPS, hta_time_kernels and
+ * hta_decode_frames_noalloc need a single-stream context. */
 
 /* Shape limits the kernels support (hta_create returns HTA_E_UNSUPPORTED otherwise):
  * head_dim 64 or 128; hidden, ffn and the q width (n_q_heads * head_dim) multiples of
@@ -161,6 +178,10 @@ int hta_set_sampling(hta_ctx* ctx, float temperature, uint64_t seed);
  * FlashRT page, section 4) and reset the delay state.  keep_len = 0 is a cold
  * start; keep_len must not exceed the current length. */
 int hta_reset(hta_ctx* ctx, int keep_len);
+
+/* Batched contexts: make stream m (0 <= m < n_streams) the one that the per-stream calls
+ * act on (stream 0 after hta_create).  HTA_E_ARG for m out of range. */
+int hta_select_stream(hta_ctx* ctx, int m);
 
 /* Teacher forcing: the next frame embeds codes_in (host, C codes each in
  * [0, codebook_size)) instead of the last chosen codes; the EOC bookkeeping

@@ -25,8 +25,9 @@ COS_MIN = 0.999
 MARGIN = 1e-2
 
 
-def gpu_context(shape, weights, precision="bf16", max_seq=256, max_prefill=128, act_scales=None, fill_byte=None):
-    ctx = hta.Hta(shape, precision, max_seq=max_seq, max_prefill=max_prefill, fill_byte=fill_byte)
+def gpu_context(shape, weights, precision="bf16", max_seq=256, max_prefill=128, act_scales=None, fill_byte=None,
+                n_streams=1):
+    ctx = hta.Hta(shape, precision, max_seq=max_seq, max_prefill=max_prefill, fill_byte=fill_byte, n_streams=n_streams)
     tensors, src = hta.weights_to_device(weights, shape.n_layers)
     ctx.load_weights(tensors, src, act_scales=act_scales)
     del tensors

@@ -305,6 +305,43 @@ def test_full_bf16_end_to_end(gpu_bf16, oracle_e, oracle_sb):
     assert len(bad) <= len(bad_s) + 2
 
 
+def test_full_batched_bf16_stream_against_exact(w, oracle_e, oracle_sb):
+    """Batched decode at the 36-layer shape: stream 0 of a two-stream BF16 context (stream 1
+    decodes another prompt alongside), teacher-forced by the exact oracle, meets the
+    single-stream end-to-end gates."""
+    prompt = S.token_ids(S.SEEDS["full_prompt"], 13, SH.text_vocab)
+    other = S.token_ids(S.SEEDS["full_prompt"] + 1, 21, SH.text_vocab)
+    oracles = {"E": oracle_e, "S": oracle_sb}
+    for o in oracles.values():
+        o.reset(0)
+        o.prefill(prompt)
+    recs = []
+    with gpu_context(SH, w, "bf16", max_seq=64, max_prefill=32, n_streams=2) as ctx:
+        ctx.select_stream(1)
+        ctx.prefill(other)
+        ctx.select_stream(0)
+        ctx.prefill(prompt)
+        for f in range(4):
+            rec = {"t": f}
+            for m, o in oracles.items():
+                codes, _ = o.decode_frame()
+                rec[m] = {"codes": codes, "hidden": o.last_hidden.copy(), "logits": o.last_logits.copy()}
+            g, _ = ctx.decode_frame()
+            rec["gpu"] = {"codes": g[0], "hidden": ctx.tap_hidden().astype(np.float64),
+                          "logits": ctx.tap_logits().astype(np.float64)}
+            for o in oracles.values():
+                o.force_codes(rec["E"]["codes"])
+            ctx.force_codes(rec["E"]["codes"])
+            recs.append(rec)
+    rel, cos = _worst(recs, "gpu", "E")
+    rel_s, cos_s = _worst(recs, "S", "E")
+    _say(f"[full] batched bf16 stream 0 of 2 (4 frames, vs exact): hidden rel {rel:.3e} (oracle bf16 storage "
+         f"{rel_s:.3e}), logits cos {cos:.6f} (oracle {cos_s:.6f})")
+    assert rel <= HIDDEN_TOL["bf16"]
+    assert rel <= E2E_RATIO * rel_s
+    assert cos >= COS_MIN
+
+
 def test_full_fp8_end_to_end(gpu_fp8, oracle_e, oracle_s8):
     prompt = S.token_ids(S.SEEDS["full_prompt"], 13, SH.text_vocab)
     recs = _teacher_forced(gpu_fp8, {"E": oracle_e, "S": oracle_s8}, prompt, 4, "E")
