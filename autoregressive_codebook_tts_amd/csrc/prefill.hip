@@ -48,19 +48,74 @@ __global__ __launch_bounds__(256) void k_embed_rows(const int32_t* __restrict__ 
 // a memory round trip per element.
 constexpr int kRowPer = 16;  // row elements per thread (rows up to 16 * 256)
 
+// The sum of a column's K-split partials in split order, scaled as k_gemm_reduce
+// scales it (the rounding sequence of k_gemm_reduce, so fusing changes no bit).
+struct SplitIn {
+  const float* part;     // [ks][M][N] partials, or null: no split to add
+  int ks;
+  long plane;            // M * N
+  const float* w_scale;  // e4m3 per-row weight scales, or null
+  float in_scale;
+};
+constexpr int kMaxSplit = 8;  // gemm_ksplit's cap
+// out[u] = the split sum at element idx[u] (column col[u]) for U elements; KS >= si.ks.
+// Every load is issued before the first add (clamped split indices, no load under a
+// condition), so a thread waits one memory round trip, not one per split.
+template <int U, int KS>
+__device__ __forceinline__ void split_sums(const SplitIn& si, const long (&idx)[U], const int (&col)[U],
+                                           float (&out)[U]) {
+  float pv[U][KS], ws[U];
+  const float* wp = si.w_scale ? si.w_scale : si.part;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k) pv[u][k] = si.part[(long)min(k, si.ks - 1) * si.plane + idx[u]];
+    ws[u] = wp[si.w_scale ? col[u] : 0];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      if (k < si.ks) s += pv[u][k];
+    if (si.w_scale) s *= si.in_scale * ws[u];
+    out[u] = s;
+  }
+}
+
+// Row RMSNorm + rounding to the GEMV input format.  With a split input, the row is first
+// updated as residual += (the split sum of the GEMM that produced it), the work of
+// k_gemm_reduce, and the updated residual is stored and normalised.
 template <int P>
-__global__ __launch_bounds__(256) void k_rmsnorm_act_rows(const float* __restrict__ X, const float* __restrict__ g,
+__global__ __launch_bounds__(256) void k_rmsnorm_act_rows(float* __restrict__ X, const float* __restrict__ g,
                                                           float eps, void* __restrict__ U, int d, float scale,
-                                                          float* amax) {
+                                                          float* amax, SplitIn si) {
   __shared__ float red[16];
   const int i = blockIdx.x;
-  const float* x = X + (size_t)i * d;
+  float* x = X + (size_t)i * d;
   float xv[kRowPer], gv[kRowPer];
 #pragma unroll
   for (int u = 0; u < kRowPer; ++u) {
     const int k = u * 256 + threadIdx.x, kc = min(k, d - 1);
     xv[u] = x[kc];
     gv[u] = g[kc];
+  }
+  if (si.part) {
+    float sv[kRowPer];
+    long idx[kRowPer];
+    int col[kRowPer];
+#pragma unroll
+    for (int u = 0; u < kRowPer; ++u) {
+      col[u] = min(u * 256 + (int)threadIdx.x, d - 1);
+      idx[u] = (long)i * d + col[u];
+    }
+    split_sums<kRowPer, kMaxSplit>(si, idx, col, sv);
+#pragma unroll
+    for (int u = 0; u < kRowPer; ++u) {
+      const int k = u * 256 + threadIdx.x;
+      xv[u] += sv[u];
+      if (k < d) x[k] = xv[u];
+    }
   }
   float ss = 0.0f;  // over k = tid, tid + 256, ... in increasing order
 #pragma unroll
@@ -121,13 +176,17 @@ __device__ __forceinline__ void norm_rope_vals(float x0, float x1, float g0, flo
   *b_out = round_bf16(b * c + a * s);
 }
 
+// The q/k/v row comes from QKV, or, with a split input, is the split sum of the GEMM's
+// partials (the work of k_gemm_reduce, element by element in the same order; at most
+// kRopeMaxSplit splits, so that every partial of a thread is loaded in one batch).
+constexpr int kRopeMaxSplit = 4;
 template <int HD>
 __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ QKV, const float* __restrict__ g_q,
                                                       const float* __restrict__ g_k, const float* __restrict__ rope_cos,
                                                       const float* __restrict__ rope_sin, float* __restrict__ Q,
                                                       uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int* __restrict__ len_at,
                                                       int Hq, int Hkv, int max_seq, float eps, int len_stride,
-                                                      long kv_stride) {
+                                                      long kv_stride, SplitIn si) {
   constexpr int H2 = HD / 2;
   // prefill (len_stride 0): row i of a prompt sits at the KV length before the prefill
   // plus i.  Batched decode: row i is stream i, at its own KV length (len_at[i *
@@ -146,11 +205,31 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
   const bool act = lane < H2;
   const int la = act ? lane : 0;
   float x0[kHeadsPerWave], x1[kHeadsPerWave];
+  if (si.part) {
+    long idx[2 * kHeadsPerWave];
+    int col[2 * kHeadsPerWave];
+    float xs[2 * kHeadsPerWave];
 #pragma unroll
-  for (int t = 0; t < kHeadsPerWave; ++t) {
-    const int h = min(w + t * nw, Hq + Hkv - 1);
-    x0[t] = row[(size_t)h * HD + la];
-    x1[t] = row[(size_t)h * HD + la + H2];
+    for (int t = 0; t < kHeadsPerWave; ++t) {
+      const int h = min(w + t * nw, Hq + Hkv - 1);
+      col[2 * t] = h * HD + la;
+      col[2 * t + 1] = h * HD + la + H2;
+      idx[2 * t] = (long)i * W + col[2 * t];
+      idx[2 * t + 1] = (long)i * W + col[2 * t + 1];
+    }
+    split_sums<2 * kHeadsPerWave, kRopeMaxSplit>(si, idx, col, xs);
+#pragma unroll
+    for (int t = 0; t < kHeadsPerWave; ++t) {
+      x0[t] = xs[2 * t];
+      x1[t] = xs[2 * t + 1];
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < kHeadsPerWave; ++t) {
+      const int h = min(w + t * nw, Hq + Hkv - 1);
+      x0[t] = row[(size_t)h * HD + la];
+      x1[t] = row[(size_t)h * HD + la + H2];
+    }
   }
   const float gq0 = g_q[la], gq1 = g_q[la + H2], gk0 = g_k[la], gk1 = g_k[la + H2];
   const float c_ = cs[la], s_ = sn[la];
@@ -176,8 +255,19 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
   }
   constexpr int kVPer = 8;  // Hkv * HD <= 8 * 256
   float vv[kVPer];
+  if (si.part) {
+    long idx[kVPer];
+    int col[kVPer];
 #pragma unroll
-  for (int u = 0; u < kVPer; ++u) vv[u] = row[(size_t)(Hq + Hkv) * HD + min(u * 256 + (int)threadIdx.x, Hkv * HD - 1)];
+    for (int u = 0; u < kVPer; ++u) {
+      col[u] = (Hq + Hkv) * HD + min(u * 256 + (int)threadIdx.x, Hkv * HD - 1);
+      idx[u] = (long)i * W + col[u];
+    }
+    split_sums<kVPer, kRopeMaxSplit>(si, idx, col, vv);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) vv[u] = row[(size_t)(Hq + Hkv) * HD + min(u * 256 + (int)threadIdx.x, Hkv * HD - 1)];
+  }
 #pragma unroll
   for (int u = 0; u < kVPer; ++u) {
     const int e = u * 256 + threadIdx.x;
@@ -626,31 +716,64 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, co
 // For M >= 64.  The products and their order are those of k_gemm (per 16x16 tile:
 // bf16 in 32-wide K chunks of increasing K; e4m3 per 64-wide chunk, the low 8 bytes
 // of every lane's 16-byte unit and then the high 8 bytes) and so is the K split, so a
-// row's result is bit-identical whichever of the two kernels computes it.
-// A block computes 128 rows x 128 columns with 4 waves of 64 x 64.  Per stage, 64
-// bytes of K of each of the 128 A rows and 128 B rows (8 KB + 8 KB) are fetched
-// straight into LDS (global_load_lds_dwordx4) through a ring of kGS stages issued
-// kGS - 1 ahead of the stage being multiplied, so no register holds data in flight
-// and the B tile is shared by the waves.  A stage's 16-byte units are swizzled within
-// each row (unit u of row r at position 4r + (u ^ ((r >> 2) & 3))), so that a fragment
-// read (16 consecutive rows, one unit each) touches 16 different bank groups.
+// row's result is bit-identical whichever of the two kernels, and whichever tile shape,
+// computes it.
+// A block computes BM rows x BN columns with 4 waves of 64 rows x BN / (4 / (BM / 64))
+// columns.  Per stage, 64 bytes of K of each of the BM A rows and BN B rows are fetched
+// straight into LDS (global_load_lds_dwordx4) through a ring of NS stages issued NS - 1
+// ahead of the stage being multiplied, so no register holds data in flight and a B tile
+// is shared by the waves.  A stage's 16-byte units are swizzled within each row (unit u
+// of row r at position 4r + (u ^ ((r >> 2) & 3))), so that a fragment read (16
+// consecutive rows, one unit each) touches 16 different bank groups.
+// Tile shapes (measured on the 36-layer shapes against the 128 x 128 four-stage tile):
+// M >= 256 takes 128 x 128 with three stages (48 KB, three blocks per CU: the 560-608
+// block grids then fit in one wave of the chip).  Below that, e4m3 takes 64 x 64 with
+// four stages (32 KB), which puts 2-4x more blocks on the CUs than one 128-row tile
+// can; bf16 keeps 128 x 128 with four stages, as a 64 x 64 bf16 tile has too few MFMAs
+// per stage (8 per wave) for its barrier.
+// The grid's blocks are dealt to the 8 XCDs round robin; the kernel maps them back so
+// that each XCD walks a contiguous run of tiles (row tiles of one column tile first),
+// which then share that column tile's weights in the XCD's L2.
 constexpr int kGemmTileMinM = 64;        // smaller M: k_gemm (weights streamed once per 16 or 32 rows)
-constexpr int kGS = 4;                    // LDS stages
-constexpr int kGT = 128;                  // tile rows (A) and columns (B)
-constexpr int kGHalf = kGT * 64;          // bytes of one operand's tile per stage
-constexpr int kGStage = 2 * kGHalf;
+constexpr int kGemmTileBigM = 256;       // from here: 128 x 128 tiles
 
-size_t gemm_tile_lds_bytes() { return (size_t)kGS * kGStage; }
+template <int BM, int BN, int NS>
+struct TileCfg {
+  static constexpr int WMW = BM / 64, WNW = 4 / WMW, WN = BN / WNW, NJ = WN / 16;
+  static constexpr int HA = BM * 64, HB = BN * 64, STG = HA + HB;  // bytes per stage
+  static constexpr int UA = BM * 4, UB = BN * 4;                  // 16-byte units per stage
+  static constexpr int LA = UA / 256, LB = UB / 256;                // fetches per wave and stage
+  static_assert(WMW * WNW == 4 && NJ >= 1 && WN % 16 == 0, "four waves of 64 x 16k");
+  static_assert(LA * 256 == UA && LB * 256 == UB, "every wave fetches the same count");
+  static_assert(NS >= 3, "ring of at least three stages");
+};
+
+template <int BM, int BN, int NS>
+size_t gemm_tile_lds_bytes() { return (size_t)NS * TileCfg<BM, BN, NS>::STG; }
 
 __device__ __forceinline__ int tile_unit_pos(int row, int u) { return row * 4 + (u ^ ((row >> 2) & 3)); }
 
-template <int P>
+template <int P, int BM, int BN, int NS>
 __global__ __launch_bounds__(256) void k_gemm_tile(const void* __restrict__ A, const void* __restrict__ B,
                                                    float* __restrict__ Cpart, int M, int N, int K, int ksplit,
                                                    GemmEpi epi) {
+  using T = TileCfg<BM, BN, NS>;
+  constexpr int NJ = T::NJ, WN = T::WN;
   extern __shared__ __align__(16) unsigned char gsm[];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int m0 = blockIdx.x * kGT, n0 = blockIdx.y * kGT, ks = blockIdx.z;
+  int mt, nt, ks;
+  {
+    // block L runs on XCD L % 8; give XCD x the contiguous tile run [start(x), start(x) + count(x))
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int total = gx * gy * (int)gridDim.z;
+    const int L = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const int x = L & 7, i = L >> 3, q = total >> 3, r = total & 7;
+    const int t = x * q + (x < r ? x : r) + i;
+    mt = t % gx;
+    nt = (t / gx) % gy;
+    ks = t / (gx * gy);
+  }
+  const int m0 = mt * BM, n0 = nt * BN;
   constexpr int EB = (P == kBF16) ? 2 : 1;
   const int rowbytes = K * EB;  // operands below 2^31 bytes
   const int nsteps = K / 128;   // the split is over 128-element steps, as in k_gemm
@@ -658,81 +781,89 @@ __global__ __launch_bounds__(256) void k_gemm_tile(const void* __restrict__ A, c
   constexpr int CPS = 128 * EB / 64;  // 64-byte chunks per 128-element step
   const int c0 = s_beg * CPS, nch = (s_end - s_beg) * CPS;
 
-  // this wave fetches units [64 * (2w + j), +64) of each operand's tile, j = 0, 1
-  int voffA[2], voffB[2];
+  // this wave fetches units [64 * (w + 4 j), +64) of each operand's tile
+  int voffA[T::LA], voffB[T::LB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int p = 64 * (2 * w + j) + lane, row = p >> 2, u = (p & 3) ^ ((row >> 2) & 3);
+  for (int j = 0; j < T::LA; ++j) {
+    const int p = 64 * (w + 4 * j) + lane, row = p >> 2, u = (p & 3) ^ ((row >> 2) & 3);
     const int ra = m0 + row < M ? m0 + row : M - 1;  // rows past M fetch row M - 1 (results unused)
     voffA[j] = ra * rowbytes + u * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < T::LB; ++j) {
+    const int p = 64 * (w + 4 * j) + lane, row = p >> 2, u = (p & 3) ^ ((row >> 2) & 3);
     voffB[j] = (n0 + row) * rowbytes + u * 16;
   }
   const unsigned char* Ab = static_cast<const unsigned char*>(A);
   const unsigned char* Bb = static_cast<const unsigned char*>(B);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)gsm);
-  auto issue = [&](int c) {  // fetch chunk c into stage c % kGS
-    const uint32_t sb = lds0 + (uint32_t)(c % kGS) * kGStage;
+  auto issue = [&](int c) {  // fetch chunk c into stage c % NS
+    const uint32_t sb = lds0 + (uint32_t)(c % NS) * T::STG;
     const unsigned char* a = Ab + (size_t)(c0 + c) * 64;
     const unsigned char* b = Bb + (size_t)(c0 + c) * 64;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t ma = __builtin_amdgcn_readfirstlane(sb + (uint32_t)(2 * w + j) * 1024u);
-      const uint32_t mb = __builtin_amdgcn_readfirstlane(sb + kGHalf + (uint32_t)(2 * w + j) * 1024u);
+    for (int j = 0; j < T::LA; ++j) {
+      const uint32_t ma = __builtin_amdgcn_readfirstlane(sb + (uint32_t)(w + 4 * j) * 1024u);
       asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                    : : "v"(voffA[j]), "s"(a), "s"(ma) : "memory", "m0");
+    }
+#pragma unroll
+    for (int j = 0; j < T::LB; ++j) {
+      const uint32_t mb = __builtin_amdgcn_readfirstlane(sb + T::HA + (uint32_t)(w + 4 * j) * 1024u);
       asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                    : : "v"(voffB[j]), "s"(b), "s"(mb) : "memory", "m0");
     }
   };
-  for (int c = 0; c < kGS - 1 && c < nch; ++c) issue(c);
+  for (int c = 0; c < NS - 1 && c < nch; ++c) issue(c);
 
-  const int wm = w >> 1, wn = w & 1, g = lane >> 4, r16 = lane & 15;
-  int fa[4], fb[4];  // byte offsets of this lane's fragment units within a stage
+  const int wm = w / T::WNW, wn = w % T::WNW, g = lane >> 4, r16 = lane & 15;
+  int fa[4], fb[NJ];  // byte offsets of this lane's fragment units within a stage
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fa[i] = tile_unit_pos(64 * wm + 16 * i + r16, g) * 16;
-    fb[i] = kGHalf + tile_unit_pos(64 * wn + 16 * i + r16, g) * 16;
-  }
-  f32x4 acc[4][4];
+  for (int i = 0; i < 4; ++i) fa[i] = tile_unit_pos(64 * wm + 16 * i + r16, g) * 16;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) fb[j] = T::HA + tile_unit_pos(WN * wn + 16 * j + r16, g) * 16;
+  f32x4 acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int c = 0; c < nch; ++c) {
-    // chunk c has landed once at most the fetches of the kGS - 2 younger chunks remain
-    // (4 per chunk and wave; loads land in issue order)
-    if (c + kGS - 2 < nch) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    // chunk c has landed once at most the fetches of the NS - 2 younger chunks remain
+    // (LA + LB per chunk and wave; loads land in issue order)
+    if (c + NS - 2 < nch) asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * (T::LA + T::LB)) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // every wave's part of chunk c is in, and chunk c - 1 is consumed
-    if (c + kGS - 1 < nch) issue(c + kGS - 1);
-    const unsigned char* st = gsm + (c % kGS) * kGStage;
-    uint4 av[4], bv[4];
+    if (c + NS - 1 < nch) issue(c + NS - 1);
+    const unsigned char* st = gsm + (c % NS) * T::STG;
+    uint4 av[4], bv[NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      av[i] = *reinterpret_cast<const uint4*>(st + fa[i]);
-      bv[i] = *reinterpret_cast<const uint4*>(st + fb[i]);
-    }
+    for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const uint4*>(st + fa[i]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bv[j] = *reinterpret_cast<const uint4*>(st + fb[j]);
     if (P == kBF16) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i]),
                                                                __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
     } else {
-      bf16x8 al[4], ah[4], bl[4], bh[4];
+      bf16x8 al[4], ah[4], bl[NJ], bh[NJ];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         al[i] = fp8x8_to_bf16(av[i].x, av[i].y);
         ah[i] = fp8x8_to_bf16(av[i].z, av[i].w);
-        bl[i] = fp8x8_to_bf16(bv[i].x, bv[i].y);
-        bh[i] = fp8x8_to_bf16(bv[i].z, bv[i].w);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        bl[j] = fp8x8_to_bf16(bv[j].x, bv[j].y);
+        bh[j] = fp8x8_to_bf16(bv[j].z, bv[j].w);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bl[j], acc[i][j], 0, 0, 0);
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
         }
@@ -745,8 +876,8 @@ __global__ __launch_bounds__(256) void k_gemm_tile(const void* __restrict__ A, c
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + 64 * wn + 16 * j + r16;
+      for (int j = 0; j < NJ; ++j) {
+        const int col = n0 + WN * wn + 16 * j + r16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = m0 + 64 * wm + 16 * i + 4 * g + r;
@@ -771,8 +902,8 @@ __global__ __launch_bounds__(256) void k_gemm_tile(const void* __restrict__ A, c
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + 64 * wn + 16 * j + r16;
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + WN * wn + 16 * j + r16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + 64 * wm + 16 * i + 4 * g + r;
@@ -811,12 +942,27 @@ static int gemm_ksplit(int N, int K) {
   return s;
 }
 
+static float* split_buffer(Ctx& c) { return c.pgu + (size_t)c.cfg.max_prefill * 2 * c.cfg.ffn; }
+
+// The split partials of the last gemm(..., defer = true) as the next row kernel's input
+// (null part when K was not split: the GEMM's epilogue then finished the output).
+template <int P>
+static SplitIn deferred_split(Ctx& c, int M, int N, int K, const float* w_scale, float in_scale) {
+  const int ks = gemm_ksplit(N, K);
+  if (ks == 1) return SplitIn{nullptr, 0, 0, nullptr, 1.0f};
+  return SplitIn{split_buffer(c), ks, (long)M * N, P == kFP8 ? w_scale : nullptr, in_scale};
+}
+
+// defer: with K split, leave the partials for the next row kernel (deferred_split)
+// instead of launching k_gemm_reduce; only for outputs without the SiLU epilogue.
 template <int P>
 static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scale, float in_scale, float* out, int M,
-                       int N, int K, int resid, void* act = nullptr, float act_scale = 1.0f, float* amax = nullptr) {
+                       int N, int K, int resid, void* act = nullptr, float act_scale = 1.0f, float* amax = nullptr,
+                       bool defer = false) {
   if (N % 64 != 0 || K % 128 != 0) return hipErrorInvalidValue;  // the kernels' tiling
+  if (defer && act) return hipErrorInvalidValue;
   const int ks = gemm_ksplit(N, K);
-  float* part = c.pgu + (size_t)c.cfg.max_prefill * 2 * c.cfg.ffn;  // split partials after the gate/up buffer
+  float* part = split_buffer(c);  // split partials after the gate/up buffer
   const GemmEpi epi{out, P == kFP8 ? w_scale : nullptr, in_scale, act ? 2 : (resid ? 1 : 0), act, act_scale, amax};
   hipError_t e;
   if (M < kGemmTileMinM) {
@@ -849,12 +995,20 @@ static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scal
         hipLaunchKernelGGL((k_gemm<P, 2, 2>), grid, dim3(128), (skinny_lds_bytes<P, 2, 2>()), c.stream, A, B, part,
                            M, N, K, ks, epi);
     }
+  } else if (N % 128 != 0 || (M < kGemmTileBigM && P == kFP8)) {
+    dim3 grid((M + 63) / 64, N / 64, ks);
+    hipLaunchKernelGGL((k_gemm_tile<P, 64, 64, 4>), grid, dim3(256), (gemm_tile_lds_bytes<64, 64, 4>()), c.stream,
+                       A, B, part, M, N, K, ks, epi);
+  } else if (M < kGemmTileBigM) {
+    dim3 grid((M + 127) / 128, N / 128, ks);
+    hipLaunchKernelGGL((k_gemm_tile<P, 128, 128, 4>), grid, dim3(256), (gemm_tile_lds_bytes<128, 128, 4>()),
+                       c.stream, A, B, part, M, N, K, ks, epi);
   } else {
-    dim3 grid((M + kGT - 1) / kGT, N / kGT, ks);
-    hipLaunchKernelGGL(k_gemm_tile<P>, grid, dim3(256), gemm_tile_lds_bytes(), c.stream, A, B, part, M, N, K, ks,
-                       epi);
+    dim3 grid((M + 127) / 128, N / 128, ks);
+    hipLaunchKernelGGL((k_gemm_tile<P, 128, 128, 3>), grid, dim3(256), (gemm_tile_lds_bytes<128, 128, 3>()),
+                       c.stream, A, B, part, M, N, K, ks, epi);
   }
-  if ((e = hipGetLastError()) != hipSuccess || ks == 1) return e;  // one split: the epilogue ran in the GEMM
+  if ((e = hipGetLastError()) != hipSuccess || ks == 1 || defer) return e;  // one split: the epilogue ran in the GEMM
   const size_t MN = (size_t)M * N;
   hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, c.stream, part, out,
                      P == kFP8 ? w_scale : nullptr, in_scale, M, N, ks, resid);
@@ -881,23 +1035,33 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
   hipLaunchKernelGGL(k_embed_rows, dim3(Pn), dim3(256), 0, c.stream, c.tok, c.e_text, c.px, d);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t tap_bytes = (size_t)Pn * d * 4;
+  const SplitIn none{nullptr, 0, 0, nullptr, 1.0f};
+  bool normed = false;  // c.pu holds this layer's attention input (normed with the last down's split sum)
   for (int layer = 0; layer < f.n_layers; ++layer) {
     const LayerW& L = c.layers[layer];
     const int s0 = kSitesPerLayer * layer;
     const bool tap = c.taps && layer == c.prefill_tap_layer;
     if (tap && (e = hipMemcpyAsync(c.taps_p, c.px, tap_bytes, hipMemcpyDeviceToDevice, c.stream)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, L.g_attn, f.rms_eps, c.pu, d,
-                       host_act_scale(c, s0), amax ? amax + s0 : nullptr);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = gemm<P>(c, c.pu, L.w_qkv, L.s_qkv, host_act_scale(c, s0), c.pqkv, Pn, W, d, 0)) != hipSuccess) return e;
-    if (hd == 128)
-      hipLaunchKernelGGL(k_qk_rope_rows<128>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
-                         c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L);
-    else
-      hipLaunchKernelGGL(k_qk_rope_rows<64>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
-                         c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!normed) {
+      hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, L.g_attn, f.rms_eps, c.pu,
+                         d, host_act_scale(c, s0), amax ? amax + s0 : nullptr, none);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const bool defer_q = gemm_ksplit(W, d) <= kRopeMaxSplit;  // else k_gemm_reduce finishes the rows
+    if ((e = gemm<P>(c, c.pu, L.w_qkv, L.s_qkv, host_act_scale(c, s0), c.pqkv, Pn, W, d, 0, nullptr, 1.0f, nullptr,
+                     defer_q)) != hipSuccess)
+      return e;
+    {
+      const SplitIn sq = defer_q ? deferred_split<P>(c, Pn, W, d, L.s_qkv, host_act_scale(c, s0)) : none;
+      if (hd == 128)
+        hipLaunchKernelGGL(k_qk_rope_rows<128>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
+                           c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L, sq);
+      else
+        hipLaunchKernelGGL(k_qk_rope_rows<64>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
+                           c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L, sq);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     {
       const int G = Hq / Hkv;
       dim3 grid(Hkv, (Pn + kAttnQT - 1) / kAttnQT);
@@ -916,14 +1080,30 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
 #undef HTA_ATTN
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if ((e = gemm<P>(c, c.po, L.w_o, L.s_o, host_act_scale(c, s0 + 1), c.px, Pn, d, qd, 1)) != hipSuccess) return e;
+    if ((e = gemm<P>(c, c.po, L.w_o, L.s_o, host_act_scale(c, s0 + 1), c.px, Pn, d, qd, 1, nullptr, 1.0f, nullptr,
+                     true)) != hipSuccess)
+      return e;
     hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, L.g_mlp, f.rms_eps, c.pu, d,
-                       host_act_scale(c, s0 + 2), amax ? amax + s0 + 2 : nullptr);
+                       host_act_scale(c, s0 + 2), amax ? amax + s0 + 2 : nullptr,
+                       deferred_split<P>(c, Pn, d, qd, L.s_o, host_act_scale(c, s0 + 1)));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = gemm<P>(c, c.pu, L.w_gu, L.s_gu, host_act_scale(c, s0 + 2), c.pgu, Pn, 2 * F, d, 0, c.pa,
                      host_act_scale(c, s0 + 3), amax ? amax + s0 + 3 : nullptr)) != hipSuccess)
       return e;
-    if ((e = gemm<P>(c, c.pa, L.w_d, L.s_d, host_act_scale(c, s0 + 3), c.px, Pn, d, F, 1)) != hipSuccess) return e;
+    // the next layer's attention norm takes the down projection's split sum (the last
+    // layer's residual is finished by the reduce: the prefill emits no norm after it)
+    const bool fuse_next = layer + 1 < f.n_layers && gemm_ksplit(d, F) > 1;
+    if ((e = gemm<P>(c, c.pa, L.w_d, L.s_d, host_act_scale(c, s0 + 3), c.px, Pn, d, F, 1, nullptr, 1.0f, nullptr,
+                     fuse_next)) != hipSuccess)
+      return e;
+    normed = fuse_next;
+    if (fuse_next) {
+      const int s1 = s0 + kSitesPerLayer;
+      hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, c.layers[layer + 1].g_attn,
+                         f.rms_eps, c.pu, d, host_act_scale(c, s1), amax ? amax + s1 : nullptr,
+                         deferred_split<P>(c, Pn, d, F, L.s_d, host_act_scale(c, s0 + 3)));
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (tap && (e = hipMemcpyAsync(c.taps_p + (size_t)f.max_prefill * d, c.px, tap_bytes, hipMemcpyDeviceToDevice,
                                    c.stream)) != hipSuccess)
       return e;
@@ -1116,22 +1296,31 @@ static hipError_t batch_step_p(Ctx& c) {
   hipLaunchKernelGGL(k_embed_codes_rows, dim3(M), dim3(256), 0, c.stream, c.state_base, c.e_aud, c.px, d,
                      f.n_codebooks, f.codebook_size);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  const SplitIn none{nullptr, 0, 0, nullptr, 1.0f};
   for (int layer = 0; layer < f.n_layers; ++layer) {
     const LayerW& L = c.layers[layer];
     const int s0 = kSitesPerLayer * layer;
-    hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px, L.g_attn, f.rms_eps, c.pu, d,
-                       host_act_scale(c, s0), nullptr);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = gemm<P>(c, c.pu, L.w_qkv, L.s_qkv, host_act_scale(c, s0), c.pqkv, M, W, d, 0)) != hipSuccess) return e;
-    if (hd == 128)
-      hipLaunchKernelGGL(k_qk_rope_rows<128>, dim3(M), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
-                         c.rope_sin, c.pq, c.k_base[layer], c.v_base[layer], &c.state_base->len, Hq, Hkv, f.max_seq,
-                         f.rms_eps, len_stride, kvs);
-    else
-      hipLaunchKernelGGL(k_qk_rope_rows<64>, dim3(M), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
-                         c.rope_sin, c.pq, c.k_base[layer], c.v_base[layer], &c.state_base->len, Hq, Hkv, f.max_seq,
-                         f.rms_eps, len_stride, kvs);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (layer == 0) {  // later layers' attention inputs are normed with the previous down's split sum
+      hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px, L.g_attn, f.rms_eps, c.pu,
+                         d, host_act_scale(c, s0), nullptr, none);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const bool defer_q = gemm_ksplit(W, d) <= kRopeMaxSplit;  // else k_gemm_reduce finishes the rows
+    if ((e = gemm<P>(c, c.pu, L.w_qkv, L.s_qkv, host_act_scale(c, s0), c.pqkv, M, W, d, 0, nullptr, 1.0f, nullptr,
+                     defer_q)) != hipSuccess)
+      return e;
+    {
+      const SplitIn sq = defer_q ? deferred_split<P>(c, M, W, d, L.s_qkv, host_act_scale(c, s0)) : none;
+      if (hd == 128)
+        hipLaunchKernelGGL(k_qk_rope_rows<128>, dim3(M), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
+                           c.rope_sin, c.pq, c.k_base[layer], c.v_base[layer], &c.state_base->len, Hq, Hkv,
+                           f.max_seq, f.rms_eps, len_stride, kvs, sq);
+      else
+        hipLaunchKernelGGL(k_qk_rope_rows<64>, dim3(M), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
+                           c.rope_sin, c.pq, c.k_base[layer], c.v_base[layer], &c.state_base->len, Hq, Hkv,
+                           f.max_seq, f.rms_eps, len_stride, kvs, sq);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (hd == 128)
       hipLaunchKernelGGL(k_attn_rows<128>, dim3(S, Hkv, M), dim3(64 * G), 0, c.stream, c.pq, c.k_base[layer],
                          c.v_base[layer], kvs, c.state_base, Hq, Hkv, f.max_seq, c.b_part);
@@ -1146,21 +1335,28 @@ static hipError_t batch_step_p(Ctx& c) {
       hipLaunchKernelGGL((k_attn_combine<P, 64>), dim3(Hq, M), dim3(64), 0, c.stream, c.b_part, S, Hq, c.po,
                          host_act_scale(c, s0 + 1));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = gemm<P>(c, c.po, L.w_o, L.s_o, host_act_scale(c, s0 + 1), c.px, M, d, qd, 1)) != hipSuccess) return e;
+    if ((e = gemm<P>(c, c.po, L.w_o, L.s_o, host_act_scale(c, s0 + 1), c.px, M, d, qd, 1, nullptr, 1.0f, nullptr,
+                     true)) != hipSuccess)
+      return e;
     hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px, L.g_mlp, f.rms_eps, c.pu, d,
-                       host_act_scale(c, s0 + 2), nullptr);
+                       host_act_scale(c, s0 + 2), nullptr, deferred_split<P>(c, M, d, qd, L.s_o, host_act_scale(c, s0 + 1)));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = gemm<P>(c, c.pu, L.w_gu, L.s_gu, host_act_scale(c, s0 + 2), c.pgu, M, 2 * F, d, 0, c.pa,
                      host_act_scale(c, s0 + 3), nullptr)) != hipSuccess)
       return e;
-    if ((e = gemm<P>(c, c.pa, L.w_d, L.s_d, host_act_scale(c, s0 + 3), c.px, M, d, F, 1)) != hipSuccess) return e;
+    if ((e = gemm<P>(c, c.pa, L.w_d, L.s_d, host_act_scale(c, s0 + 3), c.px, M, d, F, 1, nullptr, 1.0f, nullptr,
+                     true)) != hipSuccess)
+      return e;
+    // the down projection's split sum feeds the next layer's attention norm, or the final norm
+    const bool last = layer + 1 == f.n_layers;
+    const int s1 = last ? kSitesPerLayer * f.n_layers : s0 + kSitesPerLayer;
+    hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px,
+                       last ? c.g_final : c.layers[layer + 1].g_attn, f.rms_eps, c.pu, d, host_act_scale(c, s1), nullptr,
+                       deferred_split<P>(c, M, d, F, L.s_d, host_act_scale(c, s0 + 3)));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const int hs = kSitesPerLayer * f.n_layers;  // the head input's site
-  hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px, c.g_final, f.rms_eps, c.pu, d,
-                     host_act_scale(c, hs), nullptr);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = gemm<P>(c, c.pu, c.w_head, c.s_head, host_act_scale(c, hs), c.b_logits, M, c.lay.cv_pad, d, 0)) !=
-      hipSuccess)
+  if ((e = gemm<P>(c, c.pu, c.w_head, c.s_head, host_act_scale(c, kSitesPerLayer * f.n_layers), c.b_logits, M,
+                   c.lay.cv_pad, d, 0)) != hipSuccess)
     return e;
   hipLaunchKernelGGL(k_head_select, dim3(M), dim3(256), 0, c.stream, c.b_logits, c.lay.cv_pad, c.state_base,
                      c.hist_base, f.max_seq, f.n_codebooks, f.codebook_size, f.bos_id, f.eos_id);
@@ -1175,8 +1371,11 @@ hipError_t launch_batch_step(Ctx& c) {
 
 hipError_t prefill_setup() {
   const struct { const void* f; size_t lds; } kernels[] = {
-      {(const void*)k_gemm_tile<kBF16>, gemm_tile_lds_bytes()},
-      {(const void*)k_gemm_tile<kFP8>, gemm_tile_lds_bytes()},
+      {(const void*)k_gemm_tile<kBF16, 64, 64, 4>, gemm_tile_lds_bytes<64, 64, 4>()},
+      {(const void*)k_gemm_tile<kFP8, 64, 64, 4>, gemm_tile_lds_bytes<64, 64, 4>()},
+      {(const void*)k_gemm_tile<kBF16, 128, 128, 3>, gemm_tile_lds_bytes<128, 128, 3>()},
+      {(const void*)k_gemm_tile<kBF16, 128, 128, 4>, gemm_tile_lds_bytes<128, 128, 4>()},
+      {(const void*)k_gemm_tile<kFP8, 128, 128, 3>, gemm_tile_lds_bytes<128, 128, 3>()},
       {(const void*)k_gemm<kBF16, 1, 4>, skinny_lds_bytes<kBF16, 1, 4>()},
       {(const void*)k_gemm<kBF16, 2, 4>, skinny_lds_bytes<kBF16, 2, 4>()},
       {(const void*)k_gemm<kFP8, 1, 4>, skinny_lds_bytes<kFP8, 1, 4>()},
