@@ -345,11 +345,16 @@ __global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict
   for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
 
   // key/value tile loads: 16-byte segments, every load of a thread issued before its use;
-  // the next tile is fetched while the current one is used
+  // the next tile is fetched while the current one is used.  K segments are stored as
+  // they come ([key][dim]); V is stored transposed ([dim][key]) for the P V operand, so a
+  // thread loads the same segment of two neighbouring keys and writes each dim's pair of
+  // values as one 32-bit word: the 32 key pairs of a segment are consecutive words of a
+  // row, and the two segments a wave covers land on opposite halves of the banks.
   constexpr int SEG = HD / 8;
   constexpr int NKV = T * SEG / nthr;
-  static_assert(NKV * nthr == T * SEG, "key tile segments per thread");
-  uint4 kr[NKV], vr[NKV];
+  constexpr int NV2 = (T / 2) * SEG / nthr;  // key pairs per thread
+  static_assert(NKV * nthr == T * SEG && NV2 * nthr == (T / 2) * SEG, "key tile segments per thread");
+  uint4 kr[NKV], va[NV2], vb2[NV2];
   auto load_kv = [&](int t0) {
 #pragma unroll
     for (int u = 0; u < NKV; ++u) {
@@ -357,7 +362,14 @@ __global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict
       const int key = idx / SEG, seg = idx % SEG;
       const int kp = min(t0 + key, last_pos);
       kr[u] = *reinterpret_cast<const uint4*>(kb + (size_t)kp * HD + seg * 8);
-      vr[u] = *reinterpret_cast<const uint4*>(vb + (size_t)kp * HD + seg * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < NV2; ++u) {
+      const int idx = u * nthr + tid;
+      const int pr = idx % (T / 2), seg = idx / (T / 2);
+      const int k0 = min(t0 + 2 * pr, last_pos), k1 = min(t0 + 2 * pr + 1, last_pos);
+      va[u] = *reinterpret_cast<const uint4*>(vb + (size_t)k0 * HD + seg * 8);
+      vb2[u] = *reinterpret_cast<const uint4*>(vb + (size_t)k1 * HD + seg * 8);
     }
   };
   load_kv(0);
@@ -369,14 +381,21 @@ __global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict
       const int idx = u * nthr + tid;
       const int key = idx / SEG, seg = idx % SEG;
       const bool valid = t0 + key <= last_pos;  // keys past the block's last query are zero
-      const uint4 kw = valid ? kr[u] : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 vw = valid ? vr[u] : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(&sm.K[key][seg * 8]) = kw;
-      const uint32_t vs[4] = {vw.x, vw.y, vw.z, vw.w};
+      *reinterpret_cast<uint4*>(&sm.K[key][seg * 8]) = valid ? kr[u] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < NV2; ++u) {
+      const int idx = u * nthr + tid;
+      const int pr = idx % (T / 2), seg = idx / (T / 2);
+      const uint4 v0 = t0 + 2 * pr <= last_pos ? va[u] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v1 = t0 + 2 * pr + 1 <= last_pos ? vb2[u] : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t a4[4] = {v0.x, v0.y, v0.z, v0.w}, b4[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        sm.V[seg * 8 + 2 * q][key] = (uint16_t)(vs[q] & 0xffffu);
-        sm.V[seg * 8 + 2 * q + 1][key] = (uint16_t)(vs[q] >> 16);
+        // dims 2q, 2q + 1 of the segment: (key 2pr, key 2pr + 1) as one word each
+        *reinterpret_cast<uint32_t*>(&sm.V[seg * 8 + 2 * q][2 * pr]) = __builtin_amdgcn_perm(b4[q], a4[q], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(&sm.V[seg * 8 + 2 * q + 1][2 * pr]) =
+            __builtin_amdgcn_perm(b4[q], a4[q], 0x07060302u);
       }
     }
     if (tile + 1 < n_tiles) load_kv(t0 + T);

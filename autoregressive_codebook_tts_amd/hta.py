@@ -242,11 +242,12 @@ class Hta:
         self.close()
         return False
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # During interpreter teardown the HIP runtime (and a profiler's tool library)
         # may already be gone: a context still open then is left to process exit
-        # rather than destroyed through a runtime that no longer exists.
-        if sys.is_finalizing():
+        # rather than destroyed through a runtime that no longer exists.  (The check is
+        # bound at definition: module globals such as sys may already be None then.)
+        if _finalizing():
             return
         try:
             self.close()
