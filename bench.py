@@ -103,6 +103,9 @@ def main() -> int:
                     help="skip the one-layer decode step with one and rotated weight copies")
     ap.add_argument("--no-kernel-classes", action="store_true",
                     help="skip the per-kernel-class event timing that follows the timed region")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time the vendor GEMM library (torch.matmul in bf16, torch._scaled_mm in e4m3: "
+                         "hipBLASLt) on the prefill's GEMM shapes, as context for the tiled GEMM's MFMA fraction")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain elementwise copy of this many MiB before the timed region (a known-size "
                          "kernel that calibrates the HBM byte counters of a rocprofv3 --pmc run)")
@@ -233,6 +236,9 @@ def main() -> int:
     if shape.n_layers == 36 and not args.no_batched:
         log("batched multi-stream decode (FP8), M = 2, 4, 8, 16")
         extra["batched_decode_fp8"] = _batched(shape, w, scales, prompt, ms_frame)
+    if shape.n_layers == 36 and args.vendor_gemm:
+        log("vendor GEMM library on the prefill shapes")
+        extra["vendor_gemm_us"] = _vendor_gemm(shape)
     if shape.n_layers == 36 and not args.no_one_layer:
         log("one-layer decode step at KV 512 / 2048, one weight copy and rotated copies")
         extra["one_layer"] = _one_layer(shape, w, scales)
@@ -256,6 +262,42 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     hta.close_all()
     return 0
+
+
+def _vendor_gemm(shape, reps: int = 20) -> dict:
+    """Device us per call of the vendor library on the prefill GEMMs (M = P rows against
+    the [N][K] weights): torch.matmul in bf16 and torch._scaled_mm in e4m3 (unit scales),
+    random operands, after 3 warm-up calls; the e4m3 library GEMM uses the fp8 MFMA."""
+    import torch
+
+    d, F, W = shape.hidden, shape.ffn, shape.q_dim + 2 * shape.kv_dim
+    out = {}
+    for P in (128, 512):
+        for name, N, K in (("qkv", W, d), ("o", d, shape.q_dim), ("gate_up", 2 * F, d), ("down", d, F)):
+            a = torch.randn(P, K, device="cuda", dtype=torch.bfloat16)
+            b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+            a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+            one = torch.ones((), device="cuda")
+            res = {}
+            for kind, fn in (("bf16", lambda: a @ b.t()),
+                             ("e4m3", lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one,
+                                                               out_dtype=torch.bfloat16))):
+                try:
+                    for _ in range(3):
+                        fn()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(reps):
+                        fn()
+                    e1.record()
+                    e1.synchronize()
+                    us = e0.elapsed_time(e1) / reps * 1e3
+                    res[kind] = {"us": round(us, 2), "mfma_frac_of_bf16_peak": round(
+                        2.0 * P * N * K / (us * 1e-6) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4)}
+                except Exception as ex:  # a library build without the e4m3 path
+                    res[kind] = f"unavailable: {type(ex).__name__}"
+            out[f"{name}_p{P}"] = res
+    return out
 
 
 def _traffic(workload: str, shape):
