@@ -419,28 +419,37 @@ def test_full_fp8_sampling_head(gpu_fp8):
 
 
 # ----------------------------------------------------------------------------- chunked prefill
+# (total rows, chunks): 100 rows in one call take the LDS-tiled GEMM below 256 rows (64 x 64
+# tiles in e4m3, 128 x 128 in bf16) and the chunks the 32-row and 16-row skinny shapes; 300
+# rows take the 128 x 128 three-stage tiles, and its chunks every other shape.
+CHUNK_CASES = [(100, (37, 5, 16, 42)), (300, (37, 100, 163))]
+
+
 @pytest.mark.parametrize("precision", ["bf16", "fp8"])
-def test_full_chunked_prefill_is_bit_identical(request, precision):
-    """A prompt prefilled in chunks of 37, 5, 16 and 42 rows (the GEMM's 32-row and 16-row
-    skinny shapes, whose K splits span many pipelined stages here) leaves the same KV and
-    last rows, bit for bit, as the 100-row prefill in one call (the LDS-tiled GEMM)."""
+@pytest.mark.parametrize("total,chunks", CHUNK_CASES, ids=["100", "300"])
+def test_full_chunked_prefill_is_bit_identical(request, precision, total, chunks):
+    """A prompt prefilled in chunks leaves the same KV and last rows, bit for bit, as the
+    whole prompt prefilled in one call: a row's result does not depend on the GEMM kernel or
+    tile shape that computes it, nor on the attention block it shares."""
     ctx, _ = _ctx_and_oracle(request, precision)
-    ids = S.token_ids(S.SEEDS["prefill_128"], 100, SH.text_vocab)
+    ids = S.token_ids(S.SEEDS["prefill_512"], total, SH.text_vocab)
     layers = (0, SH.n_layers // 2, SH.n_layers - 1)
     ctx.reset(0)
     ctx.prefill(ids)
-    cold_rows = ctx.tap_prefill_hidden(100).copy()
-    cold_kv = [ctx.tap_kv(l, 100) for l in layers]
+    cold_rows = ctx.tap_prefill_hidden(total).copy()
+    cold_kv = [ctx.tap_kv(l, total) for l in layers]
     ctx.reset(0)
     c0 = 0
-    for n in (37, 5, 16, 42):
+    for n in chunks:
         ctx.prefill(ids[c0:c0 + n])
         c0 += n
         assert np.array_equal(ctx.tap_prefill_hidden(n), cold_rows[c0 - n:c0]), f"rows {c0 - n}..{c0} differ"
+    assert c0 == total
     for l, (kc, vc) in zip(layers, cold_kv):
-        k, v = ctx.tap_kv(l, 100)
+        k, v = ctx.tap_kv(l, total)
         assert np.array_equal(k, kc) and np.array_equal(v, vc), f"layer {l}: KV differs"
-    _say(f"[full] {precision} prefill in chunks 37/5/16/42: bit-identical to one 100-row prefill")
+    _say(f"[full] {precision} prefill in chunks {'/'.join(map(str, chunks))}: bit-identical to one "
+         f"{total}-row prefill")
 
 
 # ----------------------------------------------------------------------------- prefix reuse
