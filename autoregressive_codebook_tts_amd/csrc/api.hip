@@ -185,7 +185,7 @@ static bool shape_ok(const hta_config& f, std::string* why) {
   if (f.text_vocab < 1) return bad("text_vocab must be positive");
   if (f.max_seq < 2 || f.max_prefill < 1 || f.max_prefill > f.max_seq) return bad("bad max_seq / max_prefill");
   if (f.precision != HTA_BF16 && f.precision != HTA_FP8_E4M3) return bad("unknown precision");
-  if (f.n_streams < 0 || f.n_streams > 16) return bad("n_streams must be in 0..16");
+  if (f.n_streams < 0 || f.n_streams > 128) return bad("n_streams must be in 0..128");
   if (f.n_streams > 1 && f.n_streams > f.max_prefill) return bad("n_streams must not exceed max_prefill");
   if (f.hidden > 5120 || f.ffn > 10240 || f.n_q_heads * f.head_dim > 10240)
     return bad("hidden above 5120 or ffn / q width above 10240 exceed the GEMV prologue budget");

@@ -98,7 +98,7 @@ def main() -> int:
     ap.add_argument("--no-kv-slope", action="store_true",
                     help="skip the chunked utterance that measures frame time against KV length")
     ap.add_argument("--no-batched", action="store_true",
-                    help="skip batched multi-stream decode (M = 2, 4, 8, 16 utterances per step)")
+                    help="skip batched multi-stream decode (M = 2 .. 128 utterances per step)")
     ap.add_argument("--no-one-layer", action="store_true",
                     help="skip the one-layer decode step with one and rotated weight copies")
     ap.add_argument("--no-kernel-classes", action="store_true",
@@ -234,7 +234,7 @@ def main() -> int:
     ctx.close()
 
     if shape.n_layers == 36 and not args.no_batched:
-        log("batched multi-stream decode (FP8), M = 2, 4, 8, 16")
+        log("batched multi-stream decode (FP8), M = 2 .. 128")
         extra["batched_decode_fp8"] = _batched(shape, w, scales, prompt, ms_frame)
     if shape.n_layers == 36 and args.vendor_gemm:
         log("vendor GEMM library on the prefill shapes")
@@ -345,7 +345,7 @@ def _prefill_sizes(ctx, shape, prec: str) -> dict:
 LONG_PROMPT, LONG_FRAMES = 4095, 64
 
 
-def _batched(shape, w, scales, prompt, ms_single, Ms=(2, 4, 8, 16), warm: int = 8, frames: int = 64) -> dict:
+def _batched(shape, w, scales, prompt, ms_single, Ms=(2, 4, 8, 16, 32, 64, 128), warm: int = 8, frames: int = 64) -> dict:
     """Batched decode: M utterances (the P=13 prompt's seed plus m) prefilled into one
     FP8 context, then `warm` steps and `frames` timed steps of all M together (one
     captured step graph each); aggregate frames/s against the single-stream frame kernel."""
@@ -356,8 +356,8 @@ def _batched(shape, w, scales, prompt, ms_single, Ms=(2, 4, 8, 16), warm: int = 
     tensors, src = hta.weights_to_device(w, shape.n_layers)
     out = {"single_stream_frames_per_s": round(1e3 / ms_single, 1)}
     for M in Ms:
-        ctx = hta.Hta(shape, "fp8", max_seq=len(prompt) + warm + frames + 8, max_prefill=max(16, len(prompt)),
-                      n_streams=M)
+        rows = max(16, len(prompt), M)  # the row buffers hold one row per stream (max_prefill <= max_seq)
+        ctx = hta.Hta(shape, "fp8", max_seq=max(len(prompt) + warm + frames + 8, rows), max_prefill=rows, n_streams=M)
         ctx.load_weights(tensors, src, act_scales=scales)
         for m in range(M):
             ctx.select_stream(m)

@@ -83,7 +83,7 @@ typedef struct hta_ctx hta_ctx;
  * the head with each stream's greedy argmax and delay rule; the whole step is one captured
  * graph.  codes_out then receives n * M * C codes ([frame][stream][codebook]); *n_done
  * the number of streams whose utterance is done; HTA_DONE when all are.  Limits: 2 <= M
- * <= 16 and M <= max_prefill; greedy only (hta_set_sampling gives HTA_E_UNSUPPORTED);
+ * <= 128 and M <= max_prefill; greedy only (hta_set_sampling gives HTA_E_UNSUPPORTED);
  * hta_calibrate, hta_layer_step, HTA_OPT_TAPS, hta_time_kernels and
  * hta_decode_frames_noalloc need a single-stream context. */
 

@@ -36,22 +36,24 @@ def _prompts(lengths, seed0=7000):
     return [S.token_ids(seed0 + i, n, SH.text_vocab) for i, n in enumerate(lengths)]
 
 
-def _batched_teacher_forced(w, prompts, precision, act_scales, n_frames, modes):
+def _batched_teacher_forced(w, prompts, precision, act_scales, n_frames, modes, check=None):
+    """recs[i] for stream check[i] (default: every stream); the other streams decode freely."""
     M = len(prompts)
-    ctx = gpu_context(SH, w, precision, max_seq=128, max_prefill=16, act_scales=act_scales, n_streams=M)
-    oracles = [{mo: OracleModel(SH, w, precision, mo, act_scales=act_scales if mo == "S" else None, max_seq=128)
-                for mo in modes} for _ in range(M)]
+    check = list(range(M)) if check is None else list(check)
+    ctx = gpu_context(SH, w, precision, max_seq=128, max_prefill=max(16, M), act_scales=act_scales, n_streams=M)
+    oracles = {m: {mo: OracleModel(SH, w, precision, mo, act_scales=act_scales if mo == "S" else None, max_seq=128)
+                   for mo in modes} for m in check}
     try:
         for m, p in enumerate(prompts):
             ctx.select_stream(m)
             ctx.prefill(p)
-            for o in oracles[m].values():
+            for o in oracles.get(m, {}).values():
                 o.prefill(p)
-        recs = [[] for _ in range(M)]
+        recs = {m: [] for m in check}
         for f in range(n_frames):
             codes, _ = ctx.decode_frame()
             assert codes.shape == (M, SH.n_codebooks)
-            for m in range(M):
+            for m in check:
                 ctx.select_stream(m)
                 rec = {"t": f, "gpu": {"codes": codes[m], "hidden": ctx.tap_hidden().astype(np.float64),
                                        "logits": ctx.tap_logits().astype(np.float64)}}
@@ -65,7 +67,7 @@ def _batched_teacher_forced(w, prompts, precision, act_scales, n_frames, modes):
                     o.force_codes(forced)
                 ctx.force_codes(forced)
                 recs[m].append(rec)
-        return recs
+        return [recs[m] for m in check]
     finally:
         ctx.close()
 
@@ -95,6 +97,32 @@ def test_batched_fp8_streams_match_their_oracles(w, scales):
               f"{n} robust ids, {len(bad)} mismatches")
         assert rel_s <= HIDDEN_TOL["fp8"] and cos_s >= COS_MIN
         assert n > 30 and not bad
+
+
+@pytest.mark.parametrize("precision,M,check", [("fp8", 70, (0, 35, 69)), ("bf16", 40, (0, 39))])
+def test_batched_many_streams_match_their_oracles(w, scales, precision, M, check):
+    """Batches past one 32-row GEMM tile (40 streams: two row tiles of the skinny GEMM; 70:
+    the LDS-tiled GEMM) and down to one key split per stream: the checked streams against
+    their own oracles, to the gates of the three-stream tests."""
+    lengths = [4 + (7 * m) % 12 for m in range(M)]
+    prompts = _prompts(lengths, seed0=7100)
+    modes = ("S", "E") if precision == "fp8" else ("E", "S")
+    recs = _batched_teacher_forced(w, prompts, precision, scales if precision == "fp8" else None, 8, modes, check)
+    for m, rs in zip(check, recs):
+        if precision == "fp8":
+            rel = max(rel_l2(r["gpu"]["hidden"], r["S"]["hidden"]) for r in rs)
+            cos = min(cosines(r["gpu"]["logits"], r["S"]["logits"]).min() for r in rs)
+            n, bad = id_agreement(SH, rs, "S")
+            ok = rel <= HIDDEN_TOL["fp8"]
+        else:
+            rel = max(rel_l2(r["gpu"]["hidden"], r["S"]["hidden"]) for r in rs)
+            cos = min(cosines(r["gpu"]["logits"], r["E"]["logits"]).min() for r in rs)
+            n, bad = id_agreement(SH, rs, "E")
+            ok = rel <= 5e-3 and max(rel_l2(r["gpu"]["hidden"], r["E"]["hidden"]) for r in rs) <= HIDDEN_TOL["bf16"]
+        print(f"batched {precision} M={M} stream {m} (P={lengths[m]}): hidden rel {rel:.3e} vs the storage-faithful "
+              f"oracle; logits cos {cos:.6f}; {n} robust ids, {len(bad)} mismatches")
+        assert ok and cos >= COS_MIN
+        assert n > 15 and not bad
 
 
 def test_batched_streams_are_isolated(w):
