@@ -188,16 +188,24 @@ def main() -> int:
         ctx.decode_frames(args.frames)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    clock = {}
     for i in range(args.steps):
         ctx.reset(0)
         ctx.prefill(prompt)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # the last utterance: read the clocks on a host thread while its frames run
+        sampler = _clock_sampler(clock) if i == args.steps - 1 else None
         e0.record(ctx.stream)
         codes, done = ctx.decode_frames(args.frames)
         e1.record(ctx.stream)
         e1.synchronize()
+        if sampler is not None:
+            sampler.join(timeout=30)
         dec_ms.append(e0.elapsed_time(e1) / args.frames)
     torch.cuda.synchronize()
+    # device memory the process has held so far (weights, both contexts' workspaces: all through torch)
+    extra["peak_device_memory_gb"] = round(torch.cuda.max_memory_reserved() / 1e9, 2)
+    extra["gpu_clocks_during_decode"] = clock.get("value")
     wall = time.perf_counter() - t0
     ms_frame = statistics.mean(dec_ms)
     kv_mean = args.prompt + (args.frames + 1) / 2
@@ -262,6 +270,28 @@ def main() -> int:
     print(json.dumps(line), flush=True)
     hta.close_all()
     return 0
+
+
+def _clock_sampler(out: dict):
+    """Start a host thread that reads the GPU's current clocks once (rocm-smi, read-only)
+    while the caller's decode runs; out["value"] gets the parsed clocks or the reason none
+    were read.  Context for the timings, not part of them."""
+    import subprocess
+    import threading
+
+    def run():
+        try:
+            time.sleep(0.3)  # well inside the 1017-frame decode (about 1.3 s)
+            r = subprocess.run(["rocm-smi", "--showgpuclocks", "--json"], capture_output=True, text=True, timeout=20)
+            card = next(iter(json.loads(r.stdout).values()))
+            out["value"] = {k: v for k, v in card.items() if "clock" in k.lower() or "sclk" in k.lower()
+                            or "mclk" in k.lower() or "fclk" in k.lower()}
+        except Exception as ex:  # no rocm-smi, no permission, another output format
+            out["value"] = f"unavailable: {type(ex).__name__}"
+
+    t = threading.Thread(target=run, daemon=True)
+    t.start()
+    return t
 
 
 def _vendor_gemm(shape, reps: int = 20) -> dict:
