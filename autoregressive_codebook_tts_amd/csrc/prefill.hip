@@ -506,7 +506,8 @@ __global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict
 // B = packed weights.  A block computes 16R rows x 64 columns with 4 waves of
 // 16R x 16; the K range is split into `ksplit` contiguous parts (a function of N
 // and K only) whose partial sums land in Cpart[ksplit][M][N] and are added in
-// split order by k_gemm_reduce.  Each 16x16 MFMA tile accumulates its K range in
+// split order by the row kernel that consumes the output (split_sums) or by
+// k_gemm_reduce.  Each 16x16 MFMA tile accumulates its K range in
 // increasing order: bf16 in 32-wide chunks; e4m3 per 64-wide chunk, the low 8
 // bytes of every lane's 16-byte unit and then the high 8 bytes.  A row's result
 // therefore does not depend on M, and the LDS-tiled kernel for larger M computes
@@ -713,8 +714,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, co
         }
       }
   } else {
-    // a split's partial, for k_gemm_reduce (a last-arriving block adding the splits here
-    // would put three memory round trips on the kernel's tail, more than the reduce's launch)
+    // a split's partial, summed by the consuming row kernel or k_gemm_reduce (a
+    // last-arriving block adding the splits here would put three memory round trips on
+    // the kernel's tail, more than the reduce's launch)
     float* Cp = Cpart + (size_t)ks * M * N;
 #pragma unroll
     for (int r = 0; r < R; ++r)
