@@ -301,42 +301,27 @@ __device__ __forceinline__ uint32_t pack_bf16_trunc(float a, float b) {  // exac
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
+// The attention of one block (kv head j, query rows i0 .. i0 + 15) once this lane's
+// A fragments `qa` of its query head are formed.
 template <int P, int HD, int G>
-__global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict__ Q, const uint16_t* __restrict__ kc,
-                                                      const uint16_t* __restrict__ vc, void* __restrict__ O,
-                                                      const int* __restrict__ len_at, int n_rows, int Hq, int Hkv,
-                                                      int max_seq, float scale, float* amax) {
+__device__ __forceinline__ void attn_prefill_block(const bf16x8 (&qa)[HD / 32], const uint16_t* __restrict__ kc,
+                                                   const uint16_t* __restrict__ vc, void* __restrict__ O, int len0,
+                                                   int i0, int j, int n_rows, int Hq, int max_seq, float scale,
+                                                   float* amax, PrefillAttnLds<HD>& sm, float* red) {
   constexpr int T = kAttnTile, QT = kAttnQT;
-  constexpr int KC = HD / 32;   // 32-wide k chunks of a q row
   constexpr int NT = HD / 16;   // 16-wide output column tiles
   static_assert(T == 64, "four 16-key blocks per tile");
-  __shared__ PrefillAttnLds<HD> sm;
-  __shared__ float red[16];
   constexpr int nthr = 64 * G;  // one wave per query head of the kv group
-  const int j = blockIdx.x, i0 = blockIdx.y * QT;
+  constexpr int KC = HD / 32;   // 32-wide k chunks of a q row
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = j * G + w;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int len0 = *len_at;  // the first prompt position: the KV length before this prefill
   const int last_pos = len0 + min(i0 + QT, n_rows) - 1;
   const int n_tiles = last_pos / T + 1;
   const uint16_t* kb = kc + (size_t)j * max_seq * HD;
   const uint16_t* vb = vc + (size_t)j * max_seq * HD;
   const float inv_sqrt = 1.0f / sqrtf((float)HD);
-
-  // this lane's A fragments of the 16 query rows (row r16; clamped rows are unused)
-  bf16x8 qa[KC];
-  {
-    const float* qrow = Q + ((size_t)min(i0 + r16, n_rows - 1) * Hq + h) * HD;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const float4 a = *reinterpret_cast<const float4*>(qrow + c * 32 + 8 * g4);
-      const float4 b = *reinterpret_cast<const float4*>(qrow + c * 32 + 8 * g4 + 4);
-      const uint4 u = make_uint4(pack_bf16_trunc(a.x, a.y), pack_bf16_trunc(a.z, a.w), pack_bf16_trunc(b.x, b.y),
-                                 pack_bf16_trunc(b.z, b.w));
-      qa[c] = __builtin_bit_cast(bf16x8, u);
-    }
-  }
+  (void)KC;
   f32x4 oacc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -499,6 +484,153 @@ __global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict
     mx = block_max(mx, red);
     if (tid == 0) record_amax(amax, mx);
   }
+}
+
+// this lane's A fragments of the 16 query rows (row r16; clamped rows are unused) from
+// rotated queries held as fp32 values (bf16-exact), row stride `rs` floats
+template <int HD>
+__device__ __forceinline__ void q_fragments(const float* q0, int rs, int n_rows, int i0, bf16x8 (&qa)[HD / 32]) {
+  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+  const float* qrow = q0 + (size_t)min(i0 + r16, n_rows - 1) * rs;
+#pragma unroll
+  for (int c = 0; c < HD / 32; ++c) {
+    const float4 a = *reinterpret_cast<const float4*>(qrow + c * 32 + 8 * g4);
+    const float4 b = *reinterpret_cast<const float4*>(qrow + c * 32 + 8 * g4 + 4);
+    const uint4 u = make_uint4(pack_bf16_trunc(a.x, a.y), pack_bf16_trunc(a.z, a.w), pack_bf16_trunc(b.x, b.y),
+                               pack_bf16_trunc(b.z, b.w));
+    qa[c] = __builtin_bit_cast(bf16x8, u);
+  }
+}
+
+template <int P, int HD, int G>
+__global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict__ Q, const uint16_t* __restrict__ kc,
+                                                      const uint16_t* __restrict__ vc, void* __restrict__ O,
+                                                      const int* __restrict__ len_at, int n_rows, int Hq, int Hkv,
+                                                      int max_seq, float scale, float* amax) {
+  __shared__ PrefillAttnLds<HD> sm;
+  __shared__ float red[16];
+  const int j = blockIdx.x, i0 = blockIdx.y * kAttnQT;
+  const int h = j * G + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  bf16x8 qa[HD / 32];
+  q_fragments<HD>(Q + (size_t)h * HD, Hq * HD, n_rows, i0, qa);
+  attn_prefill_block<P, HD, G>(qa, kc, vc, O, *len_at, i0, j, n_rows, Hq, max_seq, scale, amax, sm, red);
+}
+
+// Prompts of at most 16 rows (one query block): one block per kv head rotates its
+// group's query heads and its key head for every row (q/k RMSNorm + RoPE), writes the
+// rows' keys and values into the cache, and then runs the attention of the query block.
+// The rotation is norm_rope_vals on the split sums of k_qk_rope_rows and the attention is
+// attn_prefill_block, in the same order, so every value is bit-identical to the
+// two-kernel path of longer prompts.  The rotated queries stay in LDS (in the key/value
+// tile area, free until the attention's first tile).
+template <int HD, int G>
+constexpr bool rope_attn_small_fits() {
+  return (size_t)G * kAttnQT * HD * 4 <= sizeof(uint16_t) * kAttnTile * (HD + 8) + sizeof(uint16_t) * HD * (kAttnTile + 8);
+}
+template <int P, int HD, int G>
+__global__ __launch_bounds__(64 * G) void k_rope_attn_small(
+    const float* __restrict__ QKV, SplitIn si, const float* __restrict__ g_q, const float* __restrict__ g_k,
+    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, uint16_t* __restrict__ kc,
+    uint16_t* __restrict__ vc, void* __restrict__ O, const int* __restrict__ len_at, int n_rows, int Hq, int Hkv,
+    int max_seq, float eps, float scale, float* amax) {
+  constexpr int H2 = HD / 2, QT = kAttnQT;
+  constexpr int KR = QT / G;     // key and value rows per wave: rows w, w + G, ...
+  constexpr int VE = HD / 64;    // value elements per lane and row
+  static_assert(rope_attn_small_fits<HD, G>(), "rotated queries in the tile area");
+  __shared__ PrefillAttnLds<HD> sm;
+  __shared__ float red[16];
+  float* qs = reinterpret_cast<float*>(&sm.K[0][0]);  // [G][QT][HD]
+  const int j = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hq = j * G + w;
+  const int len0 = *len_at;
+  const int W = (Hq + 2 * Hkv) * HD;
+  const bool act = lane < H2;
+  const int la = act ? lane : 0;
+  // every operand of this wave's rows, loaded before any is used: the query head's two
+  // elements per row, the key head's and the value head's of this wave's key rows
+  float xq[2 * QT], xk[2 * KR], xv[VE * KR];
+  {
+    long idx[2 * QT];
+    int col[2 * QT];
+#pragma unroll
+    for (int i = 0; i < QT; ++i) {
+      const long r = min(i, n_rows - 1);
+      col[2 * i] = hq * HD + la;
+      col[2 * i + 1] = hq * HD + la + H2;
+      idx[2 * i] = r * W + col[2 * i];
+      idx[2 * i + 1] = r * W + col[2 * i + 1];
+    }
+    if (si.part) {
+      split_sums<2 * QT, kRopeMaxSplit>(si, idx, col, xq);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2 * QT; ++u) xq[u] = QKV[idx[u]];
+    }
+  }
+  {
+    long idx[2 * KR + VE * KR];
+    int col[2 * KR + VE * KR];
+#pragma unroll
+    for (int t = 0; t < KR; ++t) {
+      const long r = min(w + G * t, n_rows - 1);
+      col[2 * t] = (Hq + j) * HD + la;
+      col[2 * t + 1] = (Hq + j) * HD + la + H2;
+      idx[2 * t] = r * W + col[2 * t];
+      idx[2 * t + 1] = r * W + col[2 * t + 1];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        col[2 * KR + VE * t + e] = (Hq + Hkv + j) * HD + lane + 64 * e;
+        idx[2 * KR + VE * t + e] = r * W + col[2 * KR + VE * t + e];
+      }
+    }
+    float xs[2 * KR + VE * KR];
+    if (si.part) {
+      split_sums<2 * KR + VE * KR, kRopeMaxSplit>(si, idx, col, xs);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2 * KR + VE * KR; ++u) xs[u] = QKV[idx[u]];
+    }
+#pragma unroll
+    for (int t = 0; t < 2 * KR; ++t) xk[t] = xs[t];
+#pragma unroll
+    for (int t = 0; t < VE * KR; ++t) xv[t] = xs[2 * KR + t];
+  }
+  const float gq0 = g_q[la], gq1 = g_q[la + H2], gk0 = g_k[la], gk1 = g_k[la + H2];
+  uint16_t* kb = kc + (size_t)j * max_seq * HD;
+  uint16_t* vb = vc + (size_t)j * max_seq * HD;
+#pragma unroll
+  for (int i = 0; i < QT; ++i) {
+    if (i >= n_rows) break;  // uniform
+    const int pos = len0 + i;
+    const float c_ = rope_cos[(size_t)pos * H2 + la], s_ = rope_sin[(size_t)pos * H2 + la];
+    float a, b;
+    norm_rope_vals<HD>(act ? xq[2 * i] : 0.0f, act ? xq[2 * i + 1] : 0.0f, gq0, gq1, c_, s_, eps, lane, &a, &b);
+    if (act) {
+      qs[(w * QT + i) * HD + lane] = a;
+      qs[(w * QT + i) * HD + lane + H2] = b;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < KR; ++t) {
+    const int r = w + G * t;
+    if (r >= n_rows) break;  // uniform
+    const int pos = len0 + r;
+    const float c_ = rope_cos[(size_t)pos * H2 + la], s_ = rope_sin[(size_t)pos * H2 + la];
+    float a, b;
+    norm_rope_vals<HD>(act ? xk[2 * t] : 0.0f, act ? xk[2 * t + 1] : 0.0f, gk0, gk1, c_, s_, eps, lane, &a, &b);
+    if (act) {
+      kb[(size_t)pos * HD + lane] = (uint16_t)f32_to_bf16(a);
+      kb[(size_t)pos * HD + lane + H2] = (uint16_t)f32_to_bf16(b);
+    }
+#pragma unroll
+    for (int e = 0; e < VE; ++e) vb[(size_t)pos * HD + lane + 64 * e] = (uint16_t)f32_to_bf16(xv[VE * t + e]);
+  }
+  __threadfence_block();  // the block's cache rows, before its tiles read them
+  __syncthreads();
+  bf16x8 qa[HD / 32];
+  q_fragments<HD>(qs + (size_t)w * QT * HD, HD, n_rows, 0, qa);
+  attn_prefill_block<P, HD, G>(qa, kc, vc, O, len0, 0, j, n_rows, Hq, max_seq, scale, amax, sm, red);
 }
 
 // ============================================================================ MFMA GEMM, small M
@@ -1073,8 +1205,26 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
     if ((e = gemm<P>(c, c.pu, L.w_qkv, L.s_qkv, host_act_scale(c, s0), c.pqkv, Pn, W, d, 0, nullptr, 1.0f, nullptr,
                      defer_q)) != hipSuccess)
       return e;
-    {
-      const SplitIn sq = defer_q ? deferred_split<P>(c, Pn, W, d, L.s_qkv, host_act_scale(c, s0)) : none;
+    const SplitIn sq = defer_q ? deferred_split<P>(c, Pn, W, d, L.s_qkv, host_act_scale(c, s0)) : none;
+    const int G = Hq / Hkv;
+    const float so = host_act_scale(c, s0 + 1);
+    float* am = amax ? amax + s0 + 1 : nullptr;
+    if (Pn <= kAttnQT) {
+      // one query block: rotation and attention in one launch per kv head
+#define HTA_RA(HDV, GV)                                                                                      \
+  hipLaunchKernelGGL((k_rope_attn_small<P, HDV, GV>), dim3(Hkv), dim3(64 * GV), 0, c.stream, c.pqkv, sq, L.g_q, \
+                     L.g_k, c.rope_cos, c.rope_sin, L.k_cache, L.v_cache, c.po, len0, Pn, Hq, Hkv, f.max_seq,     \
+                     f.rms_eps, so, am)
+      if (hd == 128 && G == 4) HTA_RA(128, 4);
+      else if (hd == 128 && G == 2) HTA_RA(128, 2);
+      else if (hd == 128 && G == 1) HTA_RA(128, 1);
+      else if (hd == 64 && G == 4) HTA_RA(64, 4);
+      else if (hd == 64 && G == 2) HTA_RA(64, 2);
+      else if (hd == 64 && G == 1) HTA_RA(64, 1);
+      else return hipErrorInvalidValue;
+#undef HTA_RA
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
       if (hd == 128)
         hipLaunchKernelGGL(k_qk_rope_rows<128>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
                            c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L, sq);
@@ -1082,12 +1232,7 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
         hipLaunchKernelGGL(k_qk_rope_rows<64>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
                            c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L, sq);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    {
-      const int G = Hq / Hkv;
       dim3 grid(Hkv, (Pn + kAttnQT - 1) / kAttnQT);
-      const float so = host_act_scale(c, s0 + 1);
-      float* am = amax ? amax + s0 + 1 : nullptr;
 #define HTA_ATTN(HDV, GV)                                                                                        \
   hipLaunchKernelGGL((k_attn_prefill<P, HDV, GV>), grid, dim3(64 * GV), 0, c.stream, c.pq, L.k_cache, L.v_cache, c.po, \
                      len0, Pn, Hq, Hkv, f.max_seq, so, am)
