@@ -66,3 +66,50 @@ def test_undelay_matches_oracle(n):
 def test_abi_weight_order_matches_generator():
     names = [n for n, _ in S.tensor_specs(S.TINY)]
     assert names == hta.abi_tensor_names(S.TINY.n_layers)
+
+
+def _cfg(**kw):
+    cfg = hta.make_config(S.QWEN3_4B, kw.pop("precision", hta.HTA_FP8_E4M3), kw.pop("max_seq", 4096),
+                          kw.pop("max_prefill", 512), kw.pop("n_streams", 1))
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+@pytest.mark.parametrize("field,value", [
+    ("head_dim", 96),          # head_dim must be 64 or 128
+    ("n_q_heads", 24),         # GQA group 3
+    ("n_kv_heads", 5),         # not a divisor of the query heads
+    ("hidden", 2560 + 64),     # not a multiple of 128
+    ("ffn", 9728 + 64),
+    ("n_codebooks", 0),
+    ("n_codebooks", 17),
+    ("codebook_size", 1),
+    ("bos_id", 1026),          # outside the codebook
+    ("eos_id", -1),
+    ("precision", 7),
+    ("n_streams", 129),
+    ("n_streams", -1),
+    ("max_prefill", 0),
+    ("max_prefill", 5000),     # above max_seq
+    ("hidden", 6144),          # above the GEMV prologue budget
+])
+def test_workspace_bytes_rejects_unsupported_shapes(field, value):
+    """hta_workspace_bytes (host only) applies hta_create's shape rules: 0 for a shape the
+    kernels do not take."""
+    assert hta.workspace_bytes(_cfg()) > 0
+    assert hta.workspace_bytes(_cfg(**{field: value})) == 0
+
+
+def test_workspace_bytes_of_batched_contexts():
+    """Streams beyond max_prefill are refused; each stream adds its own KV cache (36 layers
+    x 2 x 8 kv heads x max_seq x 128 x 2 bytes) and device state."""
+    one = hta.workspace_bytes(_cfg(max_seq=1024, max_prefill=128))
+    assert hta.workspace_bytes(_cfg(max_seq=1024, max_prefill=16, n_streams=32)) == 0
+    kv = 36 * 2 * 8 * 1024 * 128 * 2
+    prev = one
+    for m in (2, 16, 128):
+        n = hta.workspace_bytes(_cfg(max_seq=1024, max_prefill=128, n_streams=m))
+        assert n >= one + (m - 1) * kv
+        assert n > prev
+        prev = n
