@@ -131,6 +131,7 @@ Layout make_layout(const hta_config& c) {
   if (d > nmax) nmax = d;
   if (M > 1 && CVp > nmax) nmax = CVp;  // the batched step's head GEMM
   L.off_pgu = take(Pm * 2 * F * 4 + 8 * Pm * nmax * 4);  // gate/up rows, then GEMM split partials
+  L.gemm_cols = (int)nmax;
   L.off_pa = take(Pm * F * 2);  // SiLU * mul rows (the down projection's input)
   L.off_taps = take(((size_t)c.n_layers + 1) * d * 4);
   L.off_ptaps = take(2 * Pm * d * 4);
@@ -995,12 +996,38 @@ int hta_set_option(hta_ctx* x, int option, int value) {
     HIPCK(frame_write_args(c), "frame arguments");
     return HTA_OK;
   }
+  if (option == HTA_OPT_FP8_MFMA) {
+    if (value != 0 && c.cfg.precision != HTA_FP8_E4M3)
+      return fail(c, HTA_E_UNSUPPORTED, "the e4m3 MFMA option is for FP8 contexts");
+    const bool v = value != 0;
+    if (v != c.fp8_mfma) drop_graph(c);  // captured prefills and batched steps hold the kernel choice
+    c.fp8_mfma = v;
+    return HTA_OK;
+  }
   if (option == HTA_OPT_PREFILL_TAP_LAYER) {
     if (value < 0 || value >= c.cfg.n_layers) return fail(c, HTA_E_ARG, "tap layer out of range");
     c.prefill_tap_layer = value;
     return HTA_OK;
   }
   return fail(c, HTA_E_ARG, "unknown option");
+}
+
+int hta_gemm(hta_ctx* x, const void* A, const void* W, const float* w_scale, float a_scale, int M, int N, int K,
+             float* C) {
+  if (!x) return HTA_E_ARG;
+  Ctx& c = x->c;
+  if (!c.ws) return fail(c, HTA_E_STATE, "no workspace bound");
+  const bool fp8 = c.cfg.precision == HTA_FP8_E4M3;
+  if (!A || !W || !C || (fp8 && !w_scale)) return fail(c, HTA_E_ARG, "null operand");
+  if (M < 1 || M > c.cfg.max_prefill) return fail(c, HTA_E_ARG, "M must be in 1..max_prefill");
+  if (N < 64 || N % 64 != 0 || N > c.lay.gemm_cols)
+    return fail(c, HTA_E_ARG, "N must be a multiple of 64 up to the widest projection");
+  if (K < 128 || K % 128 != 0) return fail(c, HTA_E_ARG, "K must be a positive multiple of 128");
+  const size_t rows = (size_t)(M > N ? M : N), eb = fp8 ? 1 : 2;
+  if (rows * (size_t)K * eb >= ((size_t)1 << 31)) return fail(c, HTA_E_ARG, "operand of 2 GiB or more");
+  HIPCK(launch_gemm(c, A, W, w_scale, a_scale, C, M, N, K), "gemm");
+  HIPCK(hipStreamSynchronize(c.stream), "gemm sync");
+  return HTA_OK;
 }
 
 void hta_destroy(hta_ctx* x) {

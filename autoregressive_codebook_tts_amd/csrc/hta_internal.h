@@ -64,6 +64,7 @@ struct Layout {
   size_t off_blogits, off_bpart;
   size_t kv_stream_bytes;   // bytes of one stream's K (or V) cache within a layer
   int cv_pad;               // head rows padded to a multiple of 64 (the GEMM's column tile)
+  int gemm_cols;            // widest GEMM output the split partials hold (8 splits of max_prefill rows)
   int n_streams, batch_splits;
   int attn_splits;
 };
@@ -145,6 +146,7 @@ struct Ctx {
   uint16_t* taps_act = nullptr; // [5 * n_layers + 1][kActsWidth] GEMV inputs of the last frame (block 0)
   uint16_t* taps_q = nullptr;   // [n_layers][Hq * hd] rotated queries of the last frame
   bool trace = false;           // persistent frame kernel phase timestamps
+  bool fp8_mfma = false;        // e4m3 prefill and batched-step GEMMs on the e4m3 MFMA (opt-in)
   uint32_t* trace_buf = nullptr;  // [kTraceBlocks][5 * n_layers + 1][4]
   void* fargs = nullptr;          // the persistent kernel's arguments (device)
   // captured prefills, one per prompt length P (positions come from the device state)
@@ -205,6 +207,9 @@ size_t frame_sample_capacity();  // bytes of LDS that hold a sampling frame's lo
 // ---------------------------------------------------------------- launchers (prefill.hip)
 hipError_t prefill_setup();  // kernel attributes of the prefill GEMM (once per context)
 hipError_t launch_prefill(Ctx& c, int P, bool record);
+// C[M][N] = A[M][K] . W[N][K]^T with the prefill's kernels and K split (e4m3: times a_scale * w_scale[n])
+hipError_t launch_gemm(Ctx& c, const void* A, const void* W, const float* w_scale, float a_scale, float* C, int M,
+                       int N, int K);
 hipError_t launch_batch_step(Ctx& c);  // one batched decode step of all n_streams streams
 
 // ---------------------------------------------------------------- launchers (load.hip)

@@ -33,6 +33,19 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// One 16x16 tile over a 128-element step on the e4m3 MFMA (the opt-in fast form): each
+// lane gives 32 bytes of its A row and of its B row, the 16-byte units u0 and u1 of the
+// step, the same units in both operands.  The instruction sums its e4m3 products in groups
+// with fewer bits than fp32 (a product 2^-18 beside a product 1 is dropped), so its results
+// differ from fp32 accumulation by up to about 2^-19 of the sum of |products|.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_e4m3_step(uint4 a0, uint4 a1, uint4 b0, uint4 b1, f32x4 c) {
+  const i32x8 a{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8 b{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  // formats 0 / 0: e4m3 operands; scale operands 0: no block scaling
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 extern float host_act_scale(const Ctx& c, int site);
 
 // ============================================================================ rows
@@ -714,11 +727,13 @@ __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :
 template <int P, int R, int NW>
 size_t skinny_lds_bytes() { return (size_t)Skinny<P, R, NW>::NS * Skinny<P, R, NW>::STAGE; }
 
-template <int P, int R, int NW>
+// F8M (e4m3 only): the e4m3 MFMA, one instruction per 128-element step and 16-row fragment.
+template <int P, int R, int NW, bool F8M = false>
 __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, const void* __restrict__ B,
                                                   float* __restrict__ Cpart, int M, int N, int K, int ksplit,
                                                   GemmEpi epi) {
   using S = Skinny<P, R, NW>;
+  static_assert(!F8M || (P == kFP8 && S::U == 2), "the e4m3 MFMA takes a 128-byte step as two units per lane");
   extern __shared__ __align__(16) unsigned char gsm[];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m0 = blockIdx.x * 16 * R, n0 = blockIdx.y * 16 * NW, ks = blockIdx.z;
@@ -806,6 +821,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, co
         for (int r = 0; r < R; ++r)
           acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[r][q]),
                                                            __builtin_bit_cast(bf16x8, bv[q]), acc[r], 0, 0, 0);
+    } else if (F8M) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = mfma_e4m3_step(av[r][0], av[r][1], bv[0], bv[1], acc[r]);
     } else {
       // e4m3 operands are widened to bf16 in registers (exact: 4 significant bits) and
       // multiplied on the bf16 MFMA, which accumulates at full fp32 precision; the e4m3
@@ -906,12 +924,15 @@ size_t gemm_tile_lds_bytes() { return (size_t)NS * TileCfg<BM, BN, NS>::STG; }
 
 __device__ __forceinline__ int tile_unit_pos(int row, int u) { return row * 4 + (u ^ ((row >> 2) & 3)); }
 
-template <int P, int BM, int BN, int NS>
-__global__ __launch_bounds__(256) void k_gemm_tile(const void* __restrict__ A, const void* __restrict__ B,
+// F8M (e4m3 only): the e4m3 MFMA over each pair of 64-byte chunks (one 128-element step;
+// a lane's units of the two chunks are the units k_gemm's lane takes from the step).
+template <int P, int BM, int BN, int NS, bool F8M = false>
+__global__ __launch_bounds__(256, F8M ? 3 : 1) void k_gemm_tile(const void* __restrict__ A, const void* __restrict__ B,
                                                    float* __restrict__ Cpart, int M, int N, int K, int ksplit,
                                                    GemmEpi epi) {
   using T = TileCfg<BM, BN, NS>;
   constexpr int NJ = T::NJ, WN = T::WN;
+  static_assert(!F8M || P == kFP8, "the e4m3 MFMA form is for e4m3 operands");
   extern __shared__ __align__(16) unsigned char gsm[];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int mt, nt, ks;
@@ -980,6 +1001,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile(const void* __restrict__ A, c
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 hav[F8M ? 4 : 1], hbv[F8M ? NJ : 1];  // F8M: the first chunk of the step being multiplied
 
   for (int c = 0; c < nch; ++c) {
     // chunk c has landed once at most the fetches of the NS - 2 younger chunks remain
@@ -1001,6 +1023,19 @@ __global__ __launch_bounds__(256) void k_gemm_tile(const void* __restrict__ A, c
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[i]),
                                                                __builtin_bit_cast(bf16x8, bv[j]), acc[i][j], 0, 0, 0);
+    } else if (F8M) {
+      // chunks come in step pairs: c0 is even and every step has two chunks
+      if ((c & 1) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hav[i] = av[i];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) hbv[j] = bv[j];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_e4m3_step(hav[i], av[i], hbv[j], bv[j], acc[i][j]);
+      }
     } else {
       bf16x8 al[4], ah[4], bl[NJ], bh[NJ];
 #pragma unroll
@@ -1106,18 +1141,10 @@ static SplitIn deferred_split(Ctx& c, int M, int N, int K, const float* w_scale,
   return SplitIn{split_buffer(c), ks, (long)M * N, P == kFP8 ? w_scale : nullptr, in_scale};
 }
 
-// defer: with K split, leave the partials for the next row kernel (deferred_split)
-// instead of launching k_gemm_reduce; only for outputs without the SiLU epilogue.
-template <int P>
-static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scale, float in_scale, float* out, int M,
-                       int N, int K, int resid, void* act = nullptr, float act_scale = 1.0f, float* amax = nullptr,
-                       bool defer = false) {
-  if (N % 64 != 0 || K % 128 != 0) return hipErrorInvalidValue;  // the kernels' tiling
-  if (defer && act) return hipErrorInvalidValue;
-  const int ks = gemm_ksplit(N, K);
-  float* part = split_buffer(c);  // split partials after the gate/up buffer
-  const GemmEpi epi{out, P == kFP8 ? w_scale : nullptr, in_scale, act ? 2 : (resid ? 1 : 0), act, act_scale, amax};
-  hipError_t e;
+// The kernel choice for one product (F8M: the e4m3 MFMA form of the same kernels).
+template <int P, bool F8M>
+static void gemm_launch(Ctx& c, const void* A, const void* B, float* part, int M, int N, int K, int ks,
+                        const GemmEpi& epi) {
   if (M < kGemmTileMinM) {
     const int R = M <= 16 ? 1 : 2;
     const int mt = (M + 16 * R - 1) / (16 * R);
@@ -1134,32 +1161,54 @@ static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scal
     if (!narrow) {
       dim3 grid(mt, N / 64, ks);
       if (R == 1)
-        hipLaunchKernelGGL((k_gemm<P, 1, 4>), grid, dim3(256), (skinny_lds_bytes<P, 1, 4>()), c.stream, A, B, part,
-                           M, N, K, ks, epi);
+        hipLaunchKernelGGL((k_gemm<P, 1, 4, F8M>), grid, dim3(256), (skinny_lds_bytes<P, 1, 4>()), c.stream, A, B,
+                           part, M, N, K, ks, epi);
       else
-        hipLaunchKernelGGL((k_gemm<P, 2, 4>), grid, dim3(256), (skinny_lds_bytes<P, 2, 4>()), c.stream, A, B, part,
-                           M, N, K, ks, epi);
+        hipLaunchKernelGGL((k_gemm<P, 2, 4, F8M>), grid, dim3(256), (skinny_lds_bytes<P, 2, 4>()), c.stream, A, B,
+                           part, M, N, K, ks, epi);
     } else {
       dim3 grid(mt, N / 32, ks);
       if (R == 1)
-        hipLaunchKernelGGL((k_gemm<P, 1, 2>), grid, dim3(128), (skinny_lds_bytes<P, 1, 2>()), c.stream, A, B, part,
-                           M, N, K, ks, epi);
+        hipLaunchKernelGGL((k_gemm<P, 1, 2, F8M>), grid, dim3(128), (skinny_lds_bytes<P, 1, 2>()), c.stream, A, B,
+                           part, M, N, K, ks, epi);
       else
-        hipLaunchKernelGGL((k_gemm<P, 2, 2>), grid, dim3(128), (skinny_lds_bytes<P, 2, 2>()), c.stream, A, B, part,
-                           M, N, K, ks, epi);
+        hipLaunchKernelGGL((k_gemm<P, 2, 2, F8M>), grid, dim3(128), (skinny_lds_bytes<P, 2, 2>()), c.stream, A, B,
+                           part, M, N, K, ks, epi);
     }
   } else if (N % 128 != 0 || (M < kGemmTileBigM && P == kFP8)) {
     dim3 grid((M + 63) / 64, N / 64, ks);
-    hipLaunchKernelGGL((k_gemm_tile<P, 64, 64, 4>), grid, dim3(256), (gemm_tile_lds_bytes<64, 64, 4>()), c.stream,
-                       A, B, part, M, N, K, ks, epi);
-  } else if (M < kGemmTileBigM) {
-    dim3 grid((M + 127) / 128, N / 128, ks);
-    hipLaunchKernelGGL((k_gemm_tile<P, 128, 128, 4>), grid, dim3(256), (gemm_tile_lds_bytes<128, 128, 4>()),
+    hipLaunchKernelGGL((k_gemm_tile<P, 64, 64, 4, F8M>), grid, dim3(256), (gemm_tile_lds_bytes<64, 64, 4>()),
                        c.stream, A, B, part, M, N, K, ks, epi);
+  } else if (M < kGemmTileBigM) {
+    if constexpr (!F8M) {  // bf16 only (e4m3 takes 64 x 64 below 256 rows)
+      dim3 grid((M + 127) / 128, N / 128, ks);
+      hipLaunchKernelGGL((k_gemm_tile<P, 128, 128, 4>), grid, dim3(256), (gemm_tile_lds_bytes<128, 128, 4>()),
+                         c.stream, A, B, part, M, N, K, ks, epi);
+    }
   } else {
     dim3 grid((M + 127) / 128, N / 128, ks);
-    hipLaunchKernelGGL((k_gemm_tile<P, 128, 128, 3>), grid, dim3(256), (gemm_tile_lds_bytes<128, 128, 3>()),
+    hipLaunchKernelGGL((k_gemm_tile<P, 128, 128, 3, F8M>), grid, dim3(256), (gemm_tile_lds_bytes<128, 128, 3>()),
                        c.stream, A, B, part, M, N, K, ks, epi);
+  }
+}
+
+// defer: with K split, leave the partials for the next row kernel (deferred_split)
+// instead of launching k_gemm_reduce; only for outputs without the SiLU epilogue.
+template <int P>
+static hipError_t gemm(Ctx& c, const void* A, const void* B, const float* w_scale, float in_scale, float* out, int M,
+                       int N, int K, int resid, void* act = nullptr, float act_scale = 1.0f, float* amax = nullptr,
+                       bool defer = false) {
+  if (N % 64 != 0 || K % 128 != 0) return hipErrorInvalidValue;  // the kernels' tiling
+  if (defer && act) return hipErrorInvalidValue;
+  const int ks = gemm_ksplit(N, K);
+  float* part = split_buffer(c);  // split partials after the gate/up buffer
+  const GemmEpi epi{out, P == kFP8 ? w_scale : nullptr, in_scale, act ? 2 : (resid ? 1 : 0), act, act_scale, amax};
+  hipError_t e;
+  if constexpr (P == kFP8) {
+    if (c.fp8_mfma) gemm_launch<P, true>(c, A, B, part, M, N, K, ks, epi);
+    else gemm_launch<P, false>(c, A, B, part, M, N, K, ks, epi);
+  } else {
+    gemm_launch<P, false>(c, A, B, part, M, N, K, ks, epi);
   }
   if ((e = hipGetLastError()) != hipSuccess || ks == 1 || defer) return e;  // one split: the epilogue ran in the GEMM
   const size_t MN = (size_t)M * N;
@@ -1550,12 +1599,24 @@ hipError_t prefill_setup() {
       {(const void*)k_gemm<kBF16, 2, 2>, skinny_lds_bytes<kBF16, 2, 2>()},
       {(const void*)k_gemm<kFP8, 1, 2>, skinny_lds_bytes<kFP8, 1, 2>()},
       {(const void*)k_gemm<kFP8, 2, 2>, skinny_lds_bytes<kFP8, 2, 2>()},
+      {(const void*)k_gemm_tile<kFP8, 64, 64, 4, true>, gemm_tile_lds_bytes<64, 64, 4>()},
+      {(const void*)k_gemm_tile<kFP8, 128, 128, 3, true>, gemm_tile_lds_bytes<128, 128, 3>()},
+      {(const void*)k_gemm<kFP8, 1, 4, true>, skinny_lds_bytes<kFP8, 1, 4>()},
+      {(const void*)k_gemm<kFP8, 2, 4, true>, skinny_lds_bytes<kFP8, 2, 4>()},
+      {(const void*)k_gemm<kFP8, 1, 2, true>, skinny_lds_bytes<kFP8, 1, 2>()},
+      {(const void*)k_gemm<kFP8, 2, 2, true>, skinny_lds_bytes<kFP8, 2, 2>()},
   };
   for (const auto& k : kernels) {
     const hipError_t e = hipFuncSetAttribute(k.f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)k.lds);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_gemm(Ctx& c, const void* A, const void* W, const float* w_scale, float a_scale, float* C, int M,
+                       int N, int K) {
+  if (c.cfg.precision == HTA_FP8_E4M3) return gemm<kFP8>(c, A, W, w_scale, a_scale, C, M, N, K, 0);
+  return gemm<kBF16>(c, A, W, nullptr, 1.0f, C, M, N, K, 0);
 }
 
 hipError_t launch_prefill(Ctx& c, int P, bool record) {

@@ -31,6 +31,7 @@ OPT_TAPS = 2
 OPT_PREFILL_TAP_LAYER = 3
 OPT_TRACE = 4
 OPT_FORCE_TIMEOUT = 5
+OPT_FP8_MFMA = 6
 SITES_PER_LAYER = 4
 
 LAYER_TENSORS = ("g_attn", "wq", "wk", "wv", "g_q", "g_k", "wo", "g_mlp", "wg", "wu", "wd")
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "hta_read_tap": (I, [P, I, I, P, S]),
             "hta_calibrate": (I, [P, P, I, I, P, P]),
             "hta_layer_step": (I, [P, I, I, P, P, P]),
+            "hta_gemm": (I, [P, P, P, P, ctypes.c_float, I, I, I, P]),
             "hta_undelay": (I, [P, I, I, I, P, P]),
             "hta_stream_create": (I, [I, I, I, I, I, I, ctypes.POINTER(P)]),
             "hta_stream_push": (I, [P, P, I, P, I, P, P]),
@@ -404,6 +406,21 @@ class Hta:
         vp = ctypes.c_void_p(v_init.data_ptr()) if v_init is not None else None
         self._check(lib().hta_layer_step(self.ctx, layer, kv_len, kp, vp, ctypes.c_void_p(h.data_ptr())),
                     "hta_layer_step")
+
+
+    def gemm(self, A, W, w_scale, a_scale: float, C) -> None:
+        """C = A . W^T with the prefill's GEMM kernels: device tensors A [M][K] and W [N][K]
+        (uint8 e4m3 codes with float32 w_scale [N] on an FP8 context; bf16 on a BF16 one,
+        w_scale None), C float32 [M][N]."""
+        M, K = A.shape
+        N = W.shape[0]
+        if W.shape[1] != K or tuple(C.shape) != (M, N) or not (A.is_contiguous() and W.is_contiguous()
+                                                               and C.is_contiguous()):
+            raise ValueError("gemm: A [M][K], W [N][K] and C [M][N] must be contiguous and agree")
+        self.torch.cuda.synchronize()
+        ws = ctypes.c_void_p(w_scale.data_ptr()) if w_scale is not None else None
+        self._check(lib().hta_gemm(self.ctx, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(W.data_ptr()), ws,
+                                   float(a_scale), M, N, K, ctypes.c_void_p(C.data_ptr())), "hta_gemm")
 
 
 def weights_to_device(named: dict, n_layers: int):

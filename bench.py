@@ -214,6 +214,7 @@ def main() -> int:
     extra["prefill_ms_per_token_fp8_p13"] = round(_prefill_ms(ctx, prompt) / len(prompt), 4)
     if shape.n_layers == 36:
         extra.update(_prefill_sizes(ctx, shape, "fp8"))
+        extra["prefill_e4m3_mfma"] = _prefill_e4m3_mfma(ctx, shape, prompt)
     # roofline of the dominant kernel: the persistent frame kernel is the whole decode step (every
     # weight, scale, gain and the KV once per launch); its average launch duration is the event-timed
     # decode region divided by the frame count (back-to-back launches on the library's stream, so the
@@ -346,6 +347,7 @@ def _traffic(workload: str, shape):
 
 
 PEAK_MFMA_BF16_TFLOPS = 2500.0  # dense bf16; the FP8 prefill widens e4m3 weights to bf16 for the MFMA
+PEAK_MFMA_FP8_TFLOPS = 5000.0   # dense e4m3 (the opt-in e4m3 MFMA form of the prefill GEMMs)
 
 
 def prefill_flops(shape, P: int) -> float:
@@ -369,6 +371,28 @@ def _prefill_sizes(ctx, shape, prec: str) -> dict:
         out[f"prefill_ms_per_token_{prec}_p{P}"] = round(ms / P, 4)
         if P == 512:
             out[f"prefill_mfma_frac_{prec}_p512"] = round(prefill_flops(shape, P) / (ms * 1e-3) / 1e12 / PEAK_MFMA_BF16_TFLOPS, 4)
+    return out
+
+
+def _prefill_e4m3_mfma(ctx, shape, prompt) -> dict:
+    """The FP8 prefills again with the opt-in e4m3 MFMA form of the GEMMs (hta option
+    FP8_MFMA): faster contractions whose sums carry fewer bits than fp32, so not the FP8
+    path the parity tests hold to; reported beside it, MFMA fraction against the e4m3 peak."""
+    import synthetic as S
+    from autoregressive_codebook_tts_amd import hta
+
+    ctx.set_option(hta.OPT_FP8_MFMA, 1)
+    try:
+        out = {"prefill_ms_per_token_p13": round(_prefill_ms(ctx, prompt) / len(prompt), 4)}
+        for P in (128, 512):
+            ids = S.token_ids(S.SEEDS[f"prefill_{P}"], P, shape.text_vocab)
+            ms = _prefill_ms(ctx, ids, reps=5)
+            out[f"prefill_ms_per_token_p{P}"] = round(ms / P, 4)
+            if P == 512:
+                out["prefill_mfma_frac_of_e4m3_peak_p512"] = round(
+                    prefill_flops(shape, P) / (ms * 1e-3) / 1e12 / PEAK_MFMA_FP8_TFLOPS, 4)
+    finally:
+        ctx.set_option(hta.OPT_FP8_MFMA, 0)
     return out
 
 

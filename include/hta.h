@@ -133,6 +133,22 @@ int hta_load_weights(hta_ctx* ctx, const void* const* dev_tensors, int n_tensors
  * HTA_E_CAPACITY if len + P > max_seq or P > max_prefill. */
 int hta_prefill(hta_ctx* ctx, const int32_t* tokens, int P);
 
+/* One projection of the prefill on its own (FlashRT page, section 5: the W8A8 / BF16
+ * projections of the layer chain; the prefill runs them as batched GEMMs), with the
+ * kernels, tile shapes and K split that hta_prefill uses for the same (M, N, K):
+ * C[m][n] = sum over k of A[m][k] * W[n][k], products exact and summed in fp32 in
+ * 128-element steps of increasing k (split partials added in order), so a row's result
+ * does not depend on M.  FP8 context: A [M][K] and W [N][K] are e4m3 codes, the sum is
+ * multiplied by a_scale * w_scale[n] (w_scale: float32 [N]).  BF16 context: A and W are
+ * bf16 bits; w_scale and a_scale are ignored (w_scale may be NULL).  C: float32 [M][N].
+ * All arrays are row-major device memory owned by the caller; the call uses the
+ * context's split-partial scratch, runs on its stream and returns once C is written.
+ * Limits (HTA_E_ARG otherwise): 1 <= M <= max_prefill; N a multiple of 64, at most the
+ * widest projection (q + 2 kv widths, 2 ffn or hidden); K a positive multiple of 128;
+ * max(M, N) * K operand bytes below 2 GiB.  HTA_E_STATE without a bound workspace. */
+int hta_gemm(hta_ctx* ctx, const void* A, const void* W, const float* w_scale, float a_scale, int M, int N, int K,
+             float* C);
+
 /* One decode frame (FlashRT page, section 5): embed the previous codes (all
  * BOS for the first frame), run the backbone at position len, the fused head,
  * the greedy argmax under the delay pattern (lowest id on ties; a NaN logit
@@ -300,9 +316,16 @@ int hta_time_kernels(hta_ctx* ctx, int n_frames, float* avg_us_out, int n_classe
  * recovery path) makes every frame's first input wait for a tag no block writes: the
  * bounded wait runs out (0.5 s), every block leaves the kernel, and the decode call
  * returns HTA_E_TIMEOUT with the exchange words cleared; after setting it back to 0,
- * hta_reset starts a clean utterance.  Value 1 is unused. */
+ * hta_reset starts a clean utterance.  HTA_OPT_FP8_MFMA (default 0; FP8 contexts only,
+ * HTA_E_UNSUPPORTED on BF16) multiplies the e4m3 GEMMs of hta_prefill, hta_gemm and
+ * the batched step on the e4m3 MFMA instead of widening the codes to bf16: faster, but
+ * the instruction sums its products with fewer bits than fp32 (a product 2^-18 beside a
+ * product 1 is lost), so results differ from the fp32 sums by up to about 2^-19 of the
+ * sum of |products|, short of the fp32 accumulation this library reads into the FP8
+ * path (FlashRT page, section 8 names e4m3 W8A8 GEMMs and no accumulation width).  Rows
+ * stay independent of M.  Value 1 is unused. */
 enum { HTA_OPT_USE_GRAPH = 0, HTA_OPT_TAPS = 2, HTA_OPT_PREFILL_TAP_LAYER = 3, HTA_OPT_TRACE = 4,
-       HTA_OPT_FORCE_TIMEOUT = 5 };
+       HTA_OPT_FORCE_TIMEOUT = 5, HTA_OPT_FP8_MFMA = 6 };
 int hta_set_option(hta_ctx* ctx, int option, int value);
 
 void hta_destroy(hta_ctx* ctx);

@@ -181,6 +181,22 @@ def code_frames(seed: int, n_frames: int, n_codebooks: int = 8, n_codes: int = 1
     return gen.integers(0, n_codes, size=(n_frames, n_codebooks), dtype=np.int64).astype(np.int32)
 
 
+def e4m3_code_matrix(seed: int, rows: int, cols: int, max_exp_field: int, big_every: int = 0,
+                     big_exp_field: int = 9) -> np.ndarray:
+    """uint8 e4m3 codes [rows][cols] drawn field by field: a uniform sign bit, an exponent
+    field uniform in 0..max_exp_field and a uniform 3-bit mantissa (never the NaN code).
+    With big_every > 0, about one entry in big_every gets exponent field big_exp_field
+    instead (a few large products among many small ones: the operands of the GEMM
+    accumulation checks)."""
+    gen = np.random.Generator(np.random.PCG64(seed))
+    sign = gen.integers(0, 2, size=(rows, cols), dtype=np.int64)
+    exp = gen.integers(0, max_exp_field + 1, size=(rows, cols), dtype=np.int64)
+    man = gen.integers(0, 8, size=(rows, cols), dtype=np.int64)
+    if big_every > 0:
+        exp = np.where(gen.integers(0, big_every, size=(rows, cols)) == 0, big_exp_field, exp)
+    return ((sign << 7) | (exp << 3) | man).astype(np.uint8)
+
+
 # Seeds of the synthetic workloads.
 SEEDS = {
     "tiny_weights": 1001, "tiny_prompt": 2001, "calib_prompt": 3001,
@@ -188,4 +204,5 @@ SEEDS = {
     "full_weights": 1003, "full_prompt": 2004,
     "prefill_13": 2005, "prefill_128": 2006, "prefill_512": 2007,
     "preamble": 2064, "suffix_base": 2101, "long_prompt": 2409,
+    "gemm_a": 4001, "gemm_w": 4002, "gemm_scales": 4003,
 }

@@ -1,0 +1,198 @@
+"""GPU parity of the prefill's projection GEMM on its own (hta_gemm: the kernels, tile
+shapes and K split that the prefill uses for the same M, N, K) against exact sums, and the
+accumulation of the opt-in e4m3 MFMA form (HTA_OPT_FP8_MFMA).
+
+* Exact grid.  Every e4m3 value is a multiple of 2^-9, so every product of two is a
+  multiple of 2^-18.  With sum |products| < 2^6, every partial sum, in any order, is a
+  multiple of 2^-18 below 2^6 in magnitude, which fp32 holds exactly (24 bits).  A kernel
+  that forms exact products and adds them in fp32 therefore returns the exact sum bit for
+  bit, whatever its order, tile shape or K split.  The operands mix many small values with
+  a few large ones, so one sum holds products from 2^-18 to about 2^1.  The BF16 context
+  takes the same values as bf16 bits (exact).
+* Realistic operands (N(0, 1) activations and N(0, 0.02) weight rows, quantised as the FP8
+  path quantises them, with their scales): every output within the fp32 worst-case bound
+  of a K-term sum, and the e4m3 rounding of C / s at an activation scale s = max|C| / 448
+  equal to the rounding of the exact value except within the band of the decode site
+  checks (2^-16 relative, or 2^-18 of the RMS).
+* Rows do not depend on M: the first rows at M = 13, 40 and 100 (the small-M kernel with
+  one and two 16-row fragments; below 256 rows the 64 x 64 tile for e4m3 and the 128 x 128
+  four-stage tile for bf16) equal those at M = 300 (128 x 128, three stages) bit for bit,
+  and the first 300 rows at M = 512 likewise.
+* The e4m3 MFMA form keeps rows independent of M but misses the exact grid, and its site
+  roundings flip outside the band: the instruction sums e4m3 products with fewer bits than
+  fp32.  That is why the FP8 path widens e4m3 codes to bf16 (exact) and multiplies on the
+  bf16 MFMA.
+"""
+import numpy as np
+import pytest
+
+import synthetic as S
+from autoregressive_codebook_tts_amd import hta
+from gpu_common import rounding_flips
+from oracle import numerics as nx
+
+pytestmark = pytest.mark.gpu
+SH = S.QWEN3_4B.with_layers(1)
+# (name, N, K) of the four projections of one layer
+SHAPES = [("qkv", SH.q_dim + 2 * SH.kv_dim, SH.hidden), ("o", SH.hidden, SH.q_dim),
+          ("gate_up", 2 * SH.ffn, SH.hidden), ("down", SH.hidden, SH.ffn)]
+SITE_BAND = (2.0 ** -16, 2.0 ** -18)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def ctxs():
+    out = {p: hta.Hta(SH, p, max_seq=512, max_prefill=512) for p in ("fp8", "bf16")}
+    yield out
+    for c in out.values():
+        c.close()
+
+
+def _dev(a: np.ndarray):
+    import torch
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _bf16_bits_of(values: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of values that bf16 holds exactly (e4m3 values: at most 4 significant bits)."""
+    b = (values.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(nx.bf16_bits_to_float(b), values)
+    return b
+
+
+def _run(ctx, precision, a_codes, w_codes, w_scale=None, a_scale=1.0):
+    import torch
+    M, N = a_codes.shape[0], w_codes.shape[0]
+    if precision == "fp8":
+        A, W = _dev(a_codes), _dev(w_codes)
+        ws = _dev(np.ones(N, np.float32) if w_scale is None else w_scale.astype(np.float32))
+    else:
+        A, W = _dev(_bf16_bits_of(nx.e4m3_decode(a_codes))), _dev(_bf16_bits_of(nx.e4m3_decode(w_codes)))
+        ws = None
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ctx.gemm(A, W, ws, a_scale, C)
+    return C.cpu().numpy()
+
+
+def _grid_operands(N, K, M=300):
+    a = S.e4m3_code_matrix(S.SEEDS["gemm_a"] + K, M, K, max_exp_field=3, big_every=256, big_exp_field=10)
+    w = S.e4m3_code_matrix(S.SEEDS["gemm_w"] + N, N, K, max_exp_field=3)
+    av, wv = nx.e4m3_decode(a), nx.e4m3_decode(w)
+    exact = av @ wv.T
+    sabs = np.abs(av) @ np.abs(wv).T
+    assert sabs.max() < 64.0, "precondition of the exact grid: sum |products| < 2^6"
+    return a, w, exact
+
+
+@pytest.mark.parametrize("precision", ["fp8", "bf16"])
+@pytest.mark.parametrize("name,N,K", SHAPES)
+def test_gemm_exact_grid_and_rows_independent_of_m(ctxs, precision, name, N, K):
+    _say(f"[gemm] exact grid {precision} {name} N={N} K={K}")
+    ctx = ctxs[precision]
+    if precision == "fp8":
+        ctx.set_option(hta.OPT_FP8_MFMA, 0)
+    a, w, exact = _grid_operands(N, K)
+    c300 = _run(ctx, precision, a, w)
+    bad = np.flatnonzero(c300.astype(np.float64) != exact)
+    assert bad.size == 0, (f"{precision} {name}: {bad.size} of {exact.size} outputs differ from the exact sum; "
+                           f"worst {float(np.abs(c300 - exact).max()):.3e}")
+    for m in (13, 40, 100):
+        cm = _run(ctx, precision, a[:m], w)
+        assert np.array_equal(cm, c300[:m]), f"{precision} {name}: rows at M={m} differ from those at M=300"
+    a512 = np.concatenate([a, S.e4m3_code_matrix(S.SEEDS["gemm_a"] + 7, 212, K, max_exp_field=3)])
+    c512 = _run(ctx, precision, a512, w)
+    assert np.array_equal(c512[:300], c300), f"{precision} {name}: rows at M=512 differ from those at M=300"
+
+
+def _realistic(name, N, K, M=128):
+    x = S.normal_vector(S.SEEDS["gemm_a"] + 1000 + K, (M, K)).astype(np.float64)
+    a_scale = float(np.abs(x).max() / 448.0)
+    a_codes = nx.e4m3_encode(x / a_scale)
+    wf = 0.02 * S.normal_vector(S.SEEDS["gemm_w"] + 1000 + N, (N, K)).astype(np.float64)
+    wq, w_scale = nx.quantize_weight_rows(wf)
+    w_codes = nx.e4m3_encode(wq)
+    av, wv = nx.e4m3_decode(a_codes), nx.e4m3_decode(w_codes)
+    scale = a_scale * np.asarray(w_scale, np.float64)[None, :]
+    exact = (av @ wv.T) * scale
+    sabs = (np.abs(av) @ np.abs(wv).T) * scale
+    return a_codes, w_codes, np.asarray(w_scale, np.float32), np.float32(a_scale), exact, sabs
+
+
+def _site_flips(c_gpu, exact):
+    """e4m3 roundings of C / s (fp32 quotient, as the kernels round an activation) against
+    those of the exact values; returns (flips, flips outside the site band)."""
+    s = np.float32(np.abs(exact).max() / 448.0)
+    y_gpu = (c_gpu.astype(np.float32) / s).astype(np.float64)
+    x = exact / float(s)
+    idx, d_rel, d_rms = rounding_flips(nx.e4m3_round(y_gpu).ravel(), nx.e4m3_round(x).ravel(), x.ravel())
+    outside = int(np.count_nonzero((d_rel > SITE_BAND[0]) & (d_rms > SITE_BAND[1])))
+    return int(idx.size), outside
+
+
+@pytest.mark.parametrize("name,N,K", [SHAPES[0], SHAPES[3]])
+def test_gemm_fp8_realistic_operands(ctxs, name, N, K):
+    _say(f"[gemm] realistic fp8 {name} N={N} K={K}")
+    ctx = ctxs["fp8"]
+    ctx.set_option(hta.OPT_FP8_MFMA, 0)
+    a, w, ws, a_s, exact, sabs = _realistic(name, N, K)
+    c = _run(ctx, "fp8", a, w, ws, a_s).astype(np.float64)
+    err = np.abs(c - exact)
+    bound = (K + 4) * 2.0 ** -24 * sabs  # fp32 sum of K exact products, then two scale roundings
+    _say(f"[gemm] {name}: max |C - exact| / sum|p| = {float((err / sabs).max()):.3e}")
+    assert np.all(err <= bound)
+    flips, outside = _site_flips(c, exact)
+    _say(f"[gemm] {name}: e4m3 site roundings: {flips} flips, {outside} outside the band")
+    assert outside == 0
+
+
+def test_fp8_mfma_form_misses_fp32_accumulation(ctxs):
+    """The opt-in e4m3 MFMA form: rows still independent of M, but the exact grid is missed
+    and the site roundings flip outside the band (kept out of the FP8 path for that)."""
+    ctx = ctxs["fp8"]
+    name, N, K = SHAPES[0]
+    ctx.set_option(hta.OPT_FP8_MFMA, 1)
+    try:
+        a, w, exact = _grid_operands(N, K)
+        c300 = _run(ctx, "fp8", a, w)
+        for m in (13, 40, 100):
+            assert np.array_equal(_run(ctx, "fp8", a[:m], w), c300[:m]), f"e4m3 MFMA: rows at M={m} differ"
+        miss = int(np.count_nonzero(c300.astype(np.float64) != exact))
+        av, wv = nx.e4m3_decode(a), nx.e4m3_decode(w)
+        worst = float((np.abs(c300 - exact) / (np.abs(av) @ np.abs(wv).T)).max())
+        _say(f"[gemm] e4m3 MFMA on the exact grid: {miss} of {exact.size} outputs inexact "
+             f"(worst |C - exact| / sum|p| {worst:.2e})")
+        assert miss > 0
+        a, w, ws, a_s, exact, sabs = _realistic(name, N, K)
+        c = _run(ctx, "fp8", a, w, ws, a_s).astype(np.float64)
+        flips, outside = _site_flips(c, exact)
+        worst = float((np.abs(c - exact) / sabs).max())
+        _say(f"[gemm] e4m3 MFMA realistic: max |C - exact| / sum|p| = {worst:.3e}; site roundings: {flips} flips, "
+             f"{outside} outside the band")
+        assert outside > 0
+    finally:
+        ctx.set_option(hta.OPT_FP8_MFMA, 0)
+
+
+def test_fp8_mfma_option_rejected_on_bf16(ctxs):
+    with pytest.raises(hta.HtaError):
+        ctxs["bf16"].set_option(hta.OPT_FP8_MFMA, 1)
+
+
+def test_gemm_argument_errors(ctxs):
+    import torch
+    ctx = ctxs["fp8"]
+    A = torch.zeros((16, 256), dtype=torch.uint8, device="cuda")
+    W = torch.zeros((64, 256), dtype=torch.uint8, device="cuda")
+    ws = torch.ones(64, dtype=torch.float32, device="cuda")
+    C = torch.empty((16, 64), dtype=torch.float32, device="cuda")
+    lib = hta.lib()
+    p = lambda t: None if t is None else __import__("ctypes").c_void_p(t.data_ptr())
+    for (M, N, K, w_scale) in [(0, 64, 256, ws), (513, 64, 256, ws), (16, 32, 256, ws), (16, 64, 100, ws),
+                               (16, 64, 0, ws), (16, 19456 + 64, 256, ws), (16, 64, 256, None)]:
+        rc = lib.hta_gemm(ctx.ctx, p(A), p(W), p(w_scale), 1.0, M, N, K, p(C))
+        assert rc == hta.HTA_E_ARG, (M, N, K, rc)
