@@ -702,6 +702,23 @@ __device__ __forceinline__ float epi_silu(const GemmEpi& e, int N, int row, int 
   return fabsf(v);
 }
 
+// SiLU * up of one 16x16 output tile: the lane of an even column holds the gate values of
+// rows row0 .. row0 + 3 (v[0..3], already scaled), its odd neighbour the up values of the
+// same rows.  Two exchanges give the even lane the pairs of rows row0 and row0 + 1 and the
+// odd lane those of rows row0 + 2 and row0 + 3, so both lanes share the work; each pair's
+// arithmetic is that of epi_silu.  Returns the larger |SiLU * up| of the lane's two pairs.
+template <int P>
+__device__ __forceinline__ float epi_silu_tile(const GemmEpi& e, int N, int M, int row0, int pair, bool odd,
+                                               const float (&v)[4]) {
+  const float s1 = __shfl_xor(odd ? v[0] : v[2], 1, kWave);  // even: up of row0; odd: gate of row0 + 2
+  const float s2 = __shfl_xor(odd ? v[1] : v[3], 1, kWave);  // even: up of row0 + 1; odd: gate of row0 + 3
+  const int ra = row0 + (odd ? 2 : 0);
+  float mx = 0.0f;
+  if (ra < M) mx = epi_silu<P>(e, N, ra, pair, odd ? s1 : v[0], odd ? v[2] : s1);
+  if (ra + 1 < M) mx = fmaxf(mx, epi_silu<P>(e, N, ra + 1, pair, odd ? s2 : v[1], odd ? v[3] : s2));
+  return mx;
+}
+
 // NW waves per block, each computing 16R x 16 (16 NW columns per block).  The ring's
 // budget keeps two blocks per CU at NW = 4 and three at NW = 2.
 template <int P, int R, int NW>
@@ -849,20 +866,23 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, co
     // the whole K range is here: the epilogue works from the registers (0 + acc, as the
     // split sum starts from zero)
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
+      float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = m0 + 16 * r + 4 * g + i;
         float sum = 0.0f;
         sum += acc[r][i];
-        const float v = epi_scale(epi, sum, col);
-        if (epi.mode == 2) {
-          const float up = __shfl_xor(v, 1, kWave);  // the neighbouring lane holds the pair's up column
-          if (row < M && (r16 & 1) == 0) mx = fmaxf(mx, epi_silu<P>(epi, N, row, col / 2, v, up));
-        } else if (row < M) {
-          epi_store<P>(epi, N, row, col, v);
-        }
+        v[i] = epi_scale(epi, sum, col);
       }
+      const int row0 = m0 + 16 * r + 4 * g;
+      if (epi.mode == 2) {
+        mx = fmaxf(mx, epi_silu_tile<P>(epi, N, M, row0, col / 2, (r16 & 1) != 0, v));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (row0 + i < M) epi_store<P>(epi, N, row0 + i, col, v[i]);
+      }
+    }
   } else {
     // a split's partial, summed by the consuming row kernel or k_gemm_reduce (a
     // last-arriving block adding the splits here would put three memory round trips on
@@ -1066,18 +1086,20 @@ __global__ __launch_bounds__(256, F8M ? 3 : 1) void k_gemm_tile(const void* __re
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int col = n0 + WN * wn + 16 * j + r16;
+        const int row0 = m0 + 64 * wm + 16 * i + 4 * g;
+        float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = m0 + 64 * wm + 16 * i + 4 * g + r;
           float sum = 0.0f;
           sum += acc[i][j][r];
-          const float v = epi_scale(epi, sum, col);
-          if (epi.mode == 2) {
-            const float up = __shfl_xor(v, 1, kWave);  // the neighbouring lane holds the pair's up column
-            if (row < M && (r16 & 1) == 0) mx = fmaxf(mx, epi_silu<P>(epi, N, row, col / 2, v, up));
-          } else if (row < M) {
-            epi_store<P>(epi, N, row, col, v);
-          }
+          v[r] = epi_scale(epi, sum, col);
+        }
+        if (epi.mode == 2) {
+          mx = fmaxf(mx, epi_silu_tile<P>(epi, N, M, row0, col / 2, (r16 & 1) != 0, v));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (row0 + r < M) epi_store<P>(epi, N, row0 + r, col, v[r]);
         }
       }
     if (epi.mode == 2 && epi.amax) {
