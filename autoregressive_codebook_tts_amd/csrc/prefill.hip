@@ -1141,11 +1141,14 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(const float* __restrict__ C
   else out[idx] = s;
 }
 
-// Number of K splits: a function of (N, K) only, so prefix reuse stays bit-identical.
+// Number of K splits: a function of (N, K) only, so prefix reuse stays bit-identical.  About
+// 768 blocks of 16 columns: on the 36-layer shapes this takes o and down to 5 splits and
+// q/k/v to 2 (from 7 and 3 at 1024 blocks: -6 % at P = 512, -4 % at P = 128, -2 % at
+// P = 13 and -3 % per batched step; 384 and 512 blocks were slower at some P).
 static int gemm_ksplit(int N, int K) {
   const int nsteps = K / 128;
   const int nblk = N / 16;
-  int s = (1024 + nblk - 1) / nblk;
+  int s = (768 + nblk - 1) / nblk;
   if (s > 8) s = 8;
   if (s > nsteps) s = nsteps;
   if (s < 1) s = 1;
