@@ -274,20 +274,31 @@ def main() -> int:
 
 
 def _clock_sampler(out: dict):
-    """Start a host thread that reads the GPU's current clocks once (rocm-smi, read-only)
-    while the caller's decode runs; out["value"] gets the parsed clocks or the reason none
-    were read.  Context for the timings, not part of them."""
-    import subprocess
+    """Start a host thread that reads the GPU's current clock levels once (the driver's
+    pp_dpm_sclk / pp_dpm_mclk / pp_dpm_fclk files in sysfs, read-only; no child process)
+    while the caller's decode runs; out["value"] gets the current level of each, per card,
+    or the reason none were read.  Context for the timings, not part of them."""
+    import glob
     import threading
 
     def run():
         try:
             time.sleep(0.3)  # well inside the 1017-frame decode (about 1.3 s)
-            r = subprocess.run(["rocm-smi", "--showgpuclocks", "--json"], capture_output=True, text=True, timeout=20)
-            card = next(iter(json.loads(r.stdout).values()))
-            out["value"] = {k: v for k, v in card.items() if "clock" in k.lower() or "sclk" in k.lower()
-                            or "mclk" in k.lower() or "fclk" in k.lower()}
-        except Exception as ex:  # no rocm-smi, no permission, another output format
+            cards = {}
+            for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+                levels = {}
+                for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+                    try:
+                        with open(os.path.join(dev, name)) as f:
+                            cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+                    except OSError:
+                        continue
+                    if cur:
+                        levels[name[7:]] = cur[0].split(":", 1)[-1].rstrip("*").strip()
+                if levels:
+                    cards[os.path.basename(os.path.dirname(dev))] = levels
+            out["value"] = cards or "unavailable: no readable clock levels in sysfs"
+        except Exception as ex:  # another sysfs layout
             out["value"] = f"unavailable: {type(ex).__name__}"
 
     t = threading.Thread(target=run, daemon=True)
