@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_embed_rows(const int32_t* __restrict__ 
 // The row kernels issue all of a thread's loads before using any (clamped addresses,
 // no load under a condition): a loop that loads and uses one element per step waits
 // a memory round trip per element.
-constexpr int kRowPer = 16;  // row elements per thread (rows up to 16 * 256)
+constexpr int kRowPerMax = 20;  // row elements per thread of the row kernels (rows up to 20 * 256)
 
 // The sum of a column's K-split partials in split order, scaled as k_gemm_reduce
 // scales it (the rounding sequence of k_gemm_reduce, so fusing changes no bit).
@@ -99,32 +99,34 @@ __device__ __forceinline__ void split_sums(const SplitIn& si, const long (&idx)[
 // Row RMSNorm + rounding to the GEMV input format.  With a split input, the row is first
 // updated as residual += (the split sum of the GEMM that produced it), the work of
 // k_gemm_reduce, and the updated residual is stored and normalised.
-template <int P>
+// RP row elements per thread (rows up to 256 * RP); KS bounds the split count of the
+// input (0: no split input), so that no thread issues loads beyond its row and splits.
+template <int P, int RP, int KS>
 __global__ __launch_bounds__(256) void k_rmsnorm_act_rows(float* __restrict__ X, const float* __restrict__ g,
                                                           float eps, void* __restrict__ U, int d, float scale,
                                                           float* amax, SplitIn si) {
   __shared__ float red[16];
   const int i = blockIdx.x;
   float* x = X + (size_t)i * d;
-  float xv[kRowPer], gv[kRowPer];
+  float xv[RP], gv[RP];
 #pragma unroll
-  for (int u = 0; u < kRowPer; ++u) {
+  for (int u = 0; u < RP; ++u) {
     const int k = u * 256 + threadIdx.x, kc = min(k, d - 1);
     xv[u] = x[kc];
     gv[u] = g[kc];
   }
-  if (si.part) {
-    float sv[kRowPer];
-    long idx[kRowPer];
-    int col[kRowPer];
+  if (KS > 0 && si.part) {
+    float sv[RP];
+    long idx[RP];
+    int col[RP];
 #pragma unroll
-    for (int u = 0; u < kRowPer; ++u) {
+    for (int u = 0; u < RP; ++u) {
       col[u] = min(u * 256 + (int)threadIdx.x, d - 1);
       idx[u] = (long)i * d + col[u];
     }
-    split_sums<kRowPer, kMaxSplit>(si, idx, col, sv);
+    split_sums<RP, (KS > 0 ? KS : 1)>(si, idx, col, sv);
 #pragma unroll
-    for (int u = 0; u < kRowPer; ++u) {
+    for (int u = 0; u < RP; ++u) {
       const int k = u * 256 + threadIdx.x;
       xv[u] += sv[u];
       if (k < d) x[k] = xv[u];
@@ -132,13 +134,13 @@ __global__ __launch_bounds__(256) void k_rmsnorm_act_rows(float* __restrict__ X,
   }
   float ss = 0.0f;  // over k = tid, tid + 256, ... in increasing order
 #pragma unroll
-  for (int u = 0; u < kRowPer; ++u)
+  for (int u = 0; u < RP; ++u)
     if (u * 256 + threadIdx.x < d) ss = fmaf(xv[u], xv[u], ss);
   ss = block_sum(ss, red);
   const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
   float mx = 0.0f;
 #pragma unroll
-  for (int u = 0; u < kRowPer; ++u) {
+  for (int u = 0; u < RP; ++u) {
     const int k = u * 256 + threadIdx.x;
     if (k >= d) continue;
     const float v = xv[u] * rstd * gv[u];
@@ -150,6 +152,28 @@ __global__ __launch_bounds__(256) void k_rmsnorm_act_rows(float* __restrict__ X,
     mx = block_max(mx, red);
     if (threadIdx.x == 0) record_amax(amax, mx);
   }
+}
+
+// k_rmsnorm_act_rows over `rows` rows, with the narrowest instantiation for d and si.ks
+// (the split bound rounds up: 2, 5 or 8 splits).
+template <int P>
+static void launch_rmsnorm_rows(hipStream_t st, int rows, float* X, const float* g, float eps, void* U, int d,
+                                float scale, float* amax, const SplitIn& si) {
+#define HTA_NORM(RP, KS) \
+  hipLaunchKernelGGL((k_rmsnorm_act_rows<P, RP, KS>), dim3(rows), dim3(256), 0, st, X, g, eps, U, d, scale, amax, si)
+  const int ks = si.part ? si.ks : 0;
+  if (d <= 10 * 256) {
+    if (ks == 0) HTA_NORM(10, 0);
+    else if (ks <= 2) HTA_NORM(10, 2);
+    else if (ks <= 5) HTA_NORM(10, 5);
+    else HTA_NORM(10, 8);
+  } else {
+    if (ks == 0) HTA_NORM(20, 0);
+    else if (ks <= 2) HTA_NORM(20, 2);
+    else if (ks <= 5) HTA_NORM(20, 5);
+    else HTA_NORM(20, 8);
+  }
+#undef HTA_NORM
 }
 
 template <int P>
@@ -192,8 +216,11 @@ __device__ __forceinline__ void norm_rope_vals(float x0, float x1, float g0, flo
 // The q/k/v row comes from QKV, or, with a split input, is the split sum of the GEMM's
 // partials (the work of k_gemm_reduce, element by element in the same order; at most
 // kRopeMaxSplit splits, so that every partial of a thread is loaded in one batch).
+// HPW heads per wave (Hq + Hkv <= 4 HPW), VPER value elements per thread (Hkv HD <= 256
+// VPER) and KS >= the split count (0: no split input), so that no thread issues loads
+// beyond its heads and splits.
 constexpr int kRopeMaxSplit = 4;
-template <int HD>
+template <int HD, int HPW, int VPER, int KS>
 __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ QKV, const float* __restrict__ g_q,
                                                       const float* __restrict__ g_k, const float* __restrict__ rope_cos,
                                                       const float* __restrict__ rope_sin, float* __restrict__ Q,
@@ -214,11 +241,11 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
   const float* cs = rope_cos + (size_t)pos * H2;
   const float* sn = rope_sin + (size_t)pos * H2;
   // this wave's heads' values, all loaded before the first is used
-  constexpr int kHeadsPerWave = 16;  // Hq + Hkv <= 16 * waves
+  constexpr int kHeadsPerWave = HPW;
   const bool act = lane < H2;
   const int la = act ? lane : 0;
   float x0[kHeadsPerWave], x1[kHeadsPerWave];
-  if (si.part) {
+  if (KS > 0 && si.part) {
     long idx[2 * kHeadsPerWave];
     int col[2 * kHeadsPerWave];
     float xs[2 * kHeadsPerWave];
@@ -230,7 +257,7 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
       idx[2 * t] = (long)i * W + col[2 * t];
       idx[2 * t + 1] = (long)i * W + col[2 * t + 1];
     }
-    split_sums<2 * kHeadsPerWave, kRopeMaxSplit>(si, idx, col, xs);
+    split_sums<2 * kHeadsPerWave, (KS > 0 ? KS : 1)>(si, idx, col, xs);
 #pragma unroll
     for (int t = 0; t < kHeadsPerWave; ++t) {
       x0[t] = xs[2 * t];
@@ -266,9 +293,9 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
       }
     }
   }
-  constexpr int kVPer = 8;  // Hkv * HD <= 8 * 256
+  constexpr int kVPer = VPER;
   float vv[kVPer];
-  if (si.part) {
+  if (KS > 0 && si.part) {
     long idx[kVPer];
     int col[kVPer];
 #pragma unroll
@@ -276,7 +303,7 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
       col[u] = (Hq + Hkv) * HD + min(u * 256 + (int)threadIdx.x, Hkv * HD - 1);
       idx[u] = (long)i * W + col[u];
     }
-    split_sums<kVPer, kRopeMaxSplit>(si, idx, col, vv);
+    split_sums<kVPer, (KS > 0 ? KS : 1)>(si, idx, col, vv);
   } else {
 #pragma unroll
     for (int u = 0; u < kVPer; ++u) vv[u] = row[(size_t)(Hq + Hkv) * HD + min(u * 256 + (int)threadIdx.x, Hkv * HD - 1)];
@@ -288,6 +315,30 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
     const int j = e / HD, dd = e % HD;
     vc[((size_t)j * max_seq + pos) * HD + dd] = (uint16_t)f32_to_bf16(vv[u]);
   }
+}
+
+// k_qk_rope_rows over `rows` rows with the narrowest instantiation: 10 heads per wave and
+// 4 value elements per thread where the head counts allow (Hq + Hkv <= 40, Hkv HD <=
+// 1024), else 16 and 8; split bound 2 or 4.
+template <int HD>
+static void launch_qk_rope_rows(hipStream_t st, int rows, const float* QKV, const float* g_q, const float* g_k,
+                                const float* rope_cos, const float* rope_sin, float* Q, uint16_t* kc, uint16_t* vc,
+                                const int* len_at, int Hq, int Hkv, int max_seq, float eps, int len_stride,
+                                long kv_stride, const SplitIn& si) {
+#define HTA_ROPE(HPW, VPER, KS)                                                                                  \
+  hipLaunchKernelGGL((k_qk_rope_rows<HD, HPW, VPER, KS>), dim3(rows), dim3(256), 0, st, QKV, g_q, g_k, rope_cos, \
+                     rope_sin, Q, kc, vc, len_at, Hq, Hkv, max_seq, eps, len_stride, kv_stride, si)
+  const int ks = si.part ? si.ks : 0;
+  if (Hq + Hkv <= 40 && Hkv * HD <= 1024) {
+    if (ks == 0) HTA_ROPE(10, 4, 0);
+    else if (ks <= 2) HTA_ROPE(10, 4, 2);
+    else HTA_ROPE(10, 4, 4);
+  } else {
+    if (ks == 0) HTA_ROPE(16, 8, 0);
+    else if (ks <= 2) HTA_ROPE(16, 8, 2);
+    else HTA_ROPE(16, 8, 4);
+  }
+#undef HTA_ROPE
 }
 
 // ============================================================================ causal attention
@@ -540,7 +591,8 @@ template <int HD, int G>
 constexpr bool rope_attn_small_fits() {
   return (size_t)G * kAttnQT * HD * 4 <= sizeof(uint16_t) * kAttnTile * (HD + 8) + sizeof(uint16_t) * HD * (kAttnTile + 8);
 }
-template <int P, int HD, int G>
+// KS >= the split count of the q/k/v input (loads per thread bounded by it).
+template <int P, int HD, int G, int KS>
 __global__ __launch_bounds__(64 * G) void k_rope_attn_small(
     const float* __restrict__ QKV, SplitIn si, const float* __restrict__ g_q, const float* __restrict__ g_k,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, uint16_t* __restrict__ kc,
@@ -575,7 +627,7 @@ __global__ __launch_bounds__(64 * G) void k_rope_attn_small(
       idx[2 * i + 1] = r * W + col[2 * i + 1];
     }
     if (si.part) {
-      split_sums<2 * QT, kRopeMaxSplit>(si, idx, col, xq);
+      split_sums<2 * QT, KS>(si, idx, col, xq);
     } else {
 #pragma unroll
       for (int u = 0; u < 2 * QT; ++u) xq[u] = QKV[idx[u]];
@@ -599,7 +651,7 @@ __global__ __launch_bounds__(64 * G) void k_rope_attn_small(
     }
     float xs[2 * KR + VE * KR];
     if (si.part) {
-      split_sums<2 * KR + VE * KR, kRopeMaxSplit>(si, idx, col, xs);
+      split_sums<2 * KR + VE * KR, KS>(si, idx, col, xs);
     } else {
 #pragma unroll
       for (int u = 0; u < 2 * KR + VE * KR; ++u) xs[u] = QKV[idx[u]];
@@ -1256,7 +1308,7 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
   const int* len0 = &c.state->len;
   float* amax = record ? c.amax : nullptr;
   // the row kernels' per-thread register batches (k_rmsnorm_act_rows, k_qk_rope_rows)
-  if (d > kRowPer * 256 || Hq + Hkv > 16 * 4 || kvd > 8 * 256) return hipErrorInvalidValue;
+  if (d > kRowPerMax * 256 || Hq + Hkv > 16 * 4 || kvd > 8 * 256) return hipErrorInvalidValue;
   if (Hq % Hkv != 0 || (Hq / Hkv != 1 && Hq / Hkv != 2 && Hq / Hkv != 4)) return hipErrorInvalidValue;
   hipError_t e;
   hipLaunchKernelGGL(k_embed_rows, dim3(Pn), dim3(256), 0, c.stream, c.tok, c.e_text, c.px, d);
@@ -1271,7 +1323,7 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
     if (tap && (e = hipMemcpyAsync(c.taps_p, c.px, tap_bytes, hipMemcpyDeviceToDevice, c.stream)) != hipSuccess)
       return e;
     if (!normed) {
-      hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, L.g_attn, f.rms_eps, c.pu,
+      launch_rmsnorm_rows<P>(c.stream, Pn, c.px, L.g_attn, f.rms_eps, c.pu,
                          d, host_act_scale(c, s0), amax ? amax + s0 : nullptr, none);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1285,10 +1337,15 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
     float* am = amax ? amax + s0 + 1 : nullptr;
     if (Pn <= kAttnQT) {
       // one query block: rotation and attention in one launch per kv head
-#define HTA_RA(HDV, GV)                                                                                      \
-  hipLaunchKernelGGL((k_rope_attn_small<P, HDV, GV>), dim3(Hkv), dim3(64 * GV), 0, c.stream, c.pqkv, sq, L.g_q, \
-                     L.g_k, c.rope_cos, c.rope_sin, L.k_cache, L.v_cache, c.po, len0, Pn, Hq, Hkv, f.max_seq,     \
-                     f.rms_eps, so, am)
+#define HTA_RA2(HDV, GV, KSV)                                                                                \
+  hipLaunchKernelGGL((k_rope_attn_small<P, HDV, GV, KSV>), dim3(Hkv), dim3(64 * GV), 0, c.stream, c.pqkv, sq,     \
+                     L.g_q, L.g_k, c.rope_cos, c.rope_sin, L.k_cache, L.v_cache, c.po, len0, Pn, Hq, Hkv,         \
+                     f.max_seq, f.rms_eps, so, am)
+#define HTA_RA(HDV, GV)                            \
+  do {                                             \
+    if (!sq.part || sq.ks <= 2) HTA_RA2(HDV, GV, 2); \
+    else HTA_RA2(HDV, GV, kRopeMaxSplit);            \
+  } while (0)
       if (hd == 128 && G == 4) HTA_RA(128, 4);
       else if (hd == 128 && G == 2) HTA_RA(128, 2);
       else if (hd == 128 && G == 1) HTA_RA(128, 1);
@@ -1297,14 +1354,15 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
       else if (hd == 64 && G == 1) HTA_RA(64, 1);
       else return hipErrorInvalidValue;
 #undef HTA_RA
+#undef HTA_RA2
       if ((e = hipGetLastError()) != hipSuccess) return e;
     } else {
       if (hd == 128)
-        hipLaunchKernelGGL(k_qk_rope_rows<128>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
-                           c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L, sq);
+        launch_qk_rope_rows<128>(c.stream, Pn, c.pqkv, L.g_q, L.g_k, c.rope_cos, c.rope_sin, c.pq, L.k_cache,
+                                 L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L, sq);
       else
-        hipLaunchKernelGGL(k_qk_rope_rows<64>, dim3(Pn), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
-                           c.rope_sin, c.pq, L.k_cache, L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L, sq);
+        launch_qk_rope_rows<64>(c.stream, Pn, c.pqkv, L.g_q, L.g_k, c.rope_cos, c.rope_sin, c.pq, L.k_cache,
+                                L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L, sq);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       dim3 grid(Hkv, (Pn + kAttnQT - 1) / kAttnQT);
 #define HTA_ATTN(HDV, GV)                                                                                        \
@@ -1323,7 +1381,7 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
     if ((e = gemm<P>(c, c.po, L.w_o, L.s_o, host_act_scale(c, s0 + 1), c.px, Pn, d, qd, 1, nullptr, 1.0f, nullptr,
                      true)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, L.g_mlp, f.rms_eps, c.pu, d,
+    launch_rmsnorm_rows<P>(c.stream, Pn, c.px, L.g_mlp, f.rms_eps, c.pu, d,
                        host_act_scale(c, s0 + 2), amax ? amax + s0 + 2 : nullptr,
                        deferred_split<P>(c, Pn, d, qd, L.s_o, host_act_scale(c, s0 + 1)));
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1339,7 +1397,7 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
     normed = fuse_next;
     if (fuse_next) {
       const int s1 = s0 + kSitesPerLayer;
-      hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(Pn), dim3(256), 0, c.stream, c.px, c.layers[layer + 1].g_attn,
+      launch_rmsnorm_rows<P>(c.stream, Pn, c.px, c.layers[layer + 1].g_attn,
                          f.rms_eps, c.pu, d, host_act_scale(c, s1), amax ? amax + s1 : nullptr,
                          deferred_split<P>(c, Pn, d, F, L.s_d, host_act_scale(c, s0 + 3)));
       if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1541,7 +1599,7 @@ static hipError_t batch_step_p(Ctx& c) {
     const LayerW& L = c.layers[layer];
     const int s0 = kSitesPerLayer * layer;
     if (layer == 0) {  // later layers' attention inputs are normed with the previous down's split sum
-      hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px, L.g_attn, f.rms_eps, c.pu,
+      launch_rmsnorm_rows<P>(c.stream, M, c.px, L.g_attn, f.rms_eps, c.pu,
                          d, host_act_scale(c, s0), nullptr, none);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1552,13 +1610,13 @@ static hipError_t batch_step_p(Ctx& c) {
     {
       const SplitIn sq = defer_q ? deferred_split<P>(c, M, W, d, L.s_qkv, host_act_scale(c, s0)) : none;
       if (hd == 128)
-        hipLaunchKernelGGL(k_qk_rope_rows<128>, dim3(M), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
-                           c.rope_sin, c.pq, c.k_base[layer], c.v_base[layer], &c.state_base->len, Hq, Hkv,
-                           f.max_seq, f.rms_eps, len_stride, kvs, sq);
+        launch_qk_rope_rows<128>(c.stream, M, c.pqkv, L.g_q, L.g_k, c.rope_cos, c.rope_sin, c.pq, c.k_base[layer],
+                                 c.v_base[layer], &c.state_base->len, Hq, Hkv, f.max_seq, f.rms_eps, len_stride, kvs,
+                                 sq);
       else
-        hipLaunchKernelGGL(k_qk_rope_rows<64>, dim3(M), dim3(256), 0, c.stream, c.pqkv, L.g_q, L.g_k, c.rope_cos,
-                           c.rope_sin, c.pq, c.k_base[layer], c.v_base[layer], &c.state_base->len, Hq, Hkv,
-                           f.max_seq, f.rms_eps, len_stride, kvs, sq);
+        launch_qk_rope_rows<64>(c.stream, M, c.pqkv, L.g_q, L.g_k, c.rope_cos, c.rope_sin, c.pq, c.k_base[layer],
+                                c.v_base[layer], &c.state_base->len, Hq, Hkv, f.max_seq, f.rms_eps, len_stride, kvs,
+                                sq);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (hd == 128)
@@ -1578,7 +1636,7 @@ static hipError_t batch_step_p(Ctx& c) {
     if ((e = gemm<P>(c, c.po, L.w_o, L.s_o, host_act_scale(c, s0 + 1), c.px, M, d, qd, 1, nullptr, 1.0f, nullptr,
                      true)) != hipSuccess)
       return e;
-    hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px, L.g_mlp, f.rms_eps, c.pu, d,
+    launch_rmsnorm_rows<P>(c.stream, M, c.px, L.g_mlp, f.rms_eps, c.pu, d,
                        host_act_scale(c, s0 + 2), nullptr, deferred_split<P>(c, M, d, qd, L.s_o, host_act_scale(c, s0 + 1)));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = gemm<P>(c, c.pu, L.w_gu, L.s_gu, host_act_scale(c, s0 + 2), c.pgu, M, 2 * F, d, 0, c.pa,
@@ -1590,7 +1648,7 @@ static hipError_t batch_step_p(Ctx& c) {
     // the down projection's split sum feeds the next layer's attention norm, or the final norm
     const bool last = layer + 1 == f.n_layers;
     const int s1 = last ? kSitesPerLayer * f.n_layers : s0 + kSitesPerLayer;
-    hipLaunchKernelGGL((k_rmsnorm_act_rows<P>), dim3(M), dim3(256), 0, c.stream, c.px,
+    launch_rmsnorm_rows<P>(c.stream, M, c.px,
                        last ? c.g_final : c.layers[layer + 1].g_attn, f.rms_eps, c.pu, d, host_act_scale(c, s1), nullptr,
                        deferred_split<P>(c, M, d, F, L.s_d, host_act_scale(c, s0 + 3)));
     if ((e = hipGetLastError()) != hipSuccess) return e;
