@@ -1510,27 +1510,51 @@ __global__ __launch_bounds__(256) void k_attn_rows(const float* __restrict__ Q, 
 // Log-sum-exp combine of the splits (those holding keys), then the attention output in
 // GEMM units (bf16 bits, or e4m3 codes at the site's static scale): one block per
 // (query head, stream), one thread per output dimension.
-template <int P, int HD>
+// SM >= S, the step's split count (every split's partial is loaded before the first is
+// used; the clamped indices past S are loaded but not used).
+template <int P, int HD, int SM>
 __global__ __launch_bounds__(HD) void k_attn_combine(const float* __restrict__ part, int S, int Hq,
                                                       void* __restrict__ O, float scale) {
   const int h = blockIdx.x, m = blockIdx.y, dd = threadIdx.x;
   const float* pp = part + ((size_t)m * Hq + h) * S * (HD + 2);
+  float mv[SM], lv[SM], ov[SM];
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    const float* ps = pp + (size_t)min(s, S - 1) * (HD + 2);
+    mv[s] = ps[HD];
+    lv[s] = ps[HD + 1];
+    ov[s] = ps[dd];
+  }
   float mx = -INFINITY;
-  for (int s = 0; s < S; ++s)
-    if (pp[s * (HD + 2) + HD + 1] > 0.0f) mx = fmaxf(mx, pp[s * (HD + 2) + HD]);
+#pragma unroll
+  for (int s = 0; s < SM; ++s)
+    if (s < S && lv[s] > 0.0f) mx = fmaxf(mx, mv[s]);
   float num = 0.0f, den = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const float l = pp[s * (HD + 2) + HD + 1];
-    if (l > 0.0f) {
-      const float f = __expf(pp[s * (HD + 2) + HD] - mx);
-      num = fmaf(f, pp[s * (HD + 2) + dd], num);
-      den = fmaf(f, l, den);
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    if (s < S && lv[s] > 0.0f) {
+      const float f = __expf(mv[s] - mx);
+      num = fmaf(f, ov[s], num);
+      den = fmaf(f, lv[s], den);
     }
   }
   const float v = num / den;
   const size_t idx = ((size_t)m * Hq + h) * HD + dd;
   if (P == kBF16) static_cast<uint16_t*>(O)[idx] = (uint16_t)act_encode<P>(v, scale);
   else static_cast<uint8_t*>(O)[idx] = (uint8_t)act_encode<P>(v, scale);
+}
+
+// k_attn_combine with the split bound rounded up to 1, 2, 4, 8 or 16 (the step's S <= 16).
+template <int P, int HD>
+static void launch_attn_combine(hipStream_t st, int Hq, int M, const float* part, int S, void* O, float scale) {
+#define HTA_COMB(SM) \
+  hipLaunchKernelGGL((k_attn_combine<P, HD, SM>), dim3(Hq, M), dim3(HD), 0, st, part, S, Hq, O, scale)
+  if (S <= 1) HTA_COMB(1);
+  else if (S <= 2) HTA_COMB(2);
+  else if (S <= 4) HTA_COMB(4);
+  else if (S <= 8) HTA_COMB(8);
+  else HTA_COMB(16);
+#undef HTA_COMB
 }
 
 // Each stream's codes of the step: per codebook the greedy argmax over the allowed ids
@@ -1626,12 +1650,9 @@ static hipError_t batch_step_p(Ctx& c) {
       hipLaunchKernelGGL(k_attn_rows<64>, dim3(S, Hkv, M), dim3(64 * G), 0, c.stream, c.pq, c.k_base[layer],
                          c.v_base[layer], kvs, c.state_base, Hq, Hkv, f.max_seq, c.b_part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (hd == 128)
-      hipLaunchKernelGGL((k_attn_combine<P, 128>), dim3(Hq, M), dim3(128), 0, c.stream, c.b_part, S, Hq, c.po,
-                         host_act_scale(c, s0 + 1));
-    else
-      hipLaunchKernelGGL((k_attn_combine<P, 64>), dim3(Hq, M), dim3(64), 0, c.stream, c.b_part, S, Hq, c.po,
-                         host_act_scale(c, s0 + 1));
+    if (S > 16) return hipErrorInvalidValue;  // the combine's split bound
+    if (hd == 128) launch_attn_combine<P, 128>(c.stream, Hq, M, c.b_part, S, c.po, host_act_scale(c, s0 + 1));
+    else launch_attn_combine<P, 64>(c.stream, Hq, M, c.b_part, S, c.po, host_act_scale(c, s0 + 1));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = gemm<P>(c, c.po, L.w_o, L.s_o, host_act_scale(c, s0 + 1), c.px, M, d, qd, 1, nullptr, 1.0f, nullptr,
                      true)) != hipSuccess)
