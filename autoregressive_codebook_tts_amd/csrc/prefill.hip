@@ -612,8 +612,23 @@ __global__ __launch_bounds__(64 * G) void k_rope_attn_small(
   const int W = (Hq + 2 * Hkv) * HD;
   const bool act = lane < H2;
   const int la = act ? lane : 0;
-  // every operand of this wave's rows, loaded before any is used: the query head's two
-  // elements per row, the key head's and the value head's of this wave's key rows
+  // every operand of this wave's rows, loaded before any is used: the rotations of the
+  // query rows and of this wave's key rows (rows past the prompt repeat its last row),
+  // the query head's two elements per row, the key head's and the value head's of this
+  // wave's key rows
+  float rcq[QT], rsq[QT], rck[KR], rsk[KR];
+#pragma unroll
+  for (int i = 0; i < QT; ++i) {
+    const size_t rp = (size_t)(len0 + min(i, n_rows - 1)) * H2 + la;
+    rcq[i] = rope_cos[rp];
+    rsq[i] = rope_sin[rp];
+  }
+#pragma unroll
+  for (int t = 0; t < KR; ++t) {
+    const size_t rp = (size_t)(len0 + min(w + G * t, n_rows - 1)) * H2 + la;
+    rck[t] = rope_cos[rp];
+    rsk[t] = rope_sin[rp];
+  }
   float xq[2 * QT], xk[2 * KR], xv[VE * KR];
   {
     long idx[2 * QT];
@@ -667,10 +682,9 @@ __global__ __launch_bounds__(64 * G) void k_rope_attn_small(
 #pragma unroll
   for (int i = 0; i < QT; ++i) {
     if (i >= n_rows) break;  // uniform
-    const int pos = len0 + i;
-    const float c_ = rope_cos[(size_t)pos * H2 + la], s_ = rope_sin[(size_t)pos * H2 + la];
     float a, b;
-    norm_rope_vals<HD>(act ? xq[2 * i] : 0.0f, act ? xq[2 * i + 1] : 0.0f, gq0, gq1, c_, s_, eps, lane, &a, &b);
+    norm_rope_vals<HD>(act ? xq[2 * i] : 0.0f, act ? xq[2 * i + 1] : 0.0f, gq0, gq1, rcq[i], rsq[i], eps, lane, &a,
+                       &b);
     if (act) {
       qs[(w * QT + i) * HD + lane] = a;
       qs[(w * QT + i) * HD + lane + H2] = b;
@@ -681,9 +695,9 @@ __global__ __launch_bounds__(64 * G) void k_rope_attn_small(
     const int r = w + G * t;
     if (r >= n_rows) break;  // uniform
     const int pos = len0 + r;
-    const float c_ = rope_cos[(size_t)pos * H2 + la], s_ = rope_sin[(size_t)pos * H2 + la];
     float a, b;
-    norm_rope_vals<HD>(act ? xk[2 * t] : 0.0f, act ? xk[2 * t + 1] : 0.0f, gk0, gk1, c_, s_, eps, lane, &a, &b);
+    norm_rope_vals<HD>(act ? xk[2 * t] : 0.0f, act ? xk[2 * t + 1] : 0.0f, gk0, gk1, rck[t], rsk[t], eps, lane, &a,
+                       &b);
     if (act) {
       kb[(size_t)pos * HD + lane] = (uint16_t)f32_to_bf16(a);
       kb[(size_t)pos * HD + lane + H2] = (uint16_t)f32_to_bf16(b);
