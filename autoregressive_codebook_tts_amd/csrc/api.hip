@@ -291,6 +291,10 @@ static void drop_graph(Ctx& c) {
   if (c.frame_graph) (void)hipGraphDestroy(c.frame_graph);
   c.frame_exec = nullptr;
   c.frame_graph = nullptr;
+  if (c.frame_exec8) (void)hipGraphExecDestroy(c.frame_exec8);
+  if (c.frame_graph8) (void)hipGraphDestroy(c.frame_graph8);
+  c.frame_exec8 = nullptr;
+  c.frame_graph8 = nullptr;
 }
 
 // Zero the persistent kernel's tagged exchange words and its launch counter / abort flag.
@@ -300,8 +304,17 @@ static hipError_t clear_exchange(Ctx& c) {
   return launch_fill_u32(c.ws + L.off_xh, 0u, n, c.stream);
 }
 
+// The frame graph (one launch of the frame kernel) and a graph of eight launches in a row:
+// consecutive frames replayed from one graph start a few microseconds sooner than
+// back-to-back replays of the one-launch graph (measured: about 5 us per frame).
 static int ensure_graph(Ctx& c) {
-  if (c.frame_exec) return HTA_OK;
+  if (c.frame_exec8) return HTA_OK;  // captured last: both graphs are there
+  if (c.frame_exec) {                 // a capture that failed half way: start again
+    (void)hipGraphExecDestroy(c.frame_exec);
+    if (c.frame_graph) (void)hipGraphDestroy(c.frame_graph);
+    c.frame_exec = nullptr;
+    c.frame_graph = nullptr;
+  }
   HIPCK(hipStreamBeginCapture(c.stream, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
   hipError_t e = launch_frame_persistent(c);
   hipGraph_t g = nullptr;
@@ -310,6 +323,14 @@ static int ensure_graph(Ctx& c) {
   if (e2 != hipSuccess) return hip_fail(c, e2, "hipStreamEndCapture");
   c.frame_graph = g;
   HIPCK(hipGraphInstantiate(&c.frame_exec, g, nullptr, nullptr, 0), "hipGraphInstantiate");
+  HIPCK(hipStreamBeginCapture(c.stream, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
+  for (int i = 0; i < 8 && e == hipSuccess; ++i) e = launch_frame_persistent(c);
+  g = nullptr;
+  e2 = hipStreamEndCapture(c.stream, &g);
+  if (e != hipSuccess) { if (g) (void)hipGraphDestroy(g); return hip_fail(c, e, "frame capture"); }
+  if (e2 != hipSuccess) return hip_fail(c, e2, "hipStreamEndCapture");
+  c.frame_graph8 = g;
+  HIPCK(hipGraphInstantiate(&c.frame_exec8, g, nullptr, nullptr, 0), "hipGraphInstantiate");
   return HTA_OK;
 }
 
@@ -648,7 +669,9 @@ static int decode_n(Ctx& c, int n, int32_t* codes_out, int* n_done_out, bool no_
     for (int i = 0; i < n; ++i) HIPCK(launch_frame_args(c, c.fargs_s), "frame");
   } else if (c.use_graph && !c.taps) {
     if ((r = ensure_graph(c)) != HTA_OK) return r;
-    for (int i = 0; i < n; ++i) HIPCK(hipGraphLaunch(c.frame_exec, c.stream), "hipGraphLaunch");
+    int i = 0;
+    for (; i + 8 <= n; i += 8) HIPCK(hipGraphLaunch(c.frame_exec8, c.stream), "hipGraphLaunch");
+    for (; i < n; ++i) HIPCK(hipGraphLaunch(c.frame_exec, c.stream), "hipGraphLaunch");
   } else {
     for (int i = 0; i < n; ++i) HIPCK(launch_frame_persistent(c), "frame");
   }

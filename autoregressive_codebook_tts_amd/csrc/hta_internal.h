@@ -83,6 +83,8 @@ struct Ctx {
   bool done = false;
   hipGraph_t frame_graph = nullptr;
   hipGraphExec_t frame_exec = nullptr;
+  hipGraph_t frame_graph8 = nullptr;   // eight frame launches in one graph (replayed for runs of 8)
+  hipGraphExec_t frame_exec8 = nullptr;
   DevState* h_state = nullptr;  // pinned host staging
   int32_t* h_stage = nullptr;   // pinned host staging for tokens / codes
   size_t h_stage_elems = 0;

@@ -303,8 +303,8 @@ enum { HTA_K_EMBED = 0, HTA_K_QKV = 1, HTA_K_ATTN = 2, HTA_K_O = 3, HTA_K_GATEUP
 int hta_time_kernels(hta_ctx* ctx, int n_frames, float* avg_us_out, int n_classes);
 
 /* Options: HTA_OPT_USE_GRAPH (default 1) replays the captured position-agnostic
- * frame graph; 0 launches the frame kernel directly (for tests that compare the
- * two).  Every frame is one launch of the persistent decode frame kernel (one
+ * frame graph (runs of eight frames replay a graph of eight launches); 0 launches the
+ * frame kernel directly (for tests that compare the two).  Every frame is one launch of the persistent decode frame kernel (one
  * resident block per compute unit; blocks hand values to each other through
  * phase-tagged words, no grid barrier; a wait that runs out ends the frame with
  * HTA_E_TIMEOUT).  HTA_OPT_TAPS (default 0) makes decode frames and prefills also
