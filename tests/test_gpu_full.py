@@ -214,28 +214,54 @@ def test_full_decode_layers_reanchored(request, precision):
         ctx.set_option(hta.OPT_TAPS, 0)
 
 
-@pytest.mark.parametrize("precision", ["bf16", "fp8"])
-@pytest.mark.parametrize("P", [13, 128, 512])
-def test_full_prefill_layers_reanchored(request, precision, P):
-    ctx, oracle = _ctx_and_oracle(request, precision)
+def _prefill_reanchored(ctx, oracle, precision, P, what):
+    """Layers 0, 18 and 35 of a P-row prefill re-anchored on the oracle; returns the worst
+    (update rel, K rel, V rel) and the rows leaving the last layer."""
     ids = S.token_ids(S.SEEDS[f"prefill_{P}"], P, SH.text_vocab)
     ctx.set_option(hta.OPT_TAPS, 1)
     worst = [0.0, 0.0, 0.0]
+    last = None
     try:
         for layer in (0, SH.n_layers // 2, SH.n_layers - 1):
             ctx.set_option(hta.OPT_PREFILL_TAP_LAYER, layer)
             ctx.reset(0)
             ctx.prefill(ids)
             rows = ctx.tap_prefill_layer(P).astype(np.float64)
-            r = _check_layer(ctx, oracle, layer, rows[0], rows[1], np.arange(P), precision, f"{precision} prefill P={P}")
+            r = _check_layer(ctx, oracle, layer, rows[0], rows[1], np.arange(P), precision, what)
             worst = [max(a, b) for a, b in zip(worst, r)]
             if layer == SH.n_layers - 1:
                 assert np.array_equal(rows[1], ctx.tap_prefill_hidden(P).astype(np.float64))
+                last = rows[1]
     finally:
         ctx.set_option(hta.OPT_TAPS, 0)
         ctx.set_option(hta.OPT_PREFILL_TAP_LAYER, 0)
+    return worst, last
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp8"])
+@pytest.mark.parametrize("P", [13, 128, 512])
+def test_full_prefill_layers_reanchored(request, precision, P):
+    ctx, oracle = _ctx_and_oracle(request, precision)
+    worst, _ = _prefill_reanchored(ctx, oracle, precision, P, f"{precision} prefill P={P}")
     _say(f"[full] {precision} prefill P={P}: layers 0/18/35 re-anchored: worst update rel {worst[0]:.3e}, "
          f"K {worst[1]:.3e}, V {worst[2]:.3e}")
+
+
+@pytest.mark.parametrize("P", [13, 512])
+def test_full_prefill_fp8_mfma_option_reanchored(request, P):
+    """The opt-in e4m3 MFMA form of the prefill GEMMs: its sums carry fewer bits than fp32
+    (tests/test_gpu_gemm.py), yet each re-anchored layer stays within the FP8 layer
+    tolerance; the option is live (the last layer's rows differ from the default path's)."""
+    ctx, oracle = _ctx_and_oracle(request, "fp8")
+    _, base = _prefill_reanchored(ctx, oracle, "fp8", P, f"fp8 prefill P={P}")
+    ctx.set_option(hta.OPT_FP8_MFMA, 1)
+    try:
+        worst, rows = _prefill_reanchored(ctx, oracle, "fp8", P, f"fp8 e4m3-MFMA prefill P={P}")
+    finally:
+        ctx.set_option(hta.OPT_FP8_MFMA, 0)
+    assert not np.array_equal(rows, base)
+    _say(f"[full] fp8 e4m3-MFMA prefill P={P}: layers 0/18/35 re-anchored: worst update rel {worst[0]:.3e}, "
+         f"K {worst[1]:.3e}, V {worst[2]:.3e}; last layer vs default rel {rel_l2(rows, base):.3e}")
 
 
 # ----------------------------------------------------------------------------- end to end

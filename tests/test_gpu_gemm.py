@@ -150,6 +150,31 @@ def test_gemm_fp8_realistic_operands(ctxs, name, N, K):
     assert outside == 0
 
 
+@pytest.mark.parametrize("name,N,K", [SHAPES[1], SHAPES[2]])
+def test_gemm_bf16_realistic_operands(ctxs, name, N, K):
+    """BF16 context: N(0, 1) rows and N(0, 0.02) weights rounded to bf16; every output within
+    the fp32 bound of a K-term sum, and its bf16 rounding (the BF16 activation sites' format)
+    equal to the rounding of the exact value except within the site band."""
+    import torch
+    _say(f"[gemm] realistic bf16 {name} N={N} K={K}")
+    M = 100
+    a = nx.round_bf16(S.normal_vector(S.SEEDS["gemm_a"] + 2000 + K, (M, K)).astype(np.float64))
+    w = nx.round_bf16(0.02 * S.normal_vector(S.SEEDS["gemm_w"] + 2000 + N, (N, K)).astype(np.float64))
+    exact = a @ w.T
+    sabs = np.abs(a) @ np.abs(w).T
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ctxs["bf16"].gemm(_dev(_bf16_bits_of(a)), _dev(_bf16_bits_of(w)), None, 1.0, C)
+    c = C.cpu().numpy().astype(np.float64)
+    err = np.abs(c - exact)
+    _say(f"[gemm] bf16 {name}: max |C - exact| / sum|p| = {float((err / sabs).max()):.3e}")
+    assert np.all(err <= (K + 2) * 2.0 ** -24 * sabs)
+    idx, d_rel, d_rms = rounding_flips(nx.round_bf16(c.astype(np.float32).astype(np.float64)).ravel(),
+                                       nx.round_bf16(exact).ravel(), exact.ravel())
+    outside = int(np.count_nonzero((d_rel > SITE_BAND[0]) & (d_rms > SITE_BAND[1])))
+    _say(f"[gemm] bf16 {name}: bf16 roundings: {idx.size} flips, {outside} outside the band")
+    assert outside == 0
+
+
 def test_fp8_mfma_form_misses_fp32_accumulation(ctxs):
     """The opt-in e4m3 MFMA form: rows still independent of M, but the exact grid is missed
     and the site roundings flip outside the band (kept out of the FP8 path for that)."""
