@@ -199,18 +199,44 @@ __global__ __launch_bounds__(256) void k_silu_mul_rows(const float* __restrict__
 // q/k RMSNorm + RoPE for one row of heads; rotated values rounded to bf16.
 // (x0, x1: the lane's two elements of the head, lane < HD / 2; g0, g1 their gains;
 // c, s the rotation of the lane's pair)
+// round_bf16 written with selects instead of a branch (the same bits for every input,
+// NaN included), so that unrolled row loops stay straight-line code
+__device__ __forceinline__ float round_bf16_sel(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t q = (u >> 16) | 0x40u;
+  return bf16_to_f32(((u & 0x7fffffffu) > 0x7f800000u) ? q : r);
+}
+// The head row's sum of squares (the wave holds its two halves, x0 and x1, per lane).
+__device__ __forceinline__ float norm_ss(float x0, float x1) { return wave_sum(__builtin_fmaf(x0, x0, x1 * x1)); }
+// 1 / sqrt(ss / HD + eps) of the row.
 template <int HD>
-__device__ __forceinline__ void norm_rope_vals(float x0, float x1, float g0, float g1, float c_, float s_, float eps,
-                                               int lane, float* a_out, float* b_out) {
+__device__ __forceinline__ float rstd_of(float ss, float eps) { return 1.0f / sqrtf(ss / (float)HD + eps); }
+// rstd_of for N <= 64 rows at once: lane i evaluates row i's (the same operations on the
+// same value, so the same bits), and each row's result is read back from its lane.
+template <int HD, int N>
+__device__ __forceinline__ void rstd_rows(const float (&ss)[N], float eps, float (&rstd)[N]) {
+  static_assert(N <= 64, "one row per lane");
+  const int lane = threadIdx.x & 63;
+  float v = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v = lane == i ? ss[i] : v;
+  const float r = rstd_of<HD>(v, eps);
+#pragma unroll
+  for (int i = 0; i < N; ++i) rstd[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r), i));
+}
+template <int HD>
+__device__ __forceinline__ void rope_apply(float rstd, float x0, float x1, float g0, float g1, float c_, float s_,
+                                           int lane, float* a_out, float* b_out) {
   constexpr int H2 = HD / 2;
   const bool act = lane < H2;
-  const float ss = wave_sum(x0 * x0 + x1 * x1);
-  const float rstd = 1.0f / sqrtf(ss / (float)HD + eps);
   const float a = x0 * rstd * (act ? g0 : 0.0f);
   const float b = x1 * rstd * (act ? g1 : 0.0f);
   const float c = act ? c_ : 0.0f, s = act ? s_ : 0.0f;
-  *a_out = round_bf16(a * c - b * s);
-  *b_out = round_bf16(b * c + a * s);
+  // the fused forms are written out: left to contraction, the compiler picks the product
+  // to fuse per call site, and two kernels would round the same rotation differently
+  *a_out = round_bf16_sel(__builtin_fmaf(a, c, -(b * s)));
+  *b_out = round_bf16_sel(__builtin_fmaf(b, c, a * s));
 }
 
 // The q/k/v row comes from QKV, or, with a split input, is the split sum of the GEMM's
@@ -273,20 +299,25 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
   }
   const float gq0 = g_q[la], gq1 = g_q[la + H2], gk0 = g_k[la], gk1 = g_k[la + H2];
   const float c_ = cs[la], s_ = sn[la];
+  // every head's sum of squares first (independent reductions whose latency overlaps)
+  float ss[kHeadsPerWave], rstd[kHeadsPerWave];
+#pragma unroll
+  for (int t = 0; t < kHeadsPerWave; ++t) ss[t] = norm_ss(act ? x0[t] : 0.0f, act ? x1[t] : 0.0f);
+  rstd_rows<HD, kHeadsPerWave>(ss, eps, rstd);
 #pragma unroll
   for (int t = 0; t < kHeadsPerWave; ++t) {
     const int h = w + t * nw;
     if (h >= Hq + Hkv) break;
     float a, b;
     if (h < Hq) {
-      norm_rope_vals<HD>(act ? x0[t] : 0.0f, act ? x1[t] : 0.0f, gq0, gq1, c_, s_, eps, lane, &a, &b);
+      rope_apply<HD>(rstd[t], act ? x0[t] : 0.0f, act ? x1[t] : 0.0f, gq0, gq1, c_, s_, lane, &a, &b);
       if (lane < H2) {
         Q[(size_t)i * Hq * HD + (size_t)h * HD + lane] = a;
         Q[(size_t)i * Hq * HD + (size_t)h * HD + lane + H2] = b;
       }
     } else {
       const int j = h - Hq;
-      norm_rope_vals<HD>(act ? x0[t] : 0.0f, act ? x1[t] : 0.0f, gk0, gk1, c_, s_, eps, lane, &a, &b);
+      rope_apply<HD>(rstd[t], act ? x0[t] : 0.0f, act ? x1[t] : 0.0f, gk0, gk1, c_, s_, lane, &a, &b);
       if (lane < H2) {
         kc[((size_t)j * max_seq + pos) * HD + lane] = (uint16_t)f32_to_bf16(a);
         kc[((size_t)j * max_seq + pos) * HD + lane + H2] = (uint16_t)f32_to_bf16(b);
@@ -366,19 +397,26 @@ __device__ __forceinline__ uint32_t pack_bf16_trunc(float a, float b) {  // exac
 }
 
 // The attention of one block (kv head j, query rows i0 .. i0 + 15) once this lane's
-// A fragments `qa` of its query head are formed.
-template <int P, int HD, int G>
+// A fragments `qa` of its query head are formed.  CS = 1: the block's G waves are the
+// group's G query heads.  CS = G: the G waves share query head hg of the group, each
+// computes the scores and probabilities of the whole tile (the same values in every
+// wave) and P V and the output for its own HD / G output columns.
+template <int P, int HD, int G, int CS = 1>
 __device__ __forceinline__ void attn_prefill_block(const bf16x8 (&qa)[HD / 32], const uint16_t* __restrict__ kc,
                                                    const uint16_t* __restrict__ vc, void* __restrict__ O, int len0,
                                                    int i0, int j, int n_rows, int Hq, int max_seq, float scale,
-                                                   float* amax, PrefillAttnLds<HD>& sm, float* red) {
+                                                   float* amax, PrefillAttnLds<HD>& sm, float* red, int hg = 0) {
   constexpr int T = kAttnTile, QT = kAttnQT;
   constexpr int NT = HD / 16;   // 16-wide output column tiles
   static_assert(T == 64, "four 16-key blocks per tile");
-  constexpr int nthr = 64 * G;  // one wave per query head of the kv group
+  static_assert(CS == 1 || CS == G, "waves per head");
+  static_assert(NT % CS == 0, "column tiles per wave");
+  constexpr int NW = NT / CS;   // column tiles of this wave
+  constexpr int nthr = 64 * G;  // G waves
   constexpr int KC = HD / 32;   // 32-wide k chunks of a q row
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = j * G + w;
+  const int h = j * G + (CS == 1 ? w : hg);
+  const int nb = CS == 1 ? 0 : w * NW;  // first column tile of this wave
   const int r16 = lane & 15, g4 = lane >> 4;
   const int last_pos = len0 + min(i0 + QT, n_rows) - 1;
   const int n_tiles = last_pos / T + 1;
@@ -386,9 +424,9 @@ __device__ __forceinline__ void attn_prefill_block(const bf16x8 (&qa)[HD / 32], 
   const uint16_t* vb = vc + (size_t)j * max_seq * HD;
   const float inv_sqrt = 1.0f / sqrtf((float)HD);
   (void)KC;
-  f32x4 oacc[NT];
+  f32x4 oacc[NW];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NW; ++n) oacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[4], l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.0f; }
@@ -492,7 +530,7 @@ __device__ __forceinline__ void attn_prefill_block(const bf16x8 (&qa)[HD / 32], 
       m[i] = mnew[i];
     }
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+    for (int n = 0; n < NW; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[n][i] *= fs[i];
     // the wave reads back its probabilities in the other lane order: its LDS writes first
@@ -520,8 +558,8 @@ __device__ __forceinline__ void attn_prefill_block(const bf16x8 (&qa)[HD / 32], 
       const bf16x8 amid = __builtin_bit_cast(bf16x8, make_uint4(mid[0], mid[1], mid[2], mid[3]));
       const bf16x8 alo = __builtin_bit_cast(bf16x8, make_uint4(lo[0], lo[1], lo[2], lo[3]));
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const uint4 b = *reinterpret_cast<const uint4*>(&sm.V[n * 16 + r16][c2 * 32 + 8 * g4]);
+      for (int n = 0; n < NW; ++n) {
+        const uint4 b = *reinterpret_cast<const uint4*>(&sm.V[(nb + n) * 16 + r16][c2 * 32 + 8 * g4]);
         const bf16x8 bv = __builtin_bit_cast(bf16x8, b);
         oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bv, oacc[n], 0, 0, 0);
         oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(amid, bv, oacc[n], 0, 0, 0);
@@ -536,10 +574,10 @@ __device__ __forceinline__ void attn_prefill_block(const bf16x8 (&qa)[HD / 32], 
     if (qi >= n_rows) continue;
     const float inv = 1.0f / l[i];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
+    for (int n = 0; n < NW; ++n) {
       const float v = oacc[n][i] * inv;
       mx = fmaxf(mx, fabsf(v));
-      const size_t idx = ((size_t)qi * Hq + h) * HD + n * 16 + r16;
+      const size_t idx = ((size_t)qi * Hq + h) * HD + (nb + n) * 16 + r16;
       if (P == kBF16) static_cast<uint16_t*>(O)[idx] = (uint16_t)act_encode<P>(v, scale);
       else static_cast<uint8_t*>(O)[idx] = (uint8_t)act_encode<P>(v, scale);
     }
@@ -580,16 +618,19 @@ __global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict
   attn_prefill_block<P, HD, G>(qa, kc, vc, O, *len_at, i0, j, n_rows, Hq, max_seq, scale, amax, sm, red);
 }
 
-// Prompts of at most 16 rows (one query block): one block per kv head rotates its
-// group's query heads and its key head for every row (q/k RMSNorm + RoPE), writes the
-// rows' keys and values into the cache, and then runs the attention of the query block.
-// The rotation is norm_rope_vals on the split sums of k_qk_rope_rows and the attention is
-// attn_prefill_block, in the same order, so every value is bit-identical to the
-// two-kernel path of longer prompts.  The rotated queries stay in LDS (in the key/value
-// tile area, free until the attention's first tile).
-template <int HD, int G>
+// Prompts of at most 16 rows (one query block): one block per query head (grid: kv heads
+// x query heads per kv head).  The block's G waves take the prompt rows w, w + G, ...:
+// each rotates the block's query head and the group's key head for its rows (q/k RMSNorm
+// + RoPE) and writes their keys and values into the cache (the G blocks of a group store
+// the same bits into the same cache rows, and each reads back only rows it has stored
+// itself), then the waves share the attention of the query block through the column
+// split of attn_prefill_block.  The rotation is norm_ss, rstd_rows and rope_apply on the
+// split sums of k_qk_rope_rows and the attention is attn_prefill_block, in the same order,
+// so every value is bit-identical to the two-kernel path of longer prompts.  The rotated
+// queries stay in LDS (in the key tile area, free until the attention's first tile).
+template <int HD>
 constexpr bool rope_attn_small_fits() {
-  return (size_t)G * kAttnQT * HD * 4 <= sizeof(uint16_t) * kAttnTile * (HD + 8) + sizeof(uint16_t) * HD * (kAttnTile + 8);
+  return (size_t)kAttnQT * HD * 4 <= sizeof(uint16_t) * kAttnTile * (HD + 8);
 }
 // KS >= the split count of the q/k/v input (loads per thread bounded by it).
 template <int P, int HD, int G, int KS>
@@ -599,117 +640,92 @@ __global__ __launch_bounds__(64 * G) void k_rope_attn_small(
     uint16_t* __restrict__ vc, void* __restrict__ O, const int* __restrict__ len_at, int n_rows, int Hq, int Hkv,
     int max_seq, float eps, float scale, float* amax) {
   constexpr int H2 = HD / 2, QT = kAttnQT;
-  constexpr int KR = QT / G;     // key and value rows per wave: rows w, w + G, ...
+  constexpr int R = QT / G;      // prompt rows per wave: w, w + G, ...
   constexpr int VE = HD / 64;    // value elements per lane and row
-  static_assert(rope_attn_small_fits<HD, G>(), "rotated queries in the tile area");
+  constexpr int RU = 4 + VE;     // operands per row: the query pair, the key pair, the values
+  static_assert(rope_attn_small_fits<HD>(), "rotated queries in the key tile area");
   __shared__ PrefillAttnLds<HD> sm;
   __shared__ float red[16];
-  float* qs = reinterpret_cast<float*>(&sm.K[0][0]);  // [G][QT][HD]
-  const int j = blockIdx.x;
+  float* qs = reinterpret_cast<float*>(&sm.K[0][0]);  // [QT][HD]
+  const int j = blockIdx.x, hg = blockIdx.y;
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hq = j * G + w;
+  const int hq = j * G + hg;
   const int len0 = *len_at;
   const int W = (Hq + 2 * Hkv) * HD;
   const bool act = lane < H2;
   const int la = act ? lane : 0;
-  // every operand of this wave's rows, loaded before any is used: the rotations of the
-  // query rows and of this wave's key rows (rows past the prompt repeat its last row),
-  // the query head's two elements per row, the key head's and the value head's of this
-  // wave's key rows
-  float rcq[QT], rsq[QT], rck[KR], rsk[KR];
+  // every operand of this wave's rows (rows past the prompt repeat its last row), loaded
+  // before any is used: each row's rotation, the query head's and the key head's two
+  // elements and the value head's VE
+  float rc[R], rs[R];
 #pragma unroll
-  for (int i = 0; i < QT; ++i) {
-    const size_t rp = (size_t)(len0 + min(i, n_rows - 1)) * H2 + la;
-    rcq[i] = rope_cos[rp];
-    rsq[i] = rope_sin[rp];
-  }
-#pragma unroll
-  for (int t = 0; t < KR; ++t) {
+  for (int t = 0; t < R; ++t) {
     const size_t rp = (size_t)(len0 + min(w + G * t, n_rows - 1)) * H2 + la;
-    rck[t] = rope_cos[rp];
-    rsk[t] = rope_sin[rp];
+    rc[t] = rope_cos[rp];
+    rs[t] = rope_sin[rp];
   }
-  float xq[2 * QT], xk[2 * KR], xv[VE * KR];
+  float xs[R * RU];
   {
-    long idx[2 * QT];
-    int col[2 * QT];
+    long idx[R * RU];
+    int col[R * RU];
 #pragma unroll
-    for (int i = 0; i < QT; ++i) {
-      const long r = min(i, n_rows - 1);
-      col[2 * i] = hq * HD + la;
-      col[2 * i + 1] = hq * HD + la + H2;
-      idx[2 * i] = r * W + col[2 * i];
-      idx[2 * i + 1] = r * W + col[2 * i + 1];
-    }
-    if (si.part) {
-      split_sums<2 * QT, KS>(si, idx, col, xq);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 2 * QT; ++u) xq[u] = QKV[idx[u]];
-    }
-  }
-  {
-    long idx[2 * KR + VE * KR];
-    int col[2 * KR + VE * KR];
-#pragma unroll
-    for (int t = 0; t < KR; ++t) {
+    for (int t = 0; t < R; ++t) {
       const long r = min(w + G * t, n_rows - 1);
-      col[2 * t] = (Hq + j) * HD + la;
-      col[2 * t + 1] = (Hq + j) * HD + la + H2;
-      idx[2 * t] = r * W + col[2 * t];
-      idx[2 * t + 1] = r * W + col[2 * t + 1];
+      col[RU * t] = hq * HD + la;
+      col[RU * t + 1] = hq * HD + la + H2;
+      col[RU * t + 2] = (Hq + j) * HD + la;
+      col[RU * t + 3] = (Hq + j) * HD + la + H2;
 #pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        col[2 * KR + VE * t + e] = (Hq + Hkv + j) * HD + lane + 64 * e;
-        idx[2 * KR + VE * t + e] = r * W + col[2 * KR + VE * t + e];
-      }
+      for (int e = 0; e < VE; ++e) col[RU * t + 4 + e] = (Hq + Hkv + j) * HD + lane + 64 * e;
+#pragma unroll
+      for (int u = 0; u < RU; ++u) idx[RU * t + u] = r * W + col[RU * t + u];
     }
-    float xs[2 * KR + VE * KR];
     if (si.part) {
-      split_sums<2 * KR + VE * KR, KS>(si, idx, col, xs);
+      split_sums<R * RU, KS>(si, idx, col, xs);
     } else {
 #pragma unroll
-      for (int u = 0; u < 2 * KR + VE * KR; ++u) xs[u] = QKV[idx[u]];
+      for (int u = 0; u < R * RU; ++u) xs[u] = QKV[idx[u]];
     }
-#pragma unroll
-    for (int t = 0; t < 2 * KR; ++t) xk[t] = xs[t];
-#pragma unroll
-    for (int t = 0; t < VE * KR; ++t) xv[t] = xs[2 * KR + t];
   }
   const float gq0 = g_q[la], gq1 = g_q[la + H2], gk0 = g_k[la], gk1 = g_k[la + H2];
   uint16_t* kb = kc + (size_t)j * max_seq * HD;
   uint16_t* vb = vc + (size_t)j * max_seq * HD;
+  // every row's sum of squares first (independent reductions: their latency overlaps; a
+  // block has one wave per SIMD, nothing else hides it), the 1/rms of all rows in one pass
+  // over the lanes, then the rotations.  Rows past the prompt are computed and never
+  // stored, so that the row loop has no branch around its arithmetic.
+  float ss[2 * R], rstd[2 * R];
 #pragma unroll
-  for (int i = 0; i < QT; ++i) {
-    if (i >= n_rows) break;  // uniform
-    float a, b;
-    norm_rope_vals<HD>(act ? xq[2 * i] : 0.0f, act ? xq[2 * i + 1] : 0.0f, gq0, gq1, rcq[i], rsq[i], eps, lane, &a,
-                       &b);
-    if (act) {
-      qs[(w * QT + i) * HD + lane] = a;
-      qs[(w * QT + i) * HD + lane + H2] = b;
-    }
+  for (int t = 0; t < R; ++t) {
+    ss[t] = norm_ss(act ? xs[RU * t] : 0.0f, act ? xs[RU * t + 1] : 0.0f);
+    ss[R + t] = norm_ss(act ? xs[RU * t + 2] : 0.0f, act ? xs[RU * t + 3] : 0.0f);
   }
+  rstd_rows<HD, 2 * R>(ss, eps, rstd);
 #pragma unroll
-  for (int t = 0; t < KR; ++t) {
+  for (int t = 0; t < R; ++t) {
     const int r = w + G * t;
-    if (r >= n_rows) break;  // uniform
-    const int pos = len0 + r;
-    float a, b;
-    norm_rope_vals<HD>(act ? xk[2 * t] : 0.0f, act ? xk[2 * t + 1] : 0.0f, gk0, gk1, rck[t], rsk[t], eps, lane, &a,
-                       &b);
-    if (act) {
-      kb[(size_t)pos * HD + lane] = (uint16_t)f32_to_bf16(a);
-      kb[(size_t)pos * HD + lane + H2] = (uint16_t)f32_to_bf16(b);
-    }
+    float qa0, qb0, ka0, kb0;
+    rope_apply<HD>(rstd[t], act ? xs[RU * t] : 0.0f, act ? xs[RU * t + 1] : 0.0f, gq0, gq1, rc[t], rs[t], lane, &qa0,
+                   &qb0);
+    rope_apply<HD>(rstd[R + t], act ? xs[RU * t + 2] : 0.0f, act ? xs[RU * t + 3] : 0.0f, gk0, gk1, rc[t], rs[t], lane,
+                   &ka0, &kb0);
+    if (r < n_rows) {  // uniform
+      const int pos = len0 + r;
+      if (act) {
+        qs[r * HD + lane] = qa0;
+        qs[r * HD + lane + H2] = qb0;
+        kb[(size_t)pos * HD + lane] = (uint16_t)f32_to_bf16(ka0);
+        kb[(size_t)pos * HD + lane + H2] = (uint16_t)f32_to_bf16(kb0);
+      }
 #pragma unroll
-    for (int e = 0; e < VE; ++e) vb[(size_t)pos * HD + lane + 64 * e] = (uint16_t)f32_to_bf16(xv[VE * t + e]);
+      for (int e = 0; e < VE; ++e) vb[(size_t)pos * HD + lane + 64 * e] = (uint16_t)f32_to_bf16(xs[RU * t + 4 + e]);
+    }
   }
   __threadfence_block();  // the block's cache rows, before its tiles read them
   __syncthreads();
   bf16x8 qa[HD / 32];
-  q_fragments<HD>(qs + (size_t)w * QT * HD, HD, n_rows, 0, qa);
-  attn_prefill_block<P, HD, G>(qa, kc, vc, O, len0, 0, j, n_rows, Hq, max_seq, scale, amax, sm, red);
+  q_fragments<HD>(qs, HD, n_rows, 0, qa);
+  attn_prefill_block<P, HD, G, G>(qa, kc, vc, O, len0, 0, j, n_rows, Hq, max_seq, scale, amax, sm, red, hg);
 }
 
 // ============================================================================ MFMA GEMM, small M
@@ -1352,7 +1368,7 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
     if (Pn <= kAttnQT) {
       // one query block: rotation and attention in one launch per kv head
 #define HTA_RA2(HDV, GV, KSV)                                                                                \
-  hipLaunchKernelGGL((k_rope_attn_small<P, HDV, GV, KSV>), dim3(Hkv), dim3(64 * GV), 0, c.stream, c.pqkv, sq,     \
+  hipLaunchKernelGGL((k_rope_attn_small<P, HDV, GV, KSV>), dim3(Hkv, GV), dim3(64 * GV), 0, c.stream, c.pqkv, sq, \
                      L.g_q, L.g_k, c.rope_cos, c.rope_sin, L.k_cache, L.v_cache, c.po, len0, Pn, Hq, Hkv,         \
                      f.max_seq, f.rms_eps, so, am)
 #define HTA_RA(HDV, GV)                            \
