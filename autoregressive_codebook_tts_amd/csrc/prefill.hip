@@ -96,13 +96,29 @@ __device__ __forceinline__ void split_sums(const SplitIn& si, const long (&idx)[
   }
 }
 
+// block_sum for blocks of exactly NWV waves (the same additions in the same order,
+// without the loop over a run-time wave count).
+template <int NWV>
+__device__ __forceinline__ float block_sum_n(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) s += red[i];
+  return s;
+}
+
 // Row RMSNorm + rounding to the GEMV input format.  With a split input, the row is first
 // updated as residual += (the split sum of the GEMM that produced it), the work of
 // k_gemm_reduce, and the updated residual is stored and normalised.
-// RP row elements per thread (rows up to 256 * RP); KS bounds the split count of the
-// input (0: no split input), so that no thread issues loads beyond its row and splits.
-template <int P, int RP, int KS>
-__global__ __launch_bounds__(256) void k_rmsnorm_act_rows(float* __restrict__ X, const float* __restrict__ g,
+// NT threads, RP row elements per thread (rows up to NT * RP); KS bounds the split count
+// of the input (0: no split input), so that no thread issues loads beyond its row and
+// splits.
+template <int P, int RP, int KS, int NT>
+__global__ __launch_bounds__(NT) void k_rmsnorm_act_rows(float* __restrict__ X, const float* __restrict__ g,
                                                           float eps, void* __restrict__ U, int d, float scale,
                                                           float* amax, SplitIn si) {
   __shared__ float red[16];
@@ -111,7 +127,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_act_rows(float* __restrict__ X,
   float xv[RP], gv[RP];
 #pragma unroll
   for (int u = 0; u < RP; ++u) {
-    const int k = u * 256 + threadIdx.x, kc = min(k, d - 1);
+    const int k = u * NT + threadIdx.x, kc = min(k, d - 1);
     xv[u] = x[kc];
     gv[u] = g[kc];
   }
@@ -121,32 +137,47 @@ __global__ __launch_bounds__(256) void k_rmsnorm_act_rows(float* __restrict__ X,
     int col[RP];
 #pragma unroll
     for (int u = 0; u < RP; ++u) {
-      col[u] = min(u * 256 + (int)threadIdx.x, d - 1);
+      col[u] = min(u * NT + (int)threadIdx.x, d - 1);
       idx[u] = (long)i * d + col[u];
     }
     split_sums<RP, (KS > 0 ? KS : 1)>(si, idx, col, sv);
 #pragma unroll
     for (int u = 0; u < RP; ++u) {
-      const int k = u * 256 + threadIdx.x;
+      const int k = u * NT + threadIdx.x;
       xv[u] += sv[u];
       if (k < d) x[k] = xv[u];
     }
   }
-  float ss = 0.0f;  // over k = tid, tid + 256, ... in increasing order
+  float ss = 0.0f;  // over k = tid, tid + NT, ... in increasing order
 #pragma unroll
   for (int u = 0; u < RP; ++u)
-    if (u * 256 + threadIdx.x < d) ss = fmaf(xv[u], xv[u], ss);
-  ss = block_sum(ss, red);
+    if (u * NT + threadIdx.x < d) ss = fmaf(xv[u], xv[u], ss);
+  ss = block_sum_n<NT / 64>(ss, red);
   const float rstd = 1.0f / sqrtf(ss / (float)d + eps);
-  float mx = 0.0f;
+  // every element's value and code first (elements past the row are clamped copies,
+  // computed and never stored), so that the per-element divisions of the e4m3 rounding
+  // overlap instead of running one branch at a time
+  float v[RP];
+  uint32_t code[RP];
 #pragma unroll
   for (int u = 0; u < RP; ++u) {
-    const int k = u * 256 + threadIdx.x;
-    if (k >= d) continue;
-    const float v = xv[u] * rstd * gv[u];
-    mx = fmaxf(mx, fabsf(v));
-    if (P == kBF16) static_cast<uint16_t*>(U)[(size_t)i * d + k] = (uint16_t)act_encode<P>(v, scale);
-    else static_cast<uint8_t*>(U)[(size_t)i * d + k] = (uint8_t)act_encode<P>(v, scale);
+    v[u] = xv[u] * rstd * gv[u];
+    code[u] = act_encode<P>(v[u], scale);
+  }
+  float mx = 0.0f;
+  auto put = [&](int u) {
+    const int k = u * NT + threadIdx.x;
+    mx = fmaxf(mx, fabsf(v[u]));
+    if (P == kBF16) static_cast<uint16_t*>(U)[(size_t)i * d + k] = (uint16_t)code[u];
+    else static_cast<uint8_t*>(U)[(size_t)i * d + k] = (uint8_t)code[u];
+  };
+  if (d == RP * NT) {  // uniform: every element lies in the row, no store is predicated
+#pragma unroll
+    for (int u = 0; u < RP; ++u) put(u);
+  } else {
+#pragma unroll
+    for (int u = 0; u < RP; ++u)
+      if (u * NT + (int)threadIdx.x < d) put(u);
   }
   if (amax) {
     mx = block_max(mx, red);
@@ -159,19 +190,23 @@ __global__ __launch_bounds__(256) void k_rmsnorm_act_rows(float* __restrict__ X,
 template <int P>
 static void launch_rmsnorm_rows(hipStream_t st, int rows, float* X, const float* g, float eps, void* U, int d,
                                 float scale, float* amax, const SplitIn& si) {
-#define HTA_NORM(RP, KS) \
-  hipLaunchKernelGGL((k_rmsnorm_act_rows<P, RP, KS>), dim3(rows), dim3(256), 0, st, X, g, eps, U, d, scale, amax, si)
+// 512 threads (two waves per SIMD, so that each wave's dependent chains are half as long
+// and the other wave covers them); the shape depends on d only, so every caller sums a
+// row in the same order.
+#define HTA_NORM(RP, KS)                                                                                      \
+  hipLaunchKernelGGL((k_rmsnorm_act_rows<P, RP, KS, 512>), dim3(rows), dim3(512), 0, st, X, g, eps, U, d, scale, \
+                     amax, si)
   const int ks = si.part ? si.ks : 0;
-  if (d <= 10 * 256) {
+  if (d <= 5 * 512) {
+    if (ks == 0) HTA_NORM(5, 0);
+    else if (ks <= 2) HTA_NORM(5, 2);
+    else if (ks <= 5) HTA_NORM(5, 5);
+    else HTA_NORM(5, 8);
+  } else {
     if (ks == 0) HTA_NORM(10, 0);
     else if (ks <= 2) HTA_NORM(10, 2);
     else if (ks <= 5) HTA_NORM(10, 5);
     else HTA_NORM(10, 8);
-  } else {
-    if (ks == 0) HTA_NORM(20, 0);
-    else if (ks <= 2) HTA_NORM(20, 2);
-    else if (ks <= 5) HTA_NORM(20, 5);
-    else HTA_NORM(20, 8);
   }
 #undef HTA_NORM
 }
