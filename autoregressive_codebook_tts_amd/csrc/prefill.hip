@@ -277,12 +277,12 @@ __device__ __forceinline__ void rope_apply(float rstd, float x0, float x1, float
 // The q/k/v row comes from QKV, or, with a split input, is the split sum of the GEMM's
 // partials (the work of k_gemm_reduce, element by element in the same order; at most
 // kRopeMaxSplit splits, so that every partial of a thread is loaded in one batch).
-// HPW heads per wave (Hq + Hkv <= 4 HPW), VPER value elements per thread (Hkv HD <= 256
-// VPER) and KS >= the split count (0: no split input), so that no thread issues loads
-// beyond its heads and splits.
+// NT threads, HPW heads per wave (Hq + Hkv <= NT / 64 HPW), VPER value elements per
+// thread (Hkv HD <= NT VPER) and KS >= the split count (0: no split input), so that no
+// thread issues loads beyond its heads and splits.
 constexpr int kRopeMaxSplit = 4;
-template <int HD, int HPW, int VPER, int KS>
-__global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ QKV, const float* __restrict__ g_q,
+template <int HD, int HPW, int VPER, int KS, int NT>
+__global__ __launch_bounds__(NT) void k_qk_rope_rows(const float* __restrict__ QKV, const float* __restrict__ g_q,
                                                       const float* __restrict__ g_k, const float* __restrict__ rope_cos,
                                                       const float* __restrict__ rope_sin, float* __restrict__ Q,
                                                       uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int* __restrict__ len_at,
@@ -296,7 +296,8 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
   const int pos = len_stride ? len_at[(long)i * len_stride] : *len_at + i;
   kc += (long)i * kv_stride;
   vc += (long)i * kv_stride;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  constexpr int nw = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int W = (Hq + 2 * Hkv) * HD;
   const float* row = QKV + (size_t)i * W;
   const float* cs = rope_cos + (size_t)pos * H2;
@@ -366,43 +367,45 @@ __global__ __launch_bounds__(256) void k_qk_rope_rows(const float* __restrict__ 
     int col[kVPer];
 #pragma unroll
     for (int u = 0; u < kVPer; ++u) {
-      col[u] = (Hq + Hkv) * HD + min(u * 256 + (int)threadIdx.x, Hkv * HD - 1);
+      col[u] = (Hq + Hkv) * HD + min(u * NT + (int)threadIdx.x, Hkv * HD - 1);
       idx[u] = (long)i * W + col[u];
     }
     split_sums<kVPer, (KS > 0 ? KS : 1)>(si, idx, col, vv);
   } else {
 #pragma unroll
-    for (int u = 0; u < kVPer; ++u) vv[u] = row[(size_t)(Hq + Hkv) * HD + min(u * 256 + (int)threadIdx.x, Hkv * HD - 1)];
+    for (int u = 0; u < kVPer; ++u) vv[u] = row[(size_t)(Hq + Hkv) * HD + min(u * NT + (int)threadIdx.x, Hkv * HD - 1)];
   }
 #pragma unroll
   for (int u = 0; u < kVPer; ++u) {
-    const int e = u * 256 + threadIdx.x;
+    const int e = u * NT + threadIdx.x;
     if (e >= Hkv * HD) break;
     const int j = e / HD, dd = e % HD;
     vc[((size_t)j * max_seq + pos) * HD + dd] = (uint16_t)f32_to_bf16(vv[u]);
   }
 }
 
-// k_qk_rope_rows over `rows` rows with the narrowest instantiation: 10 heads per wave and
-// 4 value elements per thread where the head counts allow (Hq + Hkv <= 40, Hkv HD <=
-// 1024), else 16 and 8; split bound 2 or 4.
+// k_qk_rope_rows over `rows` rows with the narrowest instantiation, 512 threads (two
+// waves per SIMD, each with half the heads): 5 heads per wave and 2 value elements per
+// thread where the head counts allow (Hq + Hkv <= 40, Hkv HD <= 1024), else 8 and 4;
+// split bound 2 or 4.
 template <int HD>
 static void launch_qk_rope_rows(hipStream_t st, int rows, const float* QKV, const float* g_q, const float* g_k,
                                 const float* rope_cos, const float* rope_sin, float* Q, uint16_t* kc, uint16_t* vc,
                                 const int* len_at, int Hq, int Hkv, int max_seq, float eps, int len_stride,
                                 long kv_stride, const SplitIn& si) {
 #define HTA_ROPE(HPW, VPER, KS)                                                                                  \
-  hipLaunchKernelGGL((k_qk_rope_rows<HD, HPW, VPER, KS>), dim3(rows), dim3(256), 0, st, QKV, g_q, g_k, rope_cos, \
+  hipLaunchKernelGGL((k_qk_rope_rows<HD, HPW, VPER, KS, 512>), dim3(rows), dim3(512), 0, st, QKV, g_q, g_k,      \
+                     rope_cos, \
                      rope_sin, Q, kc, vc, len_at, Hq, Hkv, max_seq, eps, len_stride, kv_stride, si)
   const int ks = si.part ? si.ks : 0;
   if (Hq + Hkv <= 40 && Hkv * HD <= 1024) {
-    if (ks == 0) HTA_ROPE(10, 4, 0);
-    else if (ks <= 2) HTA_ROPE(10, 4, 2);
-    else HTA_ROPE(10, 4, 4);
+    if (ks == 0) HTA_ROPE(5, 2, 0);
+    else if (ks <= 2) HTA_ROPE(5, 2, 2);
+    else HTA_ROPE(5, 2, 4);
   } else {
-    if (ks == 0) HTA_ROPE(16, 8, 0);
-    else if (ks <= 2) HTA_ROPE(16, 8, 2);
-    else HTA_ROPE(16, 8, 4);
+    if (ks == 0) HTA_ROPE(8, 4, 0);
+    else if (ks <= 2) HTA_ROPE(8, 4, 2);
+    else HTA_ROPE(8, 4, 4);
   }
 #undef HTA_ROPE
 }
