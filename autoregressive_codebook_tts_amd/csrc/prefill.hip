@@ -423,38 +423,58 @@ static void launch_qk_rope_rows(hipStream_t st, int rows, const float* QKV, cons
 // .. + 8; the B operand column is lane & 15 with the same k; the result holds rows
 // 4 (lane >> 4) + i, column lane & 15.
 constexpr int kAttnQT = 16;
-template <int HD>
+template <int HD, int NWV = 4>
 struct __align__(16) PrefillAttnLds {
   uint16_t K[kAttnTile][HD + 8];   // [key][dim] (rows padded against bank conflicts)
   uint16_t V[HD][kAttnTile + 8];   // [dim][key], transposed for the P V operand
-  float Pm[4][kAttnQT][kAttnTile + 4];  // per wave: the tile's probabilities, [row][key]
+  float Pm[NWV][kAttnQT][kAttnTile + 4];  // per wave: the tile's probabilities, [row][key]
 };
+
+// All-reduce over each 16-lane row with DPP (no LDS round trips): the row mirror, the
+// half-row mirror, then quad swaps by 2 and by 1.  Every step pairs each lane with a
+// lane whose value has the same summation tree, so all 16 lanes end with the same bits.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_src<0x140, 0xf>(v, 0.0f);  // row_mirror
+  v += dpp_src<0x141, 0xf>(v, 0.0f);  // row_half_mirror
+  v += dpp_src<0x4e, 0xf>(v, 0.0f);   // quad_perm [2, 3, 0, 1]
+  v += dpp_src<0xb1, 0xf>(v, 0.0f);   // quad_perm [1, 0, 3, 2]
+  return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_src<0x140, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_src<0x141, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_src<0x4e, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_src<0xb1, 0xf>(v, -INFINITY));
+  return v;
+}
 
 __device__ __forceinline__ uint32_t pack_bf16_trunc(float a, float b) {  // exact for bf16 values
   return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
 }
 
 // The attention of one block (kv head j, query rows i0 .. i0 + 15) once this lane's
-// A fragments `qa` of its query head are formed.  CS = 1: the block's G waves are the
-// group's G query heads.  CS = G: the G waves share query head hg of the group, each
-// computes the scores and probabilities of the whole tile (the same values in every
-// wave) and P V and the output for its own HD / G output columns.
-template <int P, int HD, int G, int CS = 1>
+// A fragments `qa` of its query head are formed.  The block's HB * CW waves: HB = G
+// query heads of the group (wave w on head w / CW) or HB = 1 (head hg of the group), CW
+// waves per head.  The CW waves of a head each compute the scores and probabilities of
+// the whole tile (the same values in every such wave) and P V and the output for their
+// own HD / CW output columns; a column's arithmetic is the same whichever wave takes it.
+template <int P, int HD, int G, int HB = G, int CW = 1>
 __device__ __forceinline__ void attn_prefill_block(const bf16x8 (&qa)[HD / 32], const uint16_t* __restrict__ kc,
                                                    const uint16_t* __restrict__ vc, void* __restrict__ O, int len0,
                                                    int i0, int j, int n_rows, int Hq, int max_seq, float scale,
-                                                   float* amax, PrefillAttnLds<HD>& sm, float* red, int hg = 0) {
+                                                   float* amax, PrefillAttnLds<HD, HB * CW>& sm, float* red,
+                                                   int hg = 0) {
   constexpr int T = kAttnTile, QT = kAttnQT;
   constexpr int NT = HD / 16;   // 16-wide output column tiles
   static_assert(T == 64, "four 16-key blocks per tile");
-  static_assert(CS == 1 || CS == G, "waves per head");
-  static_assert(NT % CS == 0, "column tiles per wave");
-  constexpr int NW = NT / CS;   // column tiles of this wave
-  constexpr int nthr = 64 * G;  // G waves
+  static_assert(HB == G || HB == 1, "heads per block");
+  static_assert(NT % CW == 0, "column tiles per wave");
+  constexpr int NW = NT / CW;   // column tiles of this wave
+  constexpr int nthr = 64 * HB * CW;
   constexpr int KC = HD / 32;   // 32-wide k chunks of a q row
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = j * G + (CS == 1 ? w : hg);
-  const int nb = CS == 1 ? 0 : w * NW;  // first column tile of this wave
+  const int h = j * G + (HB == 1 ? hg : w / CW);
+  const int nb = (w % CW) * NW;  // first column tile of this wave
   const int r16 = lane & 15, g4 = lane >> 4;
   const int last_pos = len0 + min(i0 + QT, n_rows) - 1;
   const int n_tiles = last_pos / T + 1;
@@ -549,8 +569,7 @@ __device__ __forceinline__ void attn_prefill_block(const bf16x8 (&qa)[HD / 32], 
         sc[kb4][i] = v;
         tmax = fmaxf(tmax, v);
       }
-#pragma unroll
-      for (int o2 = 8; o2 > 0; o2 >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o2, 16));
+      tmax = row16_max(tmax);
       mnew[i] = fmaxf(m[i], tmax);
       float ps = 0.0f;
 #pragma unroll
@@ -560,8 +579,7 @@ __device__ __forceinline__ void attn_prefill_block(const bf16x8 (&qa)[HD / 32], 
         sm.Pm[w][row][kb4 * 16 + r16] = p;
         ps += p;
       }
-#pragma unroll
-      for (int o2 = 8; o2 > 0; o2 >>= 1) ps += __shfl_xor(ps, o2, 16);
+      ps = row16_sum(ps);
       psum[i] = ps;
       fs[i] = (m[i] == -INFINITY) ? 0.0f : __expf(m[i] - mnew[i]);
       l[i] = l[i] * fs[i] + psum[i];
@@ -642,18 +660,20 @@ __device__ __forceinline__ void q_fragments(const float* q0, int rs, int n_rows,
   }
 }
 
-template <int P, int HD, int G>
-__global__ __launch_bounds__(64 * G) void k_attn_prefill(const float* __restrict__ Q, const uint16_t* __restrict__ kc,
-                                                      const uint16_t* __restrict__ vc, void* __restrict__ O,
-                                                      const int* __restrict__ len_at, int n_rows, int Hq, int Hkv,
-                                                      int max_seq, float scale, float* amax) {
-  __shared__ PrefillAttnLds<HD> sm;
+// CW waves per query head (each with HD / CW output columns).
+template <int P, int HD, int G, int CW>
+__global__ __launch_bounds__(64 * G * CW) void k_attn_prefill(const float* __restrict__ Q,
+                                                           const uint16_t* __restrict__ kc,
+                                                           const uint16_t* __restrict__ vc, void* __restrict__ O,
+                                                           const int* __restrict__ len_at, int n_rows, int Hq,
+                                                           int Hkv, int max_seq, float scale, float* amax) {
+  __shared__ PrefillAttnLds<HD, G * CW> sm;
   __shared__ float red[16];
   const int j = blockIdx.x, i0 = blockIdx.y * kAttnQT;
-  const int h = j * G + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = j * G + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / CW;
   bf16x8 qa[HD / 32];
   q_fragments<HD>(Q + (size_t)h * HD, Hq * HD, n_rows, i0, qa);
-  attn_prefill_block<P, HD, G>(qa, kc, vc, O, *len_at, i0, j, n_rows, Hq, max_seq, scale, amax, sm, red);
+  attn_prefill_block<P, HD, G, G, CW>(qa, kc, vc, O, *len_at, i0, j, n_rows, Hq, max_seq, scale, amax, sm, red);
 }
 
 // Prompts of at most 16 rows (one query block): one block per query head (grid: kv heads
@@ -682,7 +702,7 @@ __global__ __launch_bounds__(64 * G) void k_rope_attn_small(
   constexpr int VE = HD / 64;    // value elements per lane and row
   constexpr int RU = 4 + VE;     // operands per row: the query pair, the key pair, the values
   static_assert(rope_attn_small_fits<HD>(), "rotated queries in the key tile area");
-  __shared__ PrefillAttnLds<HD> sm;
+  __shared__ PrefillAttnLds<HD, G> sm;
   __shared__ float red[16];
   float* qs = reinterpret_cast<float*>(&sm.K[0][0]);  // [QT][HD]
   const int j = blockIdx.x, hg = blockIdx.y;
@@ -763,7 +783,7 @@ __global__ __launch_bounds__(64 * G) void k_rope_attn_small(
   __syncthreads();
   bf16x8 qa[HD / 32];
   q_fragments<HD>(qs, HD, n_rows, 0, qa);
-  attn_prefill_block<P, HD, G, G>(qa, kc, vc, O, len0, 0, j, n_rows, Hq, max_seq, scale, amax, sm, red, hg);
+  attn_prefill_block<P, HD, G, 1, G>(qa, kc, vc, O, len0, 0, j, n_rows, Hq, max_seq, scale, amax, sm, red, hg);
 }
 
 // ============================================================================ MFMA GEMM, small M
@@ -830,8 +850,9 @@ __device__ __forceinline__ float epi_silu(const GemmEpi& e, int N, int row, int 
 template <int P>
 __device__ __forceinline__ float epi_silu_tile(const GemmEpi& e, int N, int M, int row0, int pair, bool odd,
                                                const float (&v)[4]) {
-  const float s1 = __shfl_xor(odd ? v[0] : v[2], 1, kWave);  // even: up of row0; odd: gate of row0 + 2
-  const float s2 = __shfl_xor(odd ? v[1] : v[3], 1, kWave);  // even: up of row0 + 1; odd: gate of row0 + 3
+  // the neighbouring lane's values by a DPP quad swap (lane ^ 1), no LDS round trip
+  const float s1 = dpp_src<0xb1, 0xf>(odd ? v[0] : v[2], 0.0f);  // even: up of row0; odd: gate of row0 + 2
+  const float s2 = dpp_src<0xb1, 0xf>(odd ? v[1] : v[3], 0.0f);  // even: up of row0 + 1; odd: gate of row0 + 3
   const int ra = row0 + (odd ? 2 : 0);
   float mx = 0.0f;
   if (ra < M) mx = epi_silu<P>(e, N, ra, pair, odd ? s1 : v[0], odd ? v[2] : s1);
@@ -1433,9 +1454,11 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
                                 L.v_cache, len0, Hq, Hkv, f.max_seq, f.rms_eps, 0, 0L, sq);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       dim3 grid(Hkv, (Pn + kAttnQT - 1) / kAttnQT);
-#define HTA_ATTN(HDV, GV)                                                                                        \
-  hipLaunchKernelGGL((k_attn_prefill<P, HDV, GV>), grid, dim3(64 * GV), 0, c.stream, c.pq, L.k_cache, L.v_cache, c.po, \
-                     len0, Pn, Hq, Hkv, f.max_seq, so, am)
+// one wave per query head: two (each with half the output columns, the scores and
+// probabilities computed by both) made the kernel 15 % slower at P = 512
+#define HTA_ATTN(HDV, GV)                                                                                         \
+  hipLaunchKernelGGL((k_attn_prefill<P, HDV, GV, 1>), grid, dim3(64 * GV), 0, c.stream, c.pq, L.k_cache, L.v_cache, \
+                     c.po, len0, Pn, Hq, Hkv, f.max_seq, so, am)
       if (hd == 128 && G == 4) HTA_ATTN(128, 4);
       else if (hd == 128 && G == 2) HTA_ATTN(128, 2);
       else if (hd == 128 && G == 1) HTA_ATTN(128, 1);
