@@ -45,6 +45,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+// The same roundings written with selects instead of a branch (the same bits for every
+// input, NaN included), for straight-line code on latency-bound paths.
+__device__ __forceinline__ uint32_t f32_to_bf16_sel(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r;
+}
+__device__ __forceinline__ float round_bf16_sel(float f) { return bf16_to_f32(f32_to_bf16_sel(f)); }
 
 // ---------------------------------------------------------------- OCP e4m3fn
 // The hardware convert rounds to nearest even but turns |x| > 464 into NaN, so

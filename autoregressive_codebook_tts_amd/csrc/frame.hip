@@ -346,8 +346,12 @@ __device__ __forceinline__ float row_sum(float* part, int row, const float4& zer
 // ---------------------------------------------------------------- phase inputs into LDS (bf16 pairs)
 template <int P>
 __device__ __forceinline__ uint32_t act_bits(float v, float scale) {
-  // value in GEMV units (bf16-rounded value, or the e4m3 code value), as bf16 bits (exact)
-  return f32_to_bf16(act_round<P>(v, scale));
+  // value in GEMV units (bf16-rounded value, or the e4m3 code value), as bf16 bits (exact).
+  // An e4m3 code value has at most four significant bits, so its bf16 bits are the upper
+  // half of its fp32 bits (the clamp in f32_to_e4m3 leaves no NaN); a bf16 value needs
+  // one rounding of v (rounding it again changes no bit).  Both without a branch.
+  if (P == kFP8) return __float_as_uint(act_round<P>(v, scale)) >> 16;
+  return f32_to_bf16_sel(v);
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -505,14 +509,30 @@ __device__ __forceinline__ bool norm_to_lds_n(const uint64_t* xh, unsigned tag, 
   seen[1] = (uint32_t)__builtin_amdgcn_s_memrealtime();
   const float rstd = 1.0f / sqrtf(ss / (float)K + eps);
   uint16_t* xs16 = reinterpret_cast<uint16_t*>(xs);
-  float mx = 0.0f;
+  // every element's value and code first (elements past K are clamped copies with a zero
+  // gain, computed and never stored), so that the per-element divisions overlap
+  float u[kMaxPer];
+  uint32_t code[kMaxPer];
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i) {
-    const int k = i * kFT + threadIdx.x;
-    const float u = __uint_as_float((uint32_t)wv[i]) * rstd * gv[i];
-    if (k < K) {
-      xs16[k] = (uint16_t)act_bits<P>(u, scale);
-      mx = fmaxf(mx, fabsf(u));
+    u[i] = __uint_as_float((uint32_t)wv[i]) * rstd * gv[i];
+    code[i] = act_bits<P>(u[i], scale);
+  }
+  float mx = 0.0f;
+  if (K == kMaxPer * kFT) {  // uniform: every element lies in the row, no store is predicated
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      xs16[i * kFT + threadIdx.x] = (uint16_t)code[i];
+      mx = fmaxf(mx, fabsf(u[i]));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int k = i * kFT + threadIdx.x;
+      if (k < K) {
+        xs16[k] = (uint16_t)code[i];
+        mx = fmaxf(mx, fabsf(u[i]));
+      }
     }
   }
   if (rec != nullptr) {  // calibration: the site's maximum before rounding (uniform branch)
@@ -635,8 +655,8 @@ __device__ __forceinline__ void attn_norm_rope(const uint64_t* src, unsigned tag
   if (act) {
     const float a = x0 * rstd * g0;
     const float b = x1 * rstd * g1;
-    dst[lane] = round_bf16(a * c - b * s);
-    dst[lane + H2] = round_bf16(b * c + a * s);
+    dst[lane] = round_bf16_sel(a * c - b * s);
+    dst[lane + H2] = round_bf16_sel(b * c + a * s);
   }
 }
 

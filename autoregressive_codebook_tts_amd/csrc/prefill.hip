@@ -234,14 +234,6 @@ __global__ __launch_bounds__(256) void k_silu_mul_rows(const float* __restrict__
 // q/k RMSNorm + RoPE for one row of heads; rotated values rounded to bf16.
 // (x0, x1: the lane's two elements of the head, lane < HD / 2; g0, g1 their gains;
 // c, s the rotation of the lane's pair)
-// round_bf16 written with selects instead of a branch (the same bits for every input,
-// NaN included), so that unrolled row loops stay straight-line code
-__device__ __forceinline__ float round_bf16_sel(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t q = (u >> 16) | 0x40u;
-  return bf16_to_f32(((u & 0x7fffffffu) > 0x7f800000u) ? q : r);
-}
 // The head row's sum of squares (the wave holds its two halves, x0 and x1, per lane).
 __device__ __forceinline__ float norm_ss(float x0, float x1) { return wave_sum(__builtin_fmaf(x0, x0, x1 * x1)); }
 // 1 / sqrt(ss / HD + eps) of the row.
