@@ -1417,7 +1417,7 @@ static hipError_t prefill_p(Ctx& c, int Pn, bool record) {
     const float so = host_act_scale(c, s0 + 1);
     float* am = amax ? amax + s0 + 1 : nullptr;
     if (Pn <= kAttnQT) {
-      // one query block: rotation and attention in one launch per kv head
+      // one query block: rotation and attention in one launch, one block per query head
 #define HTA_RA2(HDV, GV, KSV)                                                                                \
   hipLaunchKernelGGL((k_rope_attn_small<P, HDV, GV, KSV>), dim3(Hkv, GV), dim3(64 * GV), 0, c.stream, c.pqkv, sq, \
                      L.g_q, L.g_k, c.rope_cos, c.rope_sin, L.k_cache, L.v_cache, c.po, len0, Pn, Hq, Hkv,         \
