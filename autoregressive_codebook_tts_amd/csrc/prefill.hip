@@ -861,7 +861,7 @@ struct Skinny {
   static constexpr int NU = SK / 16;                   // 16-byte units per row and stage
   static constexpr int U = NU / 4;                     // units per lane per 16-row fragment
   static constexpr int BYTES_B = 16 * NW * SK, BYTES_A = 16 * R * SK, STAGE = BYTES_B + BYTES_A;
-  static constexpr int NS = ((NW == 4 ? 80 : 52) * 1024) / STAGE;  // NW = 4: bf16 4 (R = 1), 3 (R = 2); e4m3 8, 6
+  static constexpr int NS = ((NW >= 3 ? 80 : 52) * 1024) / STAGE;  // NW = 4: bf16 4 (R = 1), 3 (R = 2); e4m3 8, 6
   static constexpr int NB = NU / 4;                    // B fetches per wave and stage
   static constexpr int NA_ALL = R * NU / 4;            // A fetches per stage
   static constexpr int AW = NA_ALL >= NW ? NW : NA_ALL;  // waves that fetch A
@@ -878,7 +878,12 @@ template <int P, int R, int NW>
 size_t skinny_lds_bytes() { return (size_t)Skinny<P, R, NW>::NS * Skinny<P, R, NW>::STAGE; }
 
 // F8M (e4m3 only): the e4m3 MFMA, one instruction per 128-element step and 16-row fragment.
-template <int P, int R, int NW, bool F8M = false>
+// Columns: the NW 16-column tiles from blockIdx.y * 16 NW, or (BAL, the bf16 form for up
+// to 16 rows) a balanced contiguous run of the N / 16 tiles dealt over the gridDim.y
+// blocks of each K split, at most NW tiles a block.  A wave beyond its block's tiles issues no load and computes
+// nothing; it is never one of the AW waves that fetch A (the host deals at least AW tiles
+// to every block), so every wave's ring waits count exactly the loads it issued.
+template <int P, int R, int NW, bool F8M = false, bool BAL = false>
 __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, const void* __restrict__ B,
                                                   float* __restrict__ Cpart, int M, int N, int K, int ksplit,
                                                   GemmEpi epi) {
@@ -886,7 +891,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, co
   static_assert(!F8M || (P == kFP8 && S::U == 2), "the e4m3 MFMA takes a 128-byte step as two units per lane");
   extern __shared__ __align__(16) unsigned char gsm[];
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int m0 = blockIdx.x * 16 * R, n0 = blockIdx.y * 16 * NW, ks = blockIdx.z;
+  const int m0 = blockIdx.x * 16 * R, ks = blockIdx.z;
+  int n0 = blockIdx.y * 16 * NW, nt = NW;
+  if constexpr (BAL) {
+    const int ntl = N / 16, nb = gridDim.y;
+    const int t0 = (int)((long)blockIdx.y * ntl / nb), t1 = (int)((long)(blockIdx.y + 1) * ntl / nb);
+    n0 = 16 * t0;
+    nt = t1 - t0;
+  }
+  const bool on = !BAL || w < nt;  // wave-uniform (always true in the fixed form)
   const int rowbytes = K * S::EB;  // operands below 2^31 bytes
   const int nsteps = K / 128;
   const int s_beg = (int)((long)nsteps * ks / ksplit), s_end = (int)((long)nsteps * (ks + 1) / ksplit);
@@ -911,12 +924,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, co
     const uint32_t sb = lds0 + (uint32_t)(c % S::NS) * S::STAGE;
     const unsigned char* a = Ab + (size_t)(s_beg + c) * S::SK;
     const unsigned char* b = Bb + (size_t)(s_beg + c) * S::SK;
+    if (on) {
 #pragma unroll
-    for (int j = 0; j < S::NB; ++j) {
-      const uint32_t mb = __builtin_amdgcn_readfirstlane(sb + (uint32_t)(w * S::NB + j) * 1024u);
-      // weight rows, read once per call: non-temporal, past the caches
-      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-                   : : "v"(voffB[j]), "s"(b), "s"(mb) : "memory", "m0");
+      for (int j = 0; j < S::NB; ++j) {
+        const uint32_t mb = __builtin_amdgcn_readfirstlane(sb + (uint32_t)(w * S::NB + j) * 1024u);
+        // weight rows, read once per call: non-temporal, past the caches
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                     : : "v"(voffB[j]), "s"(b), "s"(mb) : "memory", "m0");
+      }
     }
     if (fetch_a) {
 #pragma unroll
@@ -957,6 +972,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, co
     __syncthreads();  // every wave's part of stage c is in, and stage c - 1 is consumed
     if (c + S::NS - 1 < nst) issue(c + S::NS - 1);
     const unsigned char* st = gsm + (c % S::NS) * S::STAGE;
+    if (!on) continue;  // wave-uniform: an idle wave only takes part in the barriers
     uint4 bv[S::U], av[R][S::U];
 #pragma unroll
     for (int q = 0; q < S::U; ++q) {
@@ -999,7 +1015,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, co
     // the whole K range is here: the epilogue works from the registers (0 + acc, as the
     // split sum starts from zero)
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+    for (int r = 0; r < R && on; ++r) {
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1021,6 +1037,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const void* __restrict__ A, co
     // last-arriving block adding the splits here would put three memory round trips on
     // the kernel's tail, more than the reduce's launch)
     float* Cp = Cpart + (size_t)ks * M * N;
+    if (!on) return;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -1315,6 +1332,26 @@ static void gemm_launch(Ctx& c, const void* A, const void* B, float* part, int M
       const long blocks = (long)mt * (N / width) * ks;
       return (blocks + cus - 1) / cus * width;  // columns x splits on the busiest CU
     };
+    const long classic = std::min(max_cols(32), max_cols(64));
+    // Balanced form (bf16, up to 16 rows): one block per CU and K split, each with a
+    // contiguous run of 4 or 5 of the N / 16 column tiles (run lengths differ by at most
+    // one), taken where it lowers the busiest CU's columns and every block gets at least
+    // the tiles of its waves that fetch A.  (e4m3 measured slower in this form: two or
+    // three resident two-wave blocks per CU keep more of its weight stream in flight.)
+    if constexpr (P == kBF16) {
+      if (R == 1) {
+        const int ntl = N / 16;
+        int nb = (int)(cus / ks);
+        if (nb > ntl) nb = ntl;
+        const int tmax = nb > 0 ? (ntl + nb - 1) / nb : 0, tmin = nb > 0 ? ntl / nb : 0;
+        if (nb > 0 && 16L * tmax < classic && tmax == 5 && tmin >= Skinny<P, 1, 5>::AW) {
+          const dim3 grid(1, nb, ks);
+          hipLaunchKernelGGL((k_gemm<P, 1, 5, F8M, true>), grid, dim3(320), (skinny_lds_bytes<P, 1, 5>()), c.stream,
+                             A, B, part, M, N, K, ks, epi);
+          return;
+        }
+      }
+    }
     const bool narrow = max_cols(32) < max_cols(64);
     if (!narrow) {
       dim3 grid(mt, N / 64, ks);
@@ -1786,6 +1823,7 @@ hipError_t prefill_setup() {
       {(const void*)k_gemm<kBF16, 2, 2>, skinny_lds_bytes<kBF16, 2, 2>()},
       {(const void*)k_gemm<kFP8, 1, 2>, skinny_lds_bytes<kFP8, 1, 2>()},
       {(const void*)k_gemm<kFP8, 2, 2>, skinny_lds_bytes<kFP8, 2, 2>()},
+      {(const void*)k_gemm<kBF16, 1, 5, false, true>, skinny_lds_bytes<kBF16, 1, 5>()},
       {(const void*)k_gemm_tile<kFP8, 64, 64, 4, true>, gemm_tile_lds_bytes<64, 64, 4>()},
       {(const void*)k_gemm_tile<kFP8, 128, 128, 3, true>, gemm_tile_lds_bytes<128, 128, 3>()},
       {(const void*)k_gemm<kFP8, 1, 4, true>, skinny_lds_bytes<kFP8, 1, 4>()},
