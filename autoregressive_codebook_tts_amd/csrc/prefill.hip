@@ -861,7 +861,10 @@ struct Skinny {
   static constexpr int NU = SK / 16;                   // 16-byte units per row and stage
   static constexpr int U = NU / 4;                     // units per lane per 16-row fragment
   static constexpr int BYTES_B = 16 * NW * SK, BYTES_A = 16 * R * SK, STAGE = BYTES_B + BYTES_A;
-  static constexpr int NS = ((NW >= 3 ? 80 : 52) * 1024) / STAGE;  // NW = 4: bf16 4 (R = 1), 3 (R = 2); e4m3 8, 6
+  // ring stages in 80 KB for four- and five-wave blocks (one per CU), 52 KB for two-wave
+  // blocks (three per CU).  NW = 4: bf16 4 (R = 1), 3 (R = 2), e4m3 8, 6; NW = 5 (bf16,
+  // R = 1): 3
+  static constexpr int NS = ((NW >= 3 ? 80 : 52) * 1024) / STAGE;
   static constexpr int NB = NU / 4;                    // B fetches per wave and stage
   static constexpr int NA_ALL = R * NU / 4;            // A fetches per stage
   static constexpr int AW = NA_ALL >= NW ? NW : NA_ALL;  // waves that fetch A
